@@ -1,0 +1,189 @@
+"""CPU oracle for the batch-1 decode GEMV (y = W . x) and its quantised forms.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers.  The GPU library never
+imports or loads anything from here, and nothing here imports the library.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64 sums of exactly decoded
+fp16 values, exact int64 sums for int8; see that file for the passages of
+the pages each function follows).  This module only marshals numpy arrays
+through ctypes and states the parity rule.
+
+Parity rule for floating point, per output element:
+    |y_hat - y| <= 1e-3 * A + 1e-6,   A = sum_k |w_k * x_k|
+and bit-exact equality for the int32 accumulators of the int8 path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+REL_TOL = 1e-3
+ABS_TOL = 1e-6
+
+ERR_NONFINITE = 1
+ERR_SHAPE = 2
+ERR_RANGE = 3
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(out_path: str = _LIB_PATH, defines: Sequence[str] = ()) -> str:
+    """Compile oracle.c with gcc (no fused multiply-add, no fast-math)."""
+    tmp = out_path + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c99",
+           "-Wall", "-shared", "-fPIC", *[f"-D{d}" for d in defines], _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.orc_f16_decode.argtypes = [P, I64, P]
+    lib.orc_gemv_f16.argtypes = [P, P, I64, I64, P, P]
+    lib.orc_gemv_w8a8.argtypes = [P, P, P, ctypes.c_float, I64, I64, P, P, P]
+    lib.orc_gemv_w4a16.argtypes = [P, P, P, I64, I64, I64, I64, P, P]
+    for f in (lib.orc_f16_decode, lib.orc_gemv_f16, lib.orc_gemv_w8a8, lib.orc_gemv_w4a16):
+        f.restype = ctypes.c_int
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_threads.restype = None
+    lib.orc_max_threads.argtypes = []
+    lib.orc_max_threads.restype = ctypes.c_int
+    return lib
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the compiled oracle, building it first only if it is absent."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise OracleError(f"{what}: oracle status {code}")
+
+
+def set_threads(n: int, lib: Optional[ctypes.CDLL] = None) -> None:
+    (lib or load()).orc_set_threads(int(n))
+
+
+def max_threads(lib: Optional[ctypes.CDLL] = None) -> int:
+    return int((lib or load()).orc_max_threads())
+
+
+def f16_decode(h: np.ndarray, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Exact fp16 -> float64 from the bit pattern (uint16 or float16 input)."""
+    bits = np.ascontiguousarray(np.asarray(h).view(np.uint16) if np.asarray(h).dtype == np.float16
+                                else np.asarray(h, dtype=np.uint16))
+    out = np.empty(bits.shape, dtype=np.float64)
+    _check((lib or load()).orc_f16_decode(_ptr(bits), bits.size, _ptr(out)), "f16_decode")
+    return out
+
+
+def _u16(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected float16 or uint16 bit patterns, got {a.dtype}")
+    return a
+
+
+def gemv_f16(W: np.ndarray, x: np.ndarray, lib: Optional[ctypes.CDLL] = None
+             ) -> Tuple[np.ndarray, np.ndarray]:
+    """(y, A) for y = W . x with W fp16 [N, K] and x fp16 [K]."""
+    W = _u16(W)
+    x = _u16(x)
+    N, K = W.shape
+    if x.shape != (K,):
+        raise ValueError("x must have shape (K,)")
+    y = np.empty(N, np.float64)
+    A = np.empty(N, np.float64)
+    _check((lib or load()).orc_gemv_f16(_ptr(W), _ptr(x), N, K, _ptr(y), _ptr(A)), "gemv_f16")
+    return y, A
+
+
+def gemv_w8a8(Wq: np.ndarray, w_scale: np.ndarray, xq: np.ndarray, x_scale: float,
+              lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(acc int32, y float64, A) for the int8 weight x int8 activation product."""
+    Wq = np.ascontiguousarray(Wq, dtype=np.int8)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    w_scale = np.ascontiguousarray(w_scale, dtype=np.float32)
+    N, K = Wq.shape
+    if xq.shape != (K,) or w_scale.shape != (N,):
+        raise ValueError("shape mismatch")
+    acc = np.empty(N, np.int32)
+    y = np.empty(N, np.float64)
+    A = np.empty(N, np.float64)
+    _check((lib or load()).orc_gemv_w8a8(_ptr(Wq), _ptr(w_scale), _ptr(xq), float(np.float32(x_scale)),
+                                         N, K, _ptr(acc), _ptr(y), _ptr(A)), "gemv_w8a8")
+    return acc, y, A
+
+
+def gemv_w4a16(Wc: np.ndarray, s4: np.ndarray, X: np.ndarray, group: int = 128,
+               lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """(Y, A) for canonical int4 words Wc uint32 [N, K/8], fp16 scales
+    s4 [N, K/group] and fp16 activations X [M, K] (or [K] for M = 1)."""
+    Wc = np.ascontiguousarray(Wc, dtype=np.uint32)
+    s4 = _u16(s4)
+    X = _u16(X)
+    squeeze = X.ndim == 1
+    if squeeze:
+        X = X.reshape(1, -1)
+    M, K = X.shape
+    N = Wc.shape[0]
+    if Wc.shape != (N, K // 8) or s4.shape != (N, K // group):
+        raise ValueError("shape mismatch")
+    Y = np.empty((M, N), np.float64)
+    A = np.empty((M, N), np.float64)
+    _check((lib or load()).orc_gemv_w4a16(_ptr(Wc), _ptr(s4), _ptr(X), M, N, K, group,
+                                          _ptr(Y), _ptr(A)), "gemv_w4a16")
+    if squeeze:
+        return Y[0], A[0]
+    return Y, A
+
+
+def decode_step_f16(linears: Iterable[Tuple[np.ndarray, np.ndarray]],
+                    lib: Optional[ctypes.CDLL] = None) -> List[Tuple[np.ndarray, np.ndarray]]:
+    """The decode step is the per-linear product on each (W, x) pair."""
+    return [gemv_f16(W, x, lib) for W, x in linears]
+
+
+def bound(A: np.ndarray) -> np.ndarray:
+    return REL_TOL * np.asarray(A, np.float64) + ABS_TOL
+
+
+def max_err_ratio(y_hat: np.ndarray, y: np.ndarray, A: np.ndarray) -> float:
+    """max over elements of |y_hat - y| / (1e-3 A + 1e-6); parity iff <= 1."""
+    err = np.abs(np.asarray(y_hat, np.float64) - np.asarray(y, np.float64))
+    r = err / bound(A)
+    if r.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(r)):
+        return float("inf")
+    return float(r.max())

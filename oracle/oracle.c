@@ -1,0 +1,200 @@
+/*
+ * CPU oracle for the batch-1 decode matrix-vector product y = W . x.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * definition that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it.  It shares
+ * no code, header, table or helper with the GPU library, and the library
+ * never loads it.
+ *
+ * What it computes (the pages describe the operation, not a formula):
+ *  - MiniCPM-V 4.6 on Orange Pi AIPro (Ascend 310B) post, baseline paragraph:
+ *    at decode M = 1, so every linear layer is a vector-matrix product; the
+ *    closing paragraph says each step reads the FP16 weights once and is bound
+ *    by memory bandwidth.  Here W is [N, K] row-major, x is [K], and
+ *    y[n] = sum_k W[n,k] * x[k].
+ *  - Same post, second change: the wide lm_head is cut into slices whose
+ *    results are reduced.  A split of the k-sum changes only the summation
+ *    order, so the oracle is the unsplit definition.
+ *  - Same post, closing paragraph, and the vLLM Arm CPU optimisation post,
+ *    "INT8 W8A8" and "INT8 W4A8" sections: 8-bit and 4-bit weights whose
+ *    dequantisation is fused into the product.  The oracle dequantises
+ *    explicitly, element by element, and forms the same sum.
+ *  - EdgeFM summary, section 2C (speculative decoding): a verify block is M
+ *    rows checked against the same W; each output row is the M = 1 product of
+ *    its own activation row.
+ *
+ * Arithmetic: every fp16 value is decoded from its bit pattern to an exact
+ * double; products of two fp16 values (at most 22 significant bits) and of a
+ * 4-bit integer with an fp16 scale are exact in double; sums are taken in
+ * increasing k in double.  The int8 product is summed exactly in int64.
+ * Rows are independent, so the OpenMP split over rows leaves every result
+ * bit-identical at any thread count.  Build: gcc -O2 -fopenmp
+ * -ffp-contract=off (no fused multiply-add, no fast-math).
+ *
+ * Status codes: 0 ok, 1 an fp16 input is Inf or NaN, 2 bad shape,
+ * 3 an int8 accumulator leaves the int32 range.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <omp.h>
+
+#define ORC_OK 0
+#define ORC_ERR_NONFINITE 1
+#define ORC_ERR_SHAPE 2
+#define ORC_ERR_RANGE 3
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Exponent field 0 encodes the subnormals m * 2^-24; fields 1..30
+ * encode (1024 + m) * 2^(e - 25); field 31 is Inf/NaN and is rejected. */
+static int f16_value(uint16_t h, double *out)
+{
+    unsigned sign = h >> 15;
+    unsigned e = (h >> 10) & 31u;
+    unsigned m = h & 1023u;
+    double v;
+    if (e == 31u)
+        return ORC_ERR_NONFINITE;
+    if (e == 0u)
+        v = ldexp((double)m, -24);
+    else
+        v = ldexp((double)(1024u + m), (int)e - 25);
+    *out = sign ? -v : v;
+    return ORC_OK;
+}
+
+static void note_error(int *shared, int code)
+{
+    if (code != ORC_OK) {
+#pragma omp atomic write
+        *shared = code;
+    }
+}
+
+int orc_f16_decode(const uint16_t *h, int64_t n, double *out)
+{
+    int err = ORC_OK;
+    for (int64_t i = 0; i < n; ++i) {
+        int e = f16_value(h[i], &out[i]);
+        if (e != ORC_OK)
+            err = e;
+    }
+    return err;
+}
+
+/* y[n] = sum_k W[n,k] x[k];  A[n] = sum_k |W[n,k] x[k]| (for the tolerance). */
+int orc_gemv_f16(const uint16_t *W, const uint16_t *x, int64_t N, int64_t K,
+                 double *y, double *A)
+{
+    if (N < 0 || K < 0)
+        return ORC_ERR_SHAPE;
+    int err = ORC_OK;
+    double *xd = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    if (!xd)
+        return ORC_ERR_SHAPE;
+    note_error(&err, orc_f16_decode(x, K, xd));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint16_t *row = W + n * K;
+        double s = 0.0, a = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double w;
+            int e = f16_value(row[k], &w);
+            if (e != ORC_OK)
+                note_error(&err, e);
+            double p = w * xd[k];
+            s += p;
+            a += fabs(p);
+        }
+        y[n] = s;
+        if (A)
+            A[n] = a;
+    }
+    free(xd);
+    return err;
+}
+
+/* acc[n] = sum_k Wq[n,k] xq[k] exactly (int64, must fit int32);
+ * y[n] = acc[n] * w_scale[n] * x_scale in double;
+ * A[n] = w_scale[n] * x_scale * sum_k |Wq[n,k] xq[k]|. */
+int orc_gemv_w8a8(const int8_t *Wq, const float *w_scale, const int8_t *xq,
+                  float x_scale, int64_t N, int64_t K,
+                  int32_t *acc, double *y, double *A)
+{
+    if (N < 0 || K < 0)
+        return ORC_ERR_SHAPE;
+    int err = ORC_OK;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const int8_t *row = Wq + n * K;
+        int64_t s = 0, a = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t p = (int64_t)row[k] * (int64_t)xq[k];
+            s += p;
+            a += p < 0 ? -p : p;
+        }
+        if (s > INT32_MAX || s < INT32_MIN)
+            note_error(&err, ORC_ERR_RANGE);
+        double scale = (double)w_scale[n] * (double)x_scale;
+        if (acc)
+            acc[n] = (int32_t)s;
+        y[n] = (double)s * scale;
+        if (A)
+            A[n] = (double)a * fabs(scale);
+    }
+    return err;
+}
+
+/* Canonical int4 layout: element k of row n is the 4-bit field at bits
+ * [4*(k%8), 4*(k%8)+3] of word Wc[n, k/8]; its value is q - 8 with q in 0..15
+ * (zero-point 8), times the fp16 scale s4[n, k/group].
+ * Y[m,n] = sum_k (q[n,k] - 8) * s4[n,k/group] * X[m,k];  A the matching sum
+ * of magnitudes. */
+int orc_gemv_w4a16(const uint32_t *Wc, const uint16_t *s4, const uint16_t *X,
+                   int64_t M, int64_t N, int64_t K, int64_t group,
+                   double *Y, double *A)
+{
+    if (M < 0 || N < 0 || K < 0 || group <= 0 || K % 8 || K % group)
+        return ORC_ERR_SHAPE;
+    int err = ORC_OK;
+    int64_t words = K / 8, groups = K / group;
+    double *xd = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    if (!xd)
+        return ORC_ERR_SHAPE;
+    note_error(&err, orc_f16_decode(X, M * K, xd));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double s = 0.0, a = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                uint32_t word = Wc[n * words + k / 8];
+                int q = (int)((word >> (4 * (k % 8))) & 15u);
+                double scale;
+                int e = f16_value(s4[n * groups + k / group], &scale);
+                if (e != ORC_OK)
+                    note_error(&err, e);
+                double w = (double)(q - 8) * scale;
+                double p = w * xd[m * K + k];
+                s += p;
+                a += fabs(p);
+            }
+            Y[m * N + n] = s;
+            if (A)
+                A[m * N + n] = a;
+        }
+    }
+    free(xd);
+    return err;
+}
+
+void orc_set_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+}
+
+int orc_max_threads(void)
+{
+    return omp_get_max_threads();
+}

@@ -1,0 +1,242 @@
+"""Pins of the CPU oracle to facts outside the oracle itself.
+
+Each ``pin_*`` function takes a loaded oracle library and raises
+AssertionError when the oracle disagrees with something the mathematics or a
+hand-derived fixture fixes: exact rational sums (Python ``fractions``),
+numpy's own fp16 conversion and float64 / int64 matrix products on an
+independent dequantisation, closed forms (identity, permutation, one-hot,
+powers of two), hand-packed int4 words and the exact int32 range boundary.
+They are plain functions so that the mutation test can run the same checks
+against deliberately broken copies of the oracle.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from weight_streaming_gemv_decode_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+U53 = 2.0 ** -53
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bits(a):
+    return np.array([[int(v, 16) for v in row] for row in a], dtype=np.uint16) if isinstance(a[0], list) \
+        else np.array([int(v, 16) for v in a], dtype=np.uint16)
+
+
+def _frac16(h: np.ndarray):
+    """Exact Fractions of fp16 values, via numpy's own conversion."""
+    return [Fraction(float(v)) for v in np.asarray(h, np.float16).astype(np.float64).ravel()]
+
+
+# ---------------------------------------------------------------- fp16 ---
+
+def pin_f16_decode_all_patterns(lib):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 10) & 31) != 31
+    got = oracle.f16_decode(bits[finite], lib=lib)
+    ref = bits[finite].view(np.float16).astype(np.float64)
+    assert np.array_equal(got.view(np.uint64), ref.view(np.uint64)), "fp16 decode differs from numpy"
+    for bad in (0x7C00, 0xFC00, 0x7E00, 0x7C01):
+        try:
+            oracle.f16_decode(np.array([bad], np.uint16), lib=lib)
+        except oracle.OracleError:
+            continue
+        raise AssertionError(f"Inf/NaN pattern {bad:#06x} not rejected")
+
+
+def pin_f16_golden(lib):
+    g = _golden("f16_tiny.json")
+    W, x = _bits(g["W_bits"]), _bits(g["x_bits"])
+    y, A = oracle.gemv_f16(W, x, lib=lib)
+    assert np.array_equal(y, np.array(g["y"])), (y, g["y"])
+    assert np.array_equal(A, np.array(g["A"])), (A, g["A"])
+
+
+def pin_f16_exact_rational(lib, N=7, K=40, seed=11):
+    W = synth.f16_normal(900, seed, (N, K), synth.W_SIGMA)
+    x = synth.f16_normal(900, seed + 1, (K,), synth.X_SIGMA)
+    W[0, :4] = np.array([2 ** -24, -(2 ** -24), 2 ** -14, 65504], np.float16)   # subnormal / extreme
+    y, A = oracle.gemv_f16(W, x, lib=lib)
+    xf = _frac16(x)
+    for n in range(N):
+        wf = _frac16(W[n])
+        exact = sum(a * b for a, b in zip(wf, xf))
+        absum = sum(abs(a * b) for a, b in zip(wf, xf))
+        tol = K * U53 * float(absum)
+        assert abs(Fraction(y[n]) - exact) <= Fraction(tol), (n, y[n], float(exact))
+        assert abs(Fraction(A[n]) - absum) <= Fraction(tol), (n, A[n], float(absum))
+
+
+def pin_f16_closed_forms(lib, K=48, seed=12):
+    x = synth.f16_normal(901, seed, (K,), synth.X_SIGMA)
+    xd = x.astype(np.float64)
+    eye = np.eye(K, dtype=np.float16)
+    y, _ = oracle.gemv_f16(eye, x, lib=lib)
+    assert np.array_equal(y, xd), "identity W must return x exactly"
+    perm = np.random.default_rng(5).permutation(K)
+    P = np.zeros((K, K), np.float16)
+    P[np.arange(K), perm] = 1
+    y, _ = oracle.gemv_f16(P, x, lib=lib)
+    assert np.array_equal(y, xd[perm]), "permutation W must permute x exactly"
+    y, A = oracle.gemv_f16(np.ones((3, K), np.float16), np.ones(K, np.float16), lib=lib)
+    assert np.array_equal(y, np.full(3, float(K))) and np.array_equal(A, np.full(3, float(K)))
+    # rows 2^j * e_{k(n)}: a rectangular W (N != K), so a transposed operand
+    # or a wrong row stride cannot pass
+    N = 5
+    ks = [3, 0, K - 1, 17, 29]
+    Wr = np.zeros((N, K), np.float16)
+    for n, k in enumerate(ks):
+        Wr[n, k] = np.float16(2.0 ** (n - 2))
+    y, _ = oracle.gemv_f16(Wr, x, lib=lib)
+    assert np.array_equal(y, np.array([2.0 ** (n - 2) * xd[k] for n, k in enumerate(ks)]))
+
+
+def pin_f16_numpy_matmul(lib, N=64, K=1000, seed=13):
+    W = synth.f16_normal(902, seed, (N, K), synth.W_SIGMA)
+    x = synth.f16_normal(902, seed + 1, (K,), synth.X_SIGMA)
+    y, A = oracle.gemv_f16(W, x, lib=lib)
+    Wd, xd = W.astype(np.float64), x.astype(np.float64)
+    ref = Wd @ xd
+    refA = np.abs(Wd) @ np.abs(xd)
+    assert np.all(np.abs(y - ref) <= 1e-12 * refA), "oracle differs from numpy float64 matmul"
+    assert np.all(np.abs(A - refA) <= 1e-12 * refA)
+
+
+def pin_f16_scaling(lib, N=9, K=64, seed=14):
+    W = synth.f16_normal(903, seed, (N, K), synth.W_SIGMA)
+    x = synth.f16_normal(903, seed + 1, (K,), synth.X_SIGMA)
+    y1, _ = oracle.gemv_f16(W, x, lib=lib)
+    y2, _ = oracle.gemv_f16(W, (x.astype(np.float32) * 4).astype(np.float16), lib=lib)
+    assert np.array_equal(y2, 4 * y1), "power-of-two scaling of x must scale y exactly"
+
+
+# ---------------------------------------------------------------- w8a8 ---
+
+def pin_w8a8_golden(lib):
+    g = _golden("w8a8_tiny.json")
+    acc, y, A = oracle.gemv_w8a8(np.array(g["Wq"], np.int8), np.array(g["w_scale"], np.float32),
+                                 np.array(g["xq"], np.int8), g["x_scale"], lib=lib)
+    assert acc.tolist() == g["acc"], acc
+    assert np.array_equal(y, np.array(g["y"])) and np.array_equal(A, np.array(g["A"])), (y, A)
+
+
+def pin_w8a8_int64_matmul(lib, N=37, K=300, seed=15):
+    Wq = synth.int8_uniform(904, seed, (N, K))
+    xq = synth.int8_uniform(904, seed + 1, (K,))
+    Wq[0, :5] = -128
+    xq[:3] = -128
+    s_w = synth.f32_uniform(904, seed + 2, (N,), 0.001, 0.01)
+    s_x = np.float32(0.02)
+    acc, y, A = oracle.gemv_w8a8(Wq, s_w, xq, s_x, lib=lib)
+    ref = Wq.astype(np.int64) @ xq.astype(np.int64)
+    assert np.array_equal(acc.astype(np.int64), ref), "int8 accumulator differs from int64 matmul"
+    absref = np.abs(Wq.astype(np.int64)) @ np.abs(xq.astype(np.int64))
+    for n in range(N):
+        sc = Fraction(float(s_w[n])) * Fraction(float(s_x))
+        assert abs(Fraction(y[n]) - int(ref[n]) * sc) <= abs(int(ref[n]) * sc) * Fraction(U53)
+        assert abs(Fraction(A[n]) - int(absref[n]) * sc) <= abs(int(absref[n]) * sc) * Fraction(U53)
+    # one-hot rows select activations; x = 1 gives row sums
+    sel = np.random.default_rng(3).integers(0, K, N)
+    oh = np.zeros((N, K), np.int8)
+    oh[np.arange(N), sel] = 1
+    acc1, _, _ = oracle.gemv_w8a8(oh, s_w, xq, s_x, lib=lib)
+    assert np.array_equal(acc1, xq[sel].astype(np.int32))
+    acc2, _, _ = oracle.gemv_w8a8(Wq, s_w, np.ones(K, np.int8), s_x, lib=lib)
+    assert np.array_equal(acc2, Wq.astype(np.int64).sum(1).astype(np.int32))
+
+
+def pin_w8a8_int32_range(lib):
+    one = np.ones(1, np.float32)
+
+    def run(K, w, xv):
+        return oracle.gemv_w8a8(np.full((1, K), w, np.int8), one, np.full(K, xv, np.int8), 1.0, lib=lib)
+
+    acc, _, _ = run(133144, 127, 127)               # 133144 * 16129 = 2147479576 <= 2^31 - 1
+    assert int(acc[0]) == 133144 * 16129
+    acc, _, _ = run(132104, -128, 127)              # -132104 * 16256 = -2147482624 >= -2^31
+    assert int(acc[0]) == -132104 * 16256
+    for K, w, xv in ((133145, 127, 127), (131072, -128, -128), (132105, -128, 127)):
+        try:
+            run(K, w, xv)
+        except oracle.OracleError as e:
+            assert f"status {oracle.ERR_RANGE}" in str(e)
+            continue
+        raise AssertionError(f"int32 overflow not detected for K={K}")
+
+
+# ---------------------------------------------------------------- w4a16 --
+
+def _unpack_canonical(Wc: np.ndarray) -> np.ndarray:
+    """Independent numpy unpack: q[n, 8j+i] = (Wc[n,j] >> 4i) & 15."""
+    shifts = (4 * np.arange(8, dtype=np.uint32))[None, None, :]
+    return ((Wc[:, :, None] >> shifts) & np.uint32(15)).reshape(Wc.shape[0], -1).astype(np.int64)
+
+
+def pin_w4_golden(lib):
+    g = _golden("w4_nibble_order.json")
+    K, group = g["K"], g["group"]
+    for row in g["rows"]:
+        Wc = np.full((1, K // 8), int(row["rest"], 16), np.uint32)
+        Wc[0, 0] = int(row["word0"], 16)
+        s4 = np.array([[int(row["scale_bits"], 16)]], np.uint16)
+        for j, want in enumerate(row["y_onehot_j0_to_7"]):
+            x = np.zeros(K, np.float16)
+            x[j] = 1
+            y, _ = oracle.gemv_w4a16(Wc, s4, x, group, lib=lib)
+            assert y[0] == want, (row["word0"], j, y[0], want)
+    tg = g["two_group_case"]
+    K2 = tg["K"]
+    s4 = np.array([[int(v, 16) for v in tg["scale_bits"]]], np.uint16)
+    for row in tg["rows"]:
+        Wc = np.concatenate([np.full(16, int(w, 16), np.uint32) for w in row["group_words"]])[None, :]
+        y, _ = oracle.gemv_w4a16(Wc, s4, np.ones(K2, np.float16), group, lib=lib)
+        assert y[0] == row["y_all_ones_x"], (row, y[0])
+
+
+def pin_w4_numpy_dequant(lib, M=3, N=40, K=512, seed=16):
+    Wc = synth.w4_words(905, seed, N, K)
+    s4 = synth.f16_uniform(905, seed + 1, (N, K // 128), 0.002, 0.02)
+    X = synth.f16_normal(905, seed + 2, (M, K), synth.X_SIGMA)
+    Y, A = oracle.gemv_w4a16(Wc, s4, X, 128, lib=lib)
+    w = (_unpack_canonical(Wc) - 8).astype(np.float64) * np.repeat(s4.astype(np.float64), 128, axis=1)
+    ref = X.astype(np.float64) @ w.T
+    refA = np.abs(X.astype(np.float64)) @ np.abs(w).T
+    assert np.all(np.abs(Y - ref) <= 1e-12 * refA + 1e-300), "w4 oracle differs from numpy dequant+matmul"
+    assert np.all(np.abs(A - refA) <= 1e-12 * refA + 1e-300)
+    # every row of a block equals the M=1 product of that row, bit for bit
+    for m in range(M):
+        y1, a1 = oracle.gemv_w4a16(Wc, s4, X[m], 128, lib=lib)
+        assert np.array_equal(y1, Y[m]) and np.array_equal(a1, A[m])
+
+
+def pin_w4_exact_rational(lib, N=3, K=256, seed=17):
+    Wc = synth.w4_words(906, seed, N, K)
+    s4 = synth.f16_uniform(906, seed + 1, (N, K // 128), 0.002, 0.02)
+    x = synth.f16_normal(906, seed + 2, (K,), synth.X_SIGMA)
+    y, _ = oracle.gemv_w4a16(Wc, s4, x, 128, lib=lib)
+    q = _unpack_canonical(Wc)
+    xf = _frac16(x)
+    for n in range(N):
+        sf = _frac16(s4[n])
+        terms = [(int(q[n, k]) - 8) * sf[k // 128] * xf[k] for k in range(K)]
+        exact = sum(terms)
+        tol = Fraction(K * U53) * sum(abs(t) for t in terms)
+        assert abs(Fraction(y[n]) - exact) <= tol, (n, y[n], float(exact))
+
+
+ALL_PINS = [
+    pin_f16_decode_all_patterns, pin_f16_golden, pin_f16_exact_rational, pin_f16_closed_forms,
+    pin_f16_numpy_matmul, pin_f16_scaling, pin_w8a8_golden, pin_w8a8_int64_matmul,
+    pin_w8a8_int32_range, pin_w4_golden, pin_w4_numpy_dequant, pin_w4_exact_rational,
+]

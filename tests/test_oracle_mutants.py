@@ -1,0 +1,50 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and checks
+that the pins catch every one of them.  The real oracle is never modified."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+# (name, unique text in oracle.c, replacement); every mutant stays in bounds.
+MUTANTS = [
+    ("f16_drop_last_term", "double p = w * xd[k];", "double p = (k == K - 1) ? 0.0 : w * xd[k];"),
+    ("f16_reversed_k", "f16_value(row[k], &w)", "f16_value(row[K - 1 - k], &w)"),
+    ("f16_abs_x", "double p = w * xd[k];", "double p = w * fabs(xd[k]);"),
+    ("f16_exponent_bias", "(int)e - 25", "(int)e - 24"),
+    ("f16_subnormal_scale", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    ("f16_sign_dropped", "*out = sign ? -v : v;", "*out = v;"),
+    ("f16_A_without_abs", "            a += fabs(p);\n        }\n        y[n] = s;",
+     "            a += p;\n        }\n        y[n] = s;"),
+    ("w8_unsigned_weight", "(int64_t)row[k] * (int64_t)xq[k]", "(int64_t)(uint8_t)row[k] * (int64_t)xq[k]"),
+    ("w8_drop_first_term", "(int64_t)row[k] * (int64_t)xq[k];", "(int64_t)row[k] * (int64_t)xq[k] * (k != 0);"),
+    ("w8_no_range_check", "if (s > INT32_MAX || s < INT32_MIN)", "if (0)"),
+    ("w8_scale_missing_x", "(double)w_scale[n] * (double)x_scale", "(double)w_scale[n]"),
+    ("w4_nibble_order", "(word >> (4 * (k % 8)))", "(word >> (4 * (7 - k % 8)))"),
+    ("w4_zero_point", "(double)(q - 8)", "(double)(q - 7)"),
+    ("w4_group_index", "s4[n * groups + k / group]", "s4[n * groups + (k / 8) % groups]"),
+    ("w4_activation_row", "w * xd[m * K + k]", "w * xd[k]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} must be unique"
+    mdir = tmp_path / "oracle"
+    mdir.mkdir()
+    (mdir / "oracle.c").write_text(src.replace(old, new))
+    so = str(mdir / "liboracle.so")
+    import subprocess
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-std=c99", "-shared", "-fPIC",
+                    str(mdir / "oracle.c"), "-o", so, "-lm"], check=True)
+    lib = oracle.load(so)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, oracle.OracleError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects mutant {name}"
