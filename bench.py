@@ -1,0 +1,268 @@
+"""Benchmark: the fp16 batch-1 decode-step linear stream on one MI355X.
+
+One step is the whole hot path once: 28 layers x {qkv 2048x1024, o
+1024x1024, gate+up 6144x1024, down 1024x3072} plus the 248320x1024 lm_head,
+each GEMV on its own seeded activation, replayed as a captured hipGraph.
+Inputs are resident in HBM before timing starts.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+METRIC = "achieved HBM GB/s (% of peak) for batch-1 GEMV; ms per decode-step stream"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extras", action="store_true", help="only the decode-step stream")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,probe,ordered)")
+    return ap.parse_args()
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def event_times(torch, fn, reps, stream):
+    """Per-call GPU durations (ms) of fn() on `stream`, calls enqueued back to back."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    with torch.cuda.stream(stream):
+        evs[0].record(stream)
+        for i in range(reps):
+            fn(i)
+            evs[i + 1].record(stream)
+    stream.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
+
+
+def summary(ts):
+    ts = sorted(ts)
+    return {"median_ms": statistics.median(ts), "p10_ms": ts[len(ts) // 10], "p90_ms": ts[(9 * len(ts)) // 10],
+            "mean_ms": sum(ts) / len(ts)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU: the batch-1 GEMV is measured on one "
+                                   "MI355X and no multi-GPU path exists; rerun with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from weight_streaming_gemv_decode_amd import synth, wsgemv
+    wsgemv.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+
+    # ---- inputs (seeded, synthetic), copied to HBM once ----
+    t0 = time.time()
+    step_in = synth.decode_step_f16(workload=3)
+    lins = []
+    for name, W, x in step_in:
+        N, K = W.shape
+        lins.append(wsgemv.Linear(wsgemv.F16, torch.from_numpy(W).to(dev), torch.from_numpy(x).to(dev),
+                                  torch.empty(N, dtype=torch.float32, device=dev), N, K))
+    torch.cuda.synchronize()
+    w_bytes = sum(W.nbytes for _, W, _ in step_in)
+    x_bytes = sum(x.nbytes for _, _, x in step_in)
+    y_bytes = sum(W.shape[0] * 4 for _, W, _ in step_in)
+    step_bytes = w_bytes + x_bytes + y_bytes
+    log(f"inputs ready in {time.time() - t0:.1f}s: {len(lins)} linears, {step_bytes} algorithmic bytes/step")
+
+    # ---- the timed configuration: GROUPED graph ----
+    with torch.cuda.stream(stream):
+        step = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED, stream=stream)
+        for _ in range(args.warmup):
+            step(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            step(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"GROUPED graph: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s")
+
+    # per-launch duration of the dominant kernel (the grouped fp16 kernel), on its own stream
+    eager = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER, stream=stream)
+    launches, units = eager.info()
+    kt = event_times(torch, lambda i: eager(stream), max(50, min(args.steps, 200)), stream)
+    ks = summary(kt)
+    achieved = step_bytes / (ks["mean_ms"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "dense_grouped_kernel<f16> (one launch per step)",
+                "bytes_per_launch": step_bytes, "launch_ms": ks}
+    log(f"grouped kernel: mean {ks['mean_ms'] * 1e3:.1f} us -> {achieved:.0f} GB/s")
+
+    extras = {}
+    only = set(filter(None, args.only.split(",")))
+    want = (lambda k: (not args.no_extras) and (not only or k in only))
+
+    if want("ordered"):
+        o = wsgemv.DecodeStep(lins, wsgemv.STEP_ORDERED, stream=stream)
+        ts = event_times(torch, lambda i: o(stream), 50, stream)
+        s = summary(ts)
+        extras["c3_ordered_graph"] = {"median_ms": s["median_ms"], "GBps": step_bytes / (s["median_ms"] * 1e-3) / 1e9,
+                                      "launches": o.info()[0]}
+        o.close()
+
+    if want("c2"):
+        lm = lins[-1]
+        Wcopy = lm.W.clone()
+        Ws = [lm.W, Wcopy]
+        b = lm.N * lm.K * 2 + lm.K * 2 + lm.N * 4
+        res = {}
+        for S in (0, 1, 2):
+            ws = wsgemv.workspace(wsgemv.F16, 1, lm.N, lm.K, S, dev)
+            y = torch.empty(lm.N, device=dev)
+            fn = lambda i: wsgemv.gemv_f16(Ws[i % 2], lm.x, y=y, splits=S, ws=ws, stream=stream)  # noqa: E731
+            for i in range(10):
+                fn(i)
+            s = summary(event_times(torch, fn, 100, stream))
+            res[f"S={S if S else wsgemv.plan_splits(0, 1, lm.N, lm.K)}{' (auto)' if S == 0 else ''}"] = {
+                "median_us": s["median_ms"] * 1e3, "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
+                "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        extras["c2_lm_head_248320x1024"] = {"bytes": b, "rotation": "2 weight copies (1.02 GB)", **res}
+        del Wcopy
+
+    if want("c1"):
+        N, K = synth.C1_SHAPE
+        W = torch.from_numpy(synth.f16_normal(1, 0, (N, K), synth.W_SIGMA)).to(dev)
+        x = torch.from_numpy(synth.f16_normal(1, 1, (K,), synth.X_SIGMA)).to(dev)
+        copies = [W] + [W.clone() for _ in range(63)]
+        ws = wsgemv.workspace(wsgemv.F16, 1, N, K, 0, dev)
+        y = torch.empty(N, device=dev)
+        fn = lambda i: wsgemv.gemv_f16(copies[i % 64], x, y=y, ws=ws, stream=stream)  # noqa: E731
+        for i in range(64):
+            fn(i)
+        s = summary(event_times(torch, fn, 640, stream))
+        b = N * K * 2 + K * 2 + N * 4
+        extras["c1_2048x2048"] = {"bytes": b, "median_us": s["median_ms"] * 1e3,
+                                  "GBps": b / (s["median_ms"] * 1e-3) / 1e9, "rotation": "64 copies (537 MB)",
+                                  "note": "back-to-back launches; launch-bound shape"}
+        del copies
+
+    if want("c4"):
+        for (N, K) in synth.C4_SHAPES:
+            Wq = torch.from_numpy(synth.int8_uniform(4, 0, (N, K))).to(dev)
+            xq = torch.from_numpy(synth.int8_uniform(4, 1, (K,))).to(dev)
+            sw = torch.from_numpy(synth.f32_uniform(4, 2, (N,), 0.001, 0.01)).to(dev)
+            xs = torch.tensor([synth.X_SCALE_W8A8], device=dev)
+            copies = [Wq] + [Wq.clone() for _ in range(8)]
+            ws = wsgemv.workspace(wsgemv.W8A8, 1, N, K, 0, dev)
+            y = torch.empty(N, device=dev)
+            acc = torch.empty(N, dtype=torch.int32, device=dev)
+            fn = lambda i: wsgemv.gemv_w8a8(copies[i % 9], sw, xq, xs, y=y, acc_out=acc, ws=ws,  # noqa: E731
+                                            stream=stream)
+            for i in range(18):
+                fn(i)
+            s = summary(event_times(torch, fn, 180, stream))
+            b = N * K + N * 4 + K + N * 4 + N * 4
+            extras[f"c4_w8a8_{N}x{K}"] = {"bytes_incl_acc_out": b, "median_us": s["median_ms"] * 1e3,
+                                          "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
+                                          "splits": wsgemv.plan_splits(1, 1, N, K), "rotation": "9 copies"}
+            del copies
+
+    if want("c5"):
+        for M in (1, 4):
+            w4 = synth.decode_step_w4(workload=5, M=M)
+            wl = []
+            keep = []
+            b = 0
+            for name, Wc, s4, X in w4:
+                N, K = Wc.shape[0], Wc.shape[1] * 8
+                Wp, Sp = wsgemv.pack_w4(torch.from_numpy(Wc.view(np.int32)).to(dev), torch.from_numpy(s4).to(dev))
+                y = torch.empty((M, N), device=dev)
+                wl.append(wsgemv.Linear(wsgemv.W4A16, Wp, torch.from_numpy(X).to(dev), y, N, K, M=M, scale=Sp,
+                                        group=128))
+                b += Wc.nbytes + s4.nbytes + X.nbytes + M * N * 4
+            torch.cuda.synchronize()
+            st = wsgemv.DecodeStep(wl, wsgemv.STEP_GROUPED, stream=stream)
+            for _ in range(5):
+                st(stream)
+            s = summary(event_times(torch, lambda i: st(stream), 100, stream))
+            extras[f"c5_w4a16_step_M{M}"] = {"bytes": b, "median_us": s["median_ms"] * 1e3,
+                                            "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
+                                            "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            st.close()
+            del wl, w4
+
+    if want("probe"):
+        nb = 2 << 30
+        buf = torch.empty(nb, dtype=torch.uint8, device=dev)
+        buf.fill_(1)
+        out = torch.empty(4096, device=dev)
+        g = wsgemv.read_probe_grid(nb)
+        fn = lambda i: wsgemv.read_probe(buf, out, grid=g, stream=stream)  # noqa: E731
+        for i in range(3):
+            fn(i)
+        s = summary(event_times(torch, fn, 20, stream))
+        extras["hbm_read_probe_2GiB"] = {"median_us": s["median_ms"] * 1e3, "GBps": nb / (s["median_ms"] * 1e-3) / 1e9}
+        del buf
+
+    # ---- CPU oracle on the host cores, same step inputs ----
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        oracle.set_threads(cores)
+        t1 = time.perf_counter()
+        for _, W, x in step_in:
+            oracle.gemv_f16(W, x)
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(step_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "ms_per_step": round(dt * 1e3, 1),
+               "sample": "one full decode step (all 113 GEMVs, 1.22 GB) through the fp64 C oracle, "
+                         f"OpenMP over rows on {cores} threads ({platform.processor() or platform.machine()})"}
+        log(f"oracle: {dt:.2f}s/step on {cores} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic: seeded fp16 weights ~N(0,0.02), activations ~N(0,1); fp32 accumulate, fp32 outputs",
+        "config": {"workload": "fp16 batch-1 decode-step linear stream: 28 x {qkv 2048x1024, o 1024x1024, "
+                               "gate_up 6144x1024, down 1024x3072} + lm_head 248320x1024, one hipGraph "
+                               "(GROUPED: one launch over a work table)",
+                   "bytes_per_step": step_bytes, "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+                   "launches_per_step": launches, "work_units": units},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line))
+    step.close()
+    eager.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * wsgemv: batch-1 weight-streaming GEMV for LLM decode on MI355X (gfx950).
+ *
+ * The operation (MiniCPM-V 4.6 on Orange Pi AIPro (Ascend 310B) post,
+ * baseline paragraph and closing paragraph): during decode M = 1, so each
+ * linear layer is a vector-matrix product, and every weight is read once per
+ * generated token; the step is bound by memory bandwidth.  With W stored
+ * [N, K] row-major (K contiguous) and activation x[K]:
+ *
+ *     y[n] = sum_k W[n, k] * x[k]          (fp32 accumulation, fp32 y)
+ *
+ * Conventions shared by every call below
+ *  - Pointers named W, x, y, ws, ... are DEVICE pointers owned by the caller;
+ *    the library never frees or retains them beyond the call (a decode-step
+ *    plan retains the pointers it was created with, see there).
+ *  - Calls are asynchronous on the caller's stream (a hipStream_t passed as
+ *    wsg_stream_t; NULL means the null stream).  They never synchronise and
+ *    never allocate device memory, except wsg_decode_step_create.
+ *  - Every argument is validated before any HIP call; on any error nothing
+ *    is launched and the outputs are untouched.
+ *  - Return value: a wsg_status (0 = WSG_OK).  No C++ exception crosses the
+ *    ABI.  WSG_ERR_HIP keeps the hipError_t in wsg_last_hip_error() (per
+ *    thread).
+ *  - N == 0 is a no-op.  K == 0 writes y = 0 (the empty sum).
+ *  - Outputs must not alias inputs.  Inputs must stay alive until the
+ *    stream has reached the work.
+ *
+ * Split-K.  A call may cut the k-sum into S contiguous slices, computed by
+ * different workgroups, whose fp32 (int32 for W8A8) partial sums are then
+ * added on the device in fixed slice order 0..S-1, so results are
+ * bit-identical from run to run.  This follows the same post, second change:
+ * the ~248k-row lm_head is cut into slices at load time and the slice
+ * results reduced (there on the host; here on the device, in the
+ * caller-provided workspace).  `splits` = 0 lets the library's per-shape
+ * launch table choose S (the EdgeFM summary, section 2B, dispatches
+ * operators by tensor-shape signature); `splits` >= 1 forces S.  The
+ * workspace must hold wsg_workspace_bytes(...) bytes, 256-byte aligned; it
+ * may be NULL when that size is 0.  One workspace must not serve two calls
+ * that are in flight at the same time.
+ */
+#ifndef WSGEMV_H
+#define WSGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *wsg_stream_t; /* a hipStream_t */
+typedef int32_t wsg_status;
+
+enum {
+    WSG_OK = 0,
+    WSG_ERR_NULL = 1,        /* a required pointer is NULL */
+    WSG_ERR_SHAPE = 2,       /* negative or inconsistent sizes, K not a multiple of the vector width */
+    WSG_ERR_ALIGN = 3,       /* a pointer is not aligned as stated */
+    WSG_ERR_UNSUPPORTED = 4, /* a valid request this build does not implement (e.g. M > 8) */
+    WSG_ERR_WORKSPACE = 5,   /* workspace missing or too small for the chosen split */
+    WSG_ERR_HIP = 6,         /* a HIP runtime call failed; see wsg_last_hip_error() */
+    WSG_ERR_NOMEM = 7,       /* host or device allocation failed (plan creation only) */
+    WSG_ERR_STATE = 8        /* NULL or destroyed plan */
+};
+
+enum { WSG_F16 = 0, WSG_W8A8 = 1, WSG_W4A16 = 2 }; /* wsg_linear.kind */
+
+const char *wsg_status_string(wsg_status s);
+int32_t wsg_last_hip_error(void);
+const char *wsg_build_info(void);
+
+/* The split S the launch table picks for this shape (kind, M, N, K). */
+int32_t wsg_plan_splits(int32_t kind, int64_t M, int64_t N, int64_t K);
+
+/* Workspace bytes a call of this shape needs with `splits` (0 = the table's
+ * choice): S * M * N * 4 when S > 1, else 0. */
+size_t wsg_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K, int32_t splits);
+
+/*
+ * fp16 weights, M = 1 (same post: FP16 weights read once per step).
+ *   W  fp16 [N, K] row-major, 16-byte aligned, K % 8 == 0
+ *   x  fp16 [K], 16-byte aligned
+ *   y  fp32 [N], 4-byte aligned:  y[n] = sum_k W[n,k] x[k], fp32 accumulate
+ */
+wsg_status gemv_f16(const void *W, const void *x, float *y, int64_t N, int64_t K,
+                    int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream);
+
+/*
+ * int8 weights x int8 activations, M = 1 (vLLM Arm CPU optimisation post,
+ * INT8 W8A8 section: 8-bit weights and 8-bit activations multiplied with an
+ * integer multiply-accumulate; same MiniCPM-V post, closing paragraph: INT8
+ * dequantisation fused into the product).
+ *   Wq      int8 [N, K] row-major, 16-byte aligned, K % 16 == 0
+ *   w_scale fp32 [N] per output channel
+ *   xq      int8 [K], 16-byte aligned
+ *   x_scale fp32 [1] per-tensor activation scale (device memory)
+ *   acc[n]  = sum_k Wq[n,k] * xq[k], exact int32 (wrap-free for |acc| < 2^31)
+ *   y[n]    = ((float)acc[n] * w_scale[n]) * x_scale, fp32, round to nearest even
+ *   acc_out int32 [N] receives acc when non-NULL.
+ */
+wsg_status gemv_w8a8(const int8_t *Wq, const float *w_scale, const int8_t *xq,
+                     const float *x_scale, float *y, int32_t *acc_out, int64_t N, int64_t K,
+                     int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream);
+
+/*
+ * INT4 weights, load-time packing (vLLM Arm CPU optimisation post, dense
+ * weight prepacking section: weights are put into the kernel's layout once
+ * during warm-up and reused).  Canonical input:
+ *   Wc  uint32 [N, K/8]; element k of row n is the 4-bit field at bits
+ *       [4*(k%8), 4*(k%8)+3] of Wc[n, k/8], value q in 0..15, weight
+ *       (q - 8) * s4[n, k/group]  (zero-point 8)
+ *   s4  fp16 [N, K/group] row-major
+ * Output: Wp (wsg_w4_packed_weight_bytes) and Sp (wsg_w4_packed_scale_bytes),
+ * 16-byte aligned device buffers in the kernels' tile layout: 16-row x 128-k
+ * tiles of 1 KiB, each 64-lane wave reading one tile with one 16-byte load
+ * per lane, the same layout for the M = 1 and the M = 2..8 kernels.  Rows are
+ * padded to a multiple of 16 with zero weights.  group must be 128,
+ * K % 128 == 0.
+ */
+size_t wsg_w4_packed_weight_bytes(int64_t N, int64_t K);
+size_t wsg_w4_packed_scale_bytes(int64_t N, int64_t K, int64_t group);
+wsg_status wsg_pack_w4(const uint32_t *Wc, const void *s4, void *Wp, void *Sp,
+                       int64_t N, int64_t K, int64_t group, wsg_stream_t stream);
+
+/*
+ * INT4 weights x fp16 activations with the dequantisation fused into the
+ * product (MiniCPM-V post, closing paragraph: fused INT4 dequantisation;
+ * vLLM Arm post, INT8 W4A8 section: 4-bit weights cut the bytes streamed).
+ * M = 1 is the decode product; M = 2..8 is a speculative-verify block
+ * (EdgeFM summary, section 2C: the base model checks a block of drafted
+ * tokens against the same weights), computed with MFMA.
+ *   Wp, Sp  packed by wsg_pack_w4 for this (N, K, group)
+ *   x       fp16 [M, K] row-major, 16-byte aligned
+ *   y       fp32 [M, N]:  y[m,n] = sum_g s4[n,g] * sum_{k in g} (q[n,k]-8) x[m,k]
+ */
+wsg_status gemv_w4a16(const void *Wp, const void *Sp, const void *x, float *y,
+                      int64_t M, int64_t N, int64_t K, int64_t group,
+                      int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream);
+
+/*
+ * Decode step: a fixed list of linears replayed once per token (EdgeFM
+ * summary, section 2C: an execution graph is captured once and reused on
+ * every decode iteration to cut kernel-launch overhead).
+ *
+ * wsg_decode_step_create validates every descriptor, builds the launch plan,
+ * allocates the plan's own split-K partials and work table (the only device
+ * allocation in this library), and captures the launches into a hipGraph on
+ * an internal stream.  The descriptors' pointers are frozen into the plan:
+ * later calls read the buffers at those addresses (write new activations into
+ * the same x buffers between steps).
+ *   mode WSG_STEP_ORDERED: one kernel node per linear, in list order.
+ *   mode WSG_STEP_GROUPED: the linears of each kind run as one launch over a
+ *     work table of (linear, row tile, k-slice) units.  Valid because every
+ *     linear of the list reads its own x and writes its own y; a list whose
+ *     linears feed each other must use ORDERED.
+ *   | WSG_STEP_EAGER: skip the graph; decode_step_linears launches directly.
+ * decode_step_linears enqueues one step on `stream`.  A plan is not
+ * thread-safe and one plan's steps must not overlap each other in time.
+ */
+typedef struct wsg_linear {
+    int32_t kind;        /* WSG_F16, WSG_W8A8 or WSG_W4A16 */
+    int32_t M;           /* 1; or 1..8 for WSG_W4A16 */
+    int64_t N, K;
+    const void *W;       /* F16: fp16 [N,K]; W8A8: int8 [N,K]; W4A16: packed Wp */
+    const void *scale;   /* W8A8: fp32 [N]; W4A16: packed Sp; F16: NULL */
+    const void *x;       /* F16, W4A16: fp16 [M,K]; W8A8: int8 [K] */
+    const float *x_scale;/* W8A8: fp32 [1]; otherwise NULL */
+    float *y;            /* fp32 [M,N] */
+    int32_t *acc_out;    /* W8A8: optional int32 [N]; otherwise NULL */
+    int32_t group;       /* W4A16: 128; otherwise 0 */
+    int32_t splits;      /* 0 = table's choice; ORDERED mode only */
+} wsg_linear;
+
+typedef struct wsg_step wsg_step;
+
+enum { WSG_STEP_ORDERED = 0, WSG_STEP_GROUPED = 1, WSG_STEP_EAGER = 0x100 };
+
+wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t mode,
+                                  wsg_stream_t stream, wsg_step **out);
+wsg_status decode_step_linears(wsg_step *step, wsg_stream_t stream);
+wsg_status wsg_decode_step_destroy(wsg_step *step);
+/* Launches per step (kernel nodes) and work units of the plan. */
+wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t *units);
+
+/*
+ * HBM read ceiling: every lane streams 16-byte loads over buf[0, bytes) and
+ * the workgroups write one fp32 partial each into out[grid] (so the loads
+ * cannot be removed).  bytes % 16 == 0; grid = 0 picks a full-chip grid.
+ * Gives the attainable read bandwidth next to the nominal peak.
+ */
+wsg_status wsg_read_probe(const void *buf, size_t bytes, float *out, int32_t grid,
+                          wsg_stream_t stream);
+int32_t wsg_read_probe_grid(size_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WSGEMV_H */

@@ -1,0 +1,126 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every function
+include/wsgemv.h declares, and rejects bad arguments before any HIP call.
+
+Pointers here are fake device addresses that are never dereferenced: every
+call below fails validation, which happens before anything is launched.
+"""
+import ctypes
+
+import pytest
+
+from weight_streaming_gemv_decode_amd import wsgemv
+
+FAKE = 0x7F0000000000          # 256-byte aligned, never dereferenced
+MIS = FAKE + 2                 # misaligned
+OK, NULL, SHAPE, ALIGN, UNSUP, WS, HIP, NOMEM, STATE = range(9)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return wsgemv.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = wsgemv.header_functions()
+    assert {"gemv_f16", "gemv_w8a8", "gemv_w4a16", "decode_step_linears", "wsg_pack_w4",
+            "wsg_decode_step_create"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/wsgemv.h but not exported"
+
+
+def test_status_strings(L):
+    for s in range(9):
+        assert L.wsg_status_string(s)
+    assert L.wsg_status_string(0) == b"ok"
+    assert b"gfx950" in L.wsg_build_info()
+
+
+def test_gemv_f16_validation(L):
+    f = L.gemv_f16
+    assert f(FAKE, FAKE, FAKE, -1, 64, 0, None, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 12, 0, None, 0, None) == SHAPE          # K % 8
+    assert f(None, FAKE, FAKE, 4, 64, 0, None, 0, None) == NULL
+    assert f(FAKE, None, FAKE, 4, 64, 0, None, 0, None) == NULL
+    assert f(FAKE, FAKE, None, 4, 64, 0, None, 0, None) == NULL
+    assert f(MIS, FAKE, FAKE, 4, 64, 0, None, 0, None) == ALIGN
+    assert f(FAKE, MIS, FAKE, 4, 64, 0, None, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE + 1, 4, 64, 0, None, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, 4, 64, -1, None, 0, None) == SHAPE          # negative split
+    assert f(FAKE, FAKE, FAKE, 4, 64, 9, None, 0, None) == SHAPE           # more slices than vectors
+    assert f(FAKE, FAKE, FAKE, 4, 1024, 2, None, 0, None) == WS            # split needs workspace
+    need = L.wsg_workspace_bytes(0, 1, 4, 1024, 2)
+    assert need == 2 * 4 * 4
+    assert f(FAKE, FAKE, FAKE, 4, 1024, 2, FAKE, need - 1, None) == WS
+    assert f(FAKE, FAKE, FAKE, 4, 1024, 2, FAKE + 16, need, None) == ALIGN
+    assert f(None, None, None, 0, 64, 0, None, 0, None) == OK               # N = 0: no-op, nothing launched
+
+
+def test_gemv_w8a8_validation(L):
+    f = L.gemv_w8a8
+    args = lambda **kw: [kw.get("W", FAKE), kw.get("ws_", FAKE), kw.get("x", FAKE), kw.get("xs", FAKE),  # noqa
+                         kw.get("y", FAKE), kw.get("acc", None), kw.get("N", 8), kw.get("K", 64),
+                         kw.get("S", 0), None, 0, None]
+    assert f(*args(K=24)) == SHAPE                                          # K % 16
+    assert f(*args(W=None)) == NULL
+    assert f(*args(ws_=None)) == NULL
+    assert f(*args(xs=None)) == NULL
+    assert f(*args(acc=FAKE + 2)) == ALIGN
+    assert f(*args(x=MIS)) == ALIGN
+    assert f(*args(N=-3)) == SHAPE
+
+
+def test_w4_validation_and_sizes(L):
+    assert L.wsg_w4_packed_weight_bytes(17, 256) == 32 * 128                 # rows padded to 16
+    assert L.wsg_w4_packed_scale_bytes(17, 256, 128) == 32 * 4 * 2          # 4 scales per (row, quad)
+    assert L.wsg_w4_packed_weight_bytes(16, 100) == 0
+    assert L.wsg_pack_w4(FAKE, FAKE, FAKE, FAKE, 16, 256, 64, None) == UNSUP
+    assert L.wsg_pack_w4(FAKE, FAKE, FAKE, FAKE, 16, 200, 128, None) == SHAPE
+    assert L.wsg_pack_w4(None, FAKE, FAKE, FAKE, 16, 256, 128, None) == NULL
+    assert L.wsg_pack_w4(FAKE, FAKE, MIS, FAKE, 16, 256, 128, None) == ALIGN
+    f = L.gemv_w4a16
+    assert f(FAKE, FAKE, FAKE, FAKE, 9, 16, 256, 128, 0, None, 0, None) == UNSUP    # M > 8
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 16, 256, 128, 0, None, 0, None) == SHAPE    # M = 0
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 16, 256, 64, 0, None, 0, None) == UNSUP     # group
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 16, 192, 128, 0, None, 0, None) == SHAPE    # K % 128
+    assert f(FAKE, None, FAKE, FAKE, 1, 16, 256, 128, 0, None, 0, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 16, 256, 128, 3, None, 0, None) == SHAPE    # slice past K
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 16, 1024, 128, 2, None, 0, None) == WS
+
+
+def test_launch_table(L):
+    # The table is a pure host function of the shape.
+    assert L.wsg_plan_splits(0, 1, 248320, 1024) >= 1
+    assert L.wsg_plan_splits(1, 1, 4096, 14336) > 1      # few rows, long rows: split k
+    assert L.wsg_plan_splits(0, 1, 248320, 1024) * 248320 * 4 == L.wsg_workspace_bytes(0, 1, 248320, 1024, 0) \
+        or L.wsg_plan_splits(0, 1, 248320, 1024) == 1
+    for S in (1, 2, 3, 4):
+        want = 0 if S == 1 else S * 2048 * 4
+        assert L.wsg_workspace_bytes(0, 1, 2048, 2048, S) == want
+
+
+def test_decode_step_validation(L):
+    out = ctypes.c_void_p()
+    lin = wsgemv.wsg_linear(0, 1, 64, 64, FAKE, None, FAKE, None, FAKE, None, 0, 0)
+    arr = (wsgemv.wsg_linear * 1)(lin)
+    assert L.wsg_decode_step_create(arr, 1, 7, None, ctypes.byref(out)) == UNSUP   # bad mode
+    assert L.wsg_decode_step_create(arr, -1, 0, None, ctypes.byref(out)) == SHAPE
+    assert L.wsg_decode_step_create(None, 1, 0, None, ctypes.byref(out)) == NULL
+    assert L.wsg_decode_step_create(arr, 1, 0, None, None) == NULL
+    bad = (wsgemv.wsg_linear * 1)(wsgemv.wsg_linear(0, 2, 64, 64, FAKE, None, FAKE, None, FAKE, None, 0, 0))
+    assert L.wsg_decode_step_create(bad, 1, 0, None, ctypes.byref(out)) == UNSUP   # fp16 with M = 2
+    bad = (wsgemv.wsg_linear * 1)(wsgemv.wsg_linear(5, 1, 64, 64, FAKE, None, FAKE, None, FAKE, None, 0, 0))
+    assert L.wsg_decode_step_create(bad, 1, 0, None, ctypes.byref(out)) == UNSUP   # unknown kind
+    bad = (wsgemv.wsg_linear * 1)(wsgemv.wsg_linear(1, 1, 64, 64, FAKE, None, FAKE, FAKE, FAKE, None, 0, 0))
+    assert L.wsg_decode_step_create(bad, 1, 0, None, ctypes.byref(out)) == NULL    # W8A8 without scales
+    bad = (wsgemv.wsg_linear * 1)(wsgemv.wsg_linear(0, 1, 64, 4096, FAKE, None, FAKE, None, FAKE, None, 0, 2))
+    assert L.wsg_decode_step_create(bad, 1, 1, None, ctypes.byref(out)) == UNSUP   # GROUPED forbids splits
+    assert L.decode_step_linears(None, None) == STATE
+    assert L.wsg_decode_step_destroy(None) == STATE
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    W = torch.zeros(4, 16, dtype=torch.float16)
+    x = torch.zeros(16, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        wsgemv.gemv_f16(W, x, y=torch.zeros(4), splits=1)

@@ -1,0 +1,134 @@
+"""Decode-step plans on the GPU: a fixed list of linears captured into a
+hipGraph (ORDERED: one node per linear; GROUPED: one launch over a work
+table) and replayed; every output against the oracle, graph replays against
+eager launches, and the frozen-pointer replay contract."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import assert_bits_equal, assert_within, dev, host, say
+from weight_streaming_gemv_decode_amd import synth, wsgemv
+
+pytestmark = pytest.mark.gpu
+
+
+def _f16_linears(step):
+    lins, refs = [], []
+    for name, W, x in step:
+        N, K = W.shape
+        y = torch.full((N,), float("nan"), device="cuda")
+        lins.append(wsgemv.Linear(wsgemv.F16, dev(W), dev(x), y, N, K))
+        refs.append(oracle.gemv_f16(W, x))
+    return lins, refs
+
+
+def _check_all(lins, refs, what):
+    for l, (y_ref, A) in zip(lins, refs):
+        assert_within(host(l.y).reshape(y_ref.shape), y_ref, A, what)
+
+
+@pytest.fixture(scope="module")
+def small_step():
+    return synth.decode_step_f16(workload=30, n_layers=2, lm_head_rows=8192 + 40)
+
+
+@pytest.mark.parametrize("mode", [wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED,
+                                  wsgemv.STEP_ORDERED | wsgemv.STEP_EAGER, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER])
+def test_f16_step_modes(small_step, mode):
+    say(f"step f16 mode={mode:#x}")
+    lins, refs = _f16_linears(small_step)
+    step = wsgemv.DecodeStep(lins, mode)
+    step()
+    _check_all(lins, refs, f"mode {mode:#x}")
+    first = [host(l.y).copy() for l in lins]
+    for _ in range(3):
+        step()
+    for l, y0 in zip(lins, first):
+        assert_bits_equal(host(l.y), y0, "replay")
+    step.close()
+
+
+def test_graph_equals_eager_and_ordered_equals_standalone(small_step):
+    say("step graph vs eager vs standalone")
+    outs = {}
+    for mode in (wsgemv.STEP_ORDERED, wsgemv.STEP_ORDERED | wsgemv.STEP_EAGER,
+                 wsgemv.STEP_GROUPED, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER):
+        lins, _ = _f16_linears(small_step)
+        st = wsgemv.DecodeStep(lins, mode)
+        st()
+        outs[mode] = [host(l.y) for l in lins]
+        st.close()
+    for a, b in zip(outs[wsgemv.STEP_ORDERED], outs[wsgemv.STEP_ORDERED | wsgemv.STEP_EAGER]):
+        assert_bits_equal(a, b, "ordered graph vs eager")
+    for a, b in zip(outs[wsgemv.STEP_GROUPED], outs[wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER]):
+        assert_bits_equal(a, b, "grouped graph vs eager")
+    # ORDERED uses the same launch table as a standalone call
+    for (name, W, x), yo in zip(small_step, outs[wsgemv.STEP_ORDERED]):
+        assert_bits_equal(host(wsgemv.gemv_f16(dev(W), dev(x))), yo, f"standalone {name}")
+
+
+def test_replay_reads_new_activations_in_place(small_step):
+    say("step replay with new x")
+    lins, _ = _f16_linears(small_step)
+    step = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED)
+    step()
+    new = []
+    for i, l in enumerate(lins):
+        x2 = synth.f16_normal(31, i, (l.K,), synth.X_SIGMA)
+        l.x.copy_(dev(x2))                  # same buffer, new contents
+        new.append(x2)
+    step()
+    for (name, W, _), l, x2 in zip(small_step, lins, new):
+        y_ref, A = oracle.gemv_f16(W, x2)
+        assert_within(host(l.y), y_ref, A, f"replay {name}")
+    step.close()
+
+
+def test_mixed_kinds_step():
+    say("step mixed f16 + w8a8 + w4 (M=1, M=4)")
+    lins, checks = [], []
+    W = synth.f16_normal(32, 0, (300, 1024), 0.02)
+    x = synth.f16_normal(32, 1, (1024,), 1.0)
+    y = torch.empty(300, device="cuda")
+    lins.append(wsgemv.Linear(wsgemv.F16, dev(W), dev(x), y, 300, 1024))
+    checks.append((y, *oracle.gemv_f16(W, x)))
+    Wq = synth.int8_uniform(32, 2, (500, 2048))
+    xq = synth.int8_uniform(32, 3, (2048,))
+    sw = synth.f32_uniform(32, 4, (500,), 0.001, 0.01)
+    xs = torch.tensor([0.02], device="cuda")
+    y8 = torch.empty(500, device="cuda")
+    acc = torch.empty(500, dtype=torch.int32, device="cuda")
+    lins.append(wsgemv.Linear(wsgemv.W8A8, dev(Wq), dev(xq), y8, 500, 2048, scale=dev(sw), x_scale=xs, acc_out=acc))
+    acc_ref, y8_ref, A8 = oracle.gemv_w8a8(Wq, sw, xq, 0.02)
+    checks.append((y8, y8_ref, A8))
+    for M in (1, 4):
+        Wc = synth.w4_words(32, 10 + M, 200, 3072)
+        s4 = synth.f16_uniform(32, 20 + M, (200, 24), 0.002, 0.02)
+        X = synth.f16_normal(32, 30 + M, (M, 3072), 1.0)
+        Wp, Sp = wsgemv.pack_w4(dev(Wc), dev(s4))
+        yw = torch.empty((M, 200), device="cuda")
+        lins.append(wsgemv.Linear(wsgemv.W4A16, Wp, dev(X), yw, 200, 3072, M=M, scale=Sp, group=128))
+        Y_ref, Aw = oracle.gemv_w4a16(Wc, s4, X)
+        checks.append((yw, Y_ref, Aw))
+    for mode in (wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED):
+        step = wsgemv.DecodeStep(lins, mode)
+        step()
+        for yt, y_ref, A in checks:
+            assert_within(host(yt).reshape(y_ref.shape), y_ref, A, f"mixed mode {mode}")
+        assert_bits_equal(host(acc), acc_ref, "w8a8 acc in a step")
+        step.close()
+
+
+def test_full_decode_step_c3():
+    """28 layers x 4 linears + the 248320x1024 lm_head, GROUPED graph (the
+    timed configuration), every output of every linear against the oracle."""
+    say("step C3 full, GROUPED graph")
+    step_in = synth.decode_step_f16(workload=3)
+    lins, refs = _f16_linears(step_in)
+    step = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED)
+    step()
+    _check_all(lins, refs, "C3")
+    launches, units = step.info()
+    assert launches == 1
+    step.close()

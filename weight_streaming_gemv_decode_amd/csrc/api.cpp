@@ -1,0 +1,872 @@
+// C ABI of wsgemv: argument validation, the per-shape launch table, the
+// GEMV entry points and the decode-step plan (hipGraph capture and replay).
+//
+// The launch table follows the operator implementation table of the EdgeFM
+// summary (section 2B): an operator call is mapped to a kernel configuration
+// by its tensor-shape signature.  Here the key is (kind, M, N, K) and the
+// value is the k-split S, the rows per work unit and the kernel variant.
+// Graph replay follows the same summary, section 2C: the launches of one
+// decode step are captured once and replayed every step.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/wsgemv.h"
+#include "wsg_common.hpp"
+
+using namespace wsg;
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+wsg_status hip_fail(hipError_t e) {
+    g_last_hip = (int32_t)e;
+    return WSG_ERR_HIP;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest k-slice, in 16-byte vectors, a dense unit stages in LDS (32 KiB).
+constexpr int kMaxSliceVec = 2048;
+// Target weight bytes of one work unit.
+constexpr int64_t kUnitBytes = 128 * 1024;
+// Work units wanted per launch (4 per compute unit on 256 CUs).
+constexpr int64_t kWantUnits = 1024;
+constexpr int kMaxM = 8;
+
+bool env_flag(const char *name, bool dflt) {
+    const char *v = std::getenv(name);
+    if (!v || !*v)
+        return dflt;
+    return v[0] == '1' || v[0] == 'y' || v[0] == 'Y' || v[0] == 't' || v[0] == 'T';
+}
+
+// Non-temporal weight loads (the weight stream has no reuse).  Results do not
+// depend on it; WSG_NT=0/1 overrides the default for sweeps.
+bool use_nt() { return env_flag("WSG_NT", false); }
+
+// ---------------------------------------------------------------- dense --
+
+struct DensePlan {
+    DenseCfg cfg;
+    int S;
+    int kvs;
+    int tile_rows;
+};
+
+int elem_per_vec(int kind) { return kind == kF16 ? 8 : 16; }
+
+int dense_min_splits(int64_t kvec) { return (int)std::max<int64_t>(1, cdiv(kvec, kMaxSliceVec)); }
+
+// Rows per unit: a multiple of 4 waves x R rows, close to kUnitBytes.
+int dense_tile_rows(int64_t slice_bytes_per_row, int R) {
+    const int q = kWavesPerBlock * R;
+    int64_t rows = kUnitBytes / std::max<int64_t>(1, slice_bytes_per_row);
+    rows = std::max<int64_t>(q, rows / q * q);
+    return (int)std::min<int64_t>(rows, 1 << 20);
+}
+
+DensePlan plan_dense(int kind, int64_t N, int64_t K, int splits) {
+    const int64_t kvec = K / elem_per_vec(kind);
+    DensePlan p;
+    p.cfg = DenseCfg{4, 2, use_nt(), false};
+    int S = splits > 0 ? splits : dense_min_splits(kvec);
+    if (splits <= 0) {
+        // Underfilled launch: first shrink the row tile, then split k in
+        // slices that stay whole 128-vector chunks.
+        int64_t tr = 16;
+        int64_t units = cdiv(N, tr) * S;
+        if (units < kWantUnits / 2 && kvec >= 256) {
+            const int64_t chunks = kvec / 128;
+            for (int s = S + 1; s <= 16 && s <= chunks; ++s) {
+                if (kvec % (128LL * s) == 0 || s == (int)chunks) {
+                    S = s;
+                    if (cdiv(N, tr) * S >= kWantUnits / 2)
+                        break;
+                }
+            }
+        }
+    }
+    p.S = S;
+    p.kvs = (int)cdiv(kvec, S);
+    const int64_t slice_row_bytes = (int64_t)p.kvs * 16;
+    int tr = dense_tile_rows(slice_row_bytes, p.cfg.R);
+    while (tr > 16 && cdiv(N, tr) * S < kWantUnits)
+        tr -= 16;
+    if (cdiv(N, tr) * S < kWantUnits / 4 && N > 0) {
+        // Very few rows: one row per wave step, 4 rows per unit.
+        p.cfg.R = 1;
+        tr = 4;
+    }
+    p.tile_rows = tr;
+    return p;
+}
+
+DenseLin make_dense(int kind, const void *W, const void *x, float *y, void *part, const float *w_scale,
+                    const float *x_scale, int32_t *acc_out, int64_t N, int64_t K, const DensePlan &p) {
+    DenseLin L{};
+    L.W = static_cast<const u32x4 *>(W);
+    L.x = static_cast<const u32x4 *>(x);
+    L.y = y;
+    L.part = part;
+    L.w_scale = w_scale;
+    L.x_scale = x_scale;
+    L.acc_out = acc_out;
+    L.N = N;
+    L.kvec = (int32_t)(K / elem_per_vec(kind));
+    L.S = p.S;
+    L.kvs = p.kvs;
+    L.tile_rows = p.tile_rows;
+    L.n_tiles = (int32_t)cdiv(N, p.tile_rows);
+    return L;
+}
+
+wsg_status check_dense_args(int kind, const void *W, const void *x, const float *y, int64_t N, int64_t K,
+                            int32_t splits) {
+    if (N < 0 || K < 0)
+        return WSG_ERR_SHAPE;
+    if (N > (int64_t)INT32_MAX * 16 || K > (1LL << 28))
+        return WSG_ERR_UNSUPPORTED;
+    if (K % elem_per_vec(kind))
+        return WSG_ERR_SHAPE;
+    if (N == 0)
+        return WSG_OK;
+    if (!y)
+        return WSG_ERR_NULL;
+    if (!aligned(y, 4))
+        return WSG_ERR_ALIGN;
+    if (K == 0)
+        return WSG_OK;
+    if (!W || !x)
+        return WSG_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(x, 16))
+        return WSG_ERR_ALIGN;
+    const int64_t kvec = K / elem_per_vec(kind);
+    if (splits < 0 || (splits > 0 && (splits > kvec || cdiv(kvec, splits) > kMaxSliceVec)))
+        return WSG_ERR_SHAPE;
+    // every slice must hold at least one vector
+    if (splits > 0 && (int64_t)(splits - 1) * cdiv(kvec, splits) >= kvec)
+        return WSG_ERR_SHAPE;
+    return WSG_OK;
+}
+
+size_t dense_ws_bytes(const DensePlan &p, int64_t N) { return p.S > 1 ? (size_t)p.S * (size_t)N * 4 : 0; }
+
+wsg_status check_ws(const void *ws, size_t ws_bytes, size_t need) {
+    if (need == 0)
+        return WSG_OK;
+    if (!ws || ws_bytes < need)
+        return WSG_ERR_WORKSPACE;
+    if (!aligned(ws, 256))
+        return WSG_ERR_ALIGN;
+    return WSG_OK;
+}
+
+wsg_status enqueue_dense(int kind, const DenseLin &L, const DenseCfg &cfg, hipStream_t s) {
+    hipError_t e = launch_dense(kind, L, cfg, s);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    if (L.S > 1) {
+        e = launch_dense_reduce(kind, L, s);
+        if (e != hipSuccess)
+            return hip_fail(e);
+    }
+    return WSG_OK;
+}
+
+// ------------------------------------------------------------------- w4 --
+
+struct W4Plan {
+    W4Cfg cfg;
+    int S;
+    int kbs;
+    int tile_rtiles;
+};
+
+W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
+    const int64_t kb = K / 128;
+    const int64_t n_rtiles = cdiv(N, 16);
+    W4Plan p;
+    p.cfg = W4Cfg{2, use_nt()};
+    // LDS holds M rows of the slice: M * kbs * 256 bytes <= 32 KiB.
+    const int64_t max_kbs = std::max<int64_t>(4, (32 * 1024 / (256 * std::max<int64_t>(1, M))) / 4 * 4);
+    int S;
+    if (splits > 0) {
+        S = splits;
+    } else {
+        S = (int)std::max<int64_t>(1, cdiv(kb, max_kbs));
+        // underfilled: split k in whole 4-block quads
+        while (n_rtiles * S < kWantUnits / 2 && (int64_t)(S + 1) * 4 <= kb)
+            ++S;
+    }
+    if (splits <= 0) {
+        // never leave a slice empty (slices are whole 4-block quads)
+        while (S > 1 && (int64_t)(S - 1) * (cdiv(cdiv(kb, S), 4) * 4) >= kb)
+            --S;
+    }
+    p.S = S;
+    p.kbs = S > 1 ? (int)(cdiv(cdiv(kb, S), 4) * 4) : (int)kb;
+    const int64_t tile_bytes = 16 * (int64_t)p.kbs * 64;  // 16 rows x kbs blocks x 64 B
+    int64_t tt = std::max<int64_t>(1, (kUnitBytes / 2) / std::max<int64_t>(1, tile_bytes));
+    while (tt > 1 && cdiv(n_rtiles, tt) * S < kWantUnits)
+        tt = tt / 2;
+    p.tile_rtiles = (int)tt;
+    if (tt < 2)
+        p.cfg.R = 1;
+    return p;
+}
+
+W4Lin make_w4(const void *Wp, const void *Sp, const void *x, float *y, float *part, int64_t M, int64_t N,
+              int64_t K, const W4Plan &p) {
+    W4Lin L{};
+    L.Wp = static_cast<const u32x4 *>(Wp);
+    L.Sp = static_cast<const u32x2 *>(Sp);
+    L.x = static_cast<const u32x4 *>(x);
+    L.y = y;
+    L.part = part;
+    L.N = N;
+    L.K = (int32_t)K;
+    L.M = (int32_t)M;
+    L.kb = (int32_t)(K / 128);
+    L.kq = (int32_t)cdiv(L.kb, 4);
+    L.S = p.S;
+    L.kbs = p.kbs;
+    L.tile_rtiles = p.tile_rtiles;
+    L.n_tiles = (int32_t)cdiv(cdiv(N, 16), p.tile_rtiles);
+    return L;
+}
+
+wsg_status check_w4_args(const void *Wp, const void *Sp, const void *x, const float *y, int64_t M, int64_t N,
+                         int64_t K, int64_t group, int32_t splits) {
+    if (M < 0 || N < 0 || K < 0)
+        return WSG_ERR_SHAPE;
+    if (group != 128)
+        return WSG_ERR_UNSUPPORTED;
+    if (K % 128)
+        return WSG_ERR_SHAPE;
+    if (M < 1 || M > kMaxM)
+        return M == 0 ? WSG_ERR_SHAPE : WSG_ERR_UNSUPPORTED;
+    if (N > (int64_t)INT32_MAX * 16 || K > (1LL << 24))
+        return WSG_ERR_UNSUPPORTED;
+    if (N == 0)
+        return WSG_OK;
+    if (!y)
+        return WSG_ERR_NULL;
+    if (!aligned(y, 4))
+        return WSG_ERR_ALIGN;
+    if (K == 0)
+        return WSG_OK;
+    if (!Wp || !Sp || !x)
+        return WSG_ERR_NULL;
+    if (!aligned(Wp, 16) || !aligned(Sp, 16) || !aligned(x, 16))
+        return WSG_ERR_ALIGN;
+    const int64_t kb = K / 128;
+    if (splits < 0 || splits > kb)
+        return WSG_ERR_SHAPE;
+    if (splits > 1) {
+        const int64_t kbs = cdiv(cdiv(kb, splits), 4) * 4;
+        if ((int64_t)(splits - 1) * kbs >= kb)  // an empty slice
+            return WSG_ERR_SHAPE;
+        if ((int64_t)M * kbs * 256 > 48 * 1024)
+            return WSG_ERR_SHAPE;
+    } else if (splits == 1 && (int64_t)M * kb * 256 > 48 * 1024) {
+        return WSG_ERR_SHAPE;
+    }
+    return WSG_OK;
+}
+
+size_t w4_ws_bytes(const W4Plan &p, int64_t M, int64_t N) {
+    return p.S > 1 ? (size_t)p.S * (size_t)M * (size_t)N * 4 : 0;
+}
+
+wsg_status enqueue_w4(const W4Lin &L, const W4Cfg &cfg, hipStream_t s) {
+    hipError_t e = launch_w4(L, cfg, s);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    if (L.S > 1) {
+        e = launch_w4_reduce(L, s);
+        if (e != hipSuccess)
+            return hip_fail(e);
+    }
+    return WSG_OK;
+}
+
+template <typename F>
+wsg_status guarded(F &&f) {
+    try {
+        return f();
+    } catch (const std::bad_alloc &) {
+        return WSG_ERR_NOMEM;
+    } catch (...) {
+        return WSG_ERR_STATE;
+    }
+}
+
+}  // namespace
+
+// ================================================================ C ABI ==
+
+extern "C" {
+
+const char *wsg_status_string(wsg_status s) {
+    switch (s) {
+    case WSG_OK: return "ok";
+    case WSG_ERR_NULL: return "a required pointer is NULL";
+    case WSG_ERR_SHAPE: return "invalid or inconsistent shape";
+    case WSG_ERR_ALIGN: return "pointer not aligned";
+    case WSG_ERR_UNSUPPORTED: return "unsupported request";
+    case WSG_ERR_WORKSPACE: return "workspace missing or too small";
+    case WSG_ERR_HIP: return "HIP runtime error";
+    case WSG_ERR_NOMEM: return "out of memory";
+    case WSG_ERR_STATE: return "invalid plan state";
+    default: return "unknown status";
+    }
+}
+
+int32_t wsg_last_hip_error(void) { return g_last_hip; }
+
+const char *wsg_build_info(void) { return "wsgemv for gfx950"; }
+
+int32_t wsg_plan_splits(int32_t kind, int64_t M, int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0)
+        return 1;
+    if (kind == kF16 || kind == kW8A8) {
+        if (K % elem_per_vec(kind))
+            return 1;
+        return plan_dense(kind, N, K, 0).S;
+    }
+    if (kind == kW4A16) {
+        if (K % 128 || M < 1)
+            return 1;
+        return plan_w4(M, N, K, 0).S;
+    }
+    return 1;
+}
+
+size_t wsg_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K, int32_t splits) {
+    if (N <= 0 || K <= 0 || splits < 0)
+        return 0;
+    if (kind == kF16 || kind == kW8A8) {
+        if (K % elem_per_vec(kind))
+            return 0;
+        return dense_ws_bytes(plan_dense(kind, N, K, splits), N);
+    }
+    if (kind == kW4A16) {
+        if (K % 128 || M < 1)
+            return 0;
+        return w4_ws_bytes(plan_w4(M, N, K, splits), M, N);
+    }
+    return 0;
+}
+
+wsg_status gemv_f16(const void *W, const void *x, float *y, int64_t N, int64_t K, int32_t splits, void *ws,
+                    size_t ws_bytes, wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_dense_args(kF16, W, x, y, N, K, splits);
+        if (st != WSG_OK || N == 0)
+            return st;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (K == 0) {
+            hipError_t e = launch_zero_f32(y, N, s);
+            return e == hipSuccess ? WSG_OK : hip_fail(e);
+        }
+        DensePlan p = plan_dense(kF16, N, K, splits);
+        st = check_ws(ws, ws_bytes, dense_ws_bytes(p, N));
+        if (st != WSG_OK)
+            return st;
+        DenseLin L = make_dense(kF16, W, x, y, ws, nullptr, nullptr, nullptr, N, K, p);
+        p.cfg.tail = dense_needs_tail(L, p.cfg.CH);
+        return enqueue_dense(kF16, L, p.cfg, s);
+    });
+}
+
+wsg_status gemv_w8a8(const int8_t *Wq, const float *w_scale, const int8_t *xq, const float *x_scale, float *y,
+                     int32_t *acc_out, int64_t N, int64_t K, int32_t splits, void *ws, size_t ws_bytes,
+                     wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_dense_args(kW8A8, Wq, xq, y, N, K, splits);
+        if (st != WSG_OK || N == 0)
+            return st;
+        if (acc_out && !aligned(acc_out, 4))
+            return WSG_ERR_ALIGN;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (K == 0) {
+            hipError_t e = launch_zero_f32(y, N, s);
+            if (e == hipSuccess && acc_out)
+                e = launch_zero_f32(reinterpret_cast<float *>(acc_out), N, s);
+            return e == hipSuccess ? WSG_OK : hip_fail(e);
+        }
+        if (!w_scale || !x_scale)
+            return WSG_ERR_NULL;
+        if (!aligned(w_scale, 4) || !aligned(x_scale, 4))
+            return WSG_ERR_ALIGN;
+        DensePlan p = plan_dense(kW8A8, N, K, splits);
+        st = check_ws(ws, ws_bytes, dense_ws_bytes(p, N));
+        if (st != WSG_OK)
+            return st;
+        DenseLin L = make_dense(kW8A8, Wq, xq, y, ws, w_scale, x_scale, acc_out, N, K, p);
+        p.cfg.tail = dense_needs_tail(L, p.cfg.CH);
+        return enqueue_dense(kW8A8, L, p.cfg, s);
+    });
+}
+
+size_t wsg_w4_packed_weight_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || K % 128)
+        return 0;
+    return (size_t)cdiv(N, 16) * 16 * (size_t)(K / 2);
+}
+
+size_t wsg_w4_packed_scale_bytes(int64_t N, int64_t K, int64_t group) {
+    if (N <= 0 || K <= 0 || group != 128 || K % 128)
+        return 0;
+    return (size_t)cdiv(N, 16) * 16 * (size_t)cdiv(K / 128, 4) * 4 * 2;
+}
+
+wsg_status wsg_pack_w4(const uint32_t *Wc, const void *s4, void *Wp, void *Sp, int64_t N, int64_t K,
+                       int64_t group, wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        if (N < 0 || K < 0)
+            return WSG_ERR_SHAPE;
+        if (group != 128)
+            return WSG_ERR_UNSUPPORTED;
+        if (K % 128)
+            return WSG_ERR_SHAPE;
+        if (K > (1LL << 24) || N > (int64_t)INT32_MAX * 16)
+            return WSG_ERR_UNSUPPORTED;
+        if (N == 0 || K == 0)
+            return WSG_OK;
+        if (!Wc || !s4 || !Wp || !Sp)
+            return WSG_ERR_NULL;
+        if (!aligned(Wc, 4) || !aligned(s4, 2) || !aligned(Wp, 16) || !aligned(Sp, 16))
+            return WSG_ERR_ALIGN;
+        hipError_t e = launch_pack_w4(Wc, static_cast<const uint16_t *>(s4), static_cast<u32x4 *>(Wp),
+                                      static_cast<u32x2 *>(Sp), N, (int32_t)K, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? WSG_OK : hip_fail(e);
+    });
+}
+
+wsg_status gemv_w4a16(const void *Wp, const void *Sp, const void *x, float *y, int64_t M, int64_t N, int64_t K,
+                      int64_t group, int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_w4_args(Wp, Sp, x, y, M, N, K, group, splits);
+        if (st != WSG_OK || N == 0)
+            return st;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (K == 0) {
+            hipError_t e = launch_zero_f32(y, M * N, s);
+            return e == hipSuccess ? WSG_OK : hip_fail(e);
+        }
+        W4Plan p = plan_w4(M, N, K, splits);
+        st = check_ws(ws, ws_bytes, w4_ws_bytes(p, M, N));
+        if (st != WSG_OK)
+            return st;
+        W4Lin L = make_w4(Wp, Sp, x, y, static_cast<float *>(ws), M, N, K, p);
+        return enqueue_w4(L, p.cfg, s);
+    });
+}
+
+int32_t wsg_read_probe_grid(size_t bytes) {
+    (void)bytes;
+    return 2048;  // 8 workgroups per compute unit on 256 CUs
+}
+
+wsg_status wsg_read_probe(const void *buf, size_t bytes, float *out, int32_t grid, wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        if (bytes % 16 || grid < 0)
+            return WSG_ERR_SHAPE;
+        if (!buf || !out)
+            return WSG_ERR_NULL;
+        if (!aligned(buf, 16) || !aligned(out, 4))
+            return WSG_ERR_ALIGN;
+        const int g = grid > 0 ? grid : wsg_read_probe_grid(bytes);
+        hipError_t e = launch_read_probe(static_cast<const u32x4 *>(buf), (int64_t)(bytes / 16), out, g,
+                                         static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? WSG_OK : hip_fail(e);
+    });
+}
+
+}  // extern "C"
+
+// ========================================================== decode step ==
+
+struct wsg_step {
+    int32_t mode = 0;
+    bool use_graph = true;
+    hipStream_t cap = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    void *dev = nullptr;  // one device allocation: partials, descriptor and unit tables
+
+    struct Op {
+        enum Type { kDense, kDenseGroup, kW4, kW4Group, kZero } type;
+        int kind = 0;
+        DenseLin d{};
+        DenseCfg dc{};
+        W4Lin w{};
+        W4Cfg wc{};
+        const void *lins = nullptr;   // device tables for grouped ops
+        const Unit *units = nullptr;
+        int n_units = 0;
+        int lds = 0;
+        int max_m = 1;
+        float *zero_p = nullptr;
+        int64_t zero_n = 0;
+    };
+    std::vector<Op> ops;
+    int32_t launches = 0;
+    int64_t units = 0;
+};
+
+namespace {
+
+wsg_status validate_linear(const wsg_linear &l) {
+    switch (l.kind) {
+    case kF16: {
+        if (l.M != 1)
+            return WSG_ERR_UNSUPPORTED;
+        return check_dense_args(kF16, l.W, l.x, l.y, l.N, l.K, l.splits);
+    }
+    case kW8A8: {
+        if (l.M != 1)
+            return WSG_ERR_UNSUPPORTED;
+        wsg_status st = check_dense_args(kW8A8, l.W, l.x, l.y, l.N, l.K, l.splits);
+        if (st != WSG_OK || l.N == 0 || l.K == 0)
+            return st;
+        if (!l.scale || !l.x_scale)
+            return WSG_ERR_NULL;
+        if (!aligned(l.scale, 4) || !aligned(l.x_scale, 4) || (l.acc_out && !aligned(l.acc_out, 4)))
+            return WSG_ERR_ALIGN;
+        return WSG_OK;
+    }
+    case kW4A16:
+        return check_w4_args(l.W, l.scale, l.x, l.y, l.M, l.N, l.K, l.group, l.splits);
+    default:
+        return WSG_ERR_UNSUPPORTED;
+    }
+}
+
+hipError_t run_ops(const wsg_step *st, hipStream_t s) {
+    for (const auto &op : st->ops) {
+        hipError_t e = hipSuccess;
+        switch (op.type) {
+        case wsg_step::Op::kDense:
+            e = launch_dense(op.kind, op.d, op.dc, s);
+            if (e == hipSuccess && op.d.S > 1)
+                e = launch_dense_reduce(op.kind, op.d, s);
+            break;
+        case wsg_step::Op::kDenseGroup:
+            e = launch_dense_grouped(op.kind, static_cast<const DenseLin *>(op.lins), op.units, op.n_units, op.lds,
+                                     op.dc, s);
+            break;
+        case wsg_step::Op::kW4:
+            e = launch_w4(op.w, op.wc, s);
+            if (e == hipSuccess && op.w.S > 1)
+                e = launch_w4_reduce(op.w, s);
+            break;
+        case wsg_step::Op::kW4Group:
+            e = launch_w4_grouped(static_cast<const W4Lin *>(op.lins), op.units, op.n_units, op.lds, op.max_m,
+                                  op.wc, s);
+            break;
+        case wsg_step::Op::kZero:
+            e = launch_zero_f32(op.zero_p, op.zero_n, s);
+            break;
+        }
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+void free_step(wsg_step *st) {
+    if (!st)
+        return;
+    if (st->exec)
+        (void)hipGraphExecDestroy(st->exec);
+    if (st->graph)
+        (void)hipGraphDestroy(st->graph);
+    if (st->cap)
+        (void)hipStreamDestroy(st->cap);
+    if (st->dev)
+        (void)hipFree(st->dev);
+    delete st;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t mode, wsg_stream_t stream,
+                                  wsg_step **out) {
+    return guarded([&]() -> wsg_status {
+        if (!out)
+            return WSG_ERR_NULL;
+        *out = nullptr;
+        if (n < 0)
+            return WSG_ERR_SHAPE;
+        if (n > 0 && !linears)
+            return WSG_ERR_NULL;
+        const int base_mode = mode & 0xFF;
+        if (base_mode != WSG_STEP_ORDERED && base_mode != WSG_STEP_GROUPED)
+            return WSG_ERR_UNSUPPORTED;
+        if (mode & ~(0xFF | WSG_STEP_EAGER))
+            return WSG_ERR_UNSUPPORTED;
+        for (int32_t i = 0; i < n; ++i) {
+            wsg_status v = validate_linear(linears[i]);
+            if (v != WSG_OK)
+                return v;
+            if (base_mode == WSG_STEP_GROUPED && linears[i].splits > 1)
+                return WSG_ERR_UNSUPPORTED;
+        }
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        wsg_step *st = new wsg_step();
+        st->mode = mode;
+        st->use_graph = !(mode & WSG_STEP_EAGER);
+
+        // Host-side plan: ops, plus the byte layout of the device block.
+        std::vector<DenseLin> dl[2];           // grouped dense linears per kind (F16, W8A8)
+        std::vector<Unit> du[2];
+        int dlds[2] = {0, 0};
+        bool dtail[2] = {false, false};
+        std::vector<W4Lin> wl[2];              // grouped W4 linears: [0] M == 1, [1] M > 1
+        std::vector<Unit> wu[2];
+        int wlds[2] = {0, 0}, wmaxm[2] = {1, 1};
+        size_t part_bytes = 0;
+        const DenseCfg gcfg{4, 2, use_nt(), false};
+
+        for (int32_t i = 0; i < n; ++i) {
+            const wsg_linear &l = linears[i];
+            if (l.N == 0)
+                continue;
+            if (l.K == 0) {
+                wsg_step::Op z{};
+                z.type = wsg_step::Op::kZero;
+                z.zero_p = l.y;
+                z.zero_n = (int64_t)l.M * l.N;
+                st->ops.push_back(z);
+                if (l.kind == kW8A8 && l.acc_out) {
+                    z.zero_p = reinterpret_cast<float *>(l.acc_out);
+                    z.zero_n = l.N;
+                    st->ops.push_back(z);
+                }
+                continue;
+            }
+            if (l.kind == kF16 || l.kind == kW8A8) {
+                const int ki = l.kind == kF16 ? 0 : 1;
+                if (base_mode == WSG_STEP_ORDERED) {
+                    DensePlan p = plan_dense(l.kind, l.N, l.K, l.splits);
+                    part_bytes = std::max(part_bytes, dense_ws_bytes(p, l.N));
+                    wsg_step::Op o{};
+                    o.type = wsg_step::Op::kDense;
+                    o.kind = l.kind;
+                    o.dc = p.cfg;
+                    o.d = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale), l.x_scale,
+                                     l.acc_out, l.N, l.K, p);
+                    o.dc.tail = dense_needs_tail(o.d, o.dc.CH);
+                    st->ops.push_back(o);
+                } else {
+                    DensePlan p{};
+                    p.cfg = gcfg;
+                    p.S = 1;
+                    p.kvs = (int)(l.K / elem_per_vec(l.kind));
+                    if (p.kvs > kMaxSliceVec) {
+                        free_step(st);
+                        return WSG_ERR_UNSUPPORTED;
+                    }
+                    p.tile_rows = dense_tile_rows((int64_t)p.kvs * 16, gcfg.R);
+                    DenseLin L = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale),
+                                            l.x_scale, l.acc_out, l.N, l.K, p);
+                    const int li = (int)dl[ki].size();
+                    dl[ki].push_back(L);
+                    for (int t = 0; t < L.n_tiles; ++t)
+                        du[ki].push_back(Unit{li, t, 0, 0});
+                    dlds[ki] = std::max(dlds[ki], dense_lds_bytes(L, gcfg.CH));
+                    dtail[ki] = dtail[ki] || dense_needs_tail(L, gcfg.CH);
+                }
+            } else {
+                if (base_mode == WSG_STEP_ORDERED) {
+                    W4Plan p = plan_w4(l.M, l.N, l.K, l.splits);
+                    part_bytes = std::max(part_bytes, w4_ws_bytes(p, l.M, l.N));
+                    wsg_step::Op o{};
+                    o.type = wsg_step::Op::kW4;
+                    o.wc = p.cfg;
+                    o.w = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
+                    st->ops.push_back(o);
+                } else {
+                    W4Plan p = plan_w4(l.M, l.N, l.K, 1);
+                    p.S = 1;
+                    p.kbs = (int)(l.K / 128);
+                    const int64_t tile_bytes = 16 * (int64_t)p.kbs * 64;
+                    p.tile_rtiles = (int)std::max<int64_t>(2, (kUnitBytes / 2) / std::max<int64_t>(1, tile_bytes));
+                    p.cfg.R = 2;
+                    W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
+                    if (w4_lds_bytes(L) > 48 * 1024) {
+                        free_step(st);
+                        return WSG_ERR_UNSUPPORTED;
+                    }
+                    const int gi = l.M > 1 ? 1 : 0;
+                    const int li = (int)wl[gi].size();
+                    wl[gi].push_back(L);
+                    for (int t = 0; t < L.n_tiles; ++t)
+                        wu[gi].push_back(Unit{li, t, 0, 0});
+                    wlds[gi] = std::max(wlds[gi], w4_lds_bytes(L));
+                    wmaxm[gi] = std::max(wmaxm[gi], (int)l.M);
+                }
+            }
+        }
+
+        // Device block: [partials][dense tables x2][w4 tables x2]
+        size_t off = 0;
+        const size_t part_off = off;
+        off = align_up(off + part_bytes, 256);
+        size_t dl_off[2], du_off[2], wl_off[2], wu_off[2];
+        for (int k = 0; k < 2; ++k) {
+            dl_off[k] = off;
+            off = align_up(off + dl[k].size() * sizeof(DenseLin), 256);
+            du_off[k] = off;
+            off = align_up(off + du[k].size() * sizeof(Unit), 256);
+        }
+        for (int k = 0; k < 2; ++k) {
+            wl_off[k] = off;
+            off = align_up(off + wl[k].size() * sizeof(W4Lin), 256);
+            wu_off[k] = off;
+            off = align_up(off + wu[k].size() * sizeof(Unit), 256);
+        }
+        if (off > 0) {
+            hipError_t e = hipMalloc(&st->dev, off);
+            if (e != hipSuccess) {
+                st->dev = nullptr;
+                free_step(st);
+                return e == hipErrorOutOfMemory ? WSG_ERR_NOMEM : hip_fail(e);
+            }
+        }
+        char *base = static_cast<char *>(st->dev);
+        std::vector<char> host(off);
+        auto put = [&](size_t o, const void *src, size_t bytes) {
+            if (bytes)
+                std::memcpy(host.data() + o, src, bytes);
+        };
+        for (int k = 0; k < 2; ++k) {
+            put(dl_off[k], dl[k].data(), dl[k].size() * sizeof(DenseLin));
+            put(du_off[k], du[k].data(), du[k].size() * sizeof(Unit));
+            put(wl_off[k], wl[k].data(), wl[k].size() * sizeof(W4Lin));
+            put(wu_off[k], wu[k].data(), wu[k].size() * sizeof(Unit));
+        }
+        // partials of ORDERED linears share one buffer (the ops run in order)
+        for (auto &op : st->ops) {
+            if (op.type == wsg_step::Op::kDense && op.d.S > 1)
+                op.d.part = base + part_off;
+            if (op.type == wsg_step::Op::kW4 && op.w.S > 1)
+                op.w.part = reinterpret_cast<float *>(base + part_off);
+        }
+        for (int k = 0; k < 2; ++k) {
+            if (!du[k].empty()) {
+                wsg_step::Op o{};
+                o.type = wsg_step::Op::kDenseGroup;
+                o.kind = k == 0 ? kF16 : kW8A8;
+                o.dc = gcfg;
+                o.dc.tail = dtail[k];
+                o.lins = base + dl_off[k];
+                o.units = reinterpret_cast<const Unit *>(base + du_off[k]);
+                o.n_units = (int)du[k].size();
+                o.lds = dlds[k];
+                st->ops.push_back(o);
+            }
+            if (!wu[k].empty()) {
+                wsg_step::Op o{};
+                o.type = wsg_step::Op::kW4Group;
+                o.wc = W4Cfg{2, use_nt()};
+                o.lins = base + wl_off[k];
+                o.units = reinterpret_cast<const Unit *>(base + wu_off[k]);
+                o.n_units = (int)wu[k].size();
+                o.lds = wlds[k];
+                o.max_m = wmaxm[k];
+                st->ops.push_back(o);
+            }
+        }
+        if (off > 0) {
+            hipError_t e = hipMemcpyAsync(st->dev, host.data(), off, hipMemcpyHostToDevice, s);
+            if (e == hipSuccess)
+                e = hipStreamSynchronize(s);
+            if (e != hipSuccess) {
+                free_step(st);
+                return hip_fail(e);
+            }
+        }
+        for (const auto &op : st->ops) {
+            st->launches += 1;
+            if (op.type == wsg_step::Op::kDense) {
+                st->units += (int64_t)op.d.n_tiles * op.d.S;
+                st->launches += op.d.S > 1;
+            } else if (op.type == wsg_step::Op::kW4) {
+                st->units += (int64_t)op.w.n_tiles * op.w.S;
+                st->launches += op.w.S > 1;
+            } else if (op.type == wsg_step::Op::kDenseGroup || op.type == wsg_step::Op::kW4Group) {
+                st->units += op.n_units;
+            }
+        }
+        if (st->use_graph && !st->ops.empty()) {
+            hipError_t e = hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking);
+            if (e == hipSuccess)
+                e = hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal);
+            if (e == hipSuccess) {
+                hipError_t le = run_ops(st, st->cap);
+                e = hipStreamEndCapture(st->cap, &st->graph);
+                if (le != hipSuccess)
+                    e = le;
+            }
+            if (e == hipSuccess)
+                e = hipGraphInstantiate(&st->exec, st->graph, nullptr, nullptr, 0);
+            if (e != hipSuccess) {
+                free_step(st);
+                return hip_fail(e);
+            }
+        }
+        *out = st;
+        return WSG_OK;
+    });
+}
+
+wsg_status decode_step_linears(wsg_step *step, wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        if (!step)
+            return WSG_ERR_STATE;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hipError_t e = hipSuccess;
+        if (step->exec)
+            e = hipGraphLaunch(step->exec, s);
+        else
+            e = run_ops(step, s);
+        return e == hipSuccess ? WSG_OK : hip_fail(e);
+    });
+}
+
+wsg_status wsg_decode_step_destroy(wsg_step *step) {
+    return guarded([&]() -> wsg_status {
+        if (!step)
+            return WSG_ERR_STATE;
+        free_step(step);
+        return WSG_OK;
+    });
+}
+
+wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t *units) {
+    if (!step)
+        return WSG_ERR_STATE;
+    if (launches)
+        *launches = step->launches;
+    if (units)
+        *units = step->units;
+    return WSG_OK;
+}
+
+}  // extern "C"

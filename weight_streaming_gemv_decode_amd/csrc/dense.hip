@@ -1,0 +1,401 @@
+// Row-major weight streaming for M = 1: fp16 weights (fp32 accumulate via
+// v_dot2_f32_f16) and int8 weights x int8 activations (exact int32 via
+// v_dot4_i32_i8), the on-device split-K reduce, and the HBM read probe.
+//
+// The product is the decode-step vector-matrix product of the MiniCPM-V 4.6
+// on Orange Pi AIPro (Ascend 310B) post (baseline paragraph: M = 1; closing
+// paragraph: the step is bound by streaming the weights from memory).  The
+// int8 form is the W8A8 product of the vLLM Arm CPU optimisation post (INT8
+// W8A8 section).  The split-K partials and their reduce follow the same
+// MiniCPM-V post, second change (the lm_head cut into slices whose results
+// are reduced; here on the device, in fixed slice order).
+//
+// Mapping onto gfx950.  A workgroup is 4 waves and owns one work unit: a
+// tile of rows and one k-slice.  Each lane streams 16-byte vectors, lane l
+// taking vectors l, l+64, ... of a row, so every wave-wide load instruction
+// reads 1 KiB of contiguous weights.  A wave step covers R rows x CH vectors
+// per lane; the next step's loads are issued before the current step is
+// consumed (two register buffers), so each lane keeps up to 2*R*CH 16-byte
+// loads in flight.  The activation slice is staged once per unit in LDS
+// (read with ds_read_b128, shared by the R rows of a step).  Row sums are
+// reduced across the wave with a halving exchange (R values per lane become
+// one row per 64/R lanes in log2(64) shuffle stages), then written as y, or
+// as a partial that a second small kernel adds in slice order.
+#include "wsg_common.hpp"
+
+namespace wsg {
+namespace {
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <int KIND>
+struct DenseOps;
+
+template <>
+struct DenseOps<kF16> {
+    using Acc = float;
+    __device__ static __forceinline__ float dot(u32x4 w, u32x4 x, float a) {
+        a = __builtin_amdgcn_fdot2(as_h2(w.x), as_h2(x.x), a, false);
+        a = __builtin_amdgcn_fdot2(as_h2(w.y), as_h2(x.y), a, false);
+        a = __builtin_amdgcn_fdot2(as_h2(w.z), as_h2(x.z), a, false);
+        a = __builtin_amdgcn_fdot2(as_h2(w.w), as_h2(x.w), a, false);
+        return a;
+    }
+};
+
+template <>
+struct DenseOps<kW8A8> {
+    using Acc = int32_t;
+    __device__ static __forceinline__ int32_t dot(u32x4 w, u32x4 x, int32_t a) {
+        a = __builtin_amdgcn_sdot4((int)w.x, (int)x.x, a, false);
+        a = __builtin_amdgcn_sdot4((int)w.y, (int)x.y, a, false);
+        a = __builtin_amdgcn_sdot4((int)w.z, (int)x.z, a, false);
+        a = __builtin_amdgcn_sdot4((int)w.w, (int)x.w, a, false);
+        return a;
+    }
+};
+
+// Sum R per-lane values over the 64 lanes of a wave.  Stage o (o = 32, 16,
+// ...) pairs lane l with l^o: the lane with bit o set keeps the upper half
+// of its remaining values and receives its partner's upper half, the other
+// keeps the lower half; after log2(R) stages each lane carries one value of
+// row lane / (64/R), and plain xor-butterflies finish the sum.  Lane
+// r * (64/R) ends with the total of row r.
+template <int R, typename T>
+__device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
+    if constexpr (R >= 8) {
+        const bool up = lane & 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            T keep = up ? v[i + 4] : v[i];
+            T send = up ? v[i] : v[i + 4];
+            v[i] = keep + __shfl_xor(send, 32);
+        }
+    }
+    if constexpr (R >= 4) {
+        constexpr int o = R >= 8 ? 16 : 32;
+        const bool up = lane & o;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            T keep = up ? v[i + 2] : v[i];
+            T send = up ? v[i] : v[i + 2];
+            v[i] = keep + __shfl_xor(send, o);
+        }
+    }
+    if constexpr (R >= 2) {
+        constexpr int o = R >= 8 ? 8 : (R >= 4 ? 16 : 32);
+        const bool up = lane & o;
+        T keep = up ? v[1] : v[0];
+        T send = up ? v[0] : v[1];
+        v[0] = keep + __shfl_xor(send, o);
+    }
+    T s = v[0];
+#pragma unroll
+    for (int o = 32 / R; o >= 1; o >>= 1)
+        s += __shfl_xor(s, o);
+    return s;
+}
+
+template <int KIND, typename Acc>
+__device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row, Acc v) {
+    if (L.S > 1) {
+        static_cast<Acc *>(L.part)[(int64_t)s * L.N + row] = v;
+    } else if constexpr (KIND == kF16) {
+        L.y[row] = v;
+    } else {
+        if (L.acc_out)
+            L.acc_out[row] = v;
+        L.y[row] = ((float)v * L.w_scale[row]) * L.x_scale[0];
+    }
+}
+
+template <int KIND, int R, int CH, bool NT, bool TAIL>
+__device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u32x4 *xs) {
+    using Ops = DenseOps<KIND>;
+    using Acc = typename Ops::Acc;
+    constexpr int CHUNK = kWave * CH;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+
+    const int kv0 = s * L.kvs;
+    const int nv = min(L.kvs, L.kvec - kv0);
+    const int nchunk = (nv + CHUNK - 1) / CHUNK;
+    const int64_t row0 = (int64_t)tile * L.tile_rows;
+    const int rows = (int)min((int64_t)L.tile_rows, L.N - row0);
+    const int64_t last_row = row0 + rows - 1;
+    const int ngroups = (rows + R - 1) / R;
+    const int mygroups = wave < ngroups ? (ngroups - 1 - wave) / kWavesPerBlock + 1 : 0;
+    const int nsteps = mygroups * nchunk;
+
+    auto load_step = [&](u32x4(&buf)[R][CH], int gi, int c) {
+        // Row pointers are wave-uniform (scalar base); only the lane offset
+        // lives in a vector register.
+        const int64_t rbase = row0 + (int64_t)(wave + gi * kWavesPerBlock) * R;
+        const int v0 = c * CHUNK;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x4 *p = L.W + (min(rbase + r, last_row) * L.kvec + kv0 + v0);
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                if constexpr (TAIL) {
+                    buf[r][j] = u32x4{0u, 0u, 0u, 0u};
+                    if (v0 + j * kWave + lane < nv)
+                        buf[r][j] = load_w<NT>(p + j * kWave + lane);
+                } else {
+                    buf[r][j] = load_w<NT>(p + j * kWave + lane);
+                }
+            }
+        }
+    };
+
+    Acc acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = 0;
+
+    auto consume = [&](const u32x4(&buf)[R][CH], int gi, int c) {
+        u32x4 xv[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            xv[j] = xs[c * CHUNK + j * kWave + lane];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                acc[r] = Ops::dot(buf[r][j], xv[j], acc[r]);
+        if (c == nchunk - 1) {
+            Acc v = reduce_rows<R>(acc, lane);
+            constexpr int span = kWave / R;
+            if ((lane & (span - 1)) == 0) {
+                const int64_t row = row0 + (int64_t)(wave + gi * kWavesPerBlock) * R + lane / span;
+                if (row <= last_row)
+                    store_row<KIND>(L, s, row, v);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[r] = 0;
+        }
+    };
+
+    u32x4 bufA[R][CH], bufB[R][CH];
+    // First weight loads go out before the activation staging and barrier.
+    if (nsteps > 0)
+        load_step(bufA, 0, 0);
+
+    const u32x4 *xg = L.x + kv0;
+    for (int i = tid; i < nchunk * CHUNK; i += kBlock)
+        xs[i] = i < nv ? xg[i] : u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    if (nsteps == 0)
+        return;
+    // Steps are (row group gi, chunk c) in order; a is the step in bufA.
+    int ga = 0, ca = 0;
+    auto next = [&](int &g, int &c) {
+        if (++c == nchunk) {
+            c = 0;
+            ++g;
+        }
+    };
+    int st = 0;
+    while (st + 2 < nsteps) {
+        int gb = ga, cb = ca;
+        next(gb, cb);
+        load_step(bufB, gb, cb);
+        consume(bufA, ga, ca);
+        int gn = gb, cn = cb;
+        next(gn, cn);
+        load_step(bufA, gn, cn);
+        consume(bufB, gb, cb);
+        ga = gn;
+        ca = cn;
+        st += 2;
+    }
+    if (st + 1 < nsteps) {
+        int gb = ga, cb = ca;
+        next(gb, cb);
+        load_step(bufB, gb, cb);
+        consume(bufA, ga, ca);
+        consume(bufB, gb, cb);
+    } else {
+        consume(bufA, ga, ca);
+    }
+}
+
+template <int KIND, int R, int CH, bool NT, bool TAIL>
+__global__ __launch_bounds__(kBlock) void dense_gemv_kernel(DenseLin L) {
+    extern __shared__ u32x4 xs_dyn[];
+    const int u = blockIdx.x;
+    dense_unit<KIND, R, CH, NT, TAIL>(L, u / L.S, u % L.S, xs_dyn);
+}
+
+template <int KIND, int R, int CH, bool NT, bool TAIL>
+__global__ __launch_bounds__(kBlock) void dense_grouped_kernel(const DenseLin *__restrict__ lins,
+                                                               const Unit *__restrict__ units) {
+    extern __shared__ u32x4 xs_dyn[];
+    const Unit u = units[blockIdx.x];
+    const DenseLin L = lins[u.lin];
+    dense_unit<KIND, R, CH, NT, TAIL>(L, u.tile, u.s, xs_dyn);
+}
+
+// y[n] = sum over slices s = 0..S-1, in that order, of part[s][n].
+template <int KIND>
+__global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
+    const int64_t n = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (n >= L.N)
+        return;
+    if constexpr (KIND == kF16) {
+        const float *p = static_cast<const float *>(L.part);
+        float a = p[n];
+        for (int s = 1; s < L.S; ++s)
+            a += p[(int64_t)s * L.N + n];
+        L.y[n] = a;
+    } else {
+        const int32_t *p = static_cast<const int32_t *>(L.part);
+        int32_t a = p[n];
+        for (int s = 1; s < L.S; ++s)
+            a += p[(int64_t)s * L.N + n];
+        if (L.acc_out)
+            L.acc_out[n] = a;
+        L.y[n] = ((float)a * L.w_scale[n]) * L.x_scale[0];
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void zero_f32_kernel(float *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < n)
+        p[i] = 0.0f;
+}
+
+// Read-only stream over buf: 8 loads in flight per lane per iteration; the
+// xor of everything read is folded per workgroup into out[blockIdx.x].
+__global__ __launch_bounds__(kBlock) void read_probe_kernel(const u32x4 *__restrict__ buf, int64_t nvec,
+                                                            float *out) {
+    constexpr int U = 8;
+    uint32_t acc = 0;
+    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
+    for (int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x; base < nvec; base += stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + (int64_t)u * kBlock;
+            v[u] = i < nvec ? buf[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (int o = 32; o >= 1; o >>= 1)
+        acc ^= __shfl_xor(acc, o);
+    __shared__ uint32_t red[kWavesPerBlock];
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        red[threadIdx.x / kWave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t a = 0;
+        for (int w = 0; w < kWavesPerBlock; ++w)
+            a ^= red[w];
+        out[blockIdx.x] = (float)(a & 0xFFFFu);
+    }
+}
+
+template <int KIND, int R, int CH, bool NT, bool TAIL>
+hipError_t launch_single(const DenseLin &L, hipStream_t s) {
+    const int units = L.n_tiles * L.S;
+    const int lds = dense_lds_bytes(L, CH);
+    hipLaunchKernelGGL((dense_gemv_kernel<KIND, R, CH, NT, TAIL>), dim3(units), dim3(kBlock), lds, s, L);
+    return hipGetLastError();
+}
+
+template <int KIND, int R, int CH, bool NT, bool TAIL>
+hipError_t launch_group(const DenseLin *lins, const Unit *units, int n_units, int lds, hipStream_t s) {
+    hipLaunchKernelGGL((dense_grouped_kernel<KIND, R, CH, NT, TAIL>), dim3(n_units), dim3(kBlock), lds, s, lins,
+                       units);
+    return hipGetLastError();
+}
+
+// The instantiated (R, CH) shapes.  The host launch table only asks for
+// these; anything else is rejected.
+template <int KIND, bool NT, bool TAIL>
+hipError_t dispatch_single(const DenseLin &L, const DenseCfg &c, hipStream_t s) {
+    if (c.CH == 2) {
+        if (c.R == 4) return launch_single<KIND, 4, 2, NT, TAIL>(L, s);
+        if (c.R == 2) return launch_single<KIND, 2, 2, NT, TAIL>(L, s);
+        if (c.R == 1) return launch_single<KIND, 1, 2, NT, TAIL>(L, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int KIND, bool NT, bool TAIL>
+hipError_t dispatch_group(const DenseLin *lins, const Unit *units, int n, int lds, const DenseCfg &c,
+                          hipStream_t s) {
+    if (c.CH == 2) {
+        if (c.R == 4) return launch_group<KIND, 4, 2, NT, TAIL>(lins, units, n, lds, s);
+        if (c.R == 2) return launch_group<KIND, 2, 2, NT, TAIL>(lins, units, n, lds, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int KIND>
+hipError_t single_kind(const DenseLin &L, const DenseCfg &c, hipStream_t s) {
+    if (c.nt)
+        return c.tail ? dispatch_single<KIND, true, true>(L, c, s) : dispatch_single<KIND, true, false>(L, c, s);
+    return c.tail ? dispatch_single<KIND, false, true>(L, c, s) : dispatch_single<KIND, false, false>(L, c, s);
+}
+
+template <int KIND>
+hipError_t group_kind(const DenseLin *lins, const Unit *units, int n, int lds, const DenseCfg &c, hipStream_t s) {
+    if (c.nt)
+        return c.tail ? dispatch_group<KIND, true, true>(lins, units, n, lds, c, s)
+                      : dispatch_group<KIND, true, false>(lins, units, n, lds, c, s);
+    return c.tail ? dispatch_group<KIND, false, true>(lins, units, n, lds, c, s)
+                  : dispatch_group<KIND, false, false>(lins, units, n, lds, c, s);
+}
+
+}  // namespace
+
+hipError_t launch_dense(int kind, const DenseLin &L, const DenseCfg &c, hipStream_t s) {
+    if (kind == kF16)
+        return single_kind<kF16>(L, c, s);
+    if (kind == kW8A8)
+        return single_kind<kW8A8>(L, c, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_dense_grouped(int kind, const DenseLin *lins, const Unit *units, int n_units, int lds_bytes,
+                                const DenseCfg &c, hipStream_t s) {
+    if (kind == kF16)
+        return group_kind<kF16>(lins, units, n_units, lds_bytes, c, s);
+    if (kind == kW8A8)
+        return group_kind<kW8A8>(lins, units, n_units, lds_bytes, c, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_dense_reduce(int kind, const DenseLin &L, hipStream_t s) {
+    const int grid = (int)((L.N + kBlock - 1) / kBlock);
+    if (kind == kF16)
+        hipLaunchKernelGGL(dense_reduce_kernel<kF16>, dim3(grid), dim3(kBlock), 0, s, L);
+    else
+        hipLaunchKernelGGL(dense_reduce_kernel<kW8A8>, dim3(grid), dim3(kBlock), 0, s, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s) {
+    if (n <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(kBlock), 0, s, buf, nvec, out);
+    return hipGetLastError();
+}
+
+}  // namespace wsg

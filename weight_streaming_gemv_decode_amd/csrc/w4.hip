@@ -1,0 +1,411 @@
+// INT4 weights x fp16 activations with the dequantisation fused into the
+// product, for the decode product (M = 1, VALU) and a speculative-verify
+// block (M = 2..8, MFMA), plus the load-time packer.
+//
+// Sources: MiniCPM-V 4.6 on Orange Pi AIPro (Ascend 310B) post, closing
+// paragraph (fused INT4 dequantisation is the next lever once the step is
+// bound by streaming weights); vLLM Arm CPU optimisation post, INT8 W4A8
+// section (4-bit weights cut memory traffic) and dense-weight prepacking
+// section (weights packed into the kernel's layout once at warm-up); EdgeFM
+// summary, section 2C (a drafted block of tokens verified by the base model
+// against the same weights).
+//
+// Weight value: w[n,k] = (q[n,k] - 8) * s[n, k/128], q in 0..15.
+//
+// Packed layout (one layout for both kernels).  Rows are cut into 16-row
+// tiles and k into 128-wide blocks (one scale group).  Tile (t, b) is 1 KiB:
+// lane l = r + 16 g (r = l % 16, g = l / 16) holds four 32-bit words; word i
+// carries the 8 weights k = 128 b + 32 i + 8 g + (0..7) of row 16 t + r.
+// Inside a word, weight j sits in 4-bit field (j >> 1) + 4 (j & 1), so that
+// masking with 0x000F000F (and 0x00F000F0, and the same after >> 8) yields
+// the fp16 pairs (j, j+1) = (0,1), (2,3), (4,5), (6,7) directly.  One wave
+// therefore reads a tile with one coalesced 16-byte load per lane, and word
+// i of lane l is exactly the B-operand fragment lane l supplies to the i-th
+// v_mfma_f32_16x16x32_f16 of the block (column n = l % 16, k = 8 g .. 8 g+7).
+//
+// Dequantisation per word, all exact in fp16: OR-ing a 4-bit field into the
+// mantissa of 1024.0 (0x6400) gives 1024 + q, minus 1032 gives q - 8; for
+// the fields shifted by 4, 1024 + 16 q times 1/16 minus 72 gives q - 8.  This
+// is the known integer-to-float magic-number conversion (the mantissa of a
+// float with a fixed exponent holds the integer).  The 32 weights of a lane
+// in one block are dotted with x in fp32 (v_dot2_f32_f16), then scaled by
+// the group's scale in fp32: the scale is never folded into fp16 weights.
+//
+// Scales are packed per (tile, 4 consecutive blocks, row): 4 fp16 in 8 bytes,
+// so a lane fetches the scales of a 4-block step with one 8-byte load.
+#include "wsg_common.hpp"
+
+namespace wsg {
+namespace {
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+// q - 8 for the 8 weights of a packed word, as the fp16 pairs (0,1) .. (6,7).
+__device__ __forceinline__ void unpack8(uint32_t w, f16x2 (&h)[4]) {
+    constexpr uint32_t kMagic = 0x64006400u;  // fp16 1024.0 in both halves
+    const uint32_t w8 = w >> 8;
+    const f16x2 a = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) | kMagic);   // 1024 + q0, 1024 + q1
+    const f16x2 b = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) | kMagic);   // 1024 + 16 q2, 1024 + 16 q3
+    const f16x2 c = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) | kMagic);  // q4, q5
+    const f16x2 d = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) | kMagic);  // 16 q6, 16 q7
+    const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const f16x2 bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    h[0] = a + bias;
+    h[1] = __builtin_elementwise_fma(b, sixteenth, bias16);
+    h[2] = c + bias;
+    h[3] = __builtin_elementwise_fma(d, sixteenth, bias16);
+}
+
+__device__ __forceinline__ float scale_of(u32x2 sc, int b) {
+    const uint32_t w = (b < 2) ? sc.x : sc.y;
+    const uint16_t h = (b & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xFFFFu);
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// One work unit: `tile_rtiles` 16-row tiles starting at unit `tile`, k-slice s.
+// MFMA = false: M = 1 on the VALU.  MFMA = true: M = 2..8 on the matrix cores.
+template <int R, bool NT, bool MFMA>
+__device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *xs) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int r16 = lane & 15, g = lane >> 4;
+
+    const int kb0 = s * L.kbs;                     // first block of the slice
+    const int nkb = min(L.kbs, L.kb - kb0);        // blocks in the slice
+    const int nquad = (nkb + 3) / 4;
+    const int nxv = nkb * 16;                      // 16-byte x vectors per row in the slice
+    const int64_t n_rtiles = (L.N + 15) / 16;
+    const int64_t rt0 = (int64_t)tile * L.tile_rtiles;
+    const int nrt = (int)min((int64_t)L.tile_rtiles, n_rtiles - rt0);
+    const int64_t last_rt = rt0 + nrt - 1;
+    const int ngroups = (nrt + R - 1) / R;
+    const int mygroups = wave < ngroups ? (ngroups - 1 - wave) / kWavesPerBlock + 1 : 0;
+    const int nsteps = mygroups * nquad;
+    const int M = MFMA ? L.M : 1;
+
+    struct Buf {
+        u32x4 w[R][4];
+        u32x2 sc[R];
+    };
+
+    auto load_step = [&](Buf &B, int gi, int c) {
+        const int64_t rtb = rt0 + (int64_t)(wave + gi * kWavesPerBlock) * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t rt = min(rtb + r, last_rt);
+            // wave-uniform tile pointers; the lane offset is the only vector part
+            const u32x4 *p = L.Wp + (rt * L.kb + kb0 + 4 * c) * kWave;
+            const u32x2 *q = L.Sp + (rt * L.kq + kb0 / 4 + c) * 16;
+            B.sc[r] = q[r16];
+            if (4 * c + 4 <= nkb) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    B.w[r][b] = load_w<NT>(p + b * kWave + lane);
+            } else {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    B.w[r][b] = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+                    if (4 * c + b < nkb)
+                        B.w[r][b] = load_w<NT>(p + b * kWave + lane);
+                }
+            }
+        }
+    };
+
+    float acc1[R];
+    f32x4 accm[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        acc1[r] = 0.0f;
+        accm[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    auto finish_group = [&](int gi) {
+        const int64_t rtb = rt0 + (int64_t)(wave + gi * kWavesPerBlock) * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t rt = rtb + r;
+            if constexpr (!MFMA) {
+                float v = acc1[r];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                const int64_t n = rt * 16 + r16;
+                if (lane < 16 && rt <= last_rt && n < L.N) {
+                    if (L.S > 1)
+                        L.part[(int64_t)s * L.N + n] = v;
+                    else
+                        L.y[n] = v;
+                }
+                acc1[r] = 0.0f;
+            } else {
+                // D layout of a 16x16 MFMA: lane l holds column l % 16 (here
+                // the output row n) and rows 4 (l / 16) + i (here m).
+                const int64_t n = rt * 16 + r16;
+                if (rt <= last_rt && n < L.N) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 4 * g + i;
+                        if (m < M) {
+                            if (L.S > 1)
+                                L.part[((int64_t)s * M + m) * L.N + n] = accm[r][i];
+                            else
+                                L.y[(int64_t)m * L.N + n] = accm[r][i];
+                        }
+                    }
+                }
+                accm[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+    };
+
+    auto consume = [&](const Buf &B, int gi, int c) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (4 * c + b >= nkb)
+                break;
+            const int xv0 = (4 * c + b) * 16 + g;  // x vector of word 0 of this lane in the block
+            if constexpr (!MFMA) {
+                u32x4 xv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xv[i] = xs[xv0 + 4 * i];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t words[4] = {B.w[r][b].x, B.w[r][b].y, B.w[r][b].z, B.w[r][b].w};
+                    float p = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        f16x2 h[4];
+                        unpack8(words[i], h);
+                        p = __builtin_amdgcn_fdot2(h[0], as_h2(xv[i].x), p, false);
+                        p = __builtin_amdgcn_fdot2(h[1], as_h2(xv[i].y), p, false);
+                        p = __builtin_amdgcn_fdot2(h[2], as_h2(xv[i].z), p, false);
+                        p = __builtin_amdgcn_fdot2(h[3], as_h2(xv[i].w), p, false);
+                    }
+                    acc1[r] += p * scale_of(B.sc[r], b);
+                }
+            } else {
+                // A operand: lane l supplies row m = l % 16 of X (zero for m >= M),
+                // k = 32 i + 8 g .. + 7 of the block.
+                f16x8 a[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                    if (r16 < M)
+                        v = xs[r16 * nxv + xv0 + 4 * i];
+                    a[i] = __builtin_bit_cast(f16x8, v);
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t words[4] = {B.w[r][b].x, B.w[r][b].y, B.w[r][b].z, B.w[r][b].w};
+                    f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        f16x2 h[4];
+                        unpack8(words[i], h);
+                        const u32x4 hb = {__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                                          __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
+                        const f16x8 bw = __builtin_bit_cast(f16x8, hb);
+                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bw, d, 0, 0, 0);
+                    }
+                    const float sc = scale_of(B.sc[r], b);
+                    accm[r] += d * sc;
+                }
+            }
+        }
+        if (c == nquad - 1)
+            finish_group(gi);
+    };
+
+    Buf bufA, bufB;
+    if (nsteps > 0)
+        load_step(bufA, 0, 0);
+
+    // Stage the activation slice of every row m < M: xs[m * nxv + v].
+    const int64_t xrow = (int64_t)L.K / 8;
+    for (int i = tid; i < M * nxv; i += kBlock) {
+        const int m = i / nxv, v = i - m * nxv;
+        xs[i] = L.x[m * xrow + (int64_t)kb0 * 16 + v];
+    }
+    __syncthreads();
+
+    if (nsteps == 0)
+        return;
+    int ga = 0, ca = 0;
+    auto next = [&](int &gg, int &cc) {
+        if (++cc == nquad) {
+            cc = 0;
+            ++gg;
+        }
+    };
+    int st = 0;
+    while (st + 2 < nsteps) {
+        int gb = ga, cb = ca;
+        next(gb, cb);
+        load_step(bufB, gb, cb);
+        consume(bufA, ga, ca);
+        int gn = gb, cn = cb;
+        next(gn, cn);
+        load_step(bufA, gn, cn);
+        consume(bufB, gb, cb);
+        ga = gn;
+        ca = cn;
+        st += 2;
+    }
+    if (st + 1 < nsteps) {
+        int gb = ga, cb = ca;
+        next(gb, cb);
+        load_step(bufB, gb, cb);
+        consume(bufA, ga, ca);
+        consume(bufB, gb, cb);
+    } else {
+        consume(bufA, ga, ca);
+    }
+}
+
+template <int R, bool NT, bool MFMA>
+__global__ __launch_bounds__(kBlock) void w4_gemv_kernel(W4Lin L) {
+    extern __shared__ u32x4 xs_dyn[];
+    const int u = blockIdx.x;
+    w4_unit<R, NT, MFMA>(L, u / L.S, u % L.S, xs_dyn);
+}
+
+template <int R, bool NT, bool MFMA>
+__global__ __launch_bounds__(kBlock) void w4_grouped_kernel(const W4Lin *__restrict__ lins,
+                                                            const Unit *__restrict__ units) {
+    extern __shared__ u32x4 xs_dyn[];
+    const Unit u = units[blockIdx.x];
+    const W4Lin L = lins[u.lin];
+    w4_unit<R, NT, MFMA>(L, u.tile, u.s, xs_dyn);
+}
+
+// y[m][n] = sum over slices s = 0..S-1, in that order, of part[s][m][n].
+__global__ __launch_bounds__(kBlock) void w4_reduce_kernel(W4Lin L) {
+    const int64_t total = (int64_t)L.M * L.N;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= total)
+        return;
+    float a = L.part[i];
+    for (int s = 1; s < L.S; ++s)
+        a += L.part[(int64_t)s * total + i];
+    L.y[i] = a;
+}
+
+// One thread per packed word: tile t, block b, lane l, word i.
+__global__ __launch_bounds__(kBlock) void pack_w4_kernel(const uint32_t *__restrict__ Wc,
+                                                         uint32_t *__restrict__ Wp, int64_t N, int32_t K) {
+    const int32_t kb = K / 128;
+    const int64_t n_rtiles = (N + 15) / 16;
+    const int64_t total = n_rtiles * kb * 256;  // 64 lanes x 4 words per tile
+    const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (idx >= total)
+        return;
+    const int i = (int)(idx & 3);
+    const int l = (int)((idx >> 2) & 63);
+    const int64_t tb = idx >> 8;             // tile index t * kb + b
+    const int64_t t = tb / kb;
+    const int b = (int)(tb - t * kb);
+    const int64_t n = t * 16 + (l & 15);
+    const int gq = l >> 4;
+    uint32_t out = 0x88888888u;              // padding rows: q = 8, weight 0
+    if (n < N) {
+        const uint32_t w = Wc[n * (K / 8) + (int64_t)b * 16 + 4 * i + gq];  // k = 128 b + 32 i + 8 g
+        out = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t q = (w >> (4 * j)) & 15u;
+            out |= q << (4 * ((j >> 1) + 4 * (j & 1)));
+        }
+    }
+    Wp[idx] = out;
+}
+
+// Scales: Sp[(t * kq + q) * 16 + r] holds s4[n = 16 t + r][4 q + (0..3)], zero past K or N.
+__global__ __launch_bounds__(kBlock) void pack_s4_kernel(const uint16_t *__restrict__ s4,
+                                                         uint16_t *__restrict__ Sp, int64_t N, int32_t K) {
+    const int32_t kb = K / 128, kq = (kb + 3) / 4;
+    const int64_t n_rtiles = (N + 15) / 16;
+    const int64_t total = n_rtiles * kq * 64;  // 16 rows x 4 scales per (tile, quad)
+    const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (idx >= total)
+        return;
+    const int j = (int)(idx & 3);
+    const int r = (int)((idx >> 2) & 15);
+    const int64_t tq = idx >> 6;
+    const int64_t t = tq / kq;
+    const int q = (int)(tq - t * kq);
+    const int64_t n = t * 16 + r;
+    const int b = 4 * q + j;
+    Sp[idx] = (n < N && b < kb) ? s4[n * kb + b] : (uint16_t)0;
+}
+
+template <int R, bool NT, bool MFMA>
+hipError_t launch_one(const W4Lin &L, hipStream_t s) {
+    const int units = L.n_tiles * L.S;
+    hipLaunchKernelGGL((w4_gemv_kernel<R, NT, MFMA>), dim3(units), dim3(kBlock), w4_lds_bytes(L), s, L);
+    return hipGetLastError();
+}
+
+template <int R, bool NT, bool MFMA>
+hipError_t launch_grp(const W4Lin *lins, const Unit *units, int n, int lds, hipStream_t s) {
+    hipLaunchKernelGGL((w4_grouped_kernel<R, NT, MFMA>), dim3(n), dim3(kBlock), lds, s, lins, units);
+    return hipGetLastError();
+}
+
+template <bool MFMA>
+hipError_t dispatch_one(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
+    if (c.R == 2) return c.nt ? launch_one<2, true, MFMA>(L, s) : launch_one<2, false, MFMA>(L, s);
+    if (c.R == 1) return c.nt ? launch_one<1, true, MFMA>(L, s) : launch_one<1, false, MFMA>(L, s);
+    return hipErrorInvalidValue;
+}
+
+template <bool MFMA>
+hipError_t dispatch_grp(const W4Lin *lins, const Unit *units, int n, int lds, const W4Cfg &c, hipStream_t s) {
+    if (c.R == 2) return c.nt ? launch_grp<2, true, MFMA>(lins, units, n, lds, s)
+                              : launch_grp<2, false, MFMA>(lins, units, n, lds, s);
+    if (c.R == 1) return c.nt ? launch_grp<1, true, MFMA>(lins, units, n, lds, s)
+                              : launch_grp<1, false, MFMA>(lins, units, n, lds, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_w4(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
+    return L.M > 1 ? dispatch_one<true>(L, c, s) : dispatch_one<false>(L, c, s);
+}
+
+hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes, int max_m,
+                             const W4Cfg &c, hipStream_t s) {
+    return max_m > 1 ? dispatch_grp<true>(lins, units, n_units, lds_bytes, c, s)
+                     : dispatch_grp<false>(lins, units, n_units, lds_bytes, c, s);
+}
+
+hipError_t launch_w4_reduce(const W4Lin &L, hipStream_t s) {
+    const int64_t total = (int64_t)L.M * L.N;
+    hipLaunchKernelGGL(w4_reduce_kernel, dim3((unsigned)((total + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, L);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_w4(const uint32_t *Wc, const uint16_t *s4, u32x4 *Wp, u32x2 *Sp, int64_t N, int32_t K,
+                          hipStream_t s) {
+    const int64_t n_rtiles = (N + 15) / 16;
+    const int32_t kb = K / 128, kq = (kb + 3) / 4;
+    const int64_t words = n_rtiles * kb * 256;
+    const int64_t scales = n_rtiles * kq * 64;
+    if (words > 0)
+        hipLaunchKernelGGL(pack_w4_kernel, dim3((unsigned)((words + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                           Wc, reinterpret_cast<uint32_t *>(Wp), N, K);
+    if (scales > 0)
+        hipLaunchKernelGGL(pack_s4_kernel, dim3((unsigned)((scales + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                           s4, reinterpret_cast<uint16_t *>(Sp), N, K);
+    return hipGetLastError();
+}
+
+}  // namespace wsg

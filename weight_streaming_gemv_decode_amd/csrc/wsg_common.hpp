@@ -1,0 +1,118 @@
+// Internal declarations shared by the wsgemv kernels and the host side of the
+// library: device descriptors of one linear, launch configurations and the
+// launcher functions each kernel file exports.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wsg {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kBlock = 256;        // 4 waves per workgroup for every streaming kernel
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum Kind : int32_t { kF16 = 0, kW8A8 = 1, kW4A16 = 2 };
+
+// Reinterpret a 32-bit word as two fp16.  Always pass a scalar copy: with
+// this toolchain, __builtin_bit_cast applied directly to an ext-vector
+// element expression (v.y, v.z, ...) lowers to element 0 for every element.
+__device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+
+// One row-major linear streamed 16 bytes per lane (fp16: 8 weights per
+// vector, int8: 16 weights per vector).
+struct DenseLin {
+    const u32x4 *W;        // [N][kvec]
+    const u32x4 *x;        // [kvec]
+    float *y;              // [N]
+    void *part;            // [S][N] fp32 (fp16) or int32 (int8) partial sums, S > 1
+    const float *w_scale;  // int8: [N]
+    const float *x_scale;  // int8: [1]
+    int32_t *acc_out;      // int8: optional [N]
+    int64_t N;
+    int32_t kvec;          // 16-byte vectors per row
+    int32_t S;             // k-slices
+    int32_t kvs;           // vectors per slice (the last slice may be shorter)
+    int32_t tile_rows;     // rows per work unit
+    int32_t n_tiles;       // ceil(N / tile_rows)
+    int32_t pad;
+};
+
+// One int4 linear in the packed tile layout (16 rows x 128 k per 1 KiB tile).
+struct W4Lin {
+    const u32x4 *Wp;       // [n_rtiles][kb][64 lanes] 16-byte words
+    const u32x2 *Sp;       // [n_rtiles][kq][16 rows] 4 fp16 scales (blocks 4q..4q+3)
+    const u32x4 *x;        // fp16 [M][K] as 16-byte vectors
+    float *y;              // [M][N]
+    float *part;           // [S][M][N], S > 1
+    int64_t N;
+    int32_t K;
+    int32_t M;
+    int32_t kb;            // 128-wide k-blocks per row (K / 128)
+    int32_t kq;            // ceil(kb / 4)
+    int32_t S;
+    int32_t kbs;           // k-blocks per slice, a multiple of 4 when S > 1
+    int32_t tile_rtiles;   // 16-row tiles per work unit
+    int32_t n_tiles;       // ceil(n_rtiles / tile_rtiles)
+};
+
+// One work unit of a grouped launch: linear `lin`, row tile `tile`, k-slice `s`.
+struct Unit {
+    int32_t lin;
+    int32_t tile;
+    int32_t s;
+    int32_t pad;
+};
+
+struct DenseCfg {
+    int R;        // rows per wave step
+    int CH;       // 16-byte vectors per lane per row per step
+    bool nt;      // non-temporal weight loads
+    bool tail;    // some k-slice is not a whole number of chunks (64 * CH vectors)
+};
+
+// True when a slice of this linear ends inside a chunk of 64 * CH vectors.
+inline bool dense_needs_tail(const DenseLin &L, int CH) {
+    const int chunk = kWave * CH;
+    const int last = L.kvec - (L.S - 1) * L.kvs;
+    return (L.kvs % chunk) != 0 || (last % chunk) != 0;
+}
+
+struct W4Cfg {
+    int R;        // 16-row tiles per wave step
+    bool nt;
+};
+
+// ----- launchers (each defined next to its kernels) -----
+hipError_t launch_dense(int kind, const DenseLin &L, const DenseCfg &c, hipStream_t s);
+hipError_t launch_dense_grouped(int kind, const DenseLin *lins, const Unit *units, int n_units,
+                                int lds_bytes, const DenseCfg &c, hipStream_t s);
+hipError_t launch_dense_reduce(int kind, const DenseLin &L, hipStream_t s);
+hipError_t launch_w4(const W4Lin &L, const W4Cfg &c, hipStream_t s);
+hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes,
+                             int max_m, const W4Cfg &c, hipStream_t s);
+hipError_t launch_w4_reduce(const W4Lin &L, hipStream_t s);
+hipError_t launch_pack_w4(const uint32_t *Wc, const uint16_t *s4, u32x4 *Wp, u32x2 *Sp,
+                          int64_t N, int32_t K, hipStream_t s);
+hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int grid, hipStream_t s);
+hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
+
+// LDS bytes a dense unit of this linear stages for x (whole slice, chunk-padded).
+inline int dense_lds_bytes(const DenseLin &L, int CH) {
+    int chunk = kWave * CH;
+    int nch = (L.kvs + chunk - 1) / chunk;
+    return nch * chunk * 16;
+}
+
+inline int w4_lds_bytes(const W4Lin &L) {
+    // x slice for all M rows: kbs blocks of 128 fp16 per row
+    return L.M * L.kbs * 128 * 2;
+}
+
+}  // namespace wsg

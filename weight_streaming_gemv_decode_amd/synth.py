@@ -113,3 +113,37 @@ def w4_words(workload: int, tensor: int, N: int, K: int) -> np.ndarray:
 def workload_tensors_f16(workload: int, N: int, K: int, w_id: int = 0, x_id: int = 1) -> Dict[str, np.ndarray]:
     return {"W": f16_normal(workload, w_id, (N, K), W_SIGMA),
             "x": f16_normal(workload, x_id, (K,), X_SIGMA)}
+
+
+def decode_step_f16(workload: int = 3, n_layers: int = N_LAYERS, lm_head_rows: int = LMHEAD[0],
+                    threads: int = 8):
+    """[(name, W fp16 [N,K], x fp16 [K])] for every linear of one step, each
+    tensor from its own stream (generated in parallel; the result does not
+    depend on the thread count)."""
+    from concurrent.futures import ThreadPoolExecutor
+    shapes = decode_step_shapes(n_layers)
+    shapes = [(n, (lm_head_rows if n == "lm_head" else N), K, wi, xi) for n, N, K, wi, xi in shapes]
+
+    def gen(s):
+        name, N, K, wi, xi = s
+        return name, f16_normal(workload, wi, (N, K), W_SIGMA), f16_normal(workload, xi, (K,), X_SIGMA)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        return list(ex.map(gen, shapes))
+
+
+def decode_step_w4(workload: int = 5, n_layers: int = N_LAYERS, lm_head_rows: int = LMHEAD[0], M: int = 1,
+                   threads: int = 8):
+    """[(name, Wc uint32 [N,K/8], s4 fp16 [N,K/128], X fp16 [M,K])] for one step."""
+    from concurrent.futures import ThreadPoolExecutor
+    shapes = decode_step_shapes(n_layers)
+    shapes = [(n, (lm_head_rows if n == "lm_head" else N), K, wi, xi) for n, N, K, wi, xi in shapes]
+
+    def gen(s):
+        name, N, K, wi, xi = s
+        X = f16_normal(workload, xi if M == 1 else 2000 + xi, (M, K), X_SIGMA)
+        return (name, w4_words(workload, wi, N, K),
+                f16_uniform(workload, 500 + wi, (N, K // GROUP), 0.002, 0.02), X)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        return list(ex.map(gen, shapes))

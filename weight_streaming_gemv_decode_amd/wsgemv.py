@@ -1,0 +1,273 @@
+"""ctypes binding of libwsgemv.so (the C ABI in include/wsgemv.h).
+
+Argument marshalling only: every function checks dtype, device, shape and
+contiguity of torch tensors, passes their device pointers and the current
+torch stream to the library, and turns a non-zero status into WsgError.  All
+arithmetic runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwsgemv.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "wsgemv.h")
+
+F16, W8A8, W4A16 = 0, 1, 2
+STEP_ORDERED, STEP_GROUPED, STEP_EAGER = 0, 1, 0x100
+STATUS = {0: "WSG_OK", 1: "WSG_ERR_NULL", 2: "WSG_ERR_SHAPE", 3: "WSG_ERR_ALIGN", 4: "WSG_ERR_UNSUPPORTED",
+          5: "WSG_ERR_WORKSPACE", 6: "WSG_ERR_HIP", 7: "WSG_ERR_NOMEM", 8: "WSG_ERR_STATE"}
+
+
+class WsgError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({detail})")
+
+
+class wsg_linear(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("M", ctypes.c_int32), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("W", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("x_scale", ctypes.c_void_p), ("y", ctypes.c_void_p), ("acc_out", ctypes.c_void_p),
+                ("group", ctypes.c_int32), ("splits", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "wsg_status_string": ([I32], ctypes.c_char_p),
+        "wsg_last_hip_error": ([], I32),
+        "wsg_build_info": ([], ctypes.c_char_p),
+        "wsg_plan_splits": ([I32, I64, I64, I64], I32),
+        "wsg_workspace_bytes": ([I32, I64, I64, I64, I32], SZ),
+        "gemv_f16": ([P, P, P, I64, I64, I32, P, SZ, P], I32),
+        "gemv_w8a8": ([P, P, P, P, P, P, I64, I64, I32, P, SZ, P], I32),
+        "wsg_w4_packed_weight_bytes": ([I64, I64], SZ),
+        "wsg_w4_packed_scale_bytes": ([I64, I64, I64], SZ),
+        "wsg_pack_w4": ([P, P, P, P, I64, I64, I64, P], I32),
+        "gemv_w4a16": ([P, P, P, P, I64, I64, I64, I64, I32, P, SZ, P], I32),
+        "wsg_decode_step_create": ([ctypes.POINTER(wsg_linear), I32, I32, P, ctypes.POINTER(P)], I32),
+        "decode_step_linears": ([P, P], I32),
+        "wsg_decode_step_destroy": ([P], I32),
+        "wsg_decode_step_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I64)], I32),
+        "wsg_read_probe": ([P, SZ, P, I32, P], I32),
+        "wsg_read_probe_grid": ([SZ], I32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m "
+                               "weight_streaming_gemv_decode_amd.build` (there is no fallback path)")
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def header_functions() -> List[str]:
+    """Names of the functions include/wsgemv.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        detail = lib().wsg_status_string(status).decode()
+        if status == 6:
+            detail += f"; hipError_t {lib().wsg_last_hip_error()}"
+        raise WsgError(status, what, detail)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def plan_splits(kind: int, M: int, N: int, K: int) -> int:
+    return int(lib().wsg_plan_splits(kind, M, N, K))
+
+
+def workspace_bytes(kind: int, M: int, N: int, K: int, splits: int = 0) -> int:
+    return int(lib().wsg_workspace_bytes(kind, M, N, K, splits))
+
+
+def workspace(kind: int, M: int, N: int, K: int, splits: int = 0, device="cuda") -> Optional[torch.Tensor]:
+    n = workspace_bytes(kind, M, N, K, splits)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _ws(ws: Optional[torch.Tensor]) -> Tuple[int, int]:
+    if ws is None:
+        return 0, 0
+    if ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def gemv_f16(W: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None, splits: int = 0,
+             ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[n] = sum_k W[n,k] x[k]; W fp16 [N,K], x fp16 [K], y fp32 [N]."""
+    N, K = W.shape
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=W.device)
+    if ws is None:
+        ws = workspace(F16, 1, N, K, splits, W.device)
+    wp, wn = _ws(ws)
+    _check(lib().gemv_f16(_dev(W, torch.float16, "W"), _dev(x, torch.float16, "x", (K,)),
+                          _dev(y, torch.float32, "y", (N,)), N, K, splits, wp, wn, _stream(stream)), "gemv_f16")
+    return y
+
+
+def gemv_w8a8(Wq: torch.Tensor, w_scale: torch.Tensor, xq: torch.Tensor, x_scale: torch.Tensor,
+              y: Optional[torch.Tensor] = None, acc_out: Optional[torch.Tensor] = None, want_acc: bool = True,
+              splits: int = 0, ws: Optional[torch.Tensor] = None, stream=None):
+    """(y, acc): acc[n] = sum_k Wq[n,k] xq[k] (int32), y = acc * w_scale[n] * x_scale."""
+    N, K = Wq.shape
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=Wq.device)
+    if acc_out is None and want_acc:
+        acc_out = torch.empty(N, dtype=torch.int32, device=Wq.device)
+    if ws is None:
+        ws = workspace(W8A8, 1, N, K, splits, Wq.device)
+    wp, wn = _ws(ws)
+    acc_p = _dev(acc_out, torch.int32, "acc_out", (N,)) if acc_out is not None else None
+    _check(lib().gemv_w8a8(_dev(Wq, torch.int8, "Wq"), _dev(w_scale, torch.float32, "w_scale", (N,)),
+                           _dev(xq, torch.int8, "xq", (K,)), _dev(x_scale, torch.float32, "x_scale", (1,)),
+                           _dev(y, torch.float32, "y", (N,)), acc_p, N, K, splits, wp, wn, _stream(stream)),
+           "gemv_w8a8")
+    return y, acc_out
+
+
+def packed_w4_bytes(N: int, K: int, group: int = 128) -> Tuple[int, int]:
+    return int(lib().wsg_w4_packed_weight_bytes(N, K)), int(lib().wsg_w4_packed_scale_bytes(N, K, group))
+
+
+def pack_w4(Wc: torch.Tensor, s4: torch.Tensor, group: int = 128, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Load-time packing of canonical int4 words Wc int32/uint32 [N, K/8] and
+    fp16 scales s4 [N, K/group] into the kernels' tile layout."""
+    N, K8 = Wc.shape
+    K = K8 * 8
+    if Wc.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("Wc must hold 32-bit words (int32 or uint32)")
+    wb, sb = packed_w4_bytes(N, K, group)
+    Wp = torch.empty(max(wb, 16), dtype=torch.uint8, device=Wc.device)
+    Sp = torch.empty(max(sb, 16), dtype=torch.uint8, device=Wc.device)
+    _check(lib().wsg_pack_w4(_dev(Wc, Wc.dtype, "Wc"), _dev(s4, torch.float16, "s4", (N, K // group)),
+                             Wp.data_ptr(), Sp.data_ptr(), N, K, group, _stream(stream)), "wsg_pack_w4")
+    return Wp, Sp
+
+
+def gemv_w4a16(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, N: int, group: int = 128,
+               y: Optional[torch.Tensor] = None, splits: int = 0, ws: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """y[m,n] = sum_k (q[n,k]-8) s4[n,k/128] x[m,k]; x fp16 [M,K] or [K]; y fp32 [M,N] (or [N])."""
+    squeeze = x.dim() == 1
+    X = x.reshape(1, -1) if squeeze else x
+    M, K = X.shape
+    if y is None:
+        y = torch.empty((M, N) if not squeeze else (N,), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(W4A16, M, N, K, splits, x.device)
+    wp, wn = _ws(ws)
+    wb, sb = packed_w4_bytes(N, K, group)
+    if Wp.numel() * Wp.element_size() < wb or Sp.numel() * Sp.element_size() < sb:
+        raise ValueError("packed buffers are smaller than this (N, K) needs")
+    _check(lib().gemv_w4a16(_dev(Wp, Wp.dtype, "Wp"), _dev(Sp, Sp.dtype, "Sp"), _dev(X, torch.float16, "x"),
+                            _dev(y, torch.float32, "y"), M, N, K, group, splits, wp, wn, _stream(stream)),
+           "gemv_w4a16")
+    return y
+
+
+def read_probe(buf: torch.Tensor, out: torch.Tensor, grid: int = 0, stream=None) -> None:
+    _check(lib().wsg_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                _dev(out, torch.float32, "out"), grid, _stream(stream)), "wsg_read_probe")
+
+
+def read_probe_grid(nbytes: int) -> int:
+    return int(lib().wsg_read_probe_grid(nbytes))
+
+
+class Linear:
+    """Description of one linear of a decode step (all tensors on the GPU)."""
+
+    def __init__(self, kind: int, W: torch.Tensor, x: torch.Tensor, y: torch.Tensor, N: int, K: int, M: int = 1,
+                 scale: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None,
+                 acc_out: Optional[torch.Tensor] = None, group: int = 0, splits: int = 0):
+        self.kind, self.W, self.x, self.y, self.N, self.K, self.M = kind, W, x, y, N, K, M
+        self.scale, self.x_scale, self.acc_out, self.group, self.splits = scale, x_scale, acc_out, group, splits
+
+    def c(self) -> wsg_linear:
+        p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        return wsg_linear(self.kind, self.M, self.N, self.K, p(self.W), p(self.scale), p(self.x), p(self.x_scale),
+                          p(self.y), p(self.acc_out), self.group, self.splits)
+
+
+class DecodeStep:
+    """A captured decode step (wsg_decode_step_create / decode_step_linears).
+
+    The tensors of every Linear are kept referenced for the plan's life,
+    because the plan holds their device addresses."""
+
+    def __init__(self, linears: Sequence[Linear], mode: int = STEP_GROUPED, stream=None):
+        self._keep = list(linears)
+        arr = (wsg_linear * max(1, len(linears)))(*[l.c() for l in linears])
+        h = ctypes.c_void_p()
+        _check(lib().wsg_decode_step_create(arr, len(linears), mode, _stream(stream), ctypes.byref(h)),
+               "wsg_decode_step_create")
+        self._h = h
+        self.mode = mode
+
+    def __call__(self, stream=None) -> None:
+        if self._h is None:
+            raise WsgError(8, "decode_step_linears", "destroyed plan")
+        _check(lib().decode_step_linears(self._h, _stream(stream)), "decode_step_linears")
+
+    def info(self) -> Tuple[int, int]:
+        a, b = ctypes.c_int32(), ctypes.c_int64()
+        _check(lib().wsg_decode_step_info(self._h, ctypes.byref(a), ctypes.byref(b)), "wsg_decode_step_info")
+        return a.value, b.value
+
+    def close(self) -> None:
+        if self._h is not None:
+            _check(lib().wsg_decode_step_destroy(self._h), "wsg_decode_step_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
