@@ -192,6 +192,21 @@ wsg_status wsg_read_probe(const void *buf, size_t bytes, float *out, int32_t gri
                           wsg_stream_t stream);
 int32_t wsg_read_probe_grid(size_t bytes);
 
+/*
+ * Launch-table overrides for tuning sweeps only.  Keys: "nt" (0/1
+ * non-temporal weight loads), "dense_R"/"dense_CH" (rows and vectors per
+ * lane per wave step of single fp16/int8 calls; set both), "dense_rows"
+ * (rows per work unit), "group_R"/"group_CH"/"group_unit_kb" (the same for
+ * grouped decode-step launches), "w4_R" (16-row tiles per wave step),
+ * "w4_tiles" / "group_w4_tiles" (tiles per work unit), "probe_U" (loads in
+ * flight per lane: 4, 8, 16), "probe_chunked" (0/1).  value < 0 restores the
+ * table's choice.  Process-wide, not thread-safe; plans capture the values
+ * in force when they are created.  No result depends on these settings
+ * beyond the summation order.  Unknown keys and kernel shapes that are not
+ * built return WSG_ERR_UNSUPPORTED and leave the setting unchanged.
+ */
+wsg_status wsg_tune_set(const char *key, int64_t value);
+
 #ifdef __cplusplus
 }
 #endif

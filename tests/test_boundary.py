@@ -90,7 +90,9 @@ def test_w4_validation_and_sizes(L):
 def test_launch_table(L):
     # The table is a pure host function of the shape.
     assert L.wsg_plan_splits(0, 1, 248320, 1024) >= 1
-    assert L.wsg_plan_splits(1, 1, 4096, 14336) > 1      # few rows, long rows: split k
+    assert L.wsg_plan_splits(0, 1, 64, 32768) >= 2       # slice must fit the LDS activation stage
+    assert L.wsg_plan_splits(0, 1, 16, 8192) > 1         # very few rows: split k
+    assert L.wsg_plan_splits(1, 1, 4096, 14336) == 1     # enough rows: no split
     assert L.wsg_plan_splits(0, 1, 248320, 1024) * 248320 * 4 == L.wsg_workspace_bytes(0, 1, 248320, 1024, 0) \
         or L.wsg_plan_splits(0, 1, 248320, 1024) == 1
     for S in (1, 2, 3, 4):

@@ -42,16 +42,29 @@ constexpr int64_t kUnitBytes = 128 * 1024;
 constexpr int64_t kWantUnits = 1024;
 constexpr int kMaxM = 8;
 
-bool env_flag(const char *name, bool dflt) {
-    const char *v = std::getenv(name);
-    if (!v || !*v)
-        return dflt;
-    return v[0] == '1' || v[0] == 'y' || v[0] == 'Y' || v[0] == 't' || v[0] == 'T';
-}
+// Launch-table overrides for tuning sweeps (wsg_tune_set).  -1 = the
+// table's own choice.  No result depends on them: every configuration
+// computes the same sums (split-K changes only the summation order).
+struct Tune {
+    int64_t nt = -1;             // non-temporal weight loads
+    int64_t dense_R = -1, dense_CH = -1, dense_rows = -1;
+    int64_t group_R = -1, group_CH = -1, group_unit_kb = -1;
+    int64_t w4_R = -1, w4_tiles = -1, group_w4_tiles = -1;
+    int64_t probe_U = -1, probe_chunked = -1;
+};
+Tune g_tune;
 
-// Non-temporal weight loads (the weight stream has no reuse).  Results do not
-// depend on it; WSG_NT=0/1 overrides the default for sweeps.
-bool use_nt() { return env_flag("WSG_NT", false); }
+// Non-temporal weight loads by default: the weight stream has no reuse, and
+// on MI355X they lift streaming reads from ~6.1 to ~7.1 TB/s.
+bool use_nt() { return g_tune.nt != 0; }
+
+bool dense_shape_ok(int64_t R, int64_t CH, bool grouped) {
+    if (CH == 2)
+        return R == 4 || R == 2 || (!grouped && R == 1);
+    if (CH == 1)
+        return R == 8 || (!grouped && R == 4);
+    return false;
+}
 
 // ---------------------------------------------------------------- dense --
 
@@ -77,35 +90,44 @@ int dense_tile_rows(int64_t slice_bytes_per_row, int R) {
 DensePlan plan_dense(int kind, int64_t N, int64_t K, int splits) {
     const int64_t kvec = K / elem_per_vec(kind);
     DensePlan p;
-    p.cfg = DenseCfg{4, 2, use_nt(), false};
     int S = splits > 0 ? splits : dense_min_splits(kvec);
-    if (splits <= 0) {
-        // Underfilled launch: first shrink the row tile, then split k in
-        // slices that stay whole 128-vector chunks.
-        int64_t tr = 16;
-        int64_t units = cdiv(N, tr) * S;
-        if (units < kWantUnits / 2 && kvec >= 256) {
-            const int64_t chunks = kvec / 128;
-            for (int s = S + 1; s <= 16 && s <= chunks; ++s) {
-                if (kvec % (128LL * s) == 0 || s == (int)chunks) {
-                    S = s;
-                    if (cdiv(N, tr) * S >= kWantUnits / 2)
-                        break;
-                }
+    // Row tile: 4 waves x R rows per unit.  Small units keep many
+    // workgroups in flight; split k only when the launch would have fewer
+    // than 256 units even with 4-row units (slices stay whole 128-vector
+    // chunks).
+    if (splits <= 0 && cdiv(N, 4) * S < 256 && kvec >= 256) {
+        const int64_t chunks = kvec / 128;
+        for (int s = S + 1; s <= 16 && s <= chunks; ++s) {
+            if (kvec % (128LL * s) == 0 || s == (int)chunks) {
+                S = s;
+                if (cdiv(N, 4) * S >= 256)
+                    break;
             }
         }
     }
     p.S = S;
     p.kvs = (int)cdiv(kvec, S);
-    const int64_t slice_row_bytes = (int64_t)p.kvs * 16;
-    int tr = dense_tile_rows(slice_row_bytes, p.cfg.R);
-    while (tr > 16 && cdiv(N, tr) * S < kWantUnits)
-        tr -= 16;
-    if (cdiv(N, tr) * S < kWantUnits / 4 && N > 0) {
-        // Very few rows: one row per wave step, 4 rows per unit.
-        p.cfg.R = 1;
+    int tr;
+    if (p.kvs % 128 != 0 && p.kvs % 64 == 0) {
+        // 64-vector slices (e.g. K = 1024 fp16 cut in two): 8 rows x 1 vector per step
+        p.cfg = DenseCfg{8, 1, use_nt(), false};
+        tr = 32;
+    } else if (cdiv(N, 16) * S >= 1024) {
+        p.cfg = DenseCfg{4, 2, use_nt(), false};
+        tr = 16;
+    } else if (cdiv(N, 8) * S >= 256) {
+        p.cfg = DenseCfg{2, 2, use_nt(), false};
+        tr = 8;
+    } else {
+        p.cfg = DenseCfg{1, 2, use_nt(), false};
         tr = 4;
     }
+    if (g_tune.dense_R > 0 && g_tune.dense_CH > 0) {
+        p.cfg.R = (int)g_tune.dense_R;
+        p.cfg.CH = (int)g_tune.dense_CH;
+    }
+    if (g_tune.dense_rows > 0)
+        tr = (int)g_tune.dense_rows;
     p.tile_rows = tr;
     return p;
 }
@@ -195,7 +217,7 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
     const int64_t kb = K / 128;
     const int64_t n_rtiles = cdiv(N, 16);
     W4Plan p;
-    p.cfg = W4Cfg{2, use_nt()};
+    p.cfg = W4Cfg{1, use_nt()};
     // LDS holds M rows of the slice: M * kbs * 256 bytes <= 32 KiB.
     const int64_t max_kbs = std::max<int64_t>(4, (32 * 1024 / (256 * std::max<int64_t>(1, M))) / 4 * 4);
     int S;
@@ -204,23 +226,24 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
     } else {
         S = (int)std::max<int64_t>(1, cdiv(kb, max_kbs));
         // underfilled: split k in whole 4-block quads
-        while (n_rtiles * S < kWantUnits / 2 && (int64_t)(S + 1) * 4 <= kb)
+        while (n_rtiles * S < 512 && (int64_t)(S + 1) * 4 <= kb)
             ++S;
-    }
-    if (splits <= 0) {
         // never leave a slice empty (slices are whole 4-block quads)
         while (S > 1 && (int64_t)(S - 1) * (cdiv(cdiv(kb, S), 4) * 4) >= kb)
             --S;
     }
     p.S = S;
     p.kbs = S > 1 ? (int)(cdiv(cdiv(kb, S), 4) * 4) : (int)kb;
-    const int64_t tile_bytes = 16 * (int64_t)p.kbs * 64;  // 16 rows x kbs blocks x 64 B
-    int64_t tt = std::max<int64_t>(1, (kUnitBytes / 2) / std::max<int64_t>(1, tile_bytes));
+    // 16-row tiles per unit: 4 (M = 1) or 8 (verify blocks), fewer when the
+    // launch would otherwise have under 1024 units.
+    int64_t tt = M > 1 ? 8 : 4;
     while (tt > 1 && cdiv(n_rtiles, tt) * S < kWantUnits)
         tt = tt / 2;
+    if (g_tune.w4_tiles > 0)
+        tt = g_tune.w4_tiles;
     p.tile_rtiles = (int)tt;
-    if (tt < 2)
-        p.cfg.R = 1;
+    if (g_tune.w4_R > 0)
+        p.cfg.R = (int)g_tune.w4_R;
     return p;
 }
 
@@ -473,6 +496,42 @@ wsg_status gemv_w4a16(const void *Wp, const void *Sp, const void *x, float *y, i
     });
 }
 
+wsg_status wsg_tune_set(const char *key, int64_t value) {
+    if (!key)
+        return WSG_ERR_NULL;
+    struct {
+        const char *name;
+        int64_t *slot;
+    } table[] = {{"nt", &g_tune.nt},
+                 {"dense_R", &g_tune.dense_R},
+                 {"dense_CH", &g_tune.dense_CH},
+                 {"dense_rows", &g_tune.dense_rows},
+                 {"group_R", &g_tune.group_R},
+                 {"group_CH", &g_tune.group_CH},
+                 {"group_unit_kb", &g_tune.group_unit_kb},
+                 {"w4_R", &g_tune.w4_R},
+                 {"w4_tiles", &g_tune.w4_tiles},
+                 {"group_w4_tiles", &g_tune.group_w4_tiles},
+                 {"probe_U", &g_tune.probe_U},
+                 {"probe_chunked", &g_tune.probe_chunked}};
+    for (auto &t : table) {
+        if (std::strcmp(key, t.name) == 0) {
+            *t.slot = value < 0 ? -1 : value;
+            if ((g_tune.dense_R > 0 && g_tune.dense_CH > 0 &&
+                 !dense_shape_ok(g_tune.dense_R, g_tune.dense_CH, false)) ||
+                (g_tune.group_R > 0 && g_tune.group_CH > 0 &&
+                 !dense_shape_ok(g_tune.group_R, g_tune.group_CH, true)) ||
+                (g_tune.w4_R > 0 && g_tune.w4_R != 1 && g_tune.w4_R != 2) ||
+                (g_tune.probe_U > 0 && g_tune.probe_U != 4 && g_tune.probe_U != 8 && g_tune.probe_U != 16)) {
+                *t.slot = -1;
+                return WSG_ERR_UNSUPPORTED;
+            }
+            return WSG_OK;
+        }
+    }
+    return WSG_ERR_UNSUPPORTED;
+}
+
 int32_t wsg_read_probe_grid(size_t bytes) {
     (void)bytes;
     return 2048;  // 8 workgroups per compute unit on 256 CUs
@@ -487,7 +546,8 @@ wsg_status wsg_read_probe(const void *buf, size_t bytes, float *out, int32_t gri
         if (!aligned(buf, 16) || !aligned(out, 4))
             return WSG_ERR_ALIGN;
         const int g = grid > 0 ? grid : wsg_read_probe_grid(bytes);
-        hipError_t e = launch_read_probe(static_cast<const u32x4 *>(buf), (int64_t)(bytes / 16), out, g,
+        const ProbeCfg pc{g_tune.probe_U > 0 ? (int)g_tune.probe_U : 8, use_nt(), g_tune.probe_chunked == 1};
+        hipError_t e = launch_read_probe(static_cast<const u32x4 *>(buf), (int64_t)(bytes / 16), out, g, pc,
                                          static_cast<hipStream_t>(stream));
         return e == hipSuccess ? WSG_OK : hip_fail(e);
     });
@@ -641,7 +701,14 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         std::vector<Unit> wu[2];
         int wlds[2] = {0, 0}, wmaxm[2] = {1, 1};
         size_t part_bytes = 0;
-        const DenseCfg gcfg{4, 2, use_nt(), false};
+        // Grouped launches: 8 rows x 1 vector per wave step, units of at least
+        // 32 rows (64 KiB at K = 1024 fp16).
+        DenseCfg gcfg{8, 1, use_nt(), false};
+        if (g_tune.group_R > 0 && g_tune.group_CH > 0) {
+            gcfg.R = (int)g_tune.group_R;
+            gcfg.CH = (int)g_tune.group_CH;
+        }
+        const int64_t unit_bytes = g_tune.group_unit_kb > 0 ? g_tune.group_unit_kb * 1024 : 32 * 1024;
 
         for (int32_t i = 0; i < n; ++i) {
             const wsg_linear &l = linears[i];
@@ -682,7 +749,11 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                         free_step(st);
                         return WSG_ERR_UNSUPPORTED;
                     }
-                    p.tile_rows = dense_tile_rows((int64_t)p.kvs * 16, gcfg.R);
+                    {
+                        const int q = kWavesPerBlock * gcfg.R;
+                        int64_t rows = unit_bytes / ((int64_t)p.kvs * 16);
+                        p.tile_rows = (int)std::min<int64_t>(1 << 20, std::max<int64_t>(q, rows / q * q));
+                    }
                     DenseLin L = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale),
                                             l.x_scale, l.acc_out, l.N, l.K, p);
                     const int li = (int)dl[ki].size();
@@ -706,8 +777,10 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     p.S = 1;
                     p.kbs = (int)(l.K / 128);
                     const int64_t tile_bytes = 16 * (int64_t)p.kbs * 64;
-                    p.tile_rtiles = (int)std::max<int64_t>(2, (kUnitBytes / 2) / std::max<int64_t>(1, tile_bytes));
-                    p.cfg.R = 2;
+                    (void)tile_bytes;
+                    // verify blocks: 1 tile per step; M = 1: 2 tiles per step; 8 tiles per unit
+                    p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles : 8;
+                    p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (l.M > 1 ? 1 : 2);
                     W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
                     if (w4_lds_bytes(L) > 48 * 1024) {
                         free_step(st);
@@ -784,7 +857,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             if (!wu[k].empty()) {
                 wsg_step::Op o{};
                 o.type = wsg_step::Op::kW4Group;
-                o.wc = W4Cfg{2, use_nt()};
+                o.wc = W4Cfg{g_tune.w4_R > 0 ? (int)g_tune.w4_R : (k == 1 ? 1 : 2), use_nt()};
                 o.lins = base + wl_off[k];
                 o.units = reinterpret_cast<const Unit *>(base + wu_off[k]);
                 o.n_units = (int)wu[k].size();

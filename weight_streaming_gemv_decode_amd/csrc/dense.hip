@@ -273,19 +273,33 @@ __global__ __launch_bounds__(kBlock) void zero_f32_kernel(float *p, int64_t n) {
         p[i] = 0.0f;
 }
 
-// Read-only stream over buf: 8 loads in flight per lane per iteration; the
-// xor of everything read is folded per workgroup into out[blockIdx.x].
+// Read-only stream over buf, U 16-byte loads in flight per lane per
+// iteration.  CHUNKED = false: grid-stride over the whole buffer; true: each
+// workgroup reads one contiguous share.  The xor of everything read is
+// folded per workgroup into out[blockIdx.x].
+template <int U, bool NT, bool CHUNKED>
 __global__ __launch_bounds__(kBlock) void read_probe_kernel(const u32x4 *__restrict__ buf, int64_t nvec,
                                                             float *out) {
-    constexpr int U = 8;
     uint32_t acc = 0;
-    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
-    for (int64_t base = (int64_t)blockIdx.x * kBlock * U + threadIdx.x; base < nvec; base += stride) {
+    int64_t begin = 0, end = nvec, first, stride;
+    if constexpr (CHUNKED) {
+        const int64_t share = (nvec + gridDim.x - 1) / gridDim.x;
+        begin = min(nvec, (int64_t)blockIdx.x * share);
+        end = min(nvec, begin + share);
+        first = begin + threadIdx.x;
+        stride = (int64_t)kBlock * U;
+    } else {
+        first = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
+        stride = (int64_t)gridDim.x * kBlock * U;
+    }
+    for (int64_t base = first; base < end; base += stride) {
         u32x4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = base + (int64_t)u * kBlock;
-            v[u] = i < nvec ? buf[i] : u32x4{0u, 0u, 0u, 0u};
+            v[u] = u32x4{0u, 0u, 0u, 0u};
+            if (i < end)
+                v[u] = load_w<NT>(buf + i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -303,6 +317,12 @@ __global__ __launch_bounds__(kBlock) void read_probe_kernel(const u32x4 *__restr
             a ^= red[w];
         out[blockIdx.x] = (float)(a & 0xFFFFu);
     }
+}
+
+template <int U, bool NT, bool CHUNKED>
+hipError_t launch_probe(const u32x4 *buf, int64_t nvec, float *out, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((read_probe_kernel<U, NT, CHUNKED>), dim3(grid), dim3(kBlock), 0, s, buf, nvec, out);
+    return hipGetLastError();
 }
 
 template <int KIND, int R, int CH, bool NT, bool TAIL>
@@ -328,6 +348,9 @@ hipError_t dispatch_single(const DenseLin &L, const DenseCfg &c, hipStream_t s) 
         if (c.R == 4) return launch_single<KIND, 4, 2, NT, TAIL>(L, s);
         if (c.R == 2) return launch_single<KIND, 2, 2, NT, TAIL>(L, s);
         if (c.R == 1) return launch_single<KIND, 1, 2, NT, TAIL>(L, s);
+    } else if (c.CH == 1) {
+        if (c.R == 8) return launch_single<KIND, 8, 1, NT, TAIL>(L, s);
+        if (c.R == 4) return launch_single<KIND, 4, 1, NT, TAIL>(L, s);
     }
     return hipErrorInvalidValue;
 }
@@ -338,6 +361,8 @@ hipError_t dispatch_group(const DenseLin *lins, const Unit *units, int n, int ld
     if (c.CH == 2) {
         if (c.R == 4) return launch_group<KIND, 4, 2, NT, TAIL>(lins, units, n, lds, s);
         if (c.R == 2) return launch_group<KIND, 2, 2, NT, TAIL>(lins, units, n, lds, s);
+    } else if (c.CH == 1) {
+        if (c.R == 8) return launch_group<KIND, 8, 1, NT, TAIL>(lins, units, n, lds, s);
     }
     return hipErrorInvalidValue;
 }
@@ -393,9 +418,19 @@ hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(kBlock), 0, s, buf, nvec, out);
-    return hipGetLastError();
+hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int grid, const ProbeCfg &c,
+                             hipStream_t s) {
+#define WSG_PROBE(Uv)                                                                              \
+    if (c.U == Uv)                                                                                 \
+        return c.nt ? (c.chunked ? launch_probe<Uv, true, true>(buf, nvec, out, grid, s)           \
+                                 : launch_probe<Uv, true, false>(buf, nvec, out, grid, s))         \
+                    : (c.chunked ? launch_probe<Uv, false, true>(buf, nvec, out, grid, s)          \
+                                 : launch_probe<Uv, false, false>(buf, nvec, out, grid, s));
+    WSG_PROBE(4)
+    WSG_PROBE(8)
+    WSG_PROBE(16)
+#undef WSG_PROBE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace wsg

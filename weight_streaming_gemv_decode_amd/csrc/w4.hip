@@ -46,14 +46,27 @@ __device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
         return *p;
 }
 
+// Constants of the unpack, pinned in registers once per kernel: gfx9 VOP3
+// instructions take no 32-bit literal, so with the masks in SGPRs and the
+// magic in a VGPR each masked field costs one v_and_or_b32.
+struct Unpack {
+    uint32_t magic;  // fp16 1024.0 in both halves (VGPR)
+    uint32_t lo;     // 0x000F000F (SGPR)
+    uint32_t hi;     // 0x00F000F0 (SGPR)
+    __device__ __forceinline__ Unpack() : magic(0x64006400u), lo(0x000F000Fu), hi(0x00F000F0u) {
+        asm volatile("" : "+v"(magic));
+        asm volatile("" : "+s"(lo));
+        asm volatile("" : "+s"(hi));
+    }
+};
+
 // q - 8 for the 8 weights of a packed word, as the fp16 pairs (0,1) .. (6,7).
-__device__ __forceinline__ void unpack8(uint32_t w, f16x2 (&h)[4]) {
-    constexpr uint32_t kMagic = 0x64006400u;  // fp16 1024.0 in both halves
+__device__ __forceinline__ void unpack8(uint32_t w, const Unpack &u, f16x2 (&h)[4]) {
     const uint32_t w8 = w >> 8;
-    const f16x2 a = __builtin_bit_cast(f16x2, (w & 0x000F000Fu) | kMagic);   // 1024 + q0, 1024 + q1
-    const f16x2 b = __builtin_bit_cast(f16x2, (w & 0x00F000F0u) | kMagic);   // 1024 + 16 q2, 1024 + 16 q3
-    const f16x2 c = __builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) | kMagic);  // q4, q5
-    const f16x2 d = __builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) | kMagic);  // 16 q6, 16 q7
+    const f16x2 a = __builtin_bit_cast(f16x2, (w & u.lo) | u.magic);   // 1024 + q0, 1024 + q1
+    const f16x2 b = __builtin_bit_cast(f16x2, (w & u.hi) | u.magic);   // 1024 + 16 q2, 1024 + 16 q3
+    const f16x2 c = __builtin_bit_cast(f16x2, (w8 & u.lo) | u.magic);  // q4, q5
+    const f16x2 d = __builtin_bit_cast(f16x2, (w8 & u.hi) | u.magic);  // 16 q6, 16 q7
     const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const f16x2 bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
@@ -89,6 +102,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     const int mygroups = wave < ngroups ? (ngroups - 1 - wave) / kWavesPerBlock + 1 : 0;
     const int nsteps = mygroups * nquad;
     const int M = MFMA ? L.M : 1;
+    const Unpack U;
 
     struct Buf {
         u32x4 w[R][4];
@@ -183,7 +197,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         f16x2 h[4];
-                        unpack8(words[i], h);
+                        unpack8(words[i], U, h);
                         p = __builtin_amdgcn_fdot2(h[0], as_h2(xv[i].x), p, false);
                         p = __builtin_amdgcn_fdot2(h[1], as_h2(xv[i].y), p, false);
                         p = __builtin_amdgcn_fdot2(h[2], as_h2(xv[i].z), p, false);
@@ -209,7 +223,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         f16x2 h[4];
-                        unpack8(words[i], h);
+                        unpack8(words[i], U, h);
                         const u32x4 hb = {__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
                                           __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
                         const f16x8 bw = __builtin_bit_cast(f16x8, hb);

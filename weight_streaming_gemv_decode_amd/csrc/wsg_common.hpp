@@ -100,7 +100,13 @@ hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, 
 hipError_t launch_w4_reduce(const W4Lin &L, hipStream_t s);
 hipError_t launch_pack_w4(const uint32_t *Wc, const uint16_t *s4, u32x4 *Wp, u32x2 *Sp,
                           int64_t N, int32_t K, hipStream_t s);
-hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int grid, hipStream_t s);
+struct ProbeCfg {
+    int U;         // 16-byte loads in flight per lane per iteration (4, 8, 16)
+    bool nt;       // non-temporal loads
+    bool chunked;  // contiguous share per workgroup instead of grid-stride
+};
+hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int grid, const ProbeCfg &c,
+                             hipStream_t s);
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
 
 // LDS bytes a dense unit of this linear stages for x (whole slice, chunk-padded).

@@ -61,6 +61,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "wsg_decode_step_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I64)], I32),
         "wsg_read_probe": ([P, SZ, P, I32, P], I32),
         "wsg_read_probe_grid": ([SZ], I32),
+        "wsg_tune_set": ([ctypes.c_char_p, I64], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -215,6 +216,11 @@ def gemv_w4a16(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, N: int, grou
 def read_probe(buf: torch.Tensor, out: torch.Tensor, grid: int = 0, stream=None) -> None:
     _check(lib().wsg_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(),
                                 _dev(out, torch.float32, "out"), grid, _stream(stream)), "wsg_read_probe")
+
+
+def tune_set(key: str, value: int) -> None:
+    """Launch-table override for tuning sweeps (value < 0 restores the default)."""
+    _check(lib().wsg_tune_set(key.encode(), int(value)), f"wsg_tune_set({key})")
 
 
 def read_probe_grid(nbytes: int) -> int:
