@@ -20,6 +20,29 @@ import time
 import numpy as np
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["weight_streaming_gemv_decode_amd/csrc/dense.hip", "weight_streaming_gemv_decode_amd/csrc/wsg_common.hpp",
+                  "weight_streaming_gemv_decode_amd/csrc/api.cpp"]
+
+
+def measured_traffic(path):
+    """Counter-measured traffic of the grouped kernel, or None when the
+    summary is missing or the kernel sources changed since it was taken."""
+    import hashlib
+    if not path or not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("traffic-json: "):
+            rec = json.loads(line[len("traffic-json: "):])
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        h.update(open(os.path.join(HERE, s), "rb").read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec
 METRIC = "achieved HBM GB/s (% of peak) for batch-1 GEMV; ms per decode-step stream"
 
 
@@ -31,6 +54,12 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="only the decode-step stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,probe,ordered)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a plain 1 GiB fp32 copy kernel (reads 1 GiB, writes 1 GiB) to calibrate "
+                         "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass")
+    ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic_decode_step_f16_grouped.md"),
+                    help="profile summary holding the counter-measured per-launch HBM traffic of the grouped "
+                         "kernel; used only while the kernel sources still hash to the measured ones")
     return ap.parse_args()
 
 
@@ -51,6 +80,33 @@ def event_times(torch, fn, reps, stream):
     return [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
 
 
+def graph_times(torch, fn, inner, reps, stream):
+    """Per-call GPU time (ms) of fn(i), i = 0..inner-1 captured once into a
+    graph and replayed `reps` times back to back (no host dispatch cost)."""
+    with torch.cuda.stream(stream):
+        for i in range(inner):
+            fn(i)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(inner):
+            fn(i)
+    with torch.cuda.stream(stream):
+        g.replay()
+    stream.synchronize()
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        stream.synchronize()
+        out.append(e0.elapsed_time(e1) / inner)
+    del g
+    return out
+
+
 def summary(ts):
     ts = sorted(ts)
     return {"median_ms": statistics.median(ts), "p10_ms": ts[len(ts) // 10], "p90_ms": ts[(9 * len(ts)) // 10],
@@ -69,6 +125,15 @@ def main():
     wsgemv.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
+
+    if args.calib_copy:
+        # plain copy of known size for the profiler's byte counters
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- inputs (seeded, synthetic), copied to HBM once ----
     t0 = time.time()
@@ -109,10 +174,14 @@ def main():
     kt = event_times(torch, lambda i: eager(stream), max(50, min(args.steps, 200)), stream)
     ks = summary(kt)
     achieved = step_bytes / (ks["mean_ms"] * 1e-3) / 1e9
+    rec = measured_traffic(args.traffic)
+    traffic = None if rec is None else rec["bytes"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": "dense_grouped_kernel<f16> (one launch per step)",
-                "bytes_per_launch": step_bytes, "launch_ms": ks}
+                "bytes_per_launch": step_bytes, "launch_ms": ks,
+                "traffic_detail": None if rec is None else {k: rec[k] for k in ("read_bytes", "write_bytes",
+                                                                               "ratio_to_algorithmic")}}
     log(f"grouped kernel: mean {ks['mean_ms'] * 1e3:.1f} us -> {achieved:.0f} GB/s")
 
     extras = {}
@@ -154,13 +223,11 @@ def main():
         ws = wsgemv.workspace(wsgemv.F16, 1, N, K, 0, dev)
         y = torch.empty(N, device=dev)
         fn = lambda i: wsgemv.gemv_f16(copies[i % 64], x, y=y, ws=ws, stream=stream)  # noqa: E731
-        for i in range(64):
-            fn(i)
-        s = summary(event_times(torch, fn, 640, stream))
+        s = summary(graph_times(torch, fn, 64, 10, stream))
         b = N * K * 2 + K * 2 + N * 4
         extras["c1_2048x2048"] = {"bytes": b, "median_us": s["median_ms"] * 1e3,
                                   "GBps": b / (s["median_ms"] * 1e-3) / 1e9, "rotation": "64 copies (537 MB)",
-                                  "note": "back-to-back launches; launch-bound shape"}
+                                  "note": "64 calls captured in one graph, per-call time; launch-bound shape"}
         del copies
 
     if want("c4"):
@@ -175,13 +242,12 @@ def main():
             acc = torch.empty(N, dtype=torch.int32, device=dev)
             fn = lambda i: wsgemv.gemv_w8a8(copies[i % 9], sw, xq, xs, y=y, acc_out=acc, ws=ws,  # noqa: E731
                                             stream=stream)
-            for i in range(18):
-                fn(i)
-            s = summary(event_times(torch, fn, 180, stream))
+            s = summary(graph_times(torch, fn, 36, 10, stream))
             b = N * K + N * 4 + K + N * 4 + N * 4
             extras[f"c4_w8a8_{N}x{K}"] = {"bytes_incl_acc_out": b, "median_us": s["median_ms"] * 1e3,
                                           "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
-                                          "splits": wsgemv.plan_splits(1, 1, N, K), "rotation": "9 copies"}
+                                          "splits": wsgemv.plan_splits(1, 1, N, K),
+                                          "rotation": "9 copies, 36 calls captured in one graph"}
             del copies
 
     if want("c5"):
