@@ -197,7 +197,8 @@ int32_t wsg_read_probe_grid(size_t bytes);
  * non-temporal weight loads), "dense_R"/"dense_CH" (rows and vectors per
  * lane per wave step of single fp16/int8 calls; set both), "dense_rows"
  * (rows per work unit), "group_R"/"group_CH"/"group_unit_kb" (the same for
- * grouped decode-step launches), "w4_R" (16-row tiles per wave step),
+ * grouped decode-step launches), "w4_R" (16-row tiles per wave step), "w4_B" (128-k blocks per
+ * wave step: 4, 8),
  * "w4_tiles" / "group_w4_tiles" (tiles per work unit), "probe_U" (loads in
  * flight per lane: 4, 8, 16), "probe_chunked" (0/1).  value < 0 restores the
  * table's choice.  Process-wide, not thread-safe; plans capture the values

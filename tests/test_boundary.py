@@ -126,3 +126,20 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(16, dtype=torch.float16)
     with pytest.raises(ValueError):
         wsgemv.gemv_f16(W, x, y=torch.zeros(4), splits=1)
+
+
+def test_tuning_overrides_validated():
+    keys = ("dense_R", "dense_CH", "w4_B")
+    try:
+        with pytest.raises(wsgemv.WsgError):
+            wsgemv.tune_set("no_such_key", 1)
+        wsgemv.tune_set("dense_R", 3)          # alone it is only recorded
+        with pytest.raises(wsgemv.WsgError):
+            wsgemv.tune_set("dense_CH", 2)     # (R=3, CH=2) is not a built kernel shape
+        with pytest.raises(wsgemv.WsgError):
+            wsgemv.tune_set("w4_B", 6)
+        wsgemv.tune_set("dense_R", 8)
+        wsgemv.tune_set("dense_CH", 1)
+    finally:
+        for k in keys:
+            wsgemv.tune_set(k, -1)

@@ -49,7 +49,7 @@ struct Tune {
     int64_t nt = -1;             // non-temporal weight loads
     int64_t dense_R = -1, dense_CH = -1, dense_rows = -1;
     int64_t group_R = -1, group_CH = -1, group_unit_kb = -1;
-    int64_t w4_R = -1, w4_tiles = -1, group_w4_tiles = -1;
+    int64_t w4_R = -1, w4_B = -1, w4_tiles = -1, group_w4_tiles = -1;
     int64_t probe_U = -1, probe_chunked = -1;
 };
 Tune g_tune;
@@ -217,7 +217,7 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
     const int64_t kb = K / 128;
     const int64_t n_rtiles = cdiv(N, 16);
     W4Plan p;
-    p.cfg = W4Cfg{1, use_nt()};
+    p.cfg = W4Cfg{1, 4, use_nt()};
     // LDS holds M rows of the slice: M * kbs * 256 bytes <= 32 KiB.
     const int64_t max_kbs = std::max<int64_t>(4, (32 * 1024 / (256 * std::max<int64_t>(1, M))) / 4 * 4);
     int S;
@@ -244,6 +244,8 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
     p.tile_rtiles = (int)tt;
     if (g_tune.w4_R > 0)
         p.cfg.R = (int)g_tune.w4_R;
+    if (g_tune.w4_B > 0)
+        p.cfg.B = (int)g_tune.w4_B;
     return p;
 }
 
@@ -510,6 +512,7 @@ wsg_status wsg_tune_set(const char *key, int64_t value) {
                  {"group_CH", &g_tune.group_CH},
                  {"group_unit_kb", &g_tune.group_unit_kb},
                  {"w4_R", &g_tune.w4_R},
+                 {"w4_B", &g_tune.w4_B},
                  {"w4_tiles", &g_tune.w4_tiles},
                  {"group_w4_tiles", &g_tune.group_w4_tiles},
                  {"probe_U", &g_tune.probe_U},
@@ -522,6 +525,7 @@ wsg_status wsg_tune_set(const char *key, int64_t value) {
                 (g_tune.group_R > 0 && g_tune.group_CH > 0 &&
                  !dense_shape_ok(g_tune.group_R, g_tune.group_CH, true)) ||
                 (g_tune.w4_R > 0 && g_tune.w4_R != 1 && g_tune.w4_R != 2) ||
+                (g_tune.w4_B > 0 && g_tune.w4_B != 4 && g_tune.w4_B != 8) ||
                 (g_tune.probe_U > 0 && g_tune.probe_U != 4 && g_tune.probe_U != 8 && g_tune.probe_U != 16)) {
                 *t.slot = -1;
                 return WSG_ERR_UNSUPPORTED;
@@ -781,6 +785,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     // verify blocks: 1 tile per step; M = 1: 2 tiles per step; 8 tiles per unit
                     p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles : 8;
                     p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (l.M > 1 ? 1 : 2);
+                    p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : 4;
                     W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
                     if (w4_lds_bytes(L) > 48 * 1024) {
                         free_step(st);
@@ -857,7 +862,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             if (!wu[k].empty()) {
                 wsg_step::Op o{};
                 o.type = wsg_step::Op::kW4Group;
-                o.wc = W4Cfg{g_tune.w4_R > 0 ? (int)g_tune.w4_R : (k == 1 ? 1 : 2), use_nt()};
+                o.wc = W4Cfg{g_tune.w4_R > 0 ? (int)g_tune.w4_R : (k == 1 ? 1 : 2), g_tune.w4_B > 0 ? (int)g_tune.w4_B : 4,
+                             use_nt()};
                 o.lins = base + wl_off[k];
                 o.units = reinterpret_cast<const Unit *>(base + wu_off[k]);
                 o.n_units = (int)wu[k].size();

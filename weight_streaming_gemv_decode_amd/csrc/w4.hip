@@ -83,16 +83,19 @@ __device__ __forceinline__ float scale_of(u32x2 sc, int b) {
 }
 
 // One work unit: `tile_rtiles` 16-row tiles starting at unit `tile`, k-slice s.
+// A wave step covers R tiles x B blocks (B = 4 or 8: 4 or 8 KiB of weights
+// per wave in flight per step, two steps in flight).
 // MFMA = false: M = 1 on the VALU.  MFMA = true: M = 2..8 on the matrix cores.
-template <int R, bool NT, bool MFMA>
+template <int R, int B, bool NT, bool MFMA>
 __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *xs) {
+    static_assert(B % 4 == 0, "steps are whole 4-block scale quads");
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int r16 = lane & 15, g = lane >> 4;
 
     const int kb0 = s * L.kbs;                     // first block of the slice
     const int nkb = min(L.kbs, L.kb - kb0);        // blocks in the slice
-    const int nquad = (nkb + 3) / 4;
+    const int nquad = (nkb + B - 1) / B;   // steps per row group
     const int nxv = nkb * 16;                      // 16-byte x vectors per row in the slice
     const int64_t n_rtiles = (L.N + 15) / 16;
     const int64_t rt0 = (int64_t)tile * L.tile_rtiles;
@@ -105,29 +108,37 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     const Unpack U;
 
     struct Buf {
-        u32x4 w[R][4];
-        u32x2 sc[R];
+        u32x4 w[R][B];
+        u32x2 sc[R][B / 4];
     };
 
-    auto load_step = [&](Buf &B, int gi, int c) {
+    auto load_step = [&](Buf &Bf, int gi, int c) {
         const int64_t rtb = rt0 + (int64_t)(wave + gi * kWavesPerBlock) * R;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int64_t rt = min(rtb + r, last_rt);
             // wave-uniform tile pointers; the lane offset is the only vector part
-            const u32x4 *p = L.Wp + (rt * L.kb + kb0 + 4 * c) * kWave;
-            const u32x2 *q = L.Sp + (rt * L.kq + kb0 / 4 + c) * 16;
-            B.sc[r] = q[r16];
-            if (4 * c + 4 <= nkb) {
+            const u32x4 *p = L.Wp + (rt * L.kb + kb0 + B * c) * kWave;
+            const u32x2 *q = L.Sp + (rt * L.kq + (kb0 + B * c) / 4) * 16;
+            if (B * c + B <= nkb) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    B.w[r][b] = load_w<NT>(p + b * kWave + lane);
+                for (int qq = 0; qq < B / 4; ++qq)
+                    Bf.sc[r][qq] = q[qq * 16 + r16];
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    Bf.w[r][b] = load_w<NT>(p + b * kWave + lane);
             } else {
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    B.w[r][b] = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-                    if (4 * c + b < nkb)
-                        B.w[r][b] = load_w<NT>(p + b * kWave + lane);
+                for (int qq = 0; qq < B / 4; ++qq) {
+                    Bf.sc[r][qq] = u32x2{0u, 0u};
+                    if (B * c + 4 * qq < nkb)
+                        Bf.sc[r][qq] = q[qq * 16 + r16];
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    Bf.w[r][b] = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+                    if (B * c + b < nkb)
+                        Bf.w[r][b] = load_w<NT>(p + b * kWave + lane);
                 }
             }
         }
@@ -179,12 +190,12 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
         }
     };
 
-    auto consume = [&](const Buf &B, int gi, int c) {
+    auto consume = [&](const Buf &Bf, int gi, int c) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if (4 * c + b >= nkb)
+        for (int b = 0; b < B; ++b) {
+            if (B * c + b >= nkb)
                 break;
-            const int xv0 = (4 * c + b) * 16 + g;  // x vector of word 0 of this lane in the block
+            const int xv0 = (B * c + b) * 16 + g;  // x vector of word 0 of this lane in the block
             if constexpr (!MFMA) {
                 u32x4 xv[4];
 #pragma unroll
@@ -192,7 +203,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                     xv[i] = xs[xv0 + 4 * i];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const uint32_t words[4] = {B.w[r][b].x, B.w[r][b].y, B.w[r][b].z, B.w[r][b].w};
+                    const uint32_t words[4] = {Bf.w[r][b].x, Bf.w[r][b].y, Bf.w[r][b].z, Bf.w[r][b].w};
                     float p = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -203,7 +214,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                         p = __builtin_amdgcn_fdot2(h[2], as_h2(xv[i].z), p, false);
                         p = __builtin_amdgcn_fdot2(h[3], as_h2(xv[i].w), p, false);
                     }
-                    acc1[r] += p * scale_of(B.sc[r], b);
+                    acc1[r] += p * scale_of(Bf.sc[r][b / 4], b % 4);
                 }
             } else {
                 // A operand: lane l supplies row m = l % 16 of X (zero for m >= M),
@@ -218,7 +229,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                 }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const uint32_t words[4] = {B.w[r][b].x, B.w[r][b].y, B.w[r][b].z, B.w[r][b].w};
+                    const uint32_t words[4] = {Bf.w[r][b].x, Bf.w[r][b].y, Bf.w[r][b].z, Bf.w[r][b].w};
                     f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -226,11 +237,9 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                         unpack8(words[i], U, h);
                         const u32x4 hb = {__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
                                           __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
-                        const f16x8 bw = __builtin_bit_cast(f16x8, hb);
-                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bw, d, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], __builtin_bit_cast(f16x8, hb), d, 0, 0, 0);
                     }
-                    const float sc = scale_of(B.sc[r], b);
-                    accm[r] += d * sc;
+                    accm[r] += d * scale_of(Bf.sc[r][b / 4], b % 4);
                 }
             }
         }
@@ -284,20 +293,20 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     }
 }
 
-template <int R, bool NT, bool MFMA>
+template <int R, int B, bool NT, bool MFMA>
 __global__ __launch_bounds__(kBlock) void w4_gemv_kernel(W4Lin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
-    w4_unit<R, NT, MFMA>(L, u / L.S, u % L.S, xs_dyn);
+    w4_unit<R, B, NT, MFMA>(L, u / L.S, u % L.S, xs_dyn);
 }
 
-template <int R, bool NT, bool MFMA>
+template <int R, int B, bool NT, bool MFMA>
 __global__ __launch_bounds__(kBlock) void w4_grouped_kernel(const W4Lin *__restrict__ lins,
                                                             const Unit *__restrict__ units) {
     extern __shared__ u32x4 xs_dyn[];
     const Unit u = units[blockIdx.x];
     const W4Lin L = lins[u.lin];
-    w4_unit<R, NT, MFMA>(L, u.tile, u.s, xs_dyn);
+    w4_unit<R, B, NT, MFMA>(L, u.tile, u.s, xs_dyn);
 }
 
 // y[m][n] = sum over slices s = 0..S-1, in that order, of part[s][m][n].
@@ -360,45 +369,53 @@ __global__ __launch_bounds__(kBlock) void pack_s4_kernel(const uint16_t *__restr
     Sp[idx] = (n < N && b < kb) ? s4[n * kb + b] : (uint16_t)0;
 }
 
-template <int R, bool NT, bool MFMA>
+template <int R, int B, bool NT, bool MFMA>
 hipError_t launch_one(const W4Lin &L, hipStream_t s) {
     const int units = L.n_tiles * L.S;
-    hipLaunchKernelGGL((w4_gemv_kernel<R, NT, MFMA>), dim3(units), dim3(kBlock), w4_lds_bytes(L), s, L);
+    hipLaunchKernelGGL((w4_gemv_kernel<R, B, NT, MFMA>), dim3(units), dim3(kBlock), w4_lds_bytes(L), s, L);
     return hipGetLastError();
 }
 
-template <int R, bool NT, bool MFMA>
+template <int R, int B, bool NT, bool MFMA>
 hipError_t launch_grp(const W4Lin *lins, const Unit *units, int n, int lds, hipStream_t s) {
-    hipLaunchKernelGGL((w4_grouped_kernel<R, NT, MFMA>), dim3(n), dim3(kBlock), lds, s, lins, units);
+    hipLaunchKernelGGL((w4_grouped_kernel<R, B, NT, MFMA>), dim3(n), dim3(kBlock), lds, s, lins, units);
     return hipGetLastError();
 }
 
-template <bool MFMA>
+// Instantiated shapes: R in {1, 2} tiles, B in {4, 8} blocks per wave step.
+template <bool MFMA, bool NT>
 hipError_t dispatch_one(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
-    if (c.R == 2) return c.nt ? launch_one<2, true, MFMA>(L, s) : launch_one<2, false, MFMA>(L, s);
-    if (c.R == 1) return c.nt ? launch_one<1, true, MFMA>(L, s) : launch_one<1, false, MFMA>(L, s);
+    if (c.R == 1 && c.B == 8) return launch_one<1, 8, NT, MFMA>(L, s);
+    if (c.R == 1 && c.B == 4) return launch_one<1, 4, NT, MFMA>(L, s);
+    if (c.R == 2 && c.B == 8) return launch_one<2, 8, NT, MFMA>(L, s);
+    if (c.R == 2 && c.B == 4) return launch_one<2, 4, NT, MFMA>(L, s);
     return hipErrorInvalidValue;
 }
 
-template <bool MFMA>
+template <bool MFMA, bool NT>
 hipError_t dispatch_grp(const W4Lin *lins, const Unit *units, int n, int lds, const W4Cfg &c, hipStream_t s) {
-    if (c.R == 2) return c.nt ? launch_grp<2, true, MFMA>(lins, units, n, lds, s)
-                              : launch_grp<2, false, MFMA>(lins, units, n, lds, s);
-    if (c.R == 1) return c.nt ? launch_grp<1, true, MFMA>(lins, units, n, lds, s)
-                              : launch_grp<1, false, MFMA>(lins, units, n, lds, s);
+    if (c.R == 1 && c.B == 8) return launch_grp<1, 8, NT, MFMA>(lins, units, n, lds, s);
+    if (c.R == 1 && c.B == 4) return launch_grp<1, 4, NT, MFMA>(lins, units, n, lds, s);
+    if (c.R == 2 && c.B == 8) return launch_grp<2, 8, NT, MFMA>(lins, units, n, lds, s);
+    if (c.R == 2 && c.B == 4) return launch_grp<2, 4, NT, MFMA>(lins, units, n, lds, s);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_w4(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
-    return L.M > 1 ? dispatch_one<true>(L, c, s) : dispatch_one<false>(L, c, s);
+    if (L.M > 1)
+        return c.nt ? dispatch_one<true, true>(L, c, s) : dispatch_one<true, false>(L, c, s);
+    return c.nt ? dispatch_one<false, true>(L, c, s) : dispatch_one<false, false>(L, c, s);
 }
 
 hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes, int max_m,
                              const W4Cfg &c, hipStream_t s) {
-    return max_m > 1 ? dispatch_grp<true>(lins, units, n_units, lds_bytes, c, s)
-                     : dispatch_grp<false>(lins, units, n_units, lds_bytes, c, s);
+    if (max_m > 1)
+        return c.nt ? dispatch_grp<true, true>(lins, units, n_units, lds_bytes, c, s)
+                    : dispatch_grp<true, false>(lins, units, n_units, lds_bytes, c, s);
+    return c.nt ? dispatch_grp<false, true>(lins, units, n_units, lds_bytes, c, s)
+                : dispatch_grp<false, false>(lins, units, n_units, lds_bytes, c, s);
 }
 
 hipError_t launch_w4_reduce(const W4Lin &L, hipStream_t s) {

@@ -86,6 +86,7 @@ inline bool dense_needs_tail(const DenseLin &L, int CH) {
 
 struct W4Cfg {
     int R;        // 16-row tiles per wave step
+    int B;        // 128-wide k-blocks per wave step (4 or 8)
     bool nt;
 };
 
