@@ -264,14 +264,17 @@ def main():
                                         group=128))
                 b += Wc.nbytes + s4.nbytes + X.nbytes + M * N * 4
             torch.cuda.synchronize()
-            st = wsgemv.DecodeStep(wl, wsgemv.STEP_GROUPED, stream=stream)
-            for _ in range(5):
-                st(stream)
-            s = summary(event_times(torch, lambda i: st(stream), 100, stream))
-            extras[f"c5_w4a16_step_M{M}"] = {"bytes": b, "median_us": s["median_ms"] * 1e3,
-                                            "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
-                                            "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
-            st.close()
+            rec = {"bytes": b}
+            # graph replay, and the same single grouped launch enqueued directly
+            for tag, mode in (("graph", wsgemv.STEP_GROUPED), ("launch", wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER)):
+                st = wsgemv.DecodeStep(wl, mode, stream=stream)
+                for _ in range(5):
+                    st(stream)
+                s = summary(event_times(torch, lambda i: st(stream), 100, stream))
+                rec[tag] = {"median_us": s["median_ms"] * 1e3, "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
+                            "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                st.close()
+            extras[f"c5_w4a16_step_M{M}"] = rec
             del wl, w4
 
     if want("probe"):

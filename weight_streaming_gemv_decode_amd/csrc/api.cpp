@@ -217,7 +217,7 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
     const int64_t kb = K / 128;
     const int64_t n_rtiles = cdiv(N, 16);
     W4Plan p;
-    p.cfg = W4Cfg{1, 4, use_nt()};
+    p.cfg = W4Cfg{1, 4, use_nt(), false};
     // LDS holds M rows of the slice: M * kbs * 256 bytes <= 32 KiB.
     const int64_t max_kbs = std::max<int64_t>(4, (32 * 1024 / (256 * std::max<int64_t>(1, M))) / 4 * 4);
     int S;
@@ -236,7 +236,7 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
     p.kbs = S > 1 ? (int)(cdiv(cdiv(kb, S), 4) * 4) : (int)kb;
     // 16-row tiles per unit: 4 (M = 1) or 8 (verify blocks), fewer when the
     // launch would otherwise have under 1024 units.
-    int64_t tt = M > 1 ? 8 : 4;
+    int64_t tt = M > 1 ? 16 : 4;
     while (tt > 1 && cdiv(n_rtiles, tt) * S < kWantUnits)
         tt = tt / 2;
     if (g_tune.w4_tiles > 0)
@@ -494,6 +494,7 @@ wsg_status gemv_w4a16(const void *Wp, const void *Sp, const void *x, float *y, i
         if (st != WSG_OK)
             return st;
         W4Lin L = make_w4(Wp, Sp, x, y, static_cast<float *>(ws), M, N, K, p);
+        p.cfg.tail = w4_needs_tail(L, p.cfg.B);
         return enqueue_w4(L, p.cfg, s);
     });
 }
@@ -704,6 +705,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         std::vector<W4Lin> wl[2];              // grouped W4 linears: [0] M == 1, [1] M > 1
         std::vector<Unit> wu[2];
         int wlds[2] = {0, 0}, wmaxm[2] = {1, 1};
+        bool wtail[2] = {false, false};
         size_t part_bytes = 0;
         // Grouped launches: 8 rows x 1 vector per wave step, units of at least
         // 32 rows (64 KiB at K = 1024 fp16).
@@ -775,6 +777,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     o.type = wsg_step::Op::kW4;
                     o.wc = p.cfg;
                     o.w = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
+                    o.wc.tail = w4_needs_tail(o.w, o.wc.B);
                     st->ops.push_back(o);
                 } else {
                     W4Plan p = plan_w4(l.M, l.N, l.K, 1);
@@ -782,10 +785,11 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     p.kbs = (int)(l.K / 128);
                     const int64_t tile_bytes = 16 * (int64_t)p.kbs * 64;
                     (void)tile_bytes;
-                    // verify blocks: 1 tile per step; M = 1: 2 tiles per step; 8 tiles per unit
-                    p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles : 8;
-                    p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (l.M > 1 ? 1 : 2);
-                    p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : 4;
+                    // M = 1: 1 tile x 8 blocks per step, 4 tiles per unit;
+                    // verify blocks: 2 tiles x 4 blocks per step, 16 tiles per unit
+                    p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles : (l.M > 1 ? 16 : 4);
+                    p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (l.M > 1 ? 2 : 1);
+                    p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (l.M > 1 ? 4 : 8);
                     W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
                     if (w4_lds_bytes(L) > 48 * 1024) {
                         free_step(st);
@@ -798,6 +802,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                         wu[gi].push_back(Unit{li, t, 0, 0});
                     wlds[gi] = std::max(wlds[gi], w4_lds_bytes(L));
                     wmaxm[gi] = std::max(wmaxm[gi], (int)l.M);
+                    wtail[gi] = wtail[gi] || w4_needs_tail(L, p.cfg.B);
                 }
             }
         }
@@ -862,8 +867,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             if (!wu[k].empty()) {
                 wsg_step::Op o{};
                 o.type = wsg_step::Op::kW4Group;
-                o.wc = W4Cfg{g_tune.w4_R > 0 ? (int)g_tune.w4_R : (k == 1 ? 1 : 2), g_tune.w4_B > 0 ? (int)g_tune.w4_B : 4,
-                             use_nt()};
+                o.wc = W4Cfg{g_tune.w4_R > 0 ? (int)g_tune.w4_R : (k == 1 ? 2 : 1),
+                             g_tune.w4_B > 0 ? (int)g_tune.w4_B : (k == 1 ? 4 : 8), use_nt(), wtail[k]};
                 o.lins = base + wl_off[k];
                 o.units = reinterpret_cast<const Unit *>(base + wu_off[k]);
                 o.n_units = (int)wu[k].size();

@@ -86,7 +86,11 @@ __device__ __forceinline__ float scale_of(u32x2 sc, int b) {
 // A wave step covers R tiles x B blocks (B = 4 or 8: 4 or 8 KiB of weights
 // per wave in flight per step, two steps in flight).
 // MFMA = false: M = 1 on the VALU.  MFMA = true: M = 2..8 on the matrix cores.
-template <int R, int B, bool NT, bool MFMA>
+// TAIL = false requires every slice to hold a whole number of steps (the
+// blocks of a slice are a multiple of B): then the step loads carry no
+// guards, and the compiler can keep the next step's loads in flight while
+// the current step is consumed (a guarded load path makes it wait for all).
+template <int R, int B, bool NT, bool MFMA, bool TAIL>
 __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *xs) {
     static_assert(B % 4 == 0, "steps are whole 4-block scale quads");
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -120,7 +124,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             // wave-uniform tile pointers; the lane offset is the only vector part
             const u32x4 *p = L.Wp + (rt * L.kb + kb0 + B * c) * kWave;
             const u32x2 *q = L.Sp + (rt * L.kq + (kb0 + B * c) / 4) * 16;
-            if (B * c + B <= nkb) {
+            if (!TAIL || B * c + B <= nkb) {
 #pragma unroll
                 for (int qq = 0; qq < B / 4; ++qq)
                     Bf.sc[r][qq] = q[qq * 16 + r16];
@@ -193,7 +197,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     auto consume = [&](const Buf &Bf, int gi, int c) {
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            if (B * c + b >= nkb)
+            if (TAIL && B * c + b >= nkb)
                 break;
             const int xv0 = (B * c + b) * 16 + g;  // x vector of word 0 of this lane in the block
             if constexpr (!MFMA) {
@@ -293,20 +297,20 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     }
 }
 
-template <int R, int B, bool NT, bool MFMA>
+template <int R, int B, bool NT, bool MFMA, bool TAIL>
 __global__ __launch_bounds__(kBlock) void w4_gemv_kernel(W4Lin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
-    w4_unit<R, B, NT, MFMA>(L, u / L.S, u % L.S, xs_dyn);
+    w4_unit<R, B, NT, MFMA, TAIL>(L, u / L.S, u % L.S, xs_dyn);
 }
 
-template <int R, int B, bool NT, bool MFMA>
+template <int R, int B, bool NT, bool MFMA, bool TAIL>
 __global__ __launch_bounds__(kBlock) void w4_grouped_kernel(const W4Lin *__restrict__ lins,
                                                             const Unit *__restrict__ units) {
     extern __shared__ u32x4 xs_dyn[];
     const Unit u = units[blockIdx.x];
     const W4Lin L = lins[u.lin];
-    w4_unit<R, B, NT, MFMA>(L, u.tile, u.s, xs_dyn);
+    w4_unit<R, B, NT, MFMA, TAIL>(L, u.tile, u.s, xs_dyn);
 }
 
 // y[m][n] = sum over slices s = 0..S-1, in that order, of part[s][m][n].
@@ -369,53 +373,64 @@ __global__ __launch_bounds__(kBlock) void pack_s4_kernel(const uint16_t *__restr
     Sp[idx] = (n < N && b < kb) ? s4[n * kb + b] : (uint16_t)0;
 }
 
-template <int R, int B, bool NT, bool MFMA>
+template <int R, int B, bool NT, bool MFMA, bool TAIL>
 hipError_t launch_one(const W4Lin &L, hipStream_t s) {
     const int units = L.n_tiles * L.S;
-    hipLaunchKernelGGL((w4_gemv_kernel<R, B, NT, MFMA>), dim3(units), dim3(kBlock), w4_lds_bytes(L), s, L);
+    hipLaunchKernelGGL((w4_gemv_kernel<R, B, NT, MFMA, TAIL>), dim3(units), dim3(kBlock), w4_lds_bytes(L), s, L);
     return hipGetLastError();
 }
 
-template <int R, int B, bool NT, bool MFMA>
+template <int R, int B, bool NT, bool MFMA, bool TAIL>
 hipError_t launch_grp(const W4Lin *lins, const Unit *units, int n, int lds, hipStream_t s) {
-    hipLaunchKernelGGL((w4_grouped_kernel<R, B, NT, MFMA>), dim3(n), dim3(kBlock), lds, s, lins, units);
+    hipLaunchKernelGGL((w4_grouped_kernel<R, B, NT, MFMA, TAIL>), dim3(n), dim3(kBlock), lds, s, lins, units);
     return hipGetLastError();
 }
 
 // Instantiated shapes: R in {1, 2} tiles, B in {4, 8} blocks per wave step.
-template <bool MFMA, bool NT>
+template <bool MFMA, bool NT, bool TAIL>
 hipError_t dispatch_one(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
-    if (c.R == 1 && c.B == 8) return launch_one<1, 8, NT, MFMA>(L, s);
-    if (c.R == 1 && c.B == 4) return launch_one<1, 4, NT, MFMA>(L, s);
-    if (c.R == 2 && c.B == 8) return launch_one<2, 8, NT, MFMA>(L, s);
-    if (c.R == 2 && c.B == 4) return launch_one<2, 4, NT, MFMA>(L, s);
+    if (c.R == 1 && c.B == 8) return launch_one<1, 8, NT, MFMA, TAIL>(L, s);
+    if (c.R == 1 && c.B == 4) return launch_one<1, 4, NT, MFMA, TAIL>(L, s);
+    if (c.R == 2 && c.B == 8) return launch_one<2, 8, NT, MFMA, TAIL>(L, s);
+    if (c.R == 2 && c.B == 4) return launch_one<2, 4, NT, MFMA, TAIL>(L, s);
     return hipErrorInvalidValue;
 }
 
-template <bool MFMA, bool NT>
+template <bool MFMA, bool NT, bool TAIL>
 hipError_t dispatch_grp(const W4Lin *lins, const Unit *units, int n, int lds, const W4Cfg &c, hipStream_t s) {
-    if (c.R == 1 && c.B == 8) return launch_grp<1, 8, NT, MFMA>(lins, units, n, lds, s);
-    if (c.R == 1 && c.B == 4) return launch_grp<1, 4, NT, MFMA>(lins, units, n, lds, s);
-    if (c.R == 2 && c.B == 8) return launch_grp<2, 8, NT, MFMA>(lins, units, n, lds, s);
-    if (c.R == 2 && c.B == 4) return launch_grp<2, 4, NT, MFMA>(lins, units, n, lds, s);
+    if (c.R == 1 && c.B == 8) return launch_grp<1, 8, NT, MFMA, TAIL>(lins, units, n, lds, s);
+    if (c.R == 1 && c.B == 4) return launch_grp<1, 4, NT, MFMA, TAIL>(lins, units, n, lds, s);
+    if (c.R == 2 && c.B == 8) return launch_grp<2, 8, NT, MFMA, TAIL>(lins, units, n, lds, s);
+    if (c.R == 2 && c.B == 4) return launch_grp<2, 4, NT, MFMA, TAIL>(lins, units, n, lds, s);
     return hipErrorInvalidValue;
+}
+
+template <bool MFMA>
+hipError_t one_mfma(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
+    if (c.nt)
+        return c.tail ? dispatch_one<MFMA, true, true>(L, c, s) : dispatch_one<MFMA, true, false>(L, c, s);
+    return c.tail ? dispatch_one<MFMA, false, true>(L, c, s) : dispatch_one<MFMA, false, false>(L, c, s);
+}
+
+template <bool MFMA>
+hipError_t grp_mfma(const W4Lin *lins, const Unit *units, int n, int lds, const W4Cfg &c, hipStream_t s) {
+    if (c.nt)
+        return c.tail ? dispatch_grp<MFMA, true, true>(lins, units, n, lds, c, s)
+                      : dispatch_grp<MFMA, true, false>(lins, units, n, lds, c, s);
+    return c.tail ? dispatch_grp<MFMA, false, true>(lins, units, n, lds, c, s)
+                  : dispatch_grp<MFMA, false, false>(lins, units, n, lds, c, s);
 }
 
 }  // namespace
 
 hipError_t launch_w4(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
-    if (L.M > 1)
-        return c.nt ? dispatch_one<true, true>(L, c, s) : dispatch_one<true, false>(L, c, s);
-    return c.nt ? dispatch_one<false, true>(L, c, s) : dispatch_one<false, false>(L, c, s);
+    return L.M > 1 ? one_mfma<true>(L, c, s) : one_mfma<false>(L, c, s);
 }
 
 hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes, int max_m,
                              const W4Cfg &c, hipStream_t s) {
-    if (max_m > 1)
-        return c.nt ? dispatch_grp<true, true>(lins, units, n_units, lds_bytes, c, s)
-                    : dispatch_grp<true, false>(lins, units, n_units, lds_bytes, c, s);
-    return c.nt ? dispatch_grp<false, true>(lins, units, n_units, lds_bytes, c, s)
-                : dispatch_grp<false, false>(lins, units, n_units, lds_bytes, c, s);
+    return max_m > 1 ? grp_mfma<true>(lins, units, n_units, lds_bytes, c, s)
+                     : grp_mfma<false>(lins, units, n_units, lds_bytes, c, s);
 }
 
 hipError_t launch_w4_reduce(const W4Lin &L, hipStream_t s) {

@@ -88,7 +88,14 @@ struct W4Cfg {
     int R;        // 16-row tiles per wave step
     int B;        // 128-wide k-blocks per wave step (4 or 8)
     bool nt;
+    bool tail;    // some k-slice is not a whole number of B-block steps
 };
+
+// True when a slice of this linear ends inside a step of B blocks.
+inline bool w4_needs_tail(const W4Lin &L, int B) {
+    const int last = L.kb - (L.S - 1) * L.kbs;
+    return (L.kbs % B) != 0 || (last % B) != 0;
+}
 
 // ----- launchers (each defined next to its kernels) -----
 hipError_t launch_dense(int kind, const DenseLin &L, const DenseCfg &c, hipStream_t s);
