@@ -55,7 +55,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_gemv_f16.argtypes = [P, P, I64, I64, P, P]
     lib.orc_gemv_w8a8.argtypes = [P, P, P, ctypes.c_float, I64, I64, P, P, P]
     lib.orc_gemv_w4a16.argtypes = [P, P, P, I64, I64, I64, I64, P, P]
-    for f in (lib.orc_f16_decode, lib.orc_gemv_f16, lib.orc_gemv_w8a8, lib.orc_gemv_w4a16):
+    lib.orc_quantize_x_i8.argtypes = [P, I64, P, P]
+    lib.orc_gemv_w4a8.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P]
+    for f in (lib.orc_f16_decode, lib.orc_gemv_f16, lib.orc_gemv_w8a8, lib.orc_gemv_w4a16,
+              lib.orc_quantize_x_i8, lib.orc_gemv_w4a8):
         f.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_set_threads.restype = None
@@ -166,6 +169,33 @@ def gemv_w4a16(Wc: np.ndarray, s4: np.ndarray, X: np.ndarray, group: int = 128,
     if squeeze:
         return Y[0], A[0]
     return Y, A
+
+
+def quantize_x_i8(x: np.ndarray, lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.float32]:
+    """(xq int8 [K], s_x fp32): per-token symmetric int8 quantisation of fp16 x."""
+    x = _u16(x)
+    K = x.shape[0]
+    xq = np.empty(K, np.int8)
+    sx = np.empty(1, np.float32)
+    _check((lib or load()).orc_quantize_x_i8(_ptr(x), K, _ptr(xq), _ptr(sx)), "quantize_x_i8")
+    return xq, sx[0]
+
+
+def gemv_w4a8(Wc: np.ndarray, s4: np.ndarray, xq: np.ndarray, s_x: float, group: int = 128,
+              lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """(y, A) for canonical int4 words times int8 activations xq with scale s_x."""
+    Wc = np.ascontiguousarray(Wc, dtype=np.uint32)
+    s4 = _u16(s4)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    N = Wc.shape[0]
+    K = xq.shape[0]
+    if Wc.shape != (N, K // 8) or s4.shape != (N, K // group):
+        raise ValueError("shape mismatch")
+    y = np.empty(N, np.float64)
+    A = np.empty(N, np.float64)
+    _check((lib or load()).orc_gemv_w4a8(_ptr(Wc), _ptr(s4), _ptr(xq), float(np.float32(s_x)), N, K, group,
+                                         _ptr(y), _ptr(A)), "gemv_w4a8")
+    return y, A
 
 
 def decode_step_f16(linears: Iterable[Tuple[np.ndarray, np.ndarray]],

@@ -64,6 +64,14 @@ static int f16_value(uint16_t h, double *out)
     return ORC_OK;
 }
 
+/* Canonical int4 layout: element k of a row is the 4-bit field at bits
+ * [4*(k%8), 4*(k%8)+3] of word k/8 of that row; q in 0..15. */
+static int q4_canonical(const uint32_t *row_words, int64_t k)
+{
+    uint32_t word = row_words[k / 8];
+    return (int)((word >> (4 * (k % 8))) & 15u);
+}
+
 static void note_error(int *shared, int code)
 {
     if (code != ORC_OK) {
@@ -168,8 +176,7 @@ int orc_gemv_w4a16(const uint32_t *Wc, const uint16_t *s4, const uint16_t *X,
         for (int64_t m = 0; m < M; ++m) {
             double s = 0.0, a = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                uint32_t word = Wc[n * words + k / 8];
-                int q = (int)((word >> (4 * (k % 8))) & 15u);
+                int q = q4_canonical(Wc + n * words, k);
                 double scale;
                 int e = f16_value(s4[n * groups + k / group], &scale);
                 if (e != ORC_OK)
@@ -185,6 +192,80 @@ int orc_gemv_w4a16(const uint32_t *Wc, const uint16_t *s4, const uint16_t *X,
         }
     }
     free(xd);
+    return err;
+}
+
+/* Dynamic per-token activation quantisation for the 4-bit-weight x 8-bit-
+ * activation product (vLLM Arm CPU optimisation post, INT8 W4A8 section:
+ * 4-bit weights, 8-bit activations).  The pages fix no quantiser; the
+ * reading used here is symmetric per token in fp32:
+ *   amax = max_k |x_k|,  s_x = amax / 127  (fp32, round to nearest even),
+ *   xq_k = clamp(rint(x_k / s_x), -127, 127)  (fp32 division, ties to even),
+ *   and amax == 0 gives s_x = 0, xq = 0.
+ * Every step is a single IEEE fp32 operation, so any IEEE implementation
+ * that performs the same operations gets the same xq bit for bit. */
+int orc_quantize_x_i8(const uint16_t *x, int64_t K, int8_t *xq, float *s_x)
+{
+    if (K < 0)
+        return ORC_ERR_SHAPE;
+    float amax = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        double v;
+        int e = f16_value(x[k], &v);
+        if (e != ORC_OK)
+            return e;
+        float a = fabsf((float)v);          /* fp16 -> fp32 is exact */
+        if (a > amax)
+            amax = a;
+    }
+    volatile float s = amax / 127.0f;      /* volatile: keep exactly these fp32 operations */
+    *s_x = s;
+    for (int64_t k = 0; k < K; ++k) {
+        double v;
+        f16_value(x[k], &v);
+        if (amax == 0.0f) {
+            xq[k] = 0;
+            continue;
+        }
+        volatile float t = (float)v / s;
+        float r = rintf(t);
+        if (r > 127.0f)
+            r = 127.0f;
+        if (r < -127.0f)
+            r = -127.0f;
+        xq[k] = (int8_t)r;
+    }
+    return ORC_OK;
+}
+
+/* 4-bit weights (canonical words, zero-point 8, fp16 group scales as in
+ * orc_gemv_w4a16) times 8-bit activations xq with scale s_x:
+ *   y[n] = s_x * sum_k (q[n,k] - 8) * s4[n, k/group] * xq[k]   in double,
+ *   A[n] = s_x * sum_k |(q[n,k] - 8) * s4[n, k/group] * xq[k]|. */
+int orc_gemv_w4a8(const uint32_t *Wc, const uint16_t *s4, const int8_t *xq, float s_x,
+                  int64_t N, int64_t K, int64_t group, double *y, double *A)
+{
+    if (N < 0 || K < 0 || group <= 0 || K % 8 || K % group)
+        return ORC_ERR_SHAPE;
+    int err = ORC_OK;
+    int64_t words = K / 8, groups = K / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double s = 0.0, a = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            int q = q4_canonical(Wc + n * words, k);
+            double scale;
+            int e = f16_value(s4[n * groups + (k / group)], &scale);
+            if (e != ORC_OK)
+                note_error(&err, e);
+            double p = (double)(q - 8) * scale * (double)xq[k];
+            s += p;
+            a += fabs(p);
+        }
+        y[n] = s * (double)s_x;
+        if (A)
+            A[n] = a * fabs((double)s_x);
+    }
     return err;
 }
 

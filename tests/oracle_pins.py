@@ -235,8 +235,69 @@ def pin_w4_exact_rational(lib, N=3, K=256, seed=17):
         assert abs(Fraction(y[n]) - exact) <= tol, (n, y[n], float(exact))
 
 
+# ---------------------------------------------------------------- w4a8 ---
+
+def pin_quant_golden(lib):
+    g = _golden("w4a8_quant.json")
+    for c in g["cases"]:
+        xq, sx = oracle.quantize_x_i8(np.array(c["x"], np.float16), lib=lib)
+        assert xq.tolist() == c["xq"], (c["x"], xq.tolist(), c["xq"])
+        assert float(sx) == c["s_x"], (sx, c["s_x"])
+
+
+def pin_quant_properties(lib, K=3000, seed=18):
+    x = synth.f16_normal(907, seed, (K,), synth.X_SIGMA)
+    xq, sx = oracle.quantize_x_i8(x, lib=lib)
+    xf = x.astype(np.float32)
+    amax = np.max(np.abs(xf))
+    assert sx == np.float32(amax) / np.float32(127), "s_x must be fp32 max|x| / 127"
+    assert np.all(np.abs(xq.astype(np.int32)) <= 127)
+    assert np.all(np.abs(xq[np.abs(xf) == amax].astype(np.int32)) == 127), "max |x| must map to +-127"
+    assert np.all(np.sign(xq) == np.sign(np.rint(xf / sx)))
+    # round to nearest: every code is within half a step of x / s_x
+    assert np.all(np.abs(xf.astype(np.float64) / float(sx) - xq) <= 0.5 + 1e-6)
+    # numpy's own IEEE fp32 division and half-to-even rounding give the same codes
+    assert np.array_equal(np.clip(np.rint(xf / sx), -127, 127).astype(np.int8), xq)
+
+
+def pin_w4a8_golden(lib):
+    g = _golden("w4_nibble_order.json")
+    K = g["K"]
+    for row in g["rows"]:
+        if row["scale_bits"] != "0x3C00":
+            continue
+        Wc = np.full((1, K // 8), int(row["rest"], 16), np.uint32)
+        Wc[0, 0] = int(row["word0"], 16)
+        s4 = np.array([[0x3C00]], np.uint16)
+        for j, want in enumerate(row["y_onehot_j0_to_7"]):
+            xq = np.zeros(K, np.int8)
+            xq[j] = 1
+            y, _ = oracle.gemv_w4a8(Wc, s4, xq, 1.0, lib=lib)
+            assert y[0] == want, (row["word0"], j, y[0])
+            y, _ = oracle.gemv_w4a8(Wc, s4, 3 * xq, 0.5, lib=lib)
+            assert y[0] == 1.5 * want
+
+
+def pin_w4a8_integer_matmul(lib, N=23, K=512, seed=19):
+    Wc = synth.w4_words(908, seed, N, K)
+    xq = synth.int8_uniform(908, seed + 1, (K,))
+    xq[:2] = -127
+    ones = np.full((N, K // 128), 0x3C00, np.uint16)
+    y, A = oracle.gemv_w4a8(Wc, ones, xq, 1.0, lib=lib)
+    w = _unpack_canonical(Wc) - 8
+    ref = w @ xq.astype(np.int64)
+    assert np.array_equal(y, ref.astype(np.float64)), "unit scales: y must be the exact integer product"
+    assert np.array_equal(A, (np.abs(w) @ np.abs(xq.astype(np.int64))).astype(np.float64))
+    s4 = synth.f16_uniform(908, seed + 2, (N, K // 128), 0.002, 0.02)
+    y2, A2 = oracle.gemv_w4a8(Wc, s4, xq, 0.03125, lib=lib)
+    wf = w.astype(np.float64) * np.repeat(s4.astype(np.float64), 128, axis=1)
+    ref2 = (wf @ xq.astype(np.float64)) * 0.03125
+    assert np.all(np.abs(y2 - ref2) <= 1e-12 * A2 + 1e-300)
+
+
 ALL_PINS = [
     pin_f16_decode_all_patterns, pin_f16_golden, pin_f16_exact_rational, pin_f16_closed_forms,
     pin_f16_numpy_matmul, pin_f16_scaling, pin_w8a8_golden, pin_w8a8_int64_matmul,
     pin_w8a8_int32_range, pin_w4_golden, pin_w4_numpy_dequant, pin_w4_exact_rational,
+    pin_quant_golden, pin_quant_properties, pin_w4a8_golden, pin_w4a8_integer_matmul,
 ]

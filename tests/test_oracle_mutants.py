@@ -23,9 +23,17 @@ MUTANTS = [
     ("w8_no_range_check", "if (s > INT32_MAX || s < INT32_MIN)", "if (0)"),
     ("w8_scale_missing_x", "(double)w_scale[n] * (double)x_scale", "(double)w_scale[n]"),
     ("w4_nibble_order", "(word >> (4 * (k % 8)))", "(word >> (4 * (7 - k % 8)))"),
-    ("w4_zero_point", "(double)(q - 8)", "(double)(q - 7)"),
+    ("w4_zero_point", "double w = (double)(q - 8) * scale;", "double w = (double)(q - 7) * scale;"),
     ("w4_group_index", "s4[n * groups + k / group]", "s4[n * groups + (k / 8) % groups]"),
+    ("w4a8_group_index", "s4[n * groups + (k / group)]", "s4[n * groups + (k / 8) % groups]"),
     ("w4_activation_row", "w * xd[m * K + k]", "w * xd[k]"),
+    ("quant_ties_away", "float r = rintf(t);", "float r = roundf(t);"),
+    ("quant_truncate", "float r = rintf(t);", "float r = truncf(t);"),
+    ("quant_signed_max", "float a = fabsf((float)v);", "float a = (float)v;"),
+    ("quant_scale_255", "volatile float s = amax / 127.0f;", "volatile float s = amax / 255.0f;"),
+    ("w4a8_zero_point", "double p = (double)(q - 8) * scale * (double)xq[k];",
+     "double p = (double)(q - 7) * scale * (double)xq[k];"),
+    ("w4a8_no_sx", "y[n] = s * (double)s_x;", "y[n] = s;"),
 ]
 
 
