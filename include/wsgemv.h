@@ -63,7 +63,7 @@ enum {
     WSG_ERR_STATE = 8        /* NULL or destroyed plan */
 };
 
-enum { WSG_F16 = 0, WSG_W8A8 = 1, WSG_W4A16 = 2 }; /* wsg_linear.kind */
+enum { WSG_F16 = 0, WSG_W8A8 = 1, WSG_W4A16 = 2, WSG_W4A8 = 3 }; /* wsg_linear.kind */
 
 const char *wsg_status_string(wsg_status s);
 int32_t wsg_last_hip_error(void);
@@ -138,6 +138,25 @@ wsg_status gemv_w4a16(const void *Wp, const void *Sp, const void *x, float *y,
                       int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream);
 
 /*
+ * INT4 weights x INT8 activations with dynamic per-token activation
+ * quantisation fused into the product, M = 1 (vLLM Arm CPU optimisation
+ * post, INT8 W4A8 section: 4-bit weights with 8-bit activations, which cut
+ * memory-bandwidth pressure further than W8A8).
+ *   Wp, Sp   packed by wsg_pack_w4 (the same packed weights as gemv_w4a16)
+ *   x        fp16 [K], 16-byte aligned
+ *   s_x      = fp32(max_k |x_k|) / 127 (fp32, round to nearest even);
+ *   xq[k]    = clamp(rint(x[k] / s_x), -127, 127) (fp32 division, ties to
+ *              even); max|x| == 0 gives s_x = 0 and xq = 0
+ *   y[n]     = s_x * sum_g s4[n,g] * sum_{k in g} (q[n,k] - 8) * xq[k], the
+ *              inner sums exact in int32, fp32 y
+ *   xq_out   optional int8 [K] (8-byte aligned) receives xq; sx_out optional
+ *            fp32 [1] receives s_x.
+ */
+wsg_status gemv_w4a8(const void *Wp, const void *Sp, const void *x, float *y, int8_t *xq_out,
+                     float *sx_out, int64_t N, int64_t K, int64_t group,
+                     int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream);
+
+/*
  * Decode step: a fixed list of linears replayed once per token (EdgeFM
  * summary, section 2C: an execution graph is captured once and reused on
  * every decode iteration to cut kernel-launch overhead).
@@ -158,16 +177,16 @@ wsg_status gemv_w4a16(const void *Wp, const void *Sp, const void *x, float *y,
  * thread-safe and one plan's steps must not overlap each other in time.
  */
 typedef struct wsg_linear {
-    int32_t kind;        /* WSG_F16, WSG_W8A8 or WSG_W4A16 */
+    int32_t kind;        /* WSG_F16, WSG_W8A8, WSG_W4A16 or WSG_W4A8 */
     int32_t M;           /* 1; or 1..8 for WSG_W4A16 */
     int64_t N, K;
-    const void *W;       /* F16: fp16 [N,K]; W8A8: int8 [N,K]; W4A16: packed Wp */
-    const void *scale;   /* W8A8: fp32 [N]; W4A16: packed Sp; F16: NULL */
-    const void *x;       /* F16, W4A16: fp16 [M,K]; W8A8: int8 [K] */
+    const void *W;       /* F16: fp16 [N,K]; W8A8: int8 [N,K]; W4A16, W4A8: packed Wp */
+    const void *scale;   /* W8A8: fp32 [N]; W4A16, W4A8: packed Sp; F16: NULL */
+    const void *x;       /* F16, W4A16, W4A8: fp16 [M,K]; W8A8: int8 [K] */
     const float *x_scale;/* W8A8: fp32 [1]; otherwise NULL */
     float *y;            /* fp32 [M,N] */
     int32_t *acc_out;    /* W8A8: optional int32 [N]; otherwise NULL */
-    int32_t group;       /* W4A16: 128; otherwise 0 */
+    int32_t group;       /* W4A16, W4A8: 128; otherwise 0 */
     int32_t splits;      /* 0 = table's choice; ORDERED mode only */
 } wsg_linear;
 

@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = wsgemv.header_functions()
-    assert {"gemv_f16", "gemv_w8a8", "gemv_w4a16", "decode_step_linears", "wsg_pack_w4",
+    assert {"gemv_f16", "gemv_w8a8", "gemv_w4a16", "gemv_w4a8", "decode_step_linears", "wsg_pack_w4",
             "wsg_decode_step_create"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/wsgemv.h but not exported"
@@ -85,6 +85,20 @@ def test_w4_validation_and_sizes(L):
     assert f(FAKE, None, FAKE, FAKE, 1, 16, 256, 128, 0, None, 0, None) == NULL
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 16, 256, 128, 3, None, 0, None) == SHAPE    # slice past K
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 16, 1024, 128, 2, None, 0, None) == WS
+    g = L.gemv_w4a8
+    a8 = lambda **kw: [kw.get("Wp", FAKE), FAKE, kw.get("x", FAKE), FAKE, kw.get("xq", None),  # noqa: E731
+                       kw.get("sx", None), kw.get("N", 16), kw.get("K", 256), kw.get("group", 128),
+                       kw.get("S", 0), None, 0, None]
+    assert g(*a8(group=64)) == UNSUP
+    assert g(*a8(K=192)) == SHAPE                                               # K % 128
+    assert g(*a8(Wp=None)) == NULL
+    assert g(*a8(x=MIS)) == ALIGN
+    assert g(*a8(xq=FAKE + 4)) == ALIGN                                         # codes 8-byte aligned
+    assert g(*a8(sx=FAKE + 2)) == ALIGN
+    assert g(*a8(S=3)) == SHAPE                                                 # slice past K
+    assert g(*a8(N=16, K=1024, S=2)) == WS
+    assert L.wsg_workspace_bytes(3, 1, 16, 1024, 2) == 2 * 16 * 4
+    assert g(*a8(N=0)) == OK                                                    # nothing to do
 
 
 def test_launch_table(L):
@@ -116,6 +130,8 @@ def test_decode_step_validation(L):
     assert L.wsg_decode_step_create(bad, 1, 0, None, ctypes.byref(out)) == NULL    # W8A8 without scales
     bad = (wsgemv.wsg_linear * 1)(wsgemv.wsg_linear(0, 1, 64, 4096, FAKE, None, FAKE, None, FAKE, None, 0, 2))
     assert L.wsg_decode_step_create(bad, 1, 1, None, ctypes.byref(out)) == UNSUP   # GROUPED forbids splits
+    bad = (wsgemv.wsg_linear * 1)(wsgemv.wsg_linear(3, 2, 64, 256, FAKE, FAKE, FAKE, None, FAKE, None, 128, 0))
+    assert L.wsg_decode_step_create(bad, 1, 0, None, ctypes.byref(out)) == UNSUP   # W4A8 with M = 2
     assert L.decode_step_linears(None, None) == STATE
     assert L.wsg_decode_step_destroy(None) == STATE
 

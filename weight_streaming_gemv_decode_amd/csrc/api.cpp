@@ -312,8 +312,8 @@ size_t w4_ws_bytes(const W4Plan &p, int64_t M, int64_t N) {
     return p.S > 1 ? (size_t)p.S * (size_t)M * (size_t)N * 4 : 0;
 }
 
-wsg_status enqueue_w4(const W4Lin &L, const W4Cfg &cfg, hipStream_t s) {
-    hipError_t e = launch_w4(L, cfg, s);
+wsg_status enqueue_w4(const W4Lin &L, int mode, const W4Cfg &cfg, hipStream_t s) {
+    hipError_t e = launch_w4(L, mode, cfg, s);
     if (e != hipSuccess)
         return hip_fail(e);
     if (L.S > 1) {
@@ -368,7 +368,7 @@ int32_t wsg_plan_splits(int32_t kind, int64_t M, int64_t N, int64_t K) {
             return 1;
         return plan_dense(kind, N, K, 0).S;
     }
-    if (kind == kW4A16) {
+    if (kind == kW4A16 || kind == kW4A8) {
         if (K % 128 || M < 1)
             return 1;
         return plan_w4(M, N, K, 0).S;
@@ -384,7 +384,7 @@ size_t wsg_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K, int32_
             return 0;
         return dense_ws_bytes(plan_dense(kind, N, K, splits), N);
     }
-    if (kind == kW4A16) {
+    if (kind == kW4A16 || kind == kW4A8) {
         if (K % 128 || M < 1)
             return 0;
         return w4_ws_bytes(plan_w4(M, N, K, splits), M, N);
@@ -495,7 +495,7 @@ wsg_status gemv_w4a16(const void *Wp, const void *Sp, const void *x, float *y, i
             return st;
         W4Lin L = make_w4(Wp, Sp, x, y, static_cast<float *>(ws), M, N, K, p);
         p.cfg.tail = w4_needs_tail(L, p.cfg.B);
-        return enqueue_w4(L, p.cfg, s);
+        return enqueue_w4(L, M > 1 ? kMfma : kA16, p.cfg, s);
     });
 }
 
@@ -535,6 +535,34 @@ wsg_status wsg_tune_set(const char *key, int64_t value) {
         }
     }
     return WSG_ERR_UNSUPPORTED;
+}
+
+wsg_status gemv_w4a8(const void *Wp, const void *Sp, const void *x, float *y, int8_t *xq_out, float *sx_out,
+                     int64_t N, int64_t K, int64_t group, int32_t splits, void *ws, size_t ws_bytes,
+                     wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_w4_args(Wp, Sp, x, y, 1, N, K, group, splits);
+        if (st != WSG_OK || N == 0)
+            return st;
+        if ((xq_out && !aligned(xq_out, 8)) || (sx_out && !aligned(sx_out, 4)))
+            return WSG_ERR_ALIGN;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (K == 0) {
+            hipError_t e = launch_zero_f32(y, N, s);
+            if (e == hipSuccess && sx_out)
+                e = launch_zero_f32(sx_out, 1, s);
+            return e == hipSuccess ? WSG_OK : hip_fail(e);
+        }
+        W4Plan p = plan_w4(1, N, K, splits);
+        st = check_ws(ws, ws_bytes, w4_ws_bytes(p, 1, N));
+        if (st != WSG_OK)
+            return st;
+        W4Lin L = make_w4(Wp, Sp, x, y, static_cast<float *>(ws), 1, N, K, p);
+        L.xq_out = xq_out;
+        L.sx_out = sx_out;
+        p.cfg.tail = w4_needs_tail(L, p.cfg.B);
+        return enqueue_w4(L, kA8, p.cfg, s);
+    });
 }
 
 int32_t wsg_read_probe_grid(size_t bytes) {
@@ -581,7 +609,7 @@ struct wsg_step {
         const Unit *units = nullptr;
         int n_units = 0;
         int lds = 0;
-        int max_m = 1;
+        int mode = 0;                 // W4 kernel mode (kA16, kMfma, kA8)
         float *zero_p = nullptr;
         int64_t zero_n = 0;
     };
@@ -613,6 +641,10 @@ wsg_status validate_linear(const wsg_linear &l) {
     }
     case kW4A16:
         return check_w4_args(l.W, l.scale, l.x, l.y, l.M, l.N, l.K, l.group, l.splits);
+    case kW4A8:
+        if (l.M != 1)
+            return WSG_ERR_UNSUPPORTED;
+        return check_w4_args(l.W, l.scale, l.x, l.y, 1, l.N, l.K, l.group, l.splits);
     default:
         return WSG_ERR_UNSUPPORTED;
     }
@@ -632,12 +664,12 @@ hipError_t run_ops(const wsg_step *st, hipStream_t s) {
                                      op.dc, s);
             break;
         case wsg_step::Op::kW4:
-            e = launch_w4(op.w, op.wc, s);
+            e = launch_w4(op.w, op.mode, op.wc, s);
             if (e == hipSuccess && op.w.S > 1)
                 e = launch_w4_reduce(op.w, s);
             break;
         case wsg_step::Op::kW4Group:
-            e = launch_w4_grouped(static_cast<const W4Lin *>(op.lins), op.units, op.n_units, op.lds, op.max_m,
+            e = launch_w4_grouped(static_cast<const W4Lin *>(op.lins), op.units, op.n_units, op.lds, op.mode,
                                   op.wc, s);
             break;
         case wsg_step::Op::kZero:
@@ -702,10 +734,11 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         std::vector<Unit> du[2];
         int dlds[2] = {0, 0};
         bool dtail[2] = {false, false};
-        std::vector<W4Lin> wl[2];              // grouped W4 linears: [0] M == 1, [1] M > 1
-        std::vector<Unit> wu[2];
-        int wlds[2] = {0, 0}, wmaxm[2] = {1, 1};
-        bool wtail[2] = {false, false};
+        std::vector<W4Lin> wl[3];              // grouped int4 linears per kernel mode (kA16, kMfma, kA8)
+        std::vector<Unit> wu[3];
+        int wlds[3] = {0, 0, 0};
+        bool wtail[3] = {false, false, false};
+        W4Cfg wcfg[3] = {};
         size_t part_bytes = 0;
         // Grouped launches: 8 rows x 1 vector per wave step, units of at least
         // 32 rows (64 KiB at K = 1024 fp16).
@@ -770,11 +803,13 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     dtail[ki] = dtail[ki] || dense_needs_tail(L, gcfg.CH);
                 }
             } else {
+                const int wmode = l.kind == kW4A8 ? kA8 : (l.M > 1 ? kMfma : kA16);
                 if (base_mode == WSG_STEP_ORDERED) {
                     W4Plan p = plan_w4(l.M, l.N, l.K, l.splits);
                     part_bytes = std::max(part_bytes, w4_ws_bytes(p, l.M, l.N));
                     wsg_step::Op o{};
                     o.type = wsg_step::Op::kW4;
+                    o.mode = wmode;
                     o.wc = p.cfg;
                     o.w = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
                     o.wc.tail = w4_needs_tail(o.w, o.wc.B);
@@ -791,34 +826,33 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (l.M > 1 ? 2 : 1);
                     p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (l.M > 1 ? 4 : 8);
                     W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
-                    if (w4_lds_bytes(L) > 48 * 1024) {
+                    if (w4_lds_bytes(L, wmode) > 48 * 1024) {
                         free_step(st);
                         return WSG_ERR_UNSUPPORTED;
                     }
-                    const int gi = l.M > 1 ? 1 : 0;
-                    const int li = (int)wl[gi].size();
-                    wl[gi].push_back(L);
+                    const int li = (int)wl[wmode].size();
+                    wl[wmode].push_back(L);
                     for (int t = 0; t < L.n_tiles; ++t)
-                        wu[gi].push_back(Unit{li, t, 0, 0});
-                    wlds[gi] = std::max(wlds[gi], w4_lds_bytes(L));
-                    wmaxm[gi] = std::max(wmaxm[gi], (int)l.M);
-                    wtail[gi] = wtail[gi] || w4_needs_tail(L, p.cfg.B);
+                        wu[wmode].push_back(Unit{li, t, 0, 0});
+                    wlds[wmode] = std::max(wlds[wmode], w4_lds_bytes(L, wmode));
+                    wtail[wmode] = wtail[wmode] || w4_needs_tail(L, p.cfg.B);
+                    wcfg[wmode] = p.cfg;
                 }
             }
         }
 
-        // Device block: [partials][dense tables x2][w4 tables x2]
+        // Device block: [partials][dense tables x2][int4 tables x3]
         size_t off = 0;
         const size_t part_off = off;
         off = align_up(off + part_bytes, 256);
-        size_t dl_off[2], du_off[2], wl_off[2], wu_off[2];
+        size_t dl_off[2], du_off[2], wl_off[3], wu_off[3];
         for (int k = 0; k < 2; ++k) {
             dl_off[k] = off;
             off = align_up(off + dl[k].size() * sizeof(DenseLin), 256);
             du_off[k] = off;
             off = align_up(off + du[k].size() * sizeof(Unit), 256);
         }
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < 3; ++k) {
             wl_off[k] = off;
             off = align_up(off + wl[k].size() * sizeof(W4Lin), 256);
             wu_off[k] = off;
@@ -841,6 +875,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         for (int k = 0; k < 2; ++k) {
             put(dl_off[k], dl[k].data(), dl[k].size() * sizeof(DenseLin));
             put(du_off[k], du[k].data(), du[k].size() * sizeof(Unit));
+        }
+        for (int k = 0; k < 3; ++k) {
             put(wl_off[k], wl[k].data(), wl[k].size() * sizeof(W4Lin));
             put(wu_off[k], wu[k].data(), wu[k].size() * sizeof(Unit));
         }
@@ -864,16 +900,18 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                 o.lds = dlds[k];
                 st->ops.push_back(o);
             }
+        }
+        for (int k = 0; k < 3; ++k) {
             if (!wu[k].empty()) {
                 wsg_step::Op o{};
                 o.type = wsg_step::Op::kW4Group;
-                o.wc = W4Cfg{g_tune.w4_R > 0 ? (int)g_tune.w4_R : (k == 1 ? 2 : 1),
-                             g_tune.w4_B > 0 ? (int)g_tune.w4_B : (k == 1 ? 4 : 8), use_nt(), wtail[k]};
+                o.wc = wcfg[k];
+                o.wc.tail = wtail[k];
                 o.lins = base + wl_off[k];
                 o.units = reinterpret_cast<const Unit *>(base + wu_off[k]);
                 o.n_units = (int)wu[k].size();
                 o.lds = wlds[k];
-                o.max_m = wmaxm[k];
+                o.mode = k;
                 st->ops.push_back(o);
             }
         }

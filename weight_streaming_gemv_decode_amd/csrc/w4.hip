@@ -33,6 +33,16 @@
 //
 // Scales are packed per (tile, 4 consecutive blocks, row): 4 fp16 in 8 bytes,
 // so a lane fetches the scales of a 4-block step with one 8-byte load.
+//
+// int8 activations (vLLM Arm CPU optimisation post, INT8 W4A8 section: 4-bit
+// weights times 8-bit activations).  Every workgroup computes the per-token
+// scale s_x = max|x| / 127 of the whole fp16 row itself (a max is order-free,
+// so all workgroups agree bit for bit), quantises its k-slice to int8 with
+// ties-to-even and a +-127 clamp into LDS, and then each packed word costs
+// two masks and two v_dot4_i32_i8: the nibbles (e0,e4,e1,e5) and
+// (e2,e6,e3,e7) of the word's interleaved order meet activation bytes staged
+// in that same order.  The zero-point enters exactly, in integers, as an
+// initial accumulator of -8 * (sum of the lane's 32 activation codes).
 #include "wsg_common.hpp"
 
 namespace wsg {
@@ -85,12 +95,14 @@ __device__ __forceinline__ float scale_of(u32x2 sc, int b) {
 // One work unit: `tile_rtiles` 16-row tiles starting at unit `tile`, k-slice s.
 // A wave step covers R tiles x B blocks (B = 4 or 8: 4 or 8 KiB of weights
 // per wave in flight per step, two steps in flight).
-// MFMA = false: M = 1 on the VALU.  MFMA = true: M = 2..8 on the matrix cores.
+// MODE kA16: fp16 activations, M = 1 on the VALU.  kMfma: fp16 activations,
+// M = 2..8 on the matrix cores.  kA8: int8 activations quantised in the
+// prologue, M = 1 on the VALU.
 // TAIL = false requires every slice to hold a whole number of steps (the
 // blocks of a slice are a multiple of B): then the step loads carry no
 // guards, and the compiler can keep the next step's loads in flight while
 // the current step is consumed (a guarded load path makes it wait for all).
-template <int R, int B, bool NT, bool MFMA, bool TAIL>
+template <int R, int B, bool NT, int MODE, bool TAIL>
 __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *xs) {
     static_assert(B % 4 == 0, "steps are whole 4-block scale quads");
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -108,7 +120,9 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     const int ngroups = (nrt + R - 1) / R;
     const int mygroups = wave < ngroups ? (ngroups - 1 - wave) / kWavesPerBlock + 1 : 0;
     const int nsteps = mygroups * nquad;
+    constexpr bool MFMA = MODE == kMfma;
     const int M = MFMA ? L.M : 1;
+    float sx = 1.0f;  // kA8: activation scale of this row
     const Unpack U;
 
     struct Buf {
@@ -165,6 +179,8 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                 float v = acc1[r];
                 v += __shfl_xor(v, 16);
                 v += __shfl_xor(v, 32);
+                if constexpr (MODE == kA8)
+                    v *= sx;
                 const int64_t n = rt * 16 + r16;
                 if (lane < 16 && rt <= last_rt && n < L.N) {
                     if (L.S > 1)
@@ -200,7 +216,28 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             if (TAIL && B * c + b >= nkb)
                 break;
             const int xv0 = (B * c + b) * 16 + g;  // x vector of word 0 of this lane in the block
-            if constexpr (!MFMA) {
+            if constexpr (MODE == kA8) {
+                // activation codes of this lane's 4 words: 2 x 16 bytes; the
+                // lane's zero-point term -8 * sum(codes) starts the chain
+                const int pg = (B * c + b) * 4 + g;
+                const u32x4 xa = xs[2 * pg], xb = xs[2 * pg + 1];
+                const int zs = -8 * reinterpret_cast<const int *>(xs + 8 * nkb)[pg];
+                constexpr uint32_t kLo = 0x0F0F0F0Fu;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t w0 = Bf.w[r][b].x, w1 = Bf.w[r][b].y, w2 = Bf.w[r][b].z, w3 = Bf.w[r][b].w;
+                    int a = zs;
+                    a = __builtin_amdgcn_sdot4((int)(w0 & kLo), (int)xa.x, a, false);
+                    a = __builtin_amdgcn_sdot4((int)((w0 >> 4) & kLo), (int)xa.y, a, false);
+                    a = __builtin_amdgcn_sdot4((int)(w1 & kLo), (int)xa.z, a, false);
+                    a = __builtin_amdgcn_sdot4((int)((w1 >> 4) & kLo), (int)xa.w, a, false);
+                    a = __builtin_amdgcn_sdot4((int)(w2 & kLo), (int)xb.x, a, false);
+                    a = __builtin_amdgcn_sdot4((int)((w2 >> 4) & kLo), (int)xb.y, a, false);
+                    a = __builtin_amdgcn_sdot4((int)(w3 & kLo), (int)xb.z, a, false);
+                    a = __builtin_amdgcn_sdot4((int)((w3 >> 4) & kLo), (int)xb.w, a, false);
+                    acc1[r] += (float)a * scale_of(Bf.sc[r][b / 4], b % 4);
+                }
+            } else if constexpr (!MFMA) {
                 u32x4 xv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -255,13 +292,81 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     if (nsteps > 0)
         load_step(bufA, 0, 0);
 
-    // Stage the activation slice of every row m < M: xs[m * nxv + v].
-    const int64_t xrow = (int64_t)L.K / 8;
-    for (int i = tid; i < M * nxv; i += kBlock) {
-        const int m = i / nxv, v = i - m * nxv;
-        xs[i] = L.x[m * xrow + (int64_t)kb0 * 16 + v];
+    if constexpr (MODE == kA8) {
+        // (1) max |x| over the whole row
+        float amax = 0.0f;
+        for (int v = tid; v < L.K / 8; v += kBlock) {
+            const u32x4 h = L.x[v];
+            const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f16x2 p = as_h2(hw[j]);
+                amax = fmaxf(amax, fmaxf(fabsf((float)p[0]), fabsf((float)p[1])));
+            }
+        }
+        for (int o = 32; o >= 1; o >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, o));
+        float *red = reinterpret_cast<float *>(reinterpret_cast<int *>(xs + 8 * nkb) + 4 * nkb);
+        if (lane == 0)
+            red[wave] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        sx = amax / 127.0f;
+        // (2) codes of this slice, one (block, lane group) pair per thread:
+        // 8 bytes per packed word in the order (e0,e4,e1,e5 | e2,e6,e3,e7)
+        u32x2 *xq8 = reinterpret_cast<u32x2 *>(xs);
+        int *sumx = reinterpret_cast<int *>(xs + 8 * nkb);
+        const bool write_codes = L.xq_out != nullptr && tile == 0;
+        for (int p = tid; p < nkb * 4; p += kBlock) {
+            const int b = p >> 2, gg = p & 3;
+            int sum = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t v = (int64_t)(kb0 + b) * 16 + 4 * i + gg;   // k = 8 v .. 8 v + 7
+                const u32x4 h = L.x[v];
+                const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+                int e[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f16x2 pr = as_h2(hw[j]);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        float r = 0.0f;
+                        if (amax != 0.0f)
+                            r = fminf(fmaxf(rintf((float)pr[t] / sx), -127.0f), 127.0f);
+                        e[2 * j + t] = (int)r;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    sum += e[j];
+                const uint32_t d0 = (uint32_t)(e[0] & 255) | (uint32_t)(e[4] & 255) << 8 |
+                                    (uint32_t)(e[1] & 255) << 16 | (uint32_t)(e[5] & 255) << 24;
+                const uint32_t d1 = (uint32_t)(e[2] & 255) | (uint32_t)(e[6] & 255) << 8 |
+                                    (uint32_t)(e[3] & 255) << 16 | (uint32_t)(e[7] & 255) << 24;
+                xq8[p * 4 + i] = u32x2{d0, d1};
+                if (write_codes) {
+                    const uint32_t n0 = (uint32_t)(e[0] & 255) | (uint32_t)(e[1] & 255) << 8 |
+                                        (uint32_t)(e[2] & 255) << 16 | (uint32_t)(e[3] & 255) << 24;
+                    const uint32_t n1 = (uint32_t)(e[4] & 255) | (uint32_t)(e[5] & 255) << 8 |
+                                        (uint32_t)(e[6] & 255) << 16 | (uint32_t)(e[7] & 255) << 24;
+                    reinterpret_cast<u32x2 *>(L.xq_out)[v] = u32x2{n0, n1};
+                }
+            }
+            sumx[p] = sum;
+        }
+        if (L.sx_out != nullptr && tile == 0 && s == 0 && tid == 0)
+            *L.sx_out = sx;
+        __syncthreads();
+    } else {
+        // Stage the activation slice of every row m < M: xs[m * nxv + v].
+        const int64_t xrow = (int64_t)L.K / 8;
+        for (int i = tid; i < M * nxv; i += kBlock) {
+            const int m = i / nxv, v = i - m * nxv;
+            xs[i] = L.x[m * xrow + (int64_t)kb0 * 16 + v];
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     if (nsteps == 0)
         return;
@@ -297,20 +402,20 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     }
 }
 
-template <int R, int B, bool NT, bool MFMA, bool TAIL>
+template <int R, int B, bool NT, int MODE, bool TAIL>
 __global__ __launch_bounds__(kBlock) void w4_gemv_kernel(W4Lin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
-    w4_unit<R, B, NT, MFMA, TAIL>(L, u / L.S, u % L.S, xs_dyn);
+    w4_unit<R, B, NT, MODE, TAIL>(L, u / L.S, u % L.S, xs_dyn);
 }
 
-template <int R, int B, bool NT, bool MFMA, bool TAIL>
+template <int R, int B, bool NT, int MODE, bool TAIL>
 __global__ __launch_bounds__(kBlock) void w4_grouped_kernel(const W4Lin *__restrict__ lins,
                                                             const Unit *__restrict__ units) {
     extern __shared__ u32x4 xs_dyn[];
     const Unit u = units[blockIdx.x];
     const W4Lin L = lins[u.lin];
-    w4_unit<R, B, NT, MFMA, TAIL>(L, u.tile, u.s, xs_dyn);
+    w4_unit<R, B, NT, MODE, TAIL>(L, u.tile, u.s, xs_dyn);
 }
 
 // y[m][n] = sum over slices s = 0..S-1, in that order, of part[s][m][n].
@@ -373,64 +478,69 @@ __global__ __launch_bounds__(kBlock) void pack_s4_kernel(const uint16_t *__restr
     Sp[idx] = (n < N && b < kb) ? s4[n * kb + b] : (uint16_t)0;
 }
 
-template <int R, int B, bool NT, bool MFMA, bool TAIL>
+template <int R, int B, bool NT, int MODE, bool TAIL>
 hipError_t launch_one(const W4Lin &L, hipStream_t s) {
     const int units = L.n_tiles * L.S;
-    hipLaunchKernelGGL((w4_gemv_kernel<R, B, NT, MFMA, TAIL>), dim3(units), dim3(kBlock), w4_lds_bytes(L), s, L);
+    hipLaunchKernelGGL((w4_gemv_kernel<R, B, NT, MODE, TAIL>), dim3(units), dim3(kBlock), w4_lds_bytes(L, MODE), s,
+                       L);
     return hipGetLastError();
 }
 
-template <int R, int B, bool NT, bool MFMA, bool TAIL>
+template <int R, int B, bool NT, int MODE, bool TAIL>
 hipError_t launch_grp(const W4Lin *lins, const Unit *units, int n, int lds, hipStream_t s) {
-    hipLaunchKernelGGL((w4_grouped_kernel<R, B, NT, MFMA, TAIL>), dim3(n), dim3(kBlock), lds, s, lins, units);
+    hipLaunchKernelGGL((w4_grouped_kernel<R, B, NT, MODE, TAIL>), dim3(n), dim3(kBlock), lds, s, lins, units);
     return hipGetLastError();
 }
 
 // Instantiated shapes: R in {1, 2} tiles, B in {4, 8} blocks per wave step.
-template <bool MFMA, bool NT, bool TAIL>
+template <int MODE, bool NT, bool TAIL>
 hipError_t dispatch_one(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
-    if (c.R == 1 && c.B == 8) return launch_one<1, 8, NT, MFMA, TAIL>(L, s);
-    if (c.R == 1 && c.B == 4) return launch_one<1, 4, NT, MFMA, TAIL>(L, s);
-    if (c.R == 2 && c.B == 8) return launch_one<2, 8, NT, MFMA, TAIL>(L, s);
-    if (c.R == 2 && c.B == 4) return launch_one<2, 4, NT, MFMA, TAIL>(L, s);
+    if (c.R == 1 && c.B == 8) return launch_one<1, 8, NT, MODE, TAIL>(L, s);
+    if (c.R == 1 && c.B == 4) return launch_one<1, 4, NT, MODE, TAIL>(L, s);
+    if (c.R == 2 && c.B == 8) return launch_one<2, 8, NT, MODE, TAIL>(L, s);
+    if (c.R == 2 && c.B == 4) return launch_one<2, 4, NT, MODE, TAIL>(L, s);
     return hipErrorInvalidValue;
 }
 
-template <bool MFMA, bool NT, bool TAIL>
+template <int MODE, bool NT, bool TAIL>
 hipError_t dispatch_grp(const W4Lin *lins, const Unit *units, int n, int lds, const W4Cfg &c, hipStream_t s) {
-    if (c.R == 1 && c.B == 8) return launch_grp<1, 8, NT, MFMA, TAIL>(lins, units, n, lds, s);
-    if (c.R == 1 && c.B == 4) return launch_grp<1, 4, NT, MFMA, TAIL>(lins, units, n, lds, s);
-    if (c.R == 2 && c.B == 8) return launch_grp<2, 8, NT, MFMA, TAIL>(lins, units, n, lds, s);
-    if (c.R == 2 && c.B == 4) return launch_grp<2, 4, NT, MFMA, TAIL>(lins, units, n, lds, s);
+    if (c.R == 1 && c.B == 8) return launch_grp<1, 8, NT, MODE, TAIL>(lins, units, n, lds, s);
+    if (c.R == 1 && c.B == 4) return launch_grp<1, 4, NT, MODE, TAIL>(lins, units, n, lds, s);
+    if (c.R == 2 && c.B == 8) return launch_grp<2, 8, NT, MODE, TAIL>(lins, units, n, lds, s);
+    if (c.R == 2 && c.B == 4) return launch_grp<2, 4, NT, MODE, TAIL>(lins, units, n, lds, s);
     return hipErrorInvalidValue;
 }
 
-template <bool MFMA>
-hipError_t one_mfma(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
+template <int MODE>
+hipError_t one_mode(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
     if (c.nt)
-        return c.tail ? dispatch_one<MFMA, true, true>(L, c, s) : dispatch_one<MFMA, true, false>(L, c, s);
-    return c.tail ? dispatch_one<MFMA, false, true>(L, c, s) : dispatch_one<MFMA, false, false>(L, c, s);
+        return c.tail ? dispatch_one<MODE, true, true>(L, c, s) : dispatch_one<MODE, true, false>(L, c, s);
+    return c.tail ? dispatch_one<MODE, false, true>(L, c, s) : dispatch_one<MODE, false, false>(L, c, s);
 }
 
-template <bool MFMA>
-hipError_t grp_mfma(const W4Lin *lins, const Unit *units, int n, int lds, const W4Cfg &c, hipStream_t s) {
+template <int MODE>
+hipError_t grp_mode(const W4Lin *lins, const Unit *units, int n, int lds, const W4Cfg &c, hipStream_t s) {
     if (c.nt)
-        return c.tail ? dispatch_grp<MFMA, true, true>(lins, units, n, lds, c, s)
-                      : dispatch_grp<MFMA, true, false>(lins, units, n, lds, c, s);
-    return c.tail ? dispatch_grp<MFMA, false, true>(lins, units, n, lds, c, s)
-                  : dispatch_grp<MFMA, false, false>(lins, units, n, lds, c, s);
+        return c.tail ? dispatch_grp<MODE, true, true>(lins, units, n, lds, c, s)
+                      : dispatch_grp<MODE, true, false>(lins, units, n, lds, c, s);
+    return c.tail ? dispatch_grp<MODE, false, true>(lins, units, n, lds, c, s)
+                  : dispatch_grp<MODE, false, false>(lins, units, n, lds, c, s);
 }
 
 }  // namespace
 
-hipError_t launch_w4(const W4Lin &L, const W4Cfg &c, hipStream_t s) {
-    return L.M > 1 ? one_mfma<true>(L, c, s) : one_mfma<false>(L, c, s);
+hipError_t launch_w4(const W4Lin &L, int mode, const W4Cfg &c, hipStream_t s) {
+    if (mode == kA8)
+        return one_mode<kA8>(L, c, s);
+    return mode == kMfma ? one_mode<kMfma>(L, c, s) : one_mode<kA16>(L, c, s);
 }
 
-hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes, int max_m,
+hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes, int mode,
                              const W4Cfg &c, hipStream_t s) {
-    return max_m > 1 ? grp_mfma<true>(lins, units, n_units, lds_bytes, c, s)
-                     : grp_mfma<false>(lins, units, n_units, lds_bytes, c, s);
+    if (mode == kA8)
+        return grp_mode<kA8>(lins, units, n_units, lds_bytes, c, s);
+    return mode == kMfma ? grp_mode<kMfma>(lins, units, n_units, lds_bytes, c, s)
+                         : grp_mode<kA16>(lins, units, n_units, lds_bytes, c, s);
 }
 
 hipError_t launch_w4_reduce(const W4Lin &L, hipStream_t s) {

@@ -18,7 +18,11 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum Kind : int32_t { kF16 = 0, kW8A8 = 1, kW4A16 = 2 };
+enum Kind : int32_t { kF16 = 0, kW8A8 = 1, kW4A16 = 2, kW4A8 = 3 };
+
+// int4-weight kernel modes: fp16 activations on the VALU (M = 1), fp16
+// activations on MFMA (M = 2..8), int8 activations quantised in-kernel (M = 1).
+enum W4Mode : int32_t { kA16 = 0, kMfma = 1, kA8 = 2 };
 
 // Reinterpret a 32-bit word as two fp16.  Always pass a scalar copy: with
 // this toolchain, __builtin_bit_cast applied directly to an ext-vector
@@ -51,6 +55,8 @@ struct W4Lin {
     const u32x4 *x;        // fp16 [M][K] as 16-byte vectors
     float *y;              // [M][N]
     float *part;           // [S][M][N], S > 1
+    int8_t *xq_out;        // kA8: optional int8 codes [K] (written by the first row tile)
+    float *sx_out;         // kA8: optional activation scale [1]
     int64_t N;
     int32_t K;
     int32_t M;
@@ -102,9 +108,9 @@ hipError_t launch_dense(int kind, const DenseLin &L, const DenseCfg &c, hipStrea
 hipError_t launch_dense_grouped(int kind, const DenseLin *lins, const Unit *units, int n_units,
                                 int lds_bytes, const DenseCfg &c, hipStream_t s);
 hipError_t launch_dense_reduce(int kind, const DenseLin &L, hipStream_t s);
-hipError_t launch_w4(const W4Lin &L, const W4Cfg &c, hipStream_t s);
+hipError_t launch_w4(const W4Lin &L, int mode, const W4Cfg &c, hipStream_t s);
 hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes,
-                             int max_m, const W4Cfg &c, hipStream_t s);
+                             int mode, const W4Cfg &c, hipStream_t s);
 hipError_t launch_w4_reduce(const W4Lin &L, hipStream_t s);
 hipError_t launch_pack_w4(const uint32_t *Wc, const uint16_t *s4, u32x4 *Wp, u32x2 *Sp,
                           int64_t N, int32_t K, hipStream_t s);
@@ -124,7 +130,9 @@ inline int dense_lds_bytes(const DenseLin &L, int CH) {
     return nch * chunk * 16;
 }
 
-inline int w4_lds_bytes(const W4Lin &L) {
+inline int w4_lds_bytes(const W4Lin &L, int mode) {
+    if (mode == kA8)  // int8 codes of the slice, one int sum per (block, lane group), 4 floats
+        return L.kbs * 128 + L.kbs * 4 * 4 + 16;
     // x slice for all M rows: kbs blocks of 128 fp16 per row
     return L.M * L.kbs * 128 * 2;
 }

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwsgemv.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "wsgemv.h")
 
-F16, W8A8, W4A16 = 0, 1, 2
+F16, W8A8, W4A16, W4A8 = 0, 1, 2, 3
 STEP_ORDERED, STEP_GROUPED, STEP_EAGER = 0, 1, 0x100
 STATUS = {0: "WSG_OK", 1: "WSG_ERR_NULL", 2: "WSG_ERR_SHAPE", 3: "WSG_ERR_ALIGN", 4: "WSG_ERR_UNSUPPORTED",
           5: "WSG_ERR_WORKSPACE", 6: "WSG_ERR_HIP", 7: "WSG_ERR_NOMEM", 8: "WSG_ERR_STATE"}
@@ -55,6 +55,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "wsg_w4_packed_scale_bytes": ([I64, I64, I64], SZ),
         "wsg_pack_w4": ([P, P, P, P, I64, I64, I64, P], I32),
         "gemv_w4a16": ([P, P, P, P, I64, I64, I64, I64, I32, P, SZ, P], I32),
+        "gemv_w4a8": ([P, P, P, P, P, P, I64, I64, I64, I32, P, SZ, P], I32),
         "wsg_decode_step_create": ([ctypes.POINTER(wsg_linear), I32, I32, P, ctypes.POINTER(P)], I32),
         "decode_step_linears": ([P, P], I32),
         "wsg_decode_step_destroy": ([P], I32),
@@ -210,6 +211,29 @@ def gemv_w4a16(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, N: int, grou
     _check(lib().gemv_w4a16(_dev(Wp, Wp.dtype, "Wp"), _dev(Sp, Sp.dtype, "Sp"), _dev(X, torch.float16, "x"),
                             _dev(y, torch.float32, "y"), M, N, K, group, splits, wp, wn, _stream(stream)),
            "gemv_w4a16")
+    return y
+
+
+def gemv_w4a8(Wp: torch.Tensor, Sp: torch.Tensor, x: torch.Tensor, N: int, group: int = 128,
+              y: Optional[torch.Tensor] = None, xq_out: Optional[torch.Tensor] = None,
+              sx_out: Optional[torch.Tensor] = None, splits: int = 0, ws: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """y[n] = s_x sum_k (q[n,k]-8) s4[n,k/128] xq[k], with x fp16 [K] quantised to int8 per token
+    inside the kernel; optional xq_out int8 [K] and sx_out fp32 [1] receive the codes and scale."""
+    K = x.shape[0]
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(W4A8, 1, N, K, splits, x.device)
+    wp, wn = _ws(ws)
+    wb, sb = packed_w4_bytes(N, K, group)
+    if Wp.numel() * Wp.element_size() < wb or Sp.numel() * Sp.element_size() < sb:
+        raise ValueError("packed buffers are smaller than this (N, K) needs")
+    xq_p = _dev(xq_out, torch.int8, "xq_out", (K,)) if xq_out is not None else None
+    sx_p = _dev(sx_out, torch.float32, "sx_out", (1,)) if sx_out is not None else None
+    _check(lib().gemv_w4a8(_dev(Wp, Wp.dtype, "Wp"), _dev(Sp, Sp.dtype, "Sp"), _dev(x, torch.float16, "x", (K,)),
+                           _dev(y, torch.float32, "y", (N,)), xq_p, sx_p, N, K, group, splits, wp, wn,
+                           _stream(stream)), "gemv_w4a8")
     return y
 
 
