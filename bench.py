@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true", help="only the decode-step stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,probe,ordered)")
+    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,probe,ordered)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB fp32 copy kernel (reads 1 GiB, writes 1 GiB) to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass")
@@ -276,6 +276,31 @@ def main():
                 st.close()
             extras[f"c5_w4a16_step_M{M}"] = rec
             del wl, w4
+
+    if want("c6"):
+        # the same int4 weights with per-token int8 activations (W4A8), M = 1
+        w4 = synth.decode_step_w4(workload=5, M=1)
+        wl = []
+        b = 0
+        for name, Wc, s4, X in w4:
+            N, K = Wc.shape[0], Wc.shape[1] * 8
+            Wp, Sp = wsgemv.pack_w4(torch.from_numpy(Wc.view(np.int32)).to(dev), torch.from_numpy(s4).to(dev))
+            y = torch.empty(N, device=dev)
+            wl.append(wsgemv.Linear(wsgemv.W4A8, Wp, torch.from_numpy(X.reshape(K)).to(dev), y, N, K, scale=Sp,
+                                    group=128))
+            b += Wc.nbytes + s4.nbytes + X.nbytes + N * 4
+        torch.cuda.synchronize()
+        rec = {"bytes": b}
+        for tag, mode in (("graph", wsgemv.STEP_GROUPED), ("launch", wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER)):
+            st = wsgemv.DecodeStep(wl, mode, stream=stream)
+            for _ in range(5):
+                st(stream)
+            s = summary(event_times(torch, lambda i: st(stream), 100, stream))
+            rec[tag] = {"median_us": s["median_ms"] * 1e3, "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
+                        "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            st.close()
+        extras["c6_w4a8_step_M1"] = rec
+        del wl, w4
 
     if want("probe"):
         nb = 2 << 30

@@ -57,8 +57,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_gemv_w4a16.argtypes = [P, P, P, I64, I64, I64, I64, P, P]
     lib.orc_quantize_x_i8.argtypes = [P, I64, P, P]
     lib.orc_gemv_w4a8.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P]
+    lib.orc_argmax_f32.argtypes = [P, I64, P]
     for f in (lib.orc_f16_decode, lib.orc_gemv_f16, lib.orc_gemv_w8a8, lib.orc_gemv_w4a16,
-              lib.orc_quantize_x_i8, lib.orc_gemv_w4a8):
+              lib.orc_quantize_x_i8, lib.orc_gemv_w4a8, lib.orc_argmax_f32):
         f.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_set_threads.restype = None
@@ -196,6 +197,27 @@ def gemv_w4a8(Wc: np.ndarray, s4: np.ndarray, xq: np.ndarray, s_x: float, group:
     _check((lib or load()).orc_gemv_w4a8(_ptr(Wc), _ptr(s4), _ptr(xq), float(np.float32(s_x)), N, K, group,
                                          _ptr(y), _ptr(A)), "gemv_w4a8")
     return y, A
+
+
+def argmax_f32(y: np.ndarray, lib: Optional[ctypes.CDLL] = None) -> int:
+    """Index of the largest fp32 value: IEEE comparison (-0 == +0), NaN below
+    every number, lowest index on ties.  This is the greedy token choice."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    if y.ndim != 1:
+        raise ValueError("y must be one-dimensional")
+    out = np.zeros(1, np.int64)
+    _check((lib or load()).orc_argmax_f32(_ptr(y), y.size, _ptr(out)), "argmax_f32")
+    return int(out[0])
+
+
+def argmax_is_valid(idx: int, y_ref: np.ndarray, A: np.ndarray) -> bool:
+    """True when token idx is a largest logit of the exact product within
+    the parity bound: no exact logit exceeds y_ref[idx] by more than the
+    two elements' bounds allow (the GPU's fp32 logits may order near-equal
+    values differently from the exact ones, never far-apart ones)."""
+    y_ref = np.asarray(y_ref, np.float64)
+    b = bound(A)
+    return bool(np.all(y_ref - b <= y_ref[idx] + b[idx]))
 
 
 def decode_step_f16(linears: Iterable[Tuple[np.ndarray, np.ndarray]],

@@ -32,6 +32,9 @@
  * bit-identical at any thread count.  Build: gcc -O2 -fopenmp
  * -ffp-contract=off (no fused multiply-add, no fast-math).
  *
+ *  - Same MiniCPM-V post, second change, read with its host reduce: the
+ *    next token is the argmax of the lm_head logits (orc_argmax_f32).
+ *
  * Status codes: 0 ok, 1 an fp16 input is Inf or NaN, 2 bad shape,
  * 3 an int8 accumulator leaves the int32 range.
  */
@@ -267,6 +270,28 @@ int orc_gemv_w4a8(const uint32_t *Wc, const uint16_t *s4, const int8_t *xq, floa
             A[n] = a * fabs((double)s_x);
     }
     return err;
+}
+
+/* Greedy decoding's token choice over the lm_head logits (MiniCPM-V 4.6 on
+ * Orange Pi AIPro post, second change: the lm_head's sliced results are
+ * reduced, there on the host, to pick the next token).  The token is the
+ * index of the largest logit.  The pages fix no rule for ties or NaN; the
+ * reading used here: values compare as IEEE numbers (so -0 equals +0), a NaN
+ * is below every number, and among equal values (or among NaNs) the lowest
+ * index wins.  n must be positive. */
+int orc_argmax_f32(const float *y, int64_t n, int64_t *idx)
+{
+    if (n <= 0)
+        return ORC_ERR_SHAPE;
+    int64_t best = 0;
+    for (int64_t i = 1; i < n; ++i) {
+        if (isnan(y[i]))
+            continue;
+        if (isnan(y[best]) || y[i] > y[best])
+            best = i;
+    }
+    *idx = best;
+    return ORC_OK;
 }
 
 void orc_set_threads(int n)

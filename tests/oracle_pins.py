@@ -295,9 +295,34 @@ def pin_w4a8_integer_matmul(lib, N=23, K=512, seed=19):
     assert np.all(np.abs(y2 - ref2) <= 1e-12 * A2 + 1e-300)
 
 
+# -------------------------------------------------------------- argmax ---
+
+def pin_argmax_golden(lib):
+    g = _golden("argmax_ties.json")
+    for c in g["cases"]:
+        y = np.array([int(v, 16) for v in c["bits"]], np.uint32).view(np.float32)
+        assert oracle.argmax_f32(y, lib=lib) == c["argmax"], c["note"]
+
+
+def pin_argmax_numpy(lib, n=5000, seed=20):
+    """numpy's argmax (first occurrence of the maximum; -0 == +0) on finite
+    values with many exact ties, and nanargmax where NaNs are present."""
+    r = synth.rng(909, seed)
+    for trial in range(20):
+        y = np.round(r.normal(0, 3, n)).astype(np.float32)      # integers: many ties
+        y[r.integers(0, n, 50)] = -0.0
+        assert oracle.argmax_f32(y, lib=lib) == int(np.argmax(y)), trial
+        y[r.integers(0, n, 200)] = np.nan
+        assert oracle.argmax_f32(y, lib=lib) == int(np.nanargmax(y)), trial
+    y = np.zeros(n, np.float32)
+    y[-1] = 1
+    assert oracle.argmax_f32(y, lib=lib) == n - 1
+
+
 ALL_PINS = [
     pin_f16_decode_all_patterns, pin_f16_golden, pin_f16_exact_rational, pin_f16_closed_forms,
     pin_f16_numpy_matmul, pin_f16_scaling, pin_w8a8_golden, pin_w8a8_int64_matmul,
     pin_w8a8_int32_range, pin_w4_golden, pin_w4_numpy_dequant, pin_w4_exact_rational,
     pin_quant_golden, pin_quant_properties, pin_w4a8_golden, pin_w4a8_integer_matmul,
+    pin_argmax_golden, pin_argmax_numpy,
 ]

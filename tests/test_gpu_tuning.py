@@ -125,3 +125,69 @@ def test_grouped_shapes_bit_identical():
             for l, b in zip(lins, base):
                 assert_bits_equal(host(l.y), b, f"grouped R={R} CH={CH} unit={kb}KB")
             st.close()
+
+
+@pytest.mark.parametrize("N,K", [(100, 1024), (40, 3072), (17, 640)])
+def test_w4a8_shapes(N, K):
+    """Every int8-activation kernel shape returns the default's bits, codes and scale."""
+    say(f"tuning w4a8 {N}x{K}")
+    Wc = synth.w4_words(84, N, N, K)
+    s4 = synth.f16_uniform(84, K, (N, K // 128), 0.002, 0.02)
+    x = synth.f16_normal(84, 1, (K,), synth.X_SIGMA)
+    xq_ref, sx_ref = oracle.quantize_x_i8(x)
+    y_ref, A = oracle.gemv_w4a8(Wc, s4, xq_ref, sx_ref)
+    Wp, Sp = wsgemv.pack_w4(dev(Wc), dev(s4))
+    xd = dev(x)
+    base = host(wsgemv.gemv_w4a8(Wp, Sp, xd, N, splits=1))
+    assert_within(base, y_ref, A, "default")
+    xq = torch.empty(K, dtype=torch.int8, device="cuda")
+    sx = torch.empty(1, device="cuda")
+    for nt in (0, 1):
+        for R in (1, 2):
+            for B in (4, 8):
+                for tiles in (1, 3):
+                    wsgemv.tune_set("nt", nt)
+                    wsgemv.tune_set("w4_R", R)
+                    wsgemv.tune_set("w4_B", B)
+                    wsgemv.tune_set("w4_tiles", tiles)
+                    xq.fill_(99)
+                    sx.fill_(float("nan"))
+                    got = host(wsgemv.gemv_w4a8(Wp, Sp, xd, N, xq_out=xq, sx_out=sx, splits=1))
+                    what = f"nt={nt} R={R} B={B} tiles={tiles}"
+                    assert_bits_equal(got, base, what)
+                    assert_bits_equal(host(xq), xq_ref, what + " codes")
+                    assert_bits_equal(host(sx), np.array([sx_ref], np.float32), what + " scale")
+
+
+def test_grouped_w4_shapes_bit_identical():
+    """Grouped int4 steps (fp16 and int8 activations) at every kernel shape."""
+    say("tuning grouped w4 step shapes")
+    lins, refs = [], []
+    for i, (N, K) in enumerate([(200, 3072), (1024, 1024), (17, 256), (333, 640)]):
+        Wc = synth.w4_words(85, 3 * i, N, K)
+        s4 = synth.f16_uniform(85, 3 * i + 1, (N, K // 128), 0.002, 0.02)
+        x = synth.f16_normal(85, 3 * i + 2, (K,), synth.X_SIGMA)
+        Wp, Sp = wsgemv.pack_w4(dev(Wc), dev(s4))
+        for kind in (wsgemv.W4A16, wsgemv.W4A8):
+            lins.append(wsgemv.Linear(kind, Wp, dev(x), torch.empty(N, device="cuda"), N, K, scale=Sp, group=128))
+            if kind == wsgemv.W4A8:
+                refs.append(oracle.gemv_w4a8(Wc, s4, *oracle.quantize_x_i8(x)))
+            else:
+                refs.append(oracle.gemv_w4a16(Wc, s4, x))
+    st = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED)
+    st()
+    base = [host(l.y).copy() for l in lins]
+    st.close()
+    for b, (y_ref, A) in zip(base, refs):
+        assert_within(b, y_ref, A, "grouped default")
+    for R in (1, 2):
+        for B in (4, 8):
+            for tiles in (1, 2, 8, 16):
+                wsgemv.tune_set("w4_R", R)
+                wsgemv.tune_set("w4_B", B)
+                wsgemv.tune_set("group_w4_tiles", tiles)
+                st = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED)
+                st()
+                for l, b in zip(lins, base):
+                    assert_bits_equal(host(l.y), b, f"grouped w4 R={R} B={B} tiles={tiles}")
+                st.close()

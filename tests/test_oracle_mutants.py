@@ -34,6 +34,12 @@ MUTANTS = [
     ("w4a8_zero_point", "double p = (double)(q - 8) * scale * (double)xq[k];",
      "double p = (double)(q - 7) * scale * (double)xq[k];"),
     ("w4a8_no_sx", "y[n] = s * (double)s_x;", "y[n] = s;"),
+    ("argmax_ties_last", "if (isnan(y[best]) || y[i] > y[best])", "if (isnan(y[best]) || y[i] >= y[best])"),
+    ("argmax_nan_above", "        if (isnan(y[i]))\n            continue;\n", ""),
+    ("argmax_nan_first", "if (isnan(y[best]) || y[i] > y[best])", "if (y[i] > y[best])"),
+    ("argmax_skip_last", "for (int64_t i = 1; i < n; ++i) {", "for (int64_t i = 1; i < n - 1; ++i) {"),
+    ("argmax_signed_zero", "if (isnan(y[best]) || y[i] > y[best])",
+     "if (isnan(y[best]) || y[i] > y[best] || (y[i] == y[best] && signbit(y[best]) && !signbit(y[i])))"),
 ]
 
 

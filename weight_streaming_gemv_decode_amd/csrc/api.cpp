@@ -234,9 +234,9 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
     }
     p.S = S;
     p.kbs = S > 1 ? (int)(cdiv(cdiv(kb, S), 4) * 4) : (int)kb;
-    // 16-row tiles per unit: 4 (M = 1) or 8 (verify blocks), fewer when the
+    // 16-row tiles per unit: 8 (M = 1) or 16 (verify blocks), fewer when the
     // launch would otherwise have under 1024 units.
-    int64_t tt = M > 1 ? 16 : 4;
+    int64_t tt = M > 1 ? 16 : 8;
     while (tt > 1 && cdiv(n_rtiles, tt) * S < kWantUnits)
         tt = tt / 2;
     if (g_tune.w4_tiles > 0)
@@ -818,13 +818,15 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     W4Plan p = plan_w4(l.M, l.N, l.K, 1);
                     p.S = 1;
                     p.kbs = (int)(l.K / 128);
-                    const int64_t tile_bytes = 16 * (int64_t)p.kbs * 64;
-                    (void)tile_bytes;
-                    // M = 1: 1 tile x 8 blocks per step, 4 tiles per unit;
+                    // fp16 activations, M = 1: 1 tile x 8 blocks per step, 4 tiles per unit;
+                    // int8 activations: 1 tile x 4 blocks per step, 8 tiles per unit (the
+                    // per-unit quantisation is amortised over more rows);
                     // verify blocks: 2 tiles x 4 blocks per step, 16 tiles per unit
-                    p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles : (l.M > 1 ? 16 : 4);
+                    const bool a8 = wmode == kA8;
+                    p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles
+                                                              : (l.M > 1 ? 16 : (a8 ? 8 : 4));
                     p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (l.M > 1 ? 2 : 1);
-                    p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (l.M > 1 ? 4 : 8);
+                    p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (l.M > 1 || a8 ? 4 : 8);
                     W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
                     if (w4_lds_bytes(L, wmode) > 48 * 1024) {
                         free_step(st);
