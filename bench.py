@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true", help="only the decode-step stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,probe,ordered)")
+    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,probe,ordered)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB fp32 copy kernel (reads 1 GiB, writes 1 GiB) to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass")
@@ -196,6 +196,20 @@ def main():
                                       "launches": o.info()[0]}
         o.close()
 
+    if want("token"):
+        # the timed step with the lm_head also taking the greedy token
+        tok = torch.empty(1, dtype=torch.int32, device=dev)
+        tl = [wsgemv.Linear(l.kind, l.W, l.x, l.y, l.N, l.K) for l in lins[:-1]]
+        lm = lins[-1]
+        tl.append(wsgemv.Linear(lm.kind, lm.W, lm.x, lm.y, lm.N, lm.K, argmax_idx=tok))
+        st = wsgemv.DecodeStep(tl, wsgemv.STEP_GROUPED, stream=stream)
+        for _ in range(5):
+            st(stream)
+        s = summary(event_times(torch, lambda i: st(stream), 100, stream))
+        extras["c3_grouped_graph_with_token"] = {"median_us": s["median_ms"] * 1e3,
+                                                 "GBps": step_bytes / (s["median_ms"] * 1e-3) / 1e9}
+        st.close()
+
     if want("c2"):
         lm = lins[-1]
         Wcopy = lm.W.clone()
@@ -212,6 +226,18 @@ def main():
             res[f"S={S if S else wsgemv.plan_splits(0, 1, lm.N, lm.K)}{' (auto)' if S == 0 else ''}"] = {
                 "median_us": s["median_ms"] * 1e3, "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
                 "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        # the same lm_head with the greedy token fused into the kernel that writes the logits
+        tok = torch.empty(1, dtype=torch.int32, device=dev)
+        ws = torch.empty(wsgemv.workspace_bytes(wsgemv.F16 | wsgemv.WITH_ARGMAX, 1, lm.N, lm.K), dtype=torch.uint8,
+                         device=dev)
+        y = torch.empty(lm.N, device=dev)
+        fn = lambda i: wsgemv.gemv_f16_argmax(Ws[i % 2], lm.x, y=y, token=tok, ws=ws, stream=stream)  # noqa: E731
+        for i in range(10):
+            fn(i)
+        s = summary(event_times(torch, fn, 100, stream))
+        res["with_token"] = {"median_us": s["median_ms"] * 1e3, "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
+                             "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "note": "the GEMV writing one key per workgroup, then the one-workgroup finish kernel"}
         extras["c2_lm_head_248320x1024"] = {"bytes": b, "rotation": "2 weight copies (1.02 GB)", **res}
         del Wcopy
 

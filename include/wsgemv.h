@@ -157,6 +157,42 @@ wsg_status gemv_w4a8(const void *Wp, const void *Sp, const void *x, float *y, in
                      int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream);
 
 /*
+ * Greedy token choice (MiniCPM-V 4.6 on Orange Pi AIPro post, second change:
+ * the lm_head's sliced results are reduced, there on the host, to pick the
+ * next token; here the reduce stays on the device and runs inside the
+ * producing kernel).  The token is the index of the largest value: values
+ * compare as IEEE numbers (-0 equals +0), a NaN is below every number, and
+ * among equal values the lowest index wins.
+ *
+ * Every workgroup that produces values folds them into one 64-bit key and
+ * stores it in its own slot of a key array in the workspace; a one-workgroup
+ * finish kernel, next on the stream, reduces the keys and writes the token.
+ * No atomics and no state between calls: the result does not depend on the
+ * order in which workgroups run, and the workspace needs no initialisation.
+ *
+ * wsg_argmax_f32: token over a given fp32 vector y [N], N = 1..INT32_MAX.
+ *   token        int32 [1] (out); token_logit optional fp32 [1] (out, y[token];
+ *                a -0 comes back as +0)
+ *   ws           at least WSG_ARGMAX_WS_BYTES, 256-byte aligned
+ */
+enum { WSG_ARGMAX_WS_BYTES = 8192, WSG_WITH_ARGMAX = 0x100 };
+wsg_status wsg_argmax_f32(const float *y, int64_t N, int32_t *token, float *token_logit, void *ws,
+                          size_t ws_bytes, wsg_stream_t stream);
+
+/*
+ * gemv_f16_argmax: gemv_f16 (y = W . x, fp32 logits, written in full) with
+ * the greedy token over y fused into the kernel that writes y (the k-split
+ * reduce when splits > 1).  This is the lm_head of a decode step.
+ *   N = 1..INT32_MAX; token int32 [1]; token_logit optional fp32 [1]
+ *   ws           wsg_workspace_bytes(WSG_F16 | WSG_WITH_ARGMAX, 1, N, K,
+ *                splits) bytes (the key array, then the split-K partials),
+ *                256-byte aligned
+ */
+wsg_status gemv_f16_argmax(const void *W, const void *x, float *y, int32_t *token, float *token_logit,
+                           int64_t N, int64_t K, int32_t splits, void *ws, size_t ws_bytes,
+                           wsg_stream_t stream);
+
+/*
  * Decode step: a fixed list of linears replayed once per token (EdgeFM
  * summary, section 2C: an execution graph is captured once and reused on
  * every decode iteration to cut kernel-launch overhead).
@@ -188,6 +224,10 @@ typedef struct wsg_linear {
     int32_t *acc_out;    /* W8A8: optional int32 [N]; otherwise NULL */
     int32_t group;       /* W4A16, W4A8: 128; otherwise 0 */
     int32_t splits;      /* 0 = table's choice; ORDERED mode only */
+    int32_t *argmax_idx; /* F16, W8A8: optional int32 [1], the greedy token over y
+                            (the rule of wsg_argmax_f32); N must be 1..INT32_MAX.
+                            Other kinds: NULL */
+    float *argmax_val;   /* optional fp32 [1]: y[*argmax_idx]; only with argmax_idx */
 } wsg_linear;
 
 typedef struct wsg_step wsg_step;

@@ -23,6 +23,7 @@ def L():
 def test_exports_every_declared_function(L):
     names = wsgemv.header_functions()
     assert {"gemv_f16", "gemv_w8a8", "gemv_w4a16", "gemv_w4a8", "decode_step_linears", "wsg_pack_w4",
+            "gemv_f16_argmax", "wsg_argmax_f32",
             "wsg_decode_step_create"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/wsgemv.h but not exported"
@@ -99,6 +100,36 @@ def test_w4_validation_and_sizes(L):
     assert g(*a8(N=16, K=1024, S=2)) == WS
     assert L.wsg_workspace_bytes(3, 1, 16, 1024, 2) == 2 * 16 * 4
     assert g(*a8(N=0)) == OK                                                    # nothing to do
+
+
+def test_argmax_validation(L):
+    g = L.wsg_argmax_f32
+    assert g(FAKE, 0, FAKE, None, FAKE, 256, None) == SHAPE                    # no values
+    assert g(FAKE, 1 << 31, FAKE, None, FAKE, 256, None) == UNSUP             # index must fit int32
+    assert g(FAKE, 10, None, None, FAKE, 256, None) == NULL                   # token required
+    assert g(None, 10, FAKE, None, FAKE, 256, None) == NULL
+    assert g(FAKE + 2, 10, FAKE, None, FAKE, 256, None) == ALIGN
+    assert g(FAKE, 10, FAKE + 1, None, FAKE, 256, None) == ALIGN
+    assert g(FAKE, 10, FAKE, FAKE + 2, FAKE, 256, None) == ALIGN
+    assert g(FAKE, 10, FAKE, None, FAKE, 255, None) == WS
+    assert g(FAKE, 10, FAKE, None, None, 0, None) == WS
+    assert g(FAKE, 10, FAKE, None, FAKE + 8, 256, None) == ALIGN
+    f = L.gemv_f16_argmax
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 0, 64, 0, FAKE, 256, None) == SHAPE   # N = 0: no token
+    assert f(FAKE, FAKE, FAKE, None, None, 4, 64, 0, FAKE, 256, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 60, 0, FAKE, 256, None) == SHAPE   # K % 8
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 64, 0, FAKE, 128, None) == WS
+    need = L.wsg_workspace_bytes(0 | 0x100, 1, 4, 1024, 2)
+    assert need == 256 + 2 * 4 * 4
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 1024, 2, FAKE, need - 1, None) == WS
+    assert L.wsg_workspace_bytes(2 | 0x100, 1, 16, 256, 0) == 0                  # int4: no fused token
+    out = ctypes.c_void_p()
+    lin = lambda kind, tok, val=None, N=64: wsgemv.wsg_linear(kind, 1, N, 256, FAKE, FAKE, FAKE, FAKE,  # noqa
+                                                             FAKE, None, 128 if kind >= 2 else 0, 0, tok, val)
+    for kind, tok, val, N, want in ((2, FAKE, None, 64, UNSUP), (0, FAKE + 2, None, 64, ALIGN),
+                                    (0, None, FAKE, 64, NULL), (0, FAKE, None, 1 << 31, UNSUP)):
+        arr = (wsgemv.wsg_linear * 1)(lin(kind, tok, val, N))
+        assert L.wsg_decode_step_create(arr, 1, 0, None, ctypes.byref(out)) == want, (kind, want)
 
 
 def test_launch_table(L):

@@ -16,7 +16,7 @@
 #include <new>
 #include <vector>
 
-#include "../../include/wsgemv.h"
+#include "wsgemv.h"
 #include "wsg_common.hpp"
 
 using namespace wsg;
@@ -188,6 +188,40 @@ wsg_status check_ws(const void *ws, size_t ws_bytes, size_t need) {
     if (!ws || ws_bytes < need)
         return WSG_ERR_WORKSPACE;
     if (!aligned(ws, 256))
+        return WSG_ERR_ALIGN;
+    return WSG_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+ArgOut arg_out(void *keys, int32_t n_keys, int32_t *token, float *token_logit) {
+    ArgOut a{};
+    a.keys = static_cast<unsigned long long *>(keys);
+    a.n_keys = n_keys;
+    a.idx = token;
+    a.val = token_logit;
+    return a;
+}
+
+// Workgroups that publish a key for a dense linear's token: its units, or
+// the reduce's workgroups when k is split.
+int32_t dense_token_keys(const DenseLin &L) { return L.S > 1 ? dense_reduce_blocks(L.N) : L.n_tiles; }
+
+int32_t dense_token_keys(const DensePlan &p, int64_t N) {
+    return p.S > 1 ? dense_reduce_blocks(N) : (int32_t)cdiv(N, p.tile_rows);
+}
+
+// Key array bytes at the start of a token-taking workspace.
+size_t token_key_bytes(int32_t n_keys) { return align256((size_t)n_keys * 8); }
+
+wsg_status check_token_args(int64_t N, const int32_t *token, const float *token_logit) {
+    if (N < 1)
+        return WSG_ERR_SHAPE;
+    if (N > (int64_t)INT32_MAX)
+        return WSG_ERR_UNSUPPORTED;
+    if (!token)
+        return WSG_ERR_NULL;
+    if (!aligned(token, 4) || (token_logit && !aligned(token_logit, 4)))
         return WSG_ERR_ALIGN;
     return WSG_OK;
 }
@@ -377,6 +411,15 @@ int32_t wsg_plan_splits(int32_t kind, int64_t M, int64_t N, int64_t K) {
 }
 
 size_t wsg_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K, int32_t splits) {
+    if (kind & WSG_WITH_ARGMAX) {
+        const int32_t base = kind & ~WSG_WITH_ARGMAX;
+        if ((base != kF16 && base != kW8A8) || M != 1 || N < 1 || N > (int64_t)INT32_MAX || K < 0 || splits < 0)
+            return 0;
+        if (K == 0 || K % elem_per_vec(base))
+            return token_key_bytes(argmax_f32_blocks(N));
+        const DensePlan p = plan_dense(base, N, K, splits);
+        return token_key_bytes(dense_token_keys(p, N)) + dense_ws_bytes(p, N);
+    }
     if (N <= 0 || K <= 0 || splits < 0)
         return 0;
     if (kind == kF16 || kind == kW8A8) {
@@ -410,6 +453,62 @@ wsg_status gemv_f16(const void *W, const void *x, float *y, int64_t N, int64_t K
         DenseLin L = make_dense(kF16, W, x, y, ws, nullptr, nullptr, nullptr, N, K, p);
         p.cfg.tail = dense_needs_tail(L, p.cfg.CH);
         return enqueue_dense(kF16, L, p.cfg, s);
+    });
+}
+
+wsg_status wsg_argmax_f32(const float *y, int64_t N, int32_t *token, float *token_logit, void *ws,
+                          size_t ws_bytes, wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_token_args(N, token, token_logit);
+        if (st != WSG_OK)
+            return st;
+        if (!y)
+            return WSG_ERR_NULL;
+        if (!aligned(y, 4))
+            return WSG_ERR_ALIGN;
+        const int32_t nk = argmax_f32_blocks(N);
+        st = check_ws(ws, ws_bytes, token_key_bytes(nk));
+        if (st != WSG_OK)
+            return st;
+        hipError_t e = launch_argmax_f32(y, N, arg_out(ws, nk, token, token_logit), static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? WSG_OK : hip_fail(e);
+    });
+}
+
+wsg_status gemv_f16_argmax(const void *W, const void *x, float *y, int32_t *token, float *token_logit,
+                           int64_t N, int64_t K, int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_dense_args(kF16, W, x, y, N, K, splits);
+        if (st != WSG_OK)
+            return st;
+        st = check_token_args(N, token, token_logit);
+        if (st != WSG_OK)
+            return st;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (K == 0) {
+            const int32_t nk = argmax_f32_blocks(N);
+            st = check_ws(ws, ws_bytes, token_key_bytes(nk));
+            if (st != WSG_OK)
+                return st;
+            hipError_t e = launch_zero_f32(y, N, s);
+            if (e == hipSuccess)
+                e = launch_argmax_f32(y, N, arg_out(ws, nk, token, token_logit), s);
+            return e == hipSuccess ? WSG_OK : hip_fail(e);
+        }
+        DensePlan p = plan_dense(kF16, N, K, splits);
+        const int32_t nk = dense_token_keys(p, N);
+        const size_t kb = token_key_bytes(nk);
+        st = check_ws(ws, ws_bytes, kb + dense_ws_bytes(p, N));
+        if (st != WSG_OK)
+            return st;
+        DenseLin L = make_dense(kF16, W, x, y, static_cast<char *>(ws) + kb, nullptr, nullptr, nullptr, N, K, p);
+        L.arg = arg_out(ws, nk, token, token_logit);
+        p.cfg.tail = dense_needs_tail(L, p.cfg.CH);
+        st = enqueue_dense(kF16, L, p.cfg, s);
+        if (st != WSG_OK)
+            return st;
+        hipError_t e = launch_argmax_finish(L.arg, s);
+        return e == hipSuccess ? WSG_OK : hip_fail(e);
     });
 }
 
@@ -599,7 +698,7 @@ struct wsg_step {
     void *dev = nullptr;  // one device allocation: partials, descriptor and unit tables
 
     struct Op {
-        enum Type { kDense, kDenseGroup, kW4, kW4Group, kZero } type;
+        enum Type { kDense, kDenseGroup, kW4, kW4Group, kZero, kArgmax, kArgFinish } type;
         int kind = 0;
         DenseLin d{};
         DenseCfg dc{};
@@ -612,6 +711,8 @@ struct wsg_step {
         int mode = 0;                 // W4 kernel mode (kA16, kMfma, kA8)
         float *zero_p = nullptr;
         int64_t zero_n = 0;
+        ArgOut arg{};                 // kArgmax: token over zero_p[0..zero_n); kArgFinish: token from keys
+        int fix = -1;                 // key array this op's token descriptor waits for (plan building)
     };
     std::vector<Op> ops;
     int32_t launches = 0;
@@ -621,6 +722,13 @@ struct wsg_step {
 namespace {
 
 wsg_status validate_linear(const wsg_linear &l) {
+    if (l.argmax_idx || l.argmax_val) {
+        if (l.kind != kF16 && l.kind != kW8A8)
+            return WSG_ERR_UNSUPPORTED;
+        wsg_status st = check_token_args(l.N, l.argmax_idx, l.argmax_val);
+        if (st != WSG_OK)
+            return st;
+    }
     switch (l.kind) {
     case kF16: {
         if (l.M != 1)
@@ -674,6 +782,12 @@ hipError_t run_ops(const wsg_step *st, hipStream_t s) {
             break;
         case wsg_step::Op::kZero:
             e = launch_zero_f32(op.zero_p, op.zero_n, s);
+            break;
+        case wsg_step::Op::kArgmax:
+            e = launch_argmax_f32(op.zero_p, op.zero_n, op.arg, s);
+            break;
+        case wsg_step::Op::kArgFinish:
+            e = launch_argmax_finish(op.arg, s);
             break;
         }
         if (e != hipSuccess)
@@ -748,6 +862,20 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             gcfg.CH = (int)g_tune.group_CH;
         }
         const int64_t unit_bytes = g_tune.group_unit_kb > 0 ? g_tune.group_unit_kb * 1024 : 32 * 1024;
+        // Greedy-token key arrays (one per linear that takes a token) open the
+        // device block; descriptors get their addresses once it exists.
+        std::vector<size_t> key_off;           // per key array: offset in the keys region
+        size_t keys_bytes = 0;
+        auto new_keys = [&](int32_t n_keys) {
+            key_off.push_back(keys_bytes);
+            keys_bytes += token_key_bytes(n_keys);
+            return (int)key_off.size() - 1;
+        };
+        struct TableFix {
+            int ki, li, keys;
+        };
+        std::vector<TableFix> table_fix;       // grouped dense descriptors that take a token
+        std::vector<wsg_step::Op> finish_after;  // their finish kernels, after the grouped launches
 
         for (int32_t i = 0; i < n; ++i) {
             const wsg_linear &l = linears[i];
@@ -764,6 +892,15 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     z.zero_n = l.N;
                     st->ops.push_back(z);
                 }
+                if (l.argmax_idx) {
+                    wsg_step::Op g{};
+                    g.type = wsg_step::Op::kArgmax;
+                    g.zero_p = l.y;
+                    g.zero_n = l.N;
+                    g.arg = arg_out(nullptr, argmax_f32_blocks(l.N), l.argmax_idx, l.argmax_val);
+                    g.fix = new_keys(g.arg.n_keys);
+                    st->ops.push_back(g);
+                }
                 continue;
             }
             if (l.kind == kF16 || l.kind == kW8A8) {
@@ -778,7 +915,18 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     o.d = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale), l.x_scale,
                                      l.acc_out, l.N, l.K, p);
                     o.dc.tail = dense_needs_tail(o.d, o.dc.CH);
+                    if (l.argmax_idx) {
+                        o.d.arg = arg_out(nullptr, dense_token_keys(o.d), l.argmax_idx, l.argmax_val);
+                        o.fix = new_keys(o.d.arg.n_keys);
+                    }
                     st->ops.push_back(o);
+                    if (l.argmax_idx) {
+                        wsg_step::Op f{};
+                        f.type = wsg_step::Op::kArgFinish;
+                        f.arg = o.d.arg;
+                        f.fix = o.fix;
+                        st->ops.push_back(f);
+                    }
                 } else {
                     DensePlan p{};
                     p.cfg = gcfg;
@@ -796,6 +944,15 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     DenseLin L = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale),
                                             l.x_scale, l.acc_out, l.N, l.K, p);
                     const int li = (int)dl[ki].size();
+                    if (l.argmax_idx) {
+                        L.arg = arg_out(nullptr, dense_token_keys(L), l.argmax_idx, l.argmax_val);
+                        wsg_step::Op f{};
+                        f.type = wsg_step::Op::kArgFinish;
+                        f.arg = L.arg;
+                        f.fix = new_keys(L.arg.n_keys);
+                        table_fix.push_back(TableFix{ki, li, f.fix});
+                        finish_after.push_back(f);
+                    }
                     dl[ki].push_back(L);
                     for (int t = 0; t < L.n_tiles; ++t)
                         du[ki].push_back(Unit{li, t, 0, 0});
@@ -843,8 +1000,10 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             }
         }
 
-        // Device block: [partials][dense tables x2][int4 tables x3]
+        // Device block: [token keys][partials][dense tables x2][int4 tables x3]
         size_t off = 0;
+        const size_t keys_off = off;
+        off = align_up(off + keys_bytes, 256);
         const size_t part_off = off;
         off = align_up(off + part_bytes, 256);
         size_t dl_off[2], du_off[2], wl_off[3], wu_off[3];
@@ -870,6 +1029,21 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         }
         char *base = static_cast<char *>(st->dev);
         std::vector<char> host(off);
+        auto keys_at = [&](int fix) {
+            return reinterpret_cast<unsigned long long *>(base + keys_off + key_off[fix]);
+        };
+        for (const TableFix &t : table_fix)
+            dl[t.ki][t.li].arg.keys = keys_at(t.keys);
+        for (auto &op : st->ops) {
+            if (op.fix < 0)
+                continue;
+            if (op.type == wsg_step::Op::kDense)
+                op.d.arg.keys = keys_at(op.fix);
+            else
+                op.arg.keys = keys_at(op.fix);
+        }
+        for (auto &op : finish_after)
+            op.arg.keys = keys_at(op.fix);
         auto put = [&](size_t o, const void *src, size_t bytes) {
             if (bytes)
                 std::memcpy(host.data() + o, src, bytes);
@@ -917,6 +1091,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                 st->ops.push_back(o);
             }
         }
+        for (const auto &op : finish_after)
+            st->ops.push_back(op);
         if (off > 0) {
             hipError_t e = hipMemcpyAsync(st->dev, host.data(), off, hipMemcpyHostToDevice, s);
             if (e == hipSuccess)

@@ -21,7 +21,9 @@
 // reduced across the wave with a halving exchange (R values per lane become
 // one row per 64/R lanes in log2(64) shuffle stages), then written as y, or
 // as a partial that a second small kernel adds in slice order.
-#include "wsg_common.hpp"
+#include "argmax.hpp"
+
+#include <algorithm>
 
 namespace wsg {
 namespace {
@@ -102,21 +104,28 @@ __device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
     return s;
 }
 
+// Writes row `row` (a partial when S > 1) and returns its y (S = 1).
 template <int KIND, typename Acc>
-__device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row, Acc v) {
+__device__ __forceinline__ float store_row(const DenseLin &L, int s, int64_t row, Acc v) {
     if (L.S > 1) {
         static_cast<Acc *>(L.part)[(int64_t)s * L.N + row] = v;
+        return 0.0f;
     } else if constexpr (KIND == kF16) {
         L.y[row] = v;
+        return v;
     } else {
         if (L.acc_out)
             L.acc_out[row] = v;
-        L.y[row] = ((float)v * L.w_scale[row]) * L.x_scale[0];
+        const float yv = ((float)v * L.w_scale[row]) * L.x_scale[0];
+        L.y[row] = yv;
+        return yv;
     }
 }
 
+// Streams one unit; returns this lane's best greedy-token key over the rows
+// it wrote (0 when the linear takes no token or the lane wrote none).
 template <int KIND, int R, int CH, bool NT, bool TAIL>
-__device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u32x4 *xs) {
+__device__ __forceinline__ unsigned long long dense_unit(const DenseLin &L, int tile, int s, u32x4 *xs) {
     using Ops = DenseOps<KIND>;
     using Acc = typename Ops::Acc;
     constexpr int CHUNK = kWave * CH;
@@ -158,6 +167,8 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
 #pragma unroll
     for (int r = 0; r < R; ++r)
         acc[r] = 0;
+    const bool take = L.arg.keys != nullptr && L.S == 1;
+    unsigned long long best = 0;
 
     auto consume = [&](const u32x4(&buf)[R][CH], int gi, int c) {
         u32x4 xv[CH];
@@ -174,8 +185,11 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
             constexpr int span = kWave / R;
             if ((lane & (span - 1)) == 0) {
                 const int64_t row = row0 + (int64_t)(wave + gi * kWavesPerBlock) * R + lane / span;
-                if (row <= last_row)
-                    store_row<KIND>(L, s, row, v);
+                if (row <= last_row) {
+                    const float yv = store_row<KIND>(L, s, row, v);
+                    if (take)
+                        best = max_u64(best, arg_key(yv, row));
+                }
             }
 #pragma unroll
             for (int r = 0; r < R; ++r)
@@ -194,7 +208,7 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
     __syncthreads();
 
     if (nsteps == 0)
-        return;
+        return 0;
     // Steps are (row group gi, chunk c) in order; a is the step in bufA.
     int ga = 0, ca = 0;
     auto next = [&](int &g, int &c) {
@@ -226,13 +240,16 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
     } else {
         consume(bufA, ga, ca);
     }
+    return best;
 }
 
 template <int KIND, int R, int CH, bool NT, bool TAIL>
 __global__ __launch_bounds__(kBlock) void dense_gemv_kernel(DenseLin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
-    dense_unit<KIND, R, CH, NT, TAIL>(L, u / L.S, u % L.S, xs_dyn);
+    const unsigned long long best = dense_unit<KIND, R, CH, NT, TAIL>(L, u / L.S, u % L.S, xs_dyn);
+    if (L.arg.keys != nullptr && L.S == 1)
+        arg_publish(L.arg, best, u);
 }
 
 template <int KIND, int R, int CH, bool NT, bool TAIL>
@@ -241,36 +258,86 @@ __global__ __launch_bounds__(kBlock) void dense_grouped_kernel(const DenseLin *_
     extern __shared__ u32x4 xs_dyn[];
     const Unit u = units[blockIdx.x];
     const DenseLin L = lins[u.lin];
-    dense_unit<KIND, R, CH, NT, TAIL>(L, u.tile, u.s, xs_dyn);
+    const unsigned long long best = dense_unit<KIND, R, CH, NT, TAIL>(L, u.tile, u.s, xs_dyn);
+    if (L.arg.keys != nullptr && L.S == 1)
+        arg_publish(L.arg, best, u.tile);
 }
 
-// y[n] = sum over slices s = 0..S-1, in that order, of part[s][n].
+// y[n] = sum over slices s = 0..S-1, in that order, of part[s][n]; and the
+// greedy token over y when the linear takes one.
 template <int KIND>
 __global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
     const int64_t n = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (n >= L.N)
-        return;
-    if constexpr (KIND == kF16) {
-        const float *p = static_cast<const float *>(L.part);
-        float a = p[n];
-        for (int s = 1; s < L.S; ++s)
-            a += p[(int64_t)s * L.N + n];
-        L.y[n] = a;
-    } else {
-        const int32_t *p = static_cast<const int32_t *>(L.part);
-        int32_t a = p[n];
-        for (int s = 1; s < L.S; ++s)
-            a += p[(int64_t)s * L.N + n];
-        if (L.acc_out)
-            L.acc_out[n] = a;
-        L.y[n] = ((float)a * L.w_scale[n]) * L.x_scale[0];
+    unsigned long long best = 0;
+    if (n < L.N) {
+        float yv;
+        if constexpr (KIND == kF16) {
+            const float *p = static_cast<const float *>(L.part);
+            float a = p[n];
+            for (int s = 1; s < L.S; ++s)
+                a += p[(int64_t)s * L.N + n];
+            yv = a;
+        } else {
+            const int32_t *p = static_cast<const int32_t *>(L.part);
+            int32_t a = p[n];
+            for (int s = 1; s < L.S; ++s)
+                a += p[(int64_t)s * L.N + n];
+            if (L.acc_out)
+                L.acc_out[n] = a;
+            yv = ((float)a * L.w_scale[n]) * L.x_scale[0];
+        }
+        L.y[n] = yv;
+        best = arg_key(yv, n);
     }
+    if (L.arg.keys != nullptr)
+        arg_publish(L.arg, best, blockIdx.x);
 }
 
 __global__ __launch_bounds__(kBlock) void zero_f32_kernel(float *p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i < n)
         p[i] = 0.0f;
+}
+
+// The token from the key array: one workgroup of 1024 threads reduces
+// a.keys[0..n_keys), each thread taking 8 consecutive keys (four 16-byte
+// loads, all in flight together) per round.
+constexpr int kFinishThreads = 1024;
+
+__global__ __launch_bounds__(kFinishThreads) void argmax_finish_kernel(ArgOut a) {
+    const int n = a.n_keys;
+    unsigned long long best = 0;
+    for (int base = threadIdx.x * 8; base < n; base += kFinishThreads * 8) {
+        if (base + 8 <= n) {
+            const u32x4 *p = reinterpret_cast<const u32x4 *>(a.keys + base);
+            u32x4 v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = p[j];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                best = max_u64(best, ((unsigned long long)v[j].y << 32) | v[j].x);
+                best = max_u64(best, ((unsigned long long)v[j].w << 32) | v[j].z);
+            }
+        } else {
+            for (int i = base; i < n; ++i)
+                best = max_u64(best, a.keys[i]);
+        }
+    }
+    best = block_max_key<kFinishThreads / kWave>(best);
+    if (threadIdx.x == 0)
+        arg_write(a, best);
+}
+
+// Greedy token over a given fp32 vector: at most kArgBlocks workgroups, each
+// striding over the vector in kBlock-wide rows, then the finish kernel.
+constexpr int kArgBlocks = 1024;
+
+__global__ __launch_bounds__(kBlock) void argmax_f32_kernel(const float *__restrict__ y, int64_t N, ArgOut a) {
+    unsigned long long best = 0;
+    for (int64_t n = (int64_t)blockIdx.x * kBlock + threadIdx.x; n < N; n += (int64_t)gridDim.x * kBlock)
+        best = max_u64(best, arg_key(y[n], n));
+    arg_publish(a, best, blockIdx.x);
 }
 
 // Read-only stream over buf, U 16-byte loads in flight per lane per
@@ -402,13 +469,34 @@ hipError_t launch_dense_grouped(int kind, const DenseLin *lins, const Unit *unit
     return hipErrorInvalidValue;
 }
 
+int dense_reduce_blocks(int64_t N) { return (int)((N + kBlock - 1) / kBlock); }
+
 hipError_t launch_dense_reduce(int kind, const DenseLin &L, hipStream_t s) {
-    const int grid = (int)((L.N + kBlock - 1) / kBlock);
+    const int grid = dense_reduce_blocks(L.N);
     if (kind == kF16)
         hipLaunchKernelGGL(dense_reduce_kernel<kF16>, dim3(grid), dim3(kBlock), 0, s, L);
     else
         hipLaunchKernelGGL(dense_reduce_kernel<kW8A8>, dim3(grid), dim3(kBlock), 0, s, L);
     return hipGetLastError();
+}
+
+// Workgroups (and keys) of the reduce over a given vector: 16 values per
+// thread, at most kArgBlocks.
+int argmax_f32_blocks(int64_t N) {
+    const int64_t b = (N + 16 * kBlock - 1) / (16 * kBlock);
+    return (int)std::min<int64_t>(std::max<int64_t>(b, 1), kArgBlocks);
+}
+
+hipError_t launch_argmax_finish(const ArgOut &a, hipStream_t s) {
+    hipLaunchKernelGGL(argmax_finish_kernel, dim3(1), dim3(kFinishThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// The reduce over y then the finish; a.n_keys must equal argmax_f32_blocks(N).
+hipError_t launch_argmax_f32(const float *y, int64_t N, ArgOut a, hipStream_t s) {
+    hipLaunchKernelGGL(argmax_f32_kernel, dim3(a.n_keys), dim3(kBlock), 0, s, y, N, a);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? launch_argmax_finish(a, s) : e;
 }
 
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s) {

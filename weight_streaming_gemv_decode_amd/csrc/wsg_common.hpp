@@ -29,6 +29,16 @@ enum W4Mode : int32_t { kA16 = 0, kMfma = 1, kA8 = 2 };
 // element expression (v.y, v.z, ...) lowers to element 0 for every element.
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
+// Fused greedy-token output of a linear (device functions in argmax.hpp).
+// keys == nullptr: no token is taken.
+struct ArgOut {
+    unsigned long long *keys;  // [n_keys] best key of each publishing workgroup
+    int32_t *idx;              // out: token (index of the largest logit)
+    float *val;                // out, optional: its logit
+    int32_t n_keys;            // workgroups that publish in one launch
+    int32_t pad;
+};
+
 // One row-major linear streamed 16 bytes per lane (fp16: 8 weights per
 // vector, int8: 16 weights per vector).
 struct DenseLin {
@@ -46,6 +56,7 @@ struct DenseLin {
     int32_t tile_rows;     // rows per work unit
     int32_t n_tiles;       // ceil(N / tile_rows)
     int32_t pad;
+    ArgOut arg;            // optional greedy token over y (S = 1: the units; S > 1: the reduce)
 };
 
 // One int4 linear in the packed tile layout (16 rows x 128 k per 1 KiB tile).
@@ -108,6 +119,7 @@ hipError_t launch_dense(int kind, const DenseLin &L, const DenseCfg &c, hipStrea
 hipError_t launch_dense_grouped(int kind, const DenseLin *lins, const Unit *units, int n_units,
                                 int lds_bytes, const DenseCfg &c, hipStream_t s);
 hipError_t launch_dense_reduce(int kind, const DenseLin &L, hipStream_t s);
+int dense_reduce_blocks(int64_t N);
 hipError_t launch_w4(const W4Lin &L, int mode, const W4Cfg &c, hipStream_t s);
 hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes,
                              int mode, const W4Cfg &c, hipStream_t s);
@@ -122,6 +134,9 @@ struct ProbeCfg {
 hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int grid, const ProbeCfg &c,
                              hipStream_t s);
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
+hipError_t launch_argmax_finish(const ArgOut &a, hipStream_t s);
+hipError_t launch_argmax_f32(const float *y, int64_t N, ArgOut a, hipStream_t s);
+int argmax_f32_blocks(int64_t N);
 
 // LDS bytes a dense unit of this linear stages for x (whole slice, chunk-padded).
 inline int dense_lds_bytes(const DenseLin &L, int CH) {

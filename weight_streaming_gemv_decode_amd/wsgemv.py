@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libwsgemv.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "wsgemv.h")
 
 F16, W8A8, W4A16, W4A8 = 0, 1, 2, 3
+ARGMAX_WS_BYTES, WITH_ARGMAX = 8192, 0x100
 STEP_ORDERED, STEP_GROUPED, STEP_EAGER = 0, 1, 0x100
 STATUS = {0: "WSG_OK", 1: "WSG_ERR_NULL", 2: "WSG_ERR_SHAPE", 3: "WSG_ERR_ALIGN", 4: "WSG_ERR_UNSUPPORTED",
           5: "WSG_ERR_WORKSPACE", 6: "WSG_ERR_HIP", 7: "WSG_ERR_NOMEM", 8: "WSG_ERR_STATE"}
@@ -35,7 +36,8 @@ class wsg_linear(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("M", ctypes.c_int32), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("W", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("x", ctypes.c_void_p),
                 ("x_scale", ctypes.c_void_p), ("y", ctypes.c_void_p), ("acc_out", ctypes.c_void_p),
-                ("group", ctypes.c_int32), ("splits", ctypes.c_int32)]
+                ("group", ctypes.c_int32), ("splits", ctypes.c_int32), ("argmax_idx", ctypes.c_void_p),
+                ("argmax_val", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -56,6 +58,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "wsg_pack_w4": ([P, P, P, P, I64, I64, I64, P], I32),
         "gemv_w4a16": ([P, P, P, P, I64, I64, I64, I64, I32, P, SZ, P], I32),
         "gemv_w4a8": ([P, P, P, P, P, P, I64, I64, I64, I32, P, SZ, P], I32),
+        "wsg_argmax_f32": ([P, I64, P, P, P, SZ, P], I32),
+        "gemv_f16_argmax": ([P, P, P, P, P, I64, I64, I32, P, SZ, P], I32),
         "wsg_decode_step_create": ([ctypes.POINTER(wsg_linear), I32, I32, P, ctypes.POINTER(P)], I32),
         "decode_step_linears": ([P, P], I32),
         "wsg_decode_step_destroy": ([P], I32),
@@ -152,6 +156,41 @@ def gemv_f16(W: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
     _check(lib().gemv_f16(_dev(W, torch.float16, "W"), _dev(x, torch.float16, "x", (K,)),
                           _dev(y, torch.float32, "y", (N,)), N, K, splits, wp, wn, _stream(stream)), "gemv_f16")
     return y
+
+
+def argmax_f32(y: torch.Tensor, token: Optional[torch.Tensor] = None, token_logit: Optional[torch.Tensor] = None,
+               ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Greedy token over fp32 y [N] (lowest index among the largest; NaN below
+    every number); returns the int32 [1] token tensor."""
+    N = y.shape[0]
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=y.device)
+    if ws is None:
+        ws = torch.empty(ARGMAX_WS_BYTES, dtype=torch.uint8, device=y.device)
+    wp, wn = _ws(ws)
+    tl = _dev(token_logit, torch.float32, "token_logit", (1,)) if token_logit is not None else None
+    _check(lib().wsg_argmax_f32(_dev(y, torch.float32, "y", (N,)), N, _dev(token, torch.int32, "token", (1,)), tl,
+                                wp, wn, _stream(stream)), "wsg_argmax_f32")
+    return token
+
+
+def gemv_f16_argmax(W: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                    token: Optional[torch.Tensor] = None, token_logit: Optional[torch.Tensor] = None,
+                    splits: int = 0, ws: Optional[torch.Tensor] = None, stream=None):
+    """(y, token): the fp16 GEMV y = W . x with the greedy token over y fused in."""
+    N, K = W.shape
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=W.device)
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=W.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(F16 | WITH_ARGMAX, 1, N, K, splits), dtype=torch.uint8, device=W.device)
+    wp, wn = _ws(ws)
+    tl = _dev(token_logit, torch.float32, "token_logit", (1,)) if token_logit is not None else None
+    _check(lib().gemv_f16_argmax(_dev(W, torch.float16, "W"), _dev(x, torch.float16, "x", (K,)),
+                                 _dev(y, torch.float32, "y", (N,)), _dev(token, torch.int32, "token", (1,)), tl,
+                                 N, K, splits, wp, wn, _stream(stream)), "gemv_f16_argmax")
+    return y, token
 
 
 def gemv_w8a8(Wq: torch.Tensor, w_scale: torch.Tensor, xq: torch.Tensor, x_scale: torch.Tensor,
@@ -256,14 +295,17 @@ class Linear:
 
     def __init__(self, kind: int, W: torch.Tensor, x: torch.Tensor, y: torch.Tensor, N: int, K: int, M: int = 1,
                  scale: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None,
-                 acc_out: Optional[torch.Tensor] = None, group: int = 0, splits: int = 0):
+                 acc_out: Optional[torch.Tensor] = None, group: int = 0, splits: int = 0,
+                 argmax_idx: Optional[torch.Tensor] = None, argmax_val: Optional[torch.Tensor] = None):
         self.kind, self.W, self.x, self.y, self.N, self.K, self.M = kind, W, x, y, N, K, M
         self.scale, self.x_scale, self.acc_out, self.group, self.splits = scale, x_scale, acc_out, group, splits
+        self.argmax_idx, self.argmax_val = argmax_idx, argmax_val
 
     def c(self) -> wsg_linear:
         p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         return wsg_linear(self.kind, self.M, self.N, self.K, p(self.W), p(self.scale), p(self.x), p(self.x_scale),
-                          p(self.y), p(self.acc_out), self.group, self.splits)
+                          p(self.y), p(self.acc_out), self.group, self.splits, p(self.argmax_idx),
+                          p(self.argmax_val))
 
 
 class DecodeStep:
