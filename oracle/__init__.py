@@ -58,8 +58,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_quantize_x_i8.argtypes = [P, I64, P, P]
     lib.orc_gemv_w4a8.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P]
     lib.orc_argmax_f32.argtypes = [P, I64, P]
+    lib.orc_round_f16.argtypes = [P, I64, P]
     for f in (lib.orc_f16_decode, lib.orc_gemv_f16, lib.orc_gemv_w8a8, lib.orc_gemv_w4a16,
-              lib.orc_quantize_x_i8, lib.orc_gemv_w4a8, lib.orc_argmax_f32):
+              lib.orc_quantize_x_i8, lib.orc_gemv_w4a8, lib.orc_argmax_f32, lib.orc_round_f16):
         f.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_set_threads.restype = None
@@ -197,6 +198,27 @@ def gemv_w4a8(Wc: np.ndarray, s4: np.ndarray, xq: np.ndarray, s_x: float, group:
     _check((lib or load()).orc_gemv_w4a8(_ptr(Wc), _ptr(s4), _ptr(xq), float(np.float32(s_x)), N, K, group,
                                          _ptr(y), _ptr(A)), "gemv_w4a8")
     return y, A
+
+
+def round_f16(v: np.ndarray, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Round doubles to IEEE binary16 (nearest, ties to even); returns float16."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    _check((lib or load()).orc_round_f16(_ptr(v), v.size, _ptr(out)), "round_f16")
+    return out.view(np.float16)
+
+
+def chain_f16(Ws: Sequence[np.ndarray], x0: np.ndarray, lib: Optional[ctypes.CDLL] = None
+              ) -> List[Tuple[np.ndarray, np.ndarray]]:
+    """A chain of linears where each one's fp16-rounded output is the next
+    one's input: returns [(y_i float64, y16_i float16)] for i = 0..len-1."""
+    out = []
+    x = np.asarray(x0, np.float16)
+    for W in Ws:
+        y, _ = gemv_f16(W, x, lib)
+        x = round_f16(y, lib)
+        out.append((y, x))
+    return out
 
 
 def argmax_f32(y: np.ndarray, lib: Optional[ctypes.CDLL] = None) -> int:

@@ -272,6 +272,48 @@ int orc_gemv_w4a8(const uint32_t *Wc, const uint16_t *s4, const int8_t *xq, floa
     return err;
 }
 
+/* A decode step's linears feed each other through fp16 activations: the
+ * output of one linear, rounded to fp16, is the input of a later one
+ * (EdgeFM summary, section 2C: the decode iteration replayed as one
+ * execution graph; the AIPro post's step is a sequence of such products).
+ * orc_round_f16 rounds each double to the nearest IEEE binary16 value, ties
+ * to the even significand, overflow to +-Inf, keeping subnormals; returns
+ * the bit patterns.  NaN input is rejected. */
+int orc_round_f16(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double a = v[i];
+        if (isnan(a))
+            return ORC_ERR_NONFINITE;
+        uint16_t sign = signbit(a) ? 0x8000u : 0u;
+        a = fabs(a);
+        /* the grid spacing at a: 2^(e - 10) for normals, 2^-24 below 2^-14 */
+        int e;
+        if (a < ldexp(1.0, -14))
+            e = -14;
+        else {
+            frexp(a, &e);
+            e -= 1;                                   /* a in [2^e, 2^(e+1)) */
+        }
+        double q = ldexp(a, 10 - e);                  /* significand in units of the grid */
+        double r = nearbyint(q);                      /* default rounding: ties to even */
+        double mag = ldexp(r, e - 10);
+        uint16_t bits;
+        if (mag >= 65520.0 || isinf(a))               /* 65504 + half a step rounds up to Inf */
+            bits = 0x7C00u;
+        else if (mag < ldexp(1.0, -14))               /* subnormal (or zero): m * 2^-24 */
+            bits = (uint16_t)ldexp(mag, 24);
+        else {
+            int me;
+            double f = frexp(mag, &me);               /* mag = f * 2^me, f in [0.5, 1) */
+            uint16_t mant = (uint16_t)(ldexp(f, 11) - 1024.0);
+            bits = (uint16_t)(((me - 1 + 15) << 10) | mant);
+        }
+        out[i] = (uint16_t)(sign | bits);
+    }
+    return ORC_OK;
+}
+
 /* Greedy decoding's token choice over the lm_head logits (MiniCPM-V 4.6 on
  * Orange Pi AIPro post, second change: the lm_head's sliced results are
  * reduced, there on the host, to pick the next token).  The token is the

@@ -319,10 +319,55 @@ def pin_argmax_numpy(lib, n=5000, seed=20):
     assert oracle.argmax_f32(y, lib=lib) == n - 1
 
 
+# ---------------------------------------------------------- fp16 chain ---
+
+def pin_round_f16_golden(lib):
+    """Hand-derived binary16 roundings: ties go to the even significand."""
+    cases = [(1.0, 0x3C00), (-0.0, 0x8000), (65504.0, 0x7BFF), (65519.99, 0x7BFF), (65520.0, 0x7C00),
+             (-1e6, 0xFC00), (2.0 ** -24, 0x0001), (2.0 ** -25, 0x0000), (3 * 2.0 ** -25, 0x0002),
+             (2.0 ** -14, 0x0400), (1 + 2.0 ** -11, 0x3C00), (1 + 3 * 2.0 ** -11, 0x3C02),
+             (2049.0, 0x6800), (2051.0, 0x6802), (0.1, 0x2E66), (-2.5, 0xC100)]
+    got = oracle.round_f16(np.array([c[0] for c in cases]), lib=lib).view(np.uint16)
+    for (v, want), g in zip(cases, got):
+        assert int(g) == want, (v, hex(int(g)), hex(want))
+
+
+def pin_round_f16_numpy(lib, seed=21):
+    """numpy's own float64 -> float16 cast, including exact midpoints."""
+    r = synth.rng(910, seed)
+    h = r.integers(0, 0x7BFF, 20000).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    v = np.concatenate([r.normal(0, 1, 20000), r.normal(0, 1e4, 5000), r.normal(0, 1e-6, 5000),
+                        (lo + hi) / 2, -(lo + hi) / 2])
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16)
+    assert np.array_equal(oracle.round_f16(v, lib=lib).view(np.uint16), want.view(np.uint16))
+
+
+def pin_chain_permutations(lib, K=256, depth=5, seed=22):
+    """Signed permutation matrices times 2^j: every fp16 value is exact, so
+    the chain's output is the input permuted, signed and scaled."""
+    r = synth.rng(911, seed)
+    x = r.integers(-1000, 1000, K).astype(np.float16)
+    Ws, want = [], x.astype(np.float64)
+    for i in range(depth):
+        perm = r.permutation(K)
+        sign = r.choice([-1.0, 1.0], K)
+        j = int(r.integers(-2, 3))
+        W = np.zeros((K, K), np.float16)
+        W[np.arange(K), perm] = sign * 2.0 ** j
+        Ws.append(W)
+        want = sign * 2.0 ** j * want[perm]
+    out = oracle.chain_f16(Ws, x, lib=lib)
+    assert np.array_equal(out[-1][0], want)
+    assert np.array_equal(out[-1][1].astype(np.float64), want)
+
+
 ALL_PINS = [
     pin_f16_decode_all_patterns, pin_f16_golden, pin_f16_exact_rational, pin_f16_closed_forms,
     pin_f16_numpy_matmul, pin_f16_scaling, pin_w8a8_golden, pin_w8a8_int64_matmul,
     pin_w8a8_int32_range, pin_w4_golden, pin_w4_numpy_dequant, pin_w4_exact_rational,
     pin_quant_golden, pin_quant_properties, pin_w4a8_golden, pin_w4a8_integer_matmul,
-    pin_argmax_golden, pin_argmax_numpy,
+    pin_argmax_golden, pin_argmax_numpy, pin_round_f16_golden, pin_round_f16_numpy, pin_chain_permutations,
 ]

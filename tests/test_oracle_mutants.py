@@ -38,6 +38,11 @@ MUTANTS = [
     ("argmax_nan_above", "        if (isnan(y[i]))\n            continue;\n", ""),
     ("argmax_nan_first", "if (isnan(y[best]) || y[i] > y[best])", "if (y[i] > y[best])"),
     ("argmax_skip_last", "for (int64_t i = 1; i < n; ++i) {", "for (int64_t i = 1; i < n - 1; ++i) {"),
+    ("round_ties_away", "double r = nearbyint(q);", "double r = round(q);"),
+    ("round_truncate", "double r = nearbyint(q);", "double r = trunc(q);"),
+    ("round_overflow_early", "if (mag >= 65520.0 || isinf(a))", "if (mag >= 65504.0 || isinf(a))"),
+    ("round_no_subnormal_grid", "        e = -14;\n", "        e = -24;\n"),
+    ("round_exponent_bias", "(me - 1 + 15) << 10", "(me + 15) << 10"),
     ("argmax_signed_zero", "if (isnan(y[best]) || y[i] > y[best])",
      "if (isnan(y[best]) || y[i] > y[best] || (y[i] == y[best] && signbit(y[best]) && !signbit(y[i])))"),
 ]
