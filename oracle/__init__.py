@@ -59,7 +59,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_gemv_w4a8.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P]
     lib.orc_argmax_f32.argtypes = [P, I64, P]
     lib.orc_round_f16.argtypes = [P, I64, P]
-    for f in (lib.orc_f16_decode, lib.orc_gemv_f16, lib.orc_gemv_w8a8, lib.orc_gemv_w4a16,
+    lib.orc_causal_conv1d_step.argtypes = [P, P, P, P, I64, I64, ctypes.c_int, P, P]
+    for f in (lib.orc_causal_conv1d_step, lib.orc_f16_decode, lib.orc_gemv_f16, lib.orc_gemv_w8a8, lib.orc_gemv_w4a16,
               lib.orc_quantize_x_i8, lib.orc_gemv_w4a8, lib.orc_argmax_f32, lib.orc_round_f16):
         f.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [ctypes.c_int]
@@ -198,6 +199,35 @@ def gemv_w4a8(Wc: np.ndarray, s4: np.ndarray, xq: np.ndarray, s_x: float, group:
     _check((lib or load()).orc_gemv_w4a8(_ptr(Wc), _ptr(s4), _ptr(xq), float(np.float32(s_x)), N, K, group,
                                          _ptr(y), _ptr(A)), "gemv_w4a8")
     return y, A
+
+
+def causal_conv1d_step(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], state: np.ndarray,
+                       silu: bool, lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(out float64 [C], A [C], new state fp32 [C, W-1]) for one decode step
+    of the causal depthwise conv: x fp32 [C], w fp16 [C, W], bias fp32 [C]
+    or None, state fp32 [C, W-1] (oldest first; not modified)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = _u16(w)
+    C, W = w.shape
+    st = np.ascontiguousarray(state, dtype=np.float32).copy()
+    if x.shape != (C,) or st.shape != (C, W - 1):
+        raise ValueError("shape mismatch")
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty(C, np.float64)
+    A = np.empty(C, np.float64)
+    _check((lib or load()).orc_causal_conv1d_step(_ptr(x), _ptr(w), None if b is None else _ptr(b), _ptr(st), C, W,
+                                                  int(bool(silu)), _ptr(out), _ptr(A)), "causal_conv1d_step")
+    return out, A, st
+
+
+def conv_bound(A: np.ndarray, out: np.ndarray, silu: bool) -> np.ndarray:
+    """Tolerance of the conv step: the GEMV rule on the pre-activation sum;
+    SiLU (slope at most 1.1) carries it over, plus a relative term for the
+    fp32 exponential and division."""
+    A = np.asarray(A, np.float64)
+    if not silu:
+        return bound(A)
+    return REL_TOL * (1.1 * A + np.abs(np.asarray(out, np.float64))) + ABS_TOL
 
 
 def round_f16(v: np.ndarray, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:

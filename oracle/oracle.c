@@ -272,6 +272,47 @@ int orc_gemv_w4a8(const uint32_t *Wc, const uint16_t *s4, const int8_t *xq, floa
     return err;
 }
 
+/* One decode step of a causal depthwise 1-D convolution (MiniCPM-V 4.6 on
+ * Orange Pi AIPro post, third change: the causal-conv1d of each decode step,
+ * replaced there by a vectorised step kernel).  The page gives no formula;
+ * the reading used here is the usual decode-time update of a short causal
+ * convolution over each channel's last W inputs:
+ *   window_c = (state[c][0], ..., state[c][W-2], x[c])   (oldest first)
+ *   pre_c    = bias[c] + sum_j w[c][j] * window_c[j]
+ *   out[c]   = silu ? pre_c / (1 + exp(-pre_c)) : pre_c
+ *   state[c] <- (window_c[1], ..., window_c[W-1])        (x[c] appended)
+ * x, state, bias and out are fp32, w is fp16 [C, W] (decoded exactly);
+ * products and sums are exact or rounded once in fp64.  A[c] = |bias[c]| +
+ * sum_j |w[c][j] * window_c[j]| is returned for the tolerance.
+ * bias may be NULL (zero). */
+int orc_causal_conv1d_step(const float *x, const uint16_t *w, const float *bias, float *state,
+                           int64_t C, int64_t W, int silu, double *out, double *A)
+{
+    if (C < 0 || W < 2)
+        return ORC_ERR_SHAPE;
+    int err = ORC_OK;
+    for (int64_t c = 0; c < C; ++c) {
+        double pre = bias ? (double)bias[c] : 0.0;
+        double a = fabs(pre);
+        for (int64_t j = 0; j < W; ++j) {
+            double wv;
+            int e = f16_value(w[c * W + j], &wv);
+            if (e != ORC_OK)
+                err = e;
+            double win = j < W - 1 ? (double)state[c * (W - 1) + j] : (double)x[c];
+            pre += wv * win;
+            a += fabs(wv * win);
+        }
+        for (int64_t j = 0; j + 1 < W - 1; ++j)
+            state[c * (W - 1) + j] = state[c * (W - 1) + j + 1];
+        state[c * (W - 1) + W - 2] = x[c];
+        out[c] = silu ? pre / (1.0 + exp(-pre)) : pre;
+        if (A)
+            A[c] = a;
+    }
+    return err;
+}
+
 /* A decode step's linears feed each other through fp16 activations: the
  * output of one linear, rounded to fp16, is the input of a later one
  * (EdgeFM summary, section 2C: the decode iteration replayed as one

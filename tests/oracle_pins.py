@@ -364,10 +364,62 @@ def pin_chain_permutations(lib, K=256, depth=5, seed=22):
     assert np.array_equal(out[-1][1].astype(np.float64), want)
 
 
+# ----------------------------------------------------- causal conv1d ---
+
+def pin_conv_golden(lib):
+    g = _golden("conv1d_step.json")
+    for c in g["cases"]:
+        w = np.array(c["w"], np.float16)
+        b = None if c["bias"] is None else np.array(c["bias"], np.float32)
+        out, A, st = oracle.causal_conv1d_step(np.array(c["x"], np.float32), w, b,
+                                               np.array(c["state"], np.float32), c["silu"], lib=lib)
+        assert np.allclose(out, c["out"], rtol=1e-15, atol=1e-15), (out, c["out"])
+        assert st.tolist() == c["new_state"]
+
+
+def pin_conv_sequence_numpy(lib, C=37, W=4, T=12, seed=23):
+    """T steps from a zero state equal numpy's correlation of each channel's
+    whole input history with its taps (y_t = sum_j w[j] x[t - W + 1 + j])."""
+    r = synth.rng(912, seed)
+    w = r.normal(0, 0.5, (C, W)).astype(np.float16)
+    b = r.normal(0, 1, C).astype(np.float32)
+    xs = r.normal(0, 1, (T, C)).astype(np.float32)
+    st = np.zeros((C, W - 1), np.float32)
+    for t in range(T):
+        out, A, st = oracle.causal_conv1d_step(xs[t], w, b, st, False, lib=lib)
+        hist = np.concatenate([np.zeros((W - 1, C)), xs[:t + 1].astype(np.float64)])  # zero history first
+        for c in range(C):
+            want = np.correlate(hist[-W:, c], w[c].astype(np.float64), mode="valid")[0] + float(b[c])
+            assert abs(out[c] - want) <= 1e-12 * (A[c] + 1), (t, c, out[c], want)
+        assert np.array_equal(st, hist[-(W - 1):].T.astype(np.float32)), t  # the last W - 1 inputs
+    # SiLU is x * sigmoid(x) on the same pre-activation
+    out_s, _, _ = oracle.causal_conv1d_step(xs[0], w, b, st, True, lib=lib)
+    pre, _, _ = oracle.causal_conv1d_step(xs[0], w, b, st, False, lib=lib)
+    assert np.allclose(out_s, pre / (1 + np.exp(-pre)), rtol=1e-14, atol=1e-300)
+
+
+def pin_conv_special_kernels(lib, C=16, W=3, seed=24):
+    """Tap W-1 only: out = x exactly; tap 0 only: out = the input W-1 steps ago."""
+    r = synth.rng(913, seed)
+    xs = r.normal(0, 1, (6, C)).astype(np.float32)
+    last = np.zeros((C, W), np.float16)
+    last[:, W - 1] = 1
+    first = np.zeros((C, W), np.float16)
+    first[:, 0] = 1
+    st1 = np.zeros((C, W - 1), np.float32)
+    st2 = st1.copy()
+    for t in range(6):
+        o1, _, st1 = oracle.causal_conv1d_step(xs[t], last, None, st1, False, lib=lib)
+        o2, _, st2 = oracle.causal_conv1d_step(xs[t], first, None, st2, False, lib=lib)
+        assert np.array_equal(o1, xs[t].astype(np.float64))
+        assert np.array_equal(o2, xs[t - W + 1].astype(np.float64) if t >= W - 1 else np.zeros(C))
+
+
 ALL_PINS = [
     pin_f16_decode_all_patterns, pin_f16_golden, pin_f16_exact_rational, pin_f16_closed_forms,
     pin_f16_numpy_matmul, pin_f16_scaling, pin_w8a8_golden, pin_w8a8_int64_matmul,
     pin_w8a8_int32_range, pin_w4_golden, pin_w4_numpy_dequant, pin_w4_exact_rational,
     pin_quant_golden, pin_quant_properties, pin_w4a8_golden, pin_w4a8_integer_matmul,
     pin_argmax_golden, pin_argmax_numpy, pin_round_f16_golden, pin_round_f16_numpy, pin_chain_permutations,
+    pin_conv_golden, pin_conv_sequence_numpy, pin_conv_special_kernels,
 ]

@@ -43,6 +43,12 @@ MUTANTS = [
     ("round_overflow_early", "if (mag >= 65520.0 || isinf(a))", "if (mag >= 65504.0 || isinf(a))"),
     ("round_no_subnormal_grid", "        e = -14;\n", "        e = -24;\n"),
     ("round_exponent_bias", "(me - 1 + 15) << 10", "(me + 15) << 10"),
+    ("conv_taps_reversed", "f16_value(w[c * W + j], &wv)", "f16_value(w[c * W + (W - 1 - j)], &wv)"),
+    ("conv_shift_wrong_way", "state[c * (W - 1) + j] = state[c * (W - 1) + j + 1];",
+     "state[c * (W - 1) + j + 1] = state[c * (W - 1) + j];"),
+    ("conv_no_bias", "double pre = bias ? (double)bias[c] : 0.0;", "double pre = 0.0;"),
+    ("conv_silu_sign", "pre / (1.0 + exp(-pre))", "pre / (1.0 + exp(pre))"),
+    ("conv_x_not_appended", "state[c * (W - 1) + W - 2] = x[c];", "state[c * (W - 1) + W - 2] = 0.0f;"),
     ("argmax_signed_zero", "if (isnan(y[best]) || y[i] > y[best])",
      "if (isnan(y[best]) || y[i] > y[best] || (y[i] == y[best] && signbit(y[best]) && !signbit(y[i])))"),
 ]
