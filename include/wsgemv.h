@@ -193,6 +193,25 @@ wsg_status gemv_f16_argmax(const void *W, const void *x, float *y, int32_t *toke
                            wsg_stream_t stream);
 
 /*
+ * One decode step of a causal depthwise 1-D convolution (MiniCPM-V 4.6 on
+ * Orange Pi AIPro post, third change: the causal-conv1d of each decode step,
+ * replaced there by a vectorised step kernel; the page gives no formula, and
+ * this is the usual short causal convolution over each channel's last W
+ * inputs).  For every channel c < C:
+ *   window = (state[c][0], ..., state[c][W-2], x[c])     (oldest first)
+ *   pre    = bias[c] + sum_j w[c][j] * window[j]         (fp32)
+ *   out[c] = silu ? pre / (1 + exp(-pre)) : pre
+ *   state[c] <- (window[1], ..., window[W-1])
+ *   x      fp32 [C];  w fp16 [C, W];  bias optional fp32 [C];  state fp32
+ *          [C, W-1] read and updated;  out fp32 [C]; W = 2..8.  out and
+ *          state must not alias each other or the inputs.
+ * A decode-step linear can run this step over its own output y inside the
+ * kernel that writes y (wsg_linear.conv_*).
+ */
+wsg_status causal_conv1d_step(const float *x, const void *w, const float *bias, float *state, float *out,
+                              int64_t C, int32_t W, int32_t silu, wsg_stream_t stream);
+
+/*
  * Decode step: a fixed list of linears replayed once per token (EdgeFM
  * summary, section 2C: an execution graph is captured once and reused on
  * every decode iteration to cut kernel-launch overhead).
@@ -228,6 +247,14 @@ typedef struct wsg_linear {
                             (the rule of wsg_argmax_f32); N must be 1..INT32_MAX.
                             Other kinds: NULL */
     float *argmax_val;   /* optional fp32 [1]: y[*argmax_idx]; only with argmax_idx */
+    /* F16, W8A8 (M = 1): optional causal-conv1d decode step over y, fused where
+       y is final (see causal_conv1d_step; its C is N).  conv_out NULL = none. */
+    const void *conv_w;  /* fp16 [N, conv_width] */
+    const float *conv_bias; /* optional fp32 [N] */
+    float *conv_state;   /* fp32 [N, conv_width - 1], updated */
+    float *conv_out;     /* fp32 [N] */
+    int32_t conv_width;  /* 2..8 */
+    int32_t conv_silu;   /* nonzero: SiLU on the conv output */
 } wsg_linear;
 
 typedef struct wsg_step wsg_step;

@@ -226,6 +226,33 @@ wsg_status check_token_args(int64_t N, const int32_t *token, const float *token_
     return WSG_OK;
 }
 
+// Causal-conv1d step arguments: W taps (2..8), C channels (or the N of the
+// linear it follows); bias optional.
+wsg_status check_conv(int64_t C, int32_t W, const void *w, const float *bias, const float *state, const float *out) {
+    if (C < 0)
+        return WSG_ERR_SHAPE;
+    if (W < 2 || W > 8)
+        return WSG_ERR_UNSUPPORTED;
+    if (C == 0)
+        return WSG_OK;
+    if (!w || !state || !out)
+        return WSG_ERR_NULL;
+    if (!aligned(w, 2) || !aligned(state, 4) || !aligned(out, 4) || (bias && !aligned(bias, 4)))
+        return WSG_ERR_ALIGN;
+    return WSG_OK;
+}
+
+ConvOut conv_out(const void *w, const float *bias, float *state, float *out, int32_t W, int32_t silu) {
+    ConvOut c{};
+    c.w = static_cast<const uint16_t *>(w);
+    c.bias = bias;
+    c.state = state;
+    c.out = out;
+    c.W = W;
+    c.silu = silu != 0;
+    return c;
+}
+
 wsg_status enqueue_dense(int kind, const DenseLin &L, const DenseCfg &cfg, hipStream_t s) {
     hipError_t e = launch_dense(kind, L, cfg, s);
     if (e != hipSuccess)
@@ -475,6 +502,22 @@ wsg_status wsg_argmax_f32(const float *y, int64_t N, int32_t *token, float *toke
     });
 }
 
+wsg_status causal_conv1d_step(const float *x, const void *w, const float *bias, float *state, float *out, int64_t C,
+                              int32_t W, int32_t silu, wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_conv(C, W, w, bias, state, out);
+        if (st != WSG_OK || C == 0)
+            return st;
+        if (!x)
+            return WSG_ERR_NULL;
+        if (!aligned(x, 4))
+            return WSG_ERR_ALIGN;
+        hipError_t e = launch_conv1d_step(x, conv_out(w, bias, state, out, W, silu), C,
+                                          static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? WSG_OK : hip_fail(e);
+    });
+}
+
 wsg_status gemv_f16_argmax(const void *W, const void *x, float *y, int32_t *token, float *token_logit,
                            int64_t N, int64_t K, int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream) {
     return guarded([&]() -> wsg_status {
@@ -698,7 +741,7 @@ struct wsg_step {
     void *dev = nullptr;  // one device allocation: partials, descriptor and unit tables
 
     struct Op {
-        enum Type { kDense, kDenseGroup, kW4, kW4Group, kZero, kArgmax, kArgFinish } type;
+        enum Type { kDense, kDenseGroup, kW4, kW4Group, kZero, kArgmax, kArgFinish, kConv } type;
         int kind = 0;
         DenseLin d{};
         DenseCfg dc{};
@@ -712,6 +755,7 @@ struct wsg_step {
         float *zero_p = nullptr;
         int64_t zero_n = 0;
         ArgOut arg{};                 // kArgmax: token over zero_p[0..zero_n); kArgFinish: token from keys
+        ConvOut conv{};               // kConv: conv step over zero_p[0..zero_n)
         int fix = -1;                 // key array this op's token descriptor waits for (plan building)
     };
     std::vector<Op> ops;
@@ -722,6 +766,13 @@ struct wsg_step {
 namespace {
 
 wsg_status validate_linear(const wsg_linear &l) {
+    if (l.conv_out || l.conv_w || l.conv_state || l.conv_bias || l.conv_width) {
+        if ((l.kind != kF16 && l.kind != kW8A8) || l.M != 1)
+            return WSG_ERR_UNSUPPORTED;
+        wsg_status st = check_conv(l.N, l.conv_width, l.conv_w, l.conv_bias, l.conv_state, l.conv_out);
+        if (st != WSG_OK)
+            return st;
+    }
     if (l.argmax_idx || l.argmax_val) {
         if (l.kind != kF16 && l.kind != kW8A8)
             return WSG_ERR_UNSUPPORTED;
@@ -788,6 +839,9 @@ hipError_t run_ops(const wsg_step *st, hipStream_t s) {
             break;
         case wsg_step::Op::kArgFinish:
             e = launch_argmax_finish(op.arg, s);
+            break;
+        case wsg_step::Op::kConv:
+            e = launch_conv1d_step(op.zero_p, op.conv, op.zero_n, s);
             break;
         }
         if (e != hipSuccess)
@@ -892,6 +946,14 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     z.zero_n = l.N;
                     st->ops.push_back(z);
                 }
+                if (l.conv_out) {
+                    wsg_step::Op c{};
+                    c.type = wsg_step::Op::kConv;
+                    c.zero_p = l.y;
+                    c.zero_n = l.N;
+                    c.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
+                    st->ops.push_back(c);
+                }
                 if (l.argmax_idx) {
                     wsg_step::Op g{};
                     g.type = wsg_step::Op::kArgmax;
@@ -915,6 +977,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     o.d = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale), l.x_scale,
                                      l.acc_out, l.N, l.K, p);
                     o.dc.tail = dense_needs_tail(o.d, o.dc.CH);
+                    if (l.conv_out)
+                        o.d.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
                     if (l.argmax_idx) {
                         o.d.arg = arg_out(nullptr, dense_token_keys(o.d), l.argmax_idx, l.argmax_val);
                         o.fix = new_keys(o.d.arg.n_keys);
@@ -944,6 +1008,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     DenseLin L = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale),
                                             l.x_scale, l.acc_out, l.N, l.K, p);
                     const int li = (int)dl[ki].size();
+                    if (l.conv_out)
+                        L.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
                     if (l.argmax_idx) {
                         L.arg = arg_out(nullptr, dense_token_keys(L), l.argmax_idx, l.argmax_val);
                         wsg_step::Op f{};

@@ -22,6 +22,7 @@
 // one row per 64/R lanes in log2(64) shuffle stages), then written as y, or
 // as a partial that a second small kernel adds in slice order.
 #include "argmax.hpp"
+#include "conv1d.hpp"
 
 #include <algorithm>
 
@@ -168,6 +169,7 @@ __device__ __forceinline__ unsigned long long dense_unit(const DenseLin &L, int 
     for (int r = 0; r < R; ++r)
         acc[r] = 0;
     const bool take = L.arg.keys != nullptr && L.S == 1;
+    const bool conv = L.conv.out != nullptr && L.S == 1;
     unsigned long long best = 0;
 
     auto consume = [&](const u32x4(&buf)[R][CH], int gi, int c) {
@@ -189,6 +191,8 @@ __device__ __forceinline__ unsigned long long dense_unit(const DenseLin &L, int 
                     const float yv = store_row<KIND>(L, s, row, v);
                     if (take)
                         best = max_u64(best, arg_key(yv, row));
+                    if (conv)
+                        conv_step(L.conv, row, yv);
                 }
             }
 #pragma unroll
@@ -288,6 +292,8 @@ __global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
         }
         L.y[n] = yv;
         best = arg_key(yv, n);
+        if (L.conv.out != nullptr)
+            conv_step(L.conv, n, yv);
     }
     if (L.arg.keys != nullptr)
         arg_publish(L.arg, best, blockIdx.x);

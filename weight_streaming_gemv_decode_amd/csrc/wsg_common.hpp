@@ -39,6 +39,17 @@ struct ArgOut {
     int32_t pad;
 };
 
+// Fused causal-conv1d decode step over a linear's output (conv1d.hpp).
+// out == nullptr: none.
+struct ConvOut {
+    const uint16_t *w;     // fp16 [N][W] taps, oldest input first
+    const float *bias;     // optional [N]
+    float *state;          // [N][W-1] previous inputs, oldest first (updated)
+    float *out;            // [N]
+    int32_t W;             // taps, 2..8
+    int32_t silu;          // apply SiLU to the output
+};
+
 // One row-major linear streamed 16 bytes per lane (fp16: 8 weights per
 // vector, int8: 16 weights per vector).
 struct DenseLin {
@@ -57,6 +68,7 @@ struct DenseLin {
     int32_t n_tiles;       // ceil(N / tile_rows)
     int32_t pad;
     ArgOut arg;            // optional greedy token over y (S = 1: the units; S > 1: the reduce)
+    ConvOut conv;          // optional causal-conv1d step over y (same place as y is final)
 };
 
 // One int4 linear in the packed tile layout (16 rows x 128 k per 1 KiB tile).
@@ -135,6 +147,7 @@ hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int gri
                              hipStream_t s);
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
 hipError_t launch_argmax_finish(const ArgOut &a, hipStream_t s);
+hipError_t launch_conv1d_step(const float *x, const ConvOut &cv, int64_t C, hipStream_t s);
 hipError_t launch_argmax_f32(const float *y, int64_t N, ArgOut a, hipStream_t s);
 int argmax_f32_blocks(int64_t N);
 

@@ -37,7 +37,9 @@ class wsg_linear(ctypes.Structure):
                 ("W", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("x", ctypes.c_void_p),
                 ("x_scale", ctypes.c_void_p), ("y", ctypes.c_void_p), ("acc_out", ctypes.c_void_p),
                 ("group", ctypes.c_int32), ("splits", ctypes.c_int32), ("argmax_idx", ctypes.c_void_p),
-                ("argmax_val", ctypes.c_void_p)]
+                ("argmax_val", ctypes.c_void_p), ("conv_w", ctypes.c_void_p), ("conv_bias", ctypes.c_void_p),
+                ("conv_state", ctypes.c_void_p), ("conv_out", ctypes.c_void_p), ("conv_width", ctypes.c_int32),
+                ("conv_silu", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -60,6 +62,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "gemv_w4a8": ([P, P, P, P, P, P, I64, I64, I64, I32, P, SZ, P], I32),
         "wsg_argmax_f32": ([P, I64, P, P, P, SZ, P], I32),
         "gemv_f16_argmax": ([P, P, P, P, P, I64, I64, I32, P, SZ, P], I32),
+        "causal_conv1d_step": ([P, P, P, P, P, I64, I32, I32, P], I32),
         "wsg_decode_step_create": ([ctypes.POINTER(wsg_linear), I32, I32, P, ctypes.POINTER(P)], I32),
         "decode_step_linears": ([P, P], I32),
         "wsg_decode_step_destroy": ([P], I32),
@@ -193,6 +196,21 @@ def gemv_f16_argmax(W: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] 
     return y, token
 
 
+def causal_conv1d_step(x: torch.Tensor, w: torch.Tensor, state: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, silu: bool = False, stream=None) -> torch.Tensor:
+    """One causal depthwise conv1d decode step: x fp32 [C], w fp16 [C, W], state fp32 [C, W-1]
+    (updated in place), bias fp32 [C] or None; returns out fp32 [C]."""
+    C, W = w.shape
+    if out is None:
+        out = torch.empty(C, dtype=torch.float32, device=x.device)
+    bp = _dev(bias, torch.float32, "bias", (C,)) if bias is not None else None
+    _check(lib().causal_conv1d_step(_dev(x, torch.float32, "x", (C,)), _dev(w, torch.float16, "w", (C, W)), bp,
+                                    _dev(state, torch.float32, "state", (C, W - 1)),
+                                    _dev(out, torch.float32, "out", (C,)), C, W, int(bool(silu)), _stream(stream)),
+           "causal_conv1d_step")
+    return out
+
+
 def gemv_w8a8(Wq: torch.Tensor, w_scale: torch.Tensor, xq: torch.Tensor, x_scale: torch.Tensor,
               y: Optional[torch.Tensor] = None, acc_out: Optional[torch.Tensor] = None, want_acc: bool = True,
               splits: int = 0, ws: Optional[torch.Tensor] = None, stream=None):
@@ -296,16 +314,23 @@ class Linear:
     def __init__(self, kind: int, W: torch.Tensor, x: torch.Tensor, y: torch.Tensor, N: int, K: int, M: int = 1,
                  scale: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None,
                  acc_out: Optional[torch.Tensor] = None, group: int = 0, splits: int = 0,
-                 argmax_idx: Optional[torch.Tensor] = None, argmax_val: Optional[torch.Tensor] = None):
+                 argmax_idx: Optional[torch.Tensor] = None, argmax_val: Optional[torch.Tensor] = None,
+                 conv_w: Optional[torch.Tensor] = None, conv_bias: Optional[torch.Tensor] = None,
+                 conv_state: Optional[torch.Tensor] = None, conv_out: Optional[torch.Tensor] = None,
+                 conv_silu: bool = False):
         self.kind, self.W, self.x, self.y, self.N, self.K, self.M = kind, W, x, y, N, K, M
         self.scale, self.x_scale, self.acc_out, self.group, self.splits = scale, x_scale, acc_out, group, splits
         self.argmax_idx, self.argmax_val = argmax_idx, argmax_val
+        self.conv_w, self.conv_bias, self.conv_state, self.conv_out = conv_w, conv_bias, conv_state, conv_out
+        self.conv_width = 0 if conv_w is None else int(conv_w.shape[1])
+        self.conv_silu = int(bool(conv_silu))
 
     def c(self) -> wsg_linear:
         p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         return wsg_linear(self.kind, self.M, self.N, self.K, p(self.W), p(self.scale), p(self.x), p(self.x_scale),
                           p(self.y), p(self.acc_out), self.group, self.splits, p(self.argmax_idx),
-                          p(self.argmax_val))
+                          p(self.argmax_val), p(self.conv_w), p(self.conv_bias), p(self.conv_state),
+                          p(self.conv_out), self.conv_width, self.conv_silu)
 
 
 class DecodeStep:
