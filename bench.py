@@ -22,6 +22,7 @@ import numpy as np
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["weight_streaming_gemv_decode_amd/csrc/dense.hip", "weight_streaming_gemv_decode_amd/csrc/wsg_common.hpp",
+                  "weight_streaming_gemv_decode_amd/csrc/argmax.hpp", "weight_streaming_gemv_decode_amd/csrc/conv1d.hpp",
                   "weight_streaming_gemv_decode_amd/csrc/api.cpp"]
 
 
@@ -53,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true", help="only the decode-step stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,probe,ordered)")
+    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,conv,probe,ordered)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB fp32 copy kernel (reads 1 GiB, writes 1 GiB) to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass")
@@ -327,6 +328,39 @@ def main():
             st.close()
         extras["c6_w4a8_step_M1"] = rec
         del wl, w4
+
+    if want("conv"):
+        # causal-conv1d decode step over a 2048-channel qkv output, W = 4, SiLU:
+        # standalone (64 calls in one graph), and fused into the 28 qkv linears of the step
+        C, W = 2048, 4
+        r = synth.rng(6, 0)
+        cw = torch.from_numpy(r.normal(0, 0.5, (C, W)).astype(np.float16)).to(dev)
+        cb = torch.from_numpy(r.normal(0, 1, C).astype(np.float32)).to(dev)
+        xs_ = [torch.from_numpy(r.normal(0, 1, C).astype(np.float32)).to(dev) for _ in range(64)]
+        st = torch.zeros((C, W - 1), device=dev)
+        out = torch.empty(C, device=dev)
+        fn = lambda i: wsgemv.causal_conv1d_step(xs_[i % 64], cw, st, bias=cb, out=out, silu=True,  # noqa: E731
+                                                 stream=stream)
+        s = summary(graph_times(torch, fn, 64, 10, stream))
+        b = C * 4 + C * W * 2 + C * 4 + 2 * C * (W - 1) * 4 + C * 4
+        rec = {"standalone_C2048_W4": {"bytes": b, "median_us": s["median_ms"] * 1e3,
+                                       "note": "64 calls captured in one graph, per-call time; latency-bound"}}
+        states, outs, tl = [], [], []
+        for l in lins:
+            kw = {}
+            if l.N == 2048 and l.K == 1024:      # the qkv linears
+                states.append(torch.zeros((l.N, W - 1), device=dev))
+                outs.append(torch.empty(l.N, device=dev))
+                kw = dict(conv_w=cw, conv_bias=cb, conv_state=states[-1], conv_out=outs[-1], conv_silu=True)
+            tl.append(wsgemv.Linear(l.kind, l.W, l.x, l.y, l.N, l.K, **kw))
+        st_ = wsgemv.DecodeStep(tl, wsgemv.STEP_GROUPED, stream=stream)
+        for _ in range(5):
+            st_(stream)
+        s2 = summary(event_times(torch, lambda i: st_(stream), 100, stream))
+        rec["c3_grouped_graph_with_28_fused_convs"] = {"median_us": s2["median_ms"] * 1e3,
+                                                        "GBps": step_bytes / (s2["median_ms"] * 1e-3) / 1e9}
+        st_.close()
+        extras["conv1d"] = rec
 
     if want("probe"):
         nb = 2 << 30
