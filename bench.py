@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true", help="only the decode-step stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,conv,probe,ordered)")
+    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,conv,graph,probe,ordered)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB fp32 copy kernel (reads 1 GiB, writes 1 GiB) to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass")
@@ -108,6 +108,34 @@ def graph_times(torch, fn, inner, reps, stream):
     return out
 
 
+def probe_same_size(torch, wsgemv, nbytes, stream, graph_inner=0, reps=30):
+    """Median time (us) of the read probe over `nbytes`, rotated over enough
+    copies to defeat the 256 MB Infinity Cache, timed like the workload it
+    is compared with: back-to-back launches with events, or graph_inner
+    calls captured in one graph.  Every kernel pays a fixed ramp and drain
+    (about 5 us here), so the attainable rate depends on the size."""
+    nb = max(16, nbytes // 16 * 16)
+    copies = max(1, min(64, -(-(768 << 20) // nb)))
+    bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    out = torch.empty(1 << 14, device="cuda")
+    g = wsgemv.read_probe_grid(nb)
+    fn = lambda i: wsgemv.read_probe(bufs[i % copies], out, grid=g, stream=stream)  # noqa: E731
+    for i in range(3):
+        fn(i)
+    if graph_inner:
+        ts = graph_times(torch, fn, graph_inner, 10, stream)
+    else:
+        ts = event_times(torch, fn, reps, stream)
+    del bufs
+    return statistics.median(ts) * 1e3
+
+
+def attainable(torch, wsgemv, nbytes, achieved_us, stream, graph_inner=0):
+    t = probe_same_size(torch, wsgemv, nbytes, stream, graph_inner)
+    return {"probe_us": round(t, 2), "probe_GBps": round(nbytes / (t * 1e-6) / 1e9, 1),
+            "frac_of_probe": round(t / achieved_us, 4)}
+
+
 def summary(ts):
     ts = sorted(ts)
     return {"median_ms": statistics.median(ts), "p10_ms": ts[len(ts) // 10], "p90_ms": ts[(9 * len(ts)) // 10],
@@ -151,7 +179,8 @@ def main():
     step_bytes = w_bytes + x_bytes + y_bytes
     log(f"inputs ready in {time.time() - t0:.1f}s: {len(lins)} linears, {step_bytes} algorithmic bytes/step")
 
-    # ---- the timed configuration: GROUPED graph ----
+    # ---- the timed configuration: the GROUPED plan (one launch over a work table;
+    # a single launch is cheaper than a one-node graph launch, so it is direct) ----
     with torch.cuda.stream(stream):
         step = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED, stream=stream)
         for _ in range(args.warmup):
@@ -167,7 +196,7 @@ def main():
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"GROUPED graph: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s")
+    log(f"GROUPED plan (graph={step.uses_graph()}): {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s")
 
     # per-launch duration of the dominant kernel (the grouped fp16 kernel), on its own stream
     eager = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER, stream=stream)
@@ -184,10 +213,30 @@ def main():
                 "traffic_detail": None if rec is None else {k: rec[k] for k in ("read_bytes", "write_bytes",
                                                                                "ratio_to_algorithmic")}}
     log(f"grouped kernel: mean {ks['mean_ms'] * 1e3:.1f} us -> {achieved:.0f} GB/s")
+    if not args.no_extras:
+        roofline["attainable_same_size"] = attainable(torch, wsgemv, step_bytes, ks["mean_ms"] * 1e3, stream)
+        log(f"read probe over the same bytes: {roofline['attainable_same_size']}")
 
     extras = {}
     only = set(filter(None, args.only.split(",")))
     want = (lambda k: (not args.no_extras) and (not only or k in only))
+
+    if want("graph"):
+        # the same GROUPED plan forced into a one-node hipGraph: a graph launch
+        # costs more than the one direct launch the plan uses
+        fg = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH, stream=stream)
+        for _ in range(5):
+            fg(stream)
+        stream.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps):
+                fg(stream)
+        stream.synchronize()
+        t = (time.perf_counter() - t0) * 1e6 / args.steps
+        extras["c3_grouped_forced_graph"] = {"us_per_step": round(t, 2),
+                                             "GBps": round(step_bytes / (t * 1e-6) / 1e9, 1)}
+        fg.close()
 
     if want("ordered"):
         o = wsgemv.DecodeStep(lins, wsgemv.STEP_ORDERED, stream=stream)
@@ -239,6 +288,7 @@ def main():
         res["with_token"] = {"median_us": s["median_ms"] * 1e3, "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
                              "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                              "note": "the GEMV writing one key per workgroup, then the one-workgroup finish kernel"}
+        res["attainable_same_size"] = attainable(torch, wsgemv, b, res["S=1"]["median_us"], stream)
         extras["c2_lm_head_248320x1024"] = {"bytes": b, "rotation": "2 weight copies (1.02 GB)", **res}
         del Wcopy
 
@@ -254,7 +304,9 @@ def main():
         b = N * K * 2 + K * 2 + N * 4
         extras["c1_2048x2048"] = {"bytes": b, "median_us": s["median_ms"] * 1e3,
                                   "GBps": b / (s["median_ms"] * 1e-3) / 1e9, "rotation": "64 copies (537 MB)",
-                                  "note": "64 calls captured in one graph, per-call time; launch-bound shape"}
+                                  "note": "64 calls captured in one graph, per-call time; launch-bound shape",
+                                  "attainable_same_size": attainable(torch, wsgemv, b, s["median_ms"] * 1e3, stream,
+                                                                     graph_inner=64)}
         del copies
 
     if want("c4"):
@@ -274,7 +326,9 @@ def main():
             extras[f"c4_w8a8_{N}x{K}"] = {"bytes_incl_acc_out": b, "median_us": s["median_ms"] * 1e3,
                                           "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
                                           "splits": wsgemv.plan_splits(1, 1, N, K),
-                                          "rotation": "9 copies, 36 calls captured in one graph"}
+                                          "rotation": "9 copies, 36 calls captured in one graph",
+                                          "attainable_same_size": attainable(torch, wsgemv, b, s["median_ms"] * 1e3,
+                                                                             stream, graph_inner=36)}
             del copies
 
     if want("c5"):
@@ -293,7 +347,7 @@ def main():
             torch.cuda.synchronize()
             rec = {"bytes": b}
             # graph replay, and the same single grouped launch enqueued directly
-            for tag, mode in (("graph", wsgemv.STEP_GROUPED), ("launch", wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER)):
+            for tag, mode in (("launch", wsgemv.STEP_GROUPED), ("forced_graph", wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH)):
                 st = wsgemv.DecodeStep(wl, mode, stream=stream)
                 for _ in range(5):
                     st(stream)
@@ -301,6 +355,7 @@ def main():
                 rec[tag] = {"median_us": s["median_ms"] * 1e3, "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
                             "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
                 st.close()
+            rec["attainable_same_size"] = attainable(torch, wsgemv, b, rec["launch"]["median_us"], stream)
             extras[f"c5_w4a16_step_M{M}"] = rec
             del wl, w4
 
@@ -318,7 +373,7 @@ def main():
             b += Wc.nbytes + s4.nbytes + X.nbytes + N * 4
         torch.cuda.synchronize()
         rec = {"bytes": b}
-        for tag, mode in (("graph", wsgemv.STEP_GROUPED), ("launch", wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER)):
+        for tag, mode in (("launch", wsgemv.STEP_GROUPED), ("forced_graph", wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH)):
             st = wsgemv.DecodeStep(wl, mode, stream=stream)
             for _ in range(5):
                 st(stream)
@@ -326,6 +381,7 @@ def main():
             rec[tag] = {"median_us": s["median_ms"] * 1e3, "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
                         "pct_peak": 100 * b / (s["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
             st.close()
+        rec["attainable_same_size"] = attainable(torch, wsgemv, b, rec["launch"]["median_us"], stream)
         extras["c6_w4a8_step_M1"] = rec
         del wl, w4
 
@@ -363,17 +419,12 @@ def main():
         extras["conv1d"] = rec
 
     if want("probe"):
-        nb = 2 << 30
-        buf = torch.empty(nb, dtype=torch.uint8, device=dev)
-        buf.fill_(1)
-        out = torch.empty(4096, device=dev)
-        g = wsgemv.read_probe_grid(nb)
-        fn = lambda i: wsgemv.read_probe(buf, out, grid=g, stream=stream)  # noqa: E731
-        for i in range(3):
-            fn(i)
-        s = summary(event_times(torch, fn, 20, stream))
-        extras["hbm_read_probe_2GiB"] = {"median_us": s["median_ms"] * 1e3, "GBps": nb / (s["median_ms"] * 1e-3) / 1e9}
-        del buf
+        # attainable streaming-read rate against transfer size (back-to-back launches)
+        rec = {}
+        for mb in (128, 512, 2048):
+            t = probe_same_size(torch, wsgemv, mb << 20, stream, reps=20)
+            rec[f"{mb}MiB"] = {"median_us": round(t, 2), "GBps": round((mb << 20) / (t * 1e-6) / 1e9, 1)}
+        extras["hbm_read_probe"] = rec
 
     # ---- CPU oracle on the host cores, same step inputs ----
     cpu = None
@@ -405,8 +456,9 @@ def main():
         "dtype": "f16",
         "data": "synthetic: seeded fp16 weights ~N(0,0.02), activations ~N(0,1); fp32 accumulate, fp32 outputs",
         "config": {"workload": "fp16 batch-1 decode-step linear stream: 28 x {qkv 2048x1024, o 1024x1024, "
-                               "gate_up 6144x1024, down 1024x3072} + lm_head 248320x1024, one hipGraph "
-                               "(GROUPED: one launch over a work table)",
+                               "gate_up 6144x1024, down 1024x3072} + lm_head 248320x1024, GROUPED plan: "
+                               "one launch over a work table of 16,720 units (ORDERED, one node per linear, "
+                               "is the captured hipGraph in extras)",
                    "bytes_per_step": step_bytes, "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
                    "launches_per_step": launches, "work_units": units},
         "roofline": roofline,

@@ -218,8 +218,13 @@ wsg_status causal_conv1d_step(const float *x, const void *w, const float *bias, 
  *
  * wsg_decode_step_create validates every descriptor, builds the launch plan,
  * allocates the plan's own split-K partials and work table (the only device
- * allocation in this library), and captures the launches into a hipGraph on
- * an internal stream.  The descriptors' pointers are frozen into the plan:
+ * allocation in this library), and, when the step has at least
+ * WSG_STEP_GRAPH_MIN_LAUNCHES launches, captures them into a hipGraph on an
+ * internal stream.  A graph launch costs more host and device time than a
+ * few direct kernel launches on this platform (about 22 us of host time per
+ * hipGraphLaunch against about 3 us per kernel launch), so shorter plans
+ * (GROUPED is usually one launch) launch directly.  The descriptors'
+ * pointers are frozen into the plan:
  * later calls read the buffers at those addresses (write new activations into
  * the same x buffers between steps).
  *   mode WSG_STEP_ORDERED: one kernel node per linear, in list order.
@@ -227,7 +232,8 @@ wsg_status causal_conv1d_step(const float *x, const void *w, const float *bias, 
  *     work table of (linear, row tile, k-slice) units.  Valid because every
  *     linear of the list reads its own x and writes its own y; a list whose
  *     linears feed each other must use ORDERED.
- *   | WSG_STEP_EAGER: skip the graph; decode_step_linears launches directly.
+ *   | WSG_STEP_EAGER: never capture; decode_step_linears launches directly.
+ *   | WSG_STEP_FORCE_GRAPH: always capture, whatever the launch count.
  * decode_step_linears enqueues one step on `stream`.  A plan is not
  * thread-safe and one plan's steps must not overlap each other in time.
  */
@@ -259,14 +265,17 @@ typedef struct wsg_linear {
 
 typedef struct wsg_step wsg_step;
 
-enum { WSG_STEP_ORDERED = 0, WSG_STEP_GROUPED = 1, WSG_STEP_EAGER = 0x100 };
+enum { WSG_STEP_ORDERED = 0, WSG_STEP_GROUPED = 1, WSG_STEP_EAGER = 0x100, WSG_STEP_FORCE_GRAPH = 0x200,
+       WSG_STEP_GRAPH_MIN_LAUNCHES = 8 };
 
 wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t mode,
                                   wsg_stream_t stream, wsg_step **out);
 wsg_status decode_step_linears(wsg_step *step, wsg_stream_t stream);
 wsg_status wsg_decode_step_destroy(wsg_step *step);
-/* Launches per step (kernel nodes) and work units of the plan. */
-wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t *units);
+/* Launches per step (kernel nodes), work units of the plan, and whether the
+ * step replays a captured graph (1) or launches directly (0).  Any output
+ * pointer may be NULL. */
+wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t *units, int32_t *graph);
 
 /*
  * HBM read ceiling: every lane streams 16-byte loads over buf[0, bytes) and

@@ -181,6 +181,8 @@ def test_decode_step_validation(L):
     lin = wsgemv.wsg_linear(0, 1, 64, 64, FAKE, None, FAKE, None, FAKE, None, 0, 0)
     arr = (wsgemv.wsg_linear * 1)(lin)
     assert L.wsg_decode_step_create(arr, 1, 7, None, ctypes.byref(out)) == UNSUP   # bad mode
+    assert L.wsg_decode_step_create(arr, 1, 0x300, None, ctypes.byref(out)) == UNSUP  # eager and forced graph
+    assert L.wsg_decode_step_create(arr, 1, 0x400, None, ctypes.byref(out)) == UNSUP  # unknown flag
     assert L.wsg_decode_step_create(arr, -1, 0, None, ctypes.byref(out)) == SHAPE
     assert L.wsg_decode_step_create(None, 1, 0, None, ctypes.byref(out)) == NULL
     assert L.wsg_decode_step_create(arr, 1, 0, None, None) == NULL

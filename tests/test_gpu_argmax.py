@@ -161,7 +161,8 @@ def _step_lins(step_in, tok, val):
     return lins, refs
 
 
-@pytest.mark.parametrize("mode", [wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER])
+@pytest.mark.parametrize("mode", [wsgemv.STEP_ORDERED, wsgemv.STEP_ORDERED | wsgemv.STEP_FORCE_GRAPH, wsgemv.STEP_GROUPED,
+                                  wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER])
 def test_decode_step_takes_the_token(mode):
     """Replays with new activations each time: every replay's token is the
     argmax of that replay's logits (the token header clears itself)."""
@@ -199,7 +200,7 @@ def test_step_w8a8_token_and_split_ordered():
     v16 = torch.empty(1, device="cuda")
     lins = [wsgemv.Linear(wsgemv.W8A8, dev(Wq), dev(xq), y8, N, K, scale=dev(sw), x_scale=xs, argmax_idx=t8),
             wsgemv.Linear(wsgemv.F16, dev(W), dev(x), y16, 20000, 3072, splits=3, argmax_idx=t16, argmax_val=v16)]
-    for mode in (wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED):
+    for mode in (wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH):
         use = lins if mode == wsgemv.STEP_ORDERED else lins[:1]
         st = wsgemv.DecodeStep(use, mode)
         st()

@@ -71,7 +71,8 @@ def _fused_case(kind, N, K, W, silu, workload):
     return cw, cb, st0
 
 
-@pytest.mark.parametrize("mode", [wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER])
+@pytest.mark.parametrize("mode", [wsgemv.STEP_ORDERED, wsgemv.STEP_ORDERED | wsgemv.STEP_FORCE_GRAPH, wsgemv.STEP_GROUPED,
+                                  wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER])
 @pytest.mark.parametrize("silu", [False, True])
 def test_fused_into_f16_linear(mode, silu):
     """The conv step over a 2048 x 1024 linear's output inside its kernel;
@@ -143,7 +144,7 @@ def test_fused_into_w8a8_split_and_zero_k():
             wsgemv.Linear(wsgemv.F16, torch.empty((64, 0), dtype=torch.float16, device="cuda"),
                           torch.empty(0, dtype=torch.float16, device="cuda"), yz, 64, 0, conv_w=dev(cw[:64]),
                           conv_bias=dev(cb[:64]), conv_state=stz, conv_out=outz)]
-    step = wsgemv.DecodeStep(lins, wsgemv.STEP_ORDERED)
+    step = wsgemv.DecodeStep(lins, wsgemv.STEP_ORDERED | wsgemv.STEP_FORCE_GRAPH)
     step()
     acc, y_ref, A_y = oracle.gemv_w8a8(Wq, sw, xq, synth.X_SCALE_W8A8)
     assert_within(host(y), y_ref, A_y, "w8a8 y")

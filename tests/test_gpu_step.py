@@ -33,7 +33,7 @@ def small_step():
     return synth.decode_step_f16(workload=30, n_layers=2, lm_head_rows=8192 + 40)
 
 
-@pytest.mark.parametrize("mode", [wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED,
+@pytest.mark.parametrize("mode", [wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED, wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH,
                                   wsgemv.STEP_ORDERED | wsgemv.STEP_EAGER, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER])
 def test_f16_step_modes(small_step, mode):
     say(f"step f16 mode={mode:#x}")
@@ -52,16 +52,22 @@ def test_f16_step_modes(small_step, mode):
 def test_graph_equals_eager_and_ordered_equals_standalone(small_step):
     say("step graph vs eager vs standalone")
     outs = {}
+    graph_used = {}
     for mode in (wsgemv.STEP_ORDERED, wsgemv.STEP_ORDERED | wsgemv.STEP_EAGER,
-                 wsgemv.STEP_GROUPED, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER):
+                 wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER):
         lins, _ = _f16_linears(small_step)
         st = wsgemv.DecodeStep(lins, mode)
         st()
         outs[mode] = [host(l.y) for l in lins]
+        graph_used[mode] = st.uses_graph()
         st.close()
+    # 9 linears: ORDERED has 9 launches (captured), GROUPED one (captured only when forced)
+    assert graph_used == {wsgemv.STEP_ORDERED: True, wsgemv.STEP_ORDERED | wsgemv.STEP_EAGER: False,
+                          wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH: True,
+                          wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER: False}
     for a, b in zip(outs[wsgemv.STEP_ORDERED], outs[wsgemv.STEP_ORDERED | wsgemv.STEP_EAGER]):
         assert_bits_equal(a, b, "ordered graph vs eager")
-    for a, b in zip(outs[wsgemv.STEP_GROUPED], outs[wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER]):
+    for a, b in zip(outs[wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH], outs[wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER]):
         assert_bits_equal(a, b, "grouped graph vs eager")
     # ORDERED uses the same launch table as a standalone call
     for (name, W, x), yo in zip(small_step, outs[wsgemv.STEP_ORDERED]):
@@ -111,7 +117,8 @@ def test_mixed_kinds_step():
         lins.append(wsgemv.Linear(wsgemv.W4A16, Wp, dev(X), yw, 200, 3072, M=M, scale=Sp, group=128))
         Y_ref, Aw = oracle.gemv_w4a16(Wc, s4, X)
         checks.append((yw, Y_ref, Aw))
-    for mode in (wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED):
+    for mode in (wsgemv.STEP_ORDERED, wsgemv.STEP_ORDERED | wsgemv.STEP_FORCE_GRAPH, wsgemv.STEP_GROUPED,
+                 wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH):
         step = wsgemv.DecodeStep(lins, mode)
         step()
         for yt, y_ref, A in checks:
@@ -144,6 +151,7 @@ def test_replays_interleaved_with_eager_work(small_step):
     want = [host(l.y).copy() for l in lins]
     eager.close()
     graph = wsgemv.DecodeStep(lins, wsgemv.STEP_ORDERED)
+    assert graph.uses_graph()
     W = dev(synth.f16_normal(33, 0, (700, 3072), 0.02))
     x = dev(synth.f16_normal(33, 1, (3072,), 1.0))
     for rep in range(4):

@@ -151,7 +151,7 @@ def test_step_with_w4a8_linears():
     lins.append(wsgemv.Linear(wsgemv.W4A16, Wp, dev(x), y, 500, 2048, scale=Sp, group=128))
     checks.append((y, *oracle.gemv_w4a16(Wc, s4, x)))
     outs = {}
-    for mode in (wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER):
+    for mode in (wsgemv.STEP_ORDERED, wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH, wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER):
         for yt, _, _ in checks:
             yt.fill_(float("nan"))
         step = wsgemv.DecodeStep(lins, mode)
@@ -161,5 +161,5 @@ def test_step_with_w4a8_linears():
             assert_within(host(yt), y_ref, A, f"mode {mode:#x}")
         outs[mode] = [host(yt).copy() for yt, _, _ in checks]
         step.close()
-    for a, b in zip(outs[wsgemv.STEP_GROUPED], outs[wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER]):
+    for a, b in zip(outs[wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH], outs[wsgemv.STEP_GROUPED | wsgemv.STEP_EAGER]):
         assert_bits_equal(a, b, "grouped graph vs eager")

@@ -883,7 +883,9 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         const int base_mode = mode & 0xFF;
         if (base_mode != WSG_STEP_ORDERED && base_mode != WSG_STEP_GROUPED)
             return WSG_ERR_UNSUPPORTED;
-        if (mode & ~(0xFF | WSG_STEP_EAGER))
+        if (mode & ~(0xFF | WSG_STEP_EAGER | WSG_STEP_FORCE_GRAPH))
+            return WSG_ERR_UNSUPPORTED;
+        if ((mode & WSG_STEP_EAGER) && (mode & WSG_STEP_FORCE_GRAPH))
             return WSG_ERR_UNSUPPORTED;
         for (int32_t i = 0; i < n; ++i) {
             wsg_status v = validate_linear(linears[i]);
@@ -1178,8 +1180,13 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                 st->launches += op.w.S > 1;
             } else if (op.type == wsg_step::Op::kDenseGroup || op.type == wsg_step::Op::kW4Group) {
                 st->units += op.n_units;
+            } else if (op.type == wsg_step::Op::kArgmax) {
+                st->launches += 1;  // the reduce over y, then the finish kernel
             }
         }
+        // A graph pays off only when it replaces enough direct launches.
+        if (!(mode & WSG_STEP_FORCE_GRAPH) && st->launches < WSG_STEP_GRAPH_MIN_LAUNCHES)
+            st->use_graph = false;
         if (st->use_graph && !st->ops.empty()) {
             hipError_t e = hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking);
             if (e == hipSuccess)
@@ -1225,13 +1232,15 @@ wsg_status wsg_decode_step_destroy(wsg_step *step) {
     });
 }
 
-wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t *units) {
+wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t *units, int32_t *graph) {
     if (!step)
         return WSG_ERR_STATE;
     if (launches)
         *launches = step->launches;
     if (units)
         *units = step->units;
+    if (graph)
+        *graph = step->exec != nullptr;
     return WSG_OK;
 }
 

@@ -21,7 +21,8 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "wsgemv.h")
 
 F16, W8A8, W4A16, W4A8 = 0, 1, 2, 3
 ARGMAX_WS_BYTES, WITH_ARGMAX = 8192, 0x100
-STEP_ORDERED, STEP_GROUPED, STEP_EAGER = 0, 1, 0x100
+STEP_ORDERED, STEP_GROUPED, STEP_EAGER, STEP_FORCE_GRAPH = 0, 1, 0x100, 0x200
+STEP_GRAPH_MIN_LAUNCHES = 8
 STATUS = {0: "WSG_OK", 1: "WSG_ERR_NULL", 2: "WSG_ERR_SHAPE", 3: "WSG_ERR_ALIGN", 4: "WSG_ERR_UNSUPPORTED",
           5: "WSG_ERR_WORKSPACE", 6: "WSG_ERR_HIP", 7: "WSG_ERR_NOMEM", 8: "WSG_ERR_STATE"}
 
@@ -66,7 +67,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "wsg_decode_step_create": ([ctypes.POINTER(wsg_linear), I32, I32, P, ctypes.POINTER(P)], I32),
         "decode_step_linears": ([P, P], I32),
         "wsg_decode_step_destroy": ([P], I32),
-        "wsg_decode_step_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I64)], I32),
+        "wsg_decode_step_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I64), ctypes.POINTER(I32)], I32),
         "wsg_read_probe": ([P, SZ, P, I32, P], I32),
         "wsg_read_probe_grid": ([SZ], I32),
         "wsg_tune_set": ([ctypes.c_char_p, I64], I32),
@@ -355,8 +356,13 @@ class DecodeStep:
 
     def info(self) -> Tuple[int, int]:
         a, b = ctypes.c_int32(), ctypes.c_int64()
-        _check(lib().wsg_decode_step_info(self._h, ctypes.byref(a), ctypes.byref(b)), "wsg_decode_step_info")
+        _check(lib().wsg_decode_step_info(self._h, ctypes.byref(a), ctypes.byref(b), None), "wsg_decode_step_info")
         return a.value, b.value
+
+    def uses_graph(self) -> bool:
+        g = ctypes.c_int32()
+        _check(lib().wsg_decode_step_info(self._h, None, None, ctypes.byref(g)), "wsg_decode_step_info")
+        return bool(g.value)
 
     def close(self) -> None:
         if self._h is not None:
