@@ -249,10 +249,10 @@ typedef struct wsg_linear {
     int32_t *acc_out;    /* W8A8: optional int32 [N]; otherwise NULL */
     int32_t group;       /* W4A16, W4A8: 128; otherwise 0 */
     int32_t splits;      /* 0 = table's choice; ORDERED mode only */
-    int32_t *argmax_idx; /* F16, W8A8: optional int32 [1], the greedy token over y
-                            (the rule of wsg_argmax_f32); N must be 1..INT32_MAX.
-                            Other kinds: NULL */
-    float *argmax_val;   /* optional fp32 [1]: y[*argmax_idx]; only with argmax_idx */
+    int32_t *argmax_idx; /* optional int32 [M]: the greedy token of each output row
+                            y[m] (the rule of wsg_argmax_f32; for a verify block, one
+                            token per drafted position); N must be 1..INT32_MAX */
+    float *argmax_val;   /* optional fp32 [M]: their logits; only with argmax_idx */
     /* F16, W8A8 (M = 1): optional causal-conv1d decode step over y, fused where
        y is final (see causal_conv1d_step; its C is N).  conv_out NULL = none. */
     const void *conv_w;  /* fp16 [N, conv_width] */

@@ -126,7 +126,7 @@ def test_argmax_validation(L):
     out = ctypes.c_void_p()
     lin = lambda kind, tok, val=None, N=64: wsgemv.wsg_linear(kind, 1, N, 256, FAKE, FAKE, FAKE, FAKE,  # noqa
                                                              FAKE, None, 128 if kind >= 2 else 0, 0, tok, val)
-    for kind, tok, val, N, want in ((2, FAKE, None, 64, UNSUP), (0, FAKE + 2, None, 64, ALIGN),
+    for kind, tok, val, N, want in ((2, FAKE, None, 1 << 31, UNSUP), (0, FAKE + 2, None, 64, ALIGN),
                                     (0, None, FAKE, 64, NULL), (0, FAKE, None, 1 << 31, UNSUP)):
         arr = (wsgemv.wsg_linear * 1)(lin(kind, tok, val, N))
         assert L.wsg_decode_step_create(arr, 1, 0, None, ctypes.byref(out)) == want, (kind, want)

@@ -213,3 +213,73 @@ def test_step_w8a8_token_and_split_ordered():
         if mode == wsgemv.STEP_ORDERED:
             _check_fused(W, x, host(y16), int(host(t16)[0]), host(v16), "ordered split")
         st.close()
+
+
+def _w4_aligned_row(x, K):
+    """Canonical int4 words of a row whose weights follow the sign of x
+    (q = 15 where x > 0, q = 0 elsewhere): a logit far above the others."""
+    q = np.where(np.asarray(x, np.float32).reshape(-1) > 0, 15, 0).astype(np.uint32)
+    words = np.zeros(K // 8, np.uint32)
+    for i in range(8):
+        words |= q[i::8] << (4 * i)
+    return words
+
+
+@pytest.mark.parametrize("kind,M", [(wsgemv.W4A16, 1), (wsgemv.W4A16, 3), (wsgemv.W4A16, 4), (wsgemv.W4A16, 8),
+                                    (wsgemv.W4A8, 1)])
+@pytest.mark.parametrize("mode,splits", [(wsgemv.STEP_ORDERED, 0), (wsgemv.STEP_ORDERED, 2),
+                                         (wsgemv.STEP_GROUPED, 0),
+                                         (wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH, 0)])
+def test_int4_tokens_per_position(kind, M, mode, splits):
+    """An int4 lm_head-shaped linear takes one token per output row (for a
+    verify block: per drafted position), with a planted maximum in one
+    position and a bit-identical copy of it at a lower row (the tie)."""
+    say(f"argmax int4 kind={kind} M={M} mode={mode:#x} S={splits}")
+    N, K = 60001, 1024
+    Wc = synth.w4_words(160, M, N, K)
+    s4 = synth.f16_uniform(160, M + 1, (N, K // 128), 0.002, 0.02)
+    X = synth.f16_normal(160, M + 2, (M, K), synth.X_SIGMA)
+    Wc[40000] = _w4_aligned_row(X[M - 1], K)       # position M-1: planted maximum ...
+    s4[40000] = np.float16(0.02)
+    Wc[777], s4[777] = Wc[40000], s4[40000]         # ... and its copy at a lower row
+    Wp, Sp = wsgemv.pack_w4(dev(Wc), dev(s4))
+    y = torch.full((M, N), float("nan"), device="cuda")
+    tok = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    val = torch.empty(M, device="cuda")
+    x_d = dev(X) if kind == wsgemv.W4A16 else dev(X.reshape(K))
+    lin = wsgemv.Linear(kind, Wp, x_d, y, N, K, M=M, scale=Sp, group=128, splits=splits, argmax_idx=tok,
+                        argmax_val=val)
+    st = wsgemv.DecodeStep([lin], mode)
+    st()
+    st()
+    yh = host(y).reshape(M, N)
+    if kind == wsgemv.W4A16:
+        Y_ref, A = oracle.gemv_w4a16(Wc, s4, X)
+        Y_ref, A = Y_ref.reshape(M, N), A.reshape(M, N)
+    else:
+        xq, sx = oracle.quantize_x_i8(X.reshape(K))
+        Y_ref, A = oracle.gemv_w4a8(Wc, s4, xq, sx)
+        Y_ref, A = Y_ref.reshape(1, N), A.reshape(1, N)
+    assert_within(yh, Y_ref, A, "logits")
+    toks, vals = host(tok), host(val)
+    for m in range(M):
+        t = int(toks[m])
+        assert t == oracle.argmax_f32(yh[m]), f"position {m}: not the argmax of the kernel's logits"
+        assert oracle.argmax_is_valid(t, Y_ref[m], A[m]), f"position {m}: not a largest exact logit"
+        assert vals[m] == yh[m, t]
+    assert int(toks[M - 1]) == 777                  # the tie goes to the lower row
+    st.close()
+
+
+def test_int4_tokens_k_zero():
+    say("argmax int4 K=0")
+    M, N = 3, 500
+    y = torch.full((M, N), 5.0, device="cuda")
+    tok = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    lin = wsgemv.Linear(wsgemv.W4A16, torch.empty(16, dtype=torch.uint8, device="cuda"),
+                        torch.empty((M, 0), dtype=torch.float16, device="cuda"), y, N, 0, M=M,
+                        scale=torch.empty(16, dtype=torch.uint8, device="cuda"), group=128, argmax_idx=tok)
+    st = wsgemv.DecodeStep([lin], wsgemv.STEP_ORDERED)
+    st()
+    assert host(tok).tolist() == [0] * M and not host(y).any()
+    st.close()

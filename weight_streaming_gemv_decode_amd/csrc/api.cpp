@@ -194,10 +194,12 @@ wsg_status check_ws(const void *ws, size_t ws_bytes, size_t need) {
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-ArgOut arg_out(void *keys, int32_t n_keys, int32_t *token, float *token_logit) {
+ArgOut arg_out(void *keys, int32_t n_keys, int32_t *token, float *token_logit, int32_t M = 1) {
     ArgOut a{};
     a.keys = static_cast<unsigned long long *>(keys);
     a.n_keys = n_keys;
+    a.stride = arg_key_stride(n_keys);
+    a.M = M;
     a.idx = token;
     a.val = token_logit;
     return a;
@@ -211,8 +213,8 @@ int32_t dense_token_keys(const DensePlan &p, int64_t N) {
     return p.S > 1 ? dense_reduce_blocks(N) : (int32_t)cdiv(N, p.tile_rows);
 }
 
-// Key array bytes at the start of a token-taking workspace.
-size_t token_key_bytes(int32_t n_keys) { return align256((size_t)n_keys * 8); }
+// Key array bytes (M rows of keys) at the start of a token-taking workspace.
+size_t token_key_bytes(int32_t n_keys, int32_t M = 1) { return align256((size_t)M * arg_key_stride(n_keys) * 8); }
 
 wsg_status check_token_args(int64_t N, const int32_t *token, const float *token_logit) {
     if (N < 1)
@@ -765,6 +767,9 @@ struct wsg_step {
 
 namespace {
 
+// Workgroups that publish keys for an int4 linear's tokens.
+int32_t w4_token_keys(const W4Lin &L) { return L.S > 1 ? w4_reduce_blocks(L.M, L.N) : L.n_tiles; }
+
 wsg_status validate_linear(const wsg_linear &l) {
     if (l.conv_out || l.conv_w || l.conv_state || l.conv_bias || l.conv_width) {
         if ((l.kind != kF16 && l.kind != kW8A8) || l.M != 1)
@@ -774,7 +779,7 @@ wsg_status validate_linear(const wsg_linear &l) {
             return st;
     }
     if (l.argmax_idx || l.argmax_val) {
-        if (l.kind != kF16 && l.kind != kW8A8)
+        if (l.kind != kF16 && l.kind != kW8A8 && l.kind != kW4A16 && l.kind != kW4A8)
             return WSG_ERR_UNSUPPORTED;
         wsg_status st = check_token_args(l.N, l.argmax_idx, l.argmax_val);
         if (st != WSG_OK)
@@ -922,12 +927,13 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         // device block; descriptors get their addresses once it exists.
         std::vector<size_t> key_off;           // per key array: offset in the keys region
         size_t keys_bytes = 0;
-        auto new_keys = [&](int32_t n_keys) {
+        auto new_keys = [&](int32_t n_keys, int32_t M = 1) {
             key_off.push_back(keys_bytes);
-            keys_bytes += token_key_bytes(n_keys);
+            keys_bytes += token_key_bytes(n_keys, M);
             return (int)key_off.size() - 1;
         };
         struct TableFix {
+            bool w4;      // false: dl[ki][li]; true: wl[ki][li]
             int ki, li, keys;
         };
         std::vector<TableFix> table_fix;       // grouped dense descriptors that take a token
@@ -956,12 +962,13 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     c.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
                     st->ops.push_back(c);
                 }
-                if (l.argmax_idx) {
+                for (int32_t m = 0; l.argmax_idx && m < l.M; ++m) {
                     wsg_step::Op g{};
                     g.type = wsg_step::Op::kArgmax;
-                    g.zero_p = l.y;
+                    g.zero_p = l.y + (int64_t)m * l.N;
                     g.zero_n = l.N;
-                    g.arg = arg_out(nullptr, argmax_f32_blocks(l.N), l.argmax_idx, l.argmax_val);
+                    g.arg = arg_out(nullptr, argmax_f32_blocks(l.N), l.argmax_idx + m,
+                                    l.argmax_val ? l.argmax_val + m : nullptr);
                     g.fix = new_keys(g.arg.n_keys);
                     st->ops.push_back(g);
                 }
@@ -1018,7 +1025,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                         f.type = wsg_step::Op::kArgFinish;
                         f.arg = L.arg;
                         f.fix = new_keys(L.arg.n_keys);
-                        table_fix.push_back(TableFix{ki, li, f.fix});
+                        table_fix.push_back(TableFix{false, ki, li, f.fix});
                         finish_after.push_back(f);
                     }
                     dl[ki].push_back(L);
@@ -1038,7 +1045,18 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     o.wc = p.cfg;
                     o.w = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
                     o.wc.tail = w4_needs_tail(o.w, o.wc.B);
+                    if (l.argmax_idx) {
+                        o.w.arg = arg_out(nullptr, w4_token_keys(o.w), l.argmax_idx, l.argmax_val, l.M);
+                        o.fix = new_keys(o.w.arg.n_keys, l.M);
+                    }
                     st->ops.push_back(o);
+                    if (l.argmax_idx) {
+                        wsg_step::Op f{};
+                        f.type = wsg_step::Op::kArgFinish;
+                        f.arg = o.w.arg;
+                        f.fix = o.fix;
+                        st->ops.push_back(f);
+                    }
                 } else {
                     W4Plan p = plan_w4(l.M, l.N, l.K, 1);
                     p.S = 1;
@@ -1058,6 +1076,15 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                         return WSG_ERR_UNSUPPORTED;
                     }
                     const int li = (int)wl[wmode].size();
+                    if (l.argmax_idx) {
+                        L.arg = arg_out(nullptr, w4_token_keys(L), l.argmax_idx, l.argmax_val, l.M);
+                        wsg_step::Op f{};
+                        f.type = wsg_step::Op::kArgFinish;
+                        f.arg = L.arg;
+                        f.fix = new_keys(L.arg.n_keys, l.M);
+                        table_fix.push_back(TableFix{true, wmode, li, f.fix});
+                        finish_after.push_back(f);
+                    }
                     wl[wmode].push_back(L);
                     for (int t = 0; t < L.n_tiles; ++t)
                         wu[wmode].push_back(Unit{li, t, 0, 0});
@@ -1101,12 +1128,14 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             return reinterpret_cast<unsigned long long *>(base + keys_off + key_off[fix]);
         };
         for (const TableFix &t : table_fix)
-            dl[t.ki][t.li].arg.keys = keys_at(t.keys);
+            (t.w4 ? wl[t.ki][t.li].arg : dl[t.ki][t.li].arg).keys = keys_at(t.keys);
         for (auto &op : st->ops) {
             if (op.fix < 0)
                 continue;
             if (op.type == wsg_step::Op::kDense)
                 op.d.arg.keys = keys_at(op.fix);
+            else if (op.type == wsg_step::Op::kW4)
+                op.w.arg.keys = keys_at(op.fix);
             else
                 op.arg.keys = keys_at(op.fix);
         }

@@ -51,25 +51,39 @@ __device__ __forceinline__ unsigned long long block_max_key(unsigned long long b
 #pragma unroll
     for (int w = 1; w < WAVES; ++w)
         best = max_u64(best, red[w]);
+    __syncthreads();  // red[] may be rewritten by the next call
     return best;
 }
 
-// Called by every thread of the workgroup (it contains a barrier), with the
-// thread's best key (0 when it holds no logit); slot `k` of the key array
-// receives the workgroup's best.
-__device__ __forceinline__ void arg_publish(const ArgOut &a, unsigned long long best, int64_t k) {
+// Called by every thread of the workgroup (it contains barriers), with the
+// thread's best key for position m (0 when it holds no logit of that
+// position); slot k of position m's key row receives the workgroup's best.
+__device__ __forceinline__ void arg_publish(const ArgOut &a, unsigned long long best, int64_t k, int m = 0) {
     best = block_max_key(best);
     if (threadIdx.x == 0)
-        a.keys[k] = best;
+        a.keys[(int64_t)m * a.stride + k] = best;
 }
 
-// The token from a key (written by the finish kernel).
-__device__ __forceinline__ void arg_write(const ArgOut &a, unsigned long long key) {
+// After a work unit has written rows [r0, r0 + nrows) of output row y (one
+// position), the whole workgroup re-reads them and publishes their best key
+// in slot k of position m.  Keeping no key in registers during the weight
+// stream costs one barrier and a few L2 reads per unit.
+__device__ __forceinline__ void publish_rows(const ArgOut &a, const float *y, int64_t r0, int64_t nrows,
+                                             int64_t k, int m = 0) {
+    __syncthreads();  // the unit's stores of y are visible to the whole workgroup
+    unsigned long long best = 0;
+    for (int64_t i = threadIdx.x; i < nrows; i += kBlock)
+        best = max_u64(best, arg_key(y[r0 + i], r0 + i));
+    arg_publish(a, best, k, m);
+}
+
+// The token of position m from its best key (written by the finish kernel).
+__device__ __forceinline__ void arg_write(const ArgOut &a, unsigned long long key, int m) {
     const uint32_t u = (uint32_t)(key >> 32);
     const uint32_t bits = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-    *a.idx = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+    a.idx[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
     if (a.val)
-        *a.val = __builtin_bit_cast(float, bits);
+        a.val[m] = __builtin_bit_cast(float, bits);
 }
 
 }  // namespace wsg

@@ -123,10 +123,8 @@ __device__ __forceinline__ float store_row(const DenseLin &L, int s, int64_t row
     }
 }
 
-// Streams one unit; returns this lane's best greedy-token key over the rows
-// it wrote (0 when the linear takes no token or the lane wrote none).
 template <int KIND, int R, int CH, bool NT, bool TAIL>
-__device__ __forceinline__ unsigned long long dense_unit(const DenseLin &L, int tile, int s, u32x4 *xs) {
+__device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u32x4 *xs) {
     using Ops = DenseOps<KIND>;
     using Acc = typename Ops::Acc;
     constexpr int CHUNK = kWave * CH;
@@ -168,9 +166,6 @@ __device__ __forceinline__ unsigned long long dense_unit(const DenseLin &L, int 
 #pragma unroll
     for (int r = 0; r < R; ++r)
         acc[r] = 0;
-    const bool take = L.arg.keys != nullptr && L.S == 1;
-    const bool conv = L.conv.out != nullptr && L.S == 1;
-    unsigned long long best = 0;
 
     auto consume = [&](const u32x4(&buf)[R][CH], int gi, int c) {
         u32x4 xv[CH];
@@ -188,11 +183,7 @@ __device__ __forceinline__ unsigned long long dense_unit(const DenseLin &L, int 
             if ((lane & (span - 1)) == 0) {
                 const int64_t row = row0 + (int64_t)(wave + gi * kWavesPerBlock) * R + lane / span;
                 if (row <= last_row) {
-                    const float yv = store_row<KIND>(L, s, row, v);
-                    if (take)
-                        best = max_u64(best, arg_key(yv, row));
-                    if (conv)
-                        conv_step(L.conv, row, yv);
+                    store_row<KIND>(L, s, row, v);
                 }
             }
 #pragma unroll
@@ -212,7 +203,7 @@ __device__ __forceinline__ unsigned long long dense_unit(const DenseLin &L, int 
     __syncthreads();
 
     if (nsteps == 0)
-        return 0;
+        return;
     // Steps are (row group gi, chunk c) in order; a is the step in bufA.
     int ga = 0, ca = 0;
     auto next = [&](int &g, int &c) {
@@ -244,16 +235,30 @@ __device__ __forceinline__ unsigned long long dense_unit(const DenseLin &L, int 
     } else {
         consume(bufA, ga, ca);
     }
-    return best;
+}
+
+// The epilogues of a finished unit (S = 1) that read its rows of y back:
+// the causal-conv1d step of each row, then the greedy-token key.  Nothing
+// of them stays live in registers during the weight stream.
+__device__ __forceinline__ void dense_after_unit(const DenseLin &L, int tile) {
+    const int64_t r0 = (int64_t)tile * L.tile_rows;
+    const int64_t nrows = min((int64_t)L.tile_rows, L.N - r0);
+    if (L.conv.out != nullptr) {
+        __syncthreads();  // the unit's stores of y are visible to the whole workgroup
+        for (int64_t i = threadIdx.x; i < nrows; i += kBlock)
+            conv_step(L.conv, r0 + i, L.y[r0 + i]);
+    }
+    if (L.arg.keys != nullptr)
+        publish_rows(L.arg, L.y, r0, nrows, tile);
 }
 
 template <int KIND, int R, int CH, bool NT, bool TAIL>
 __global__ __launch_bounds__(kBlock) void dense_gemv_kernel(DenseLin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
-    const unsigned long long best = dense_unit<KIND, R, CH, NT, TAIL>(L, u / L.S, u % L.S, xs_dyn);
-    if (L.arg.keys != nullptr && L.S == 1)
-        arg_publish(L.arg, best, u);
+    dense_unit<KIND, R, CH, NT, TAIL>(L, u / L.S, u % L.S, xs_dyn);
+    if (L.S == 1 && (L.arg.keys != nullptr || L.conv.out != nullptr))
+        dense_after_unit(L, u);
 }
 
 template <int KIND, int R, int CH, bool NT, bool TAIL>
@@ -262,9 +267,9 @@ __global__ __launch_bounds__(kBlock) void dense_grouped_kernel(const DenseLin *_
     extern __shared__ u32x4 xs_dyn[];
     const Unit u = units[blockIdx.x];
     const DenseLin L = lins[u.lin];
-    const unsigned long long best = dense_unit<KIND, R, CH, NT, TAIL>(L, u.tile, u.s, xs_dyn);
-    if (L.arg.keys != nullptr && L.S == 1)
-        arg_publish(L.arg, best, u.tile);
+    dense_unit<KIND, R, CH, NT, TAIL>(L, u.tile, u.s, xs_dyn);
+    if (L.S == 1 && (L.arg.keys != nullptr || L.conv.out != nullptr))
+        dense_after_unit(L, u.tile);
 }
 
 // y[n] = sum over slices s = 0..S-1, in that order, of part[s][n]; and the
@@ -310,12 +315,14 @@ __global__ __launch_bounds__(kBlock) void zero_f32_kernel(float *p, int64_t n) {
 // loads, all in flight together) per round.
 constexpr int kFinishThreads = 1024;
 
+// One workgroup per position m (blockIdx.x).
 __global__ __launch_bounds__(kFinishThreads) void argmax_finish_kernel(ArgOut a) {
-    const int n = a.n_keys;
+    const int n = a.n_keys, m = blockIdx.x;
+    const unsigned long long *keys = a.keys + (int64_t)m * a.stride;
     unsigned long long best = 0;
     for (int base = threadIdx.x * 8; base < n; base += kFinishThreads * 8) {
         if (base + 8 <= n) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(a.keys + base);
+            const u32x4 *p = reinterpret_cast<const u32x4 *>(keys + base);
             u32x4 v[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -327,12 +334,12 @@ __global__ __launch_bounds__(kFinishThreads) void argmax_finish_kernel(ArgOut a)
             }
         } else {
             for (int i = base; i < n; ++i)
-                best = max_u64(best, a.keys[i]);
+                best = max_u64(best, keys[i]);
         }
     }
     best = block_max_key<kFinishThreads / kWave>(best);
     if (threadIdx.x == 0)
-        arg_write(a, best);
+        arg_write(a, best, m);
 }
 
 // Greedy token over a given fp32 vector: at most kArgBlocks workgroups, each
@@ -494,7 +501,7 @@ int argmax_f32_blocks(int64_t N) {
 }
 
 hipError_t launch_argmax_finish(const ArgOut &a, hipStream_t s) {
-    hipLaunchKernelGGL(argmax_finish_kernel, dim3(1), dim3(kFinishThreads), 0, s, a);
+    hipLaunchKernelGGL(argmax_finish_kernel, dim3(a.M > 1 ? a.M : 1), dim3(kFinishThreads), 0, s, a);
     return hipGetLastError();
 }
 

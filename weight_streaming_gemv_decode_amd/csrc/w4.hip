@@ -43,7 +43,7 @@
 // (e2,e6,e3,e7) of the word's interleaved order meet activation bytes staged
 // in that same order.  The zero-point enters exactly, in integers, as an
 // initial accumulator of -8 * (sum of the lane's 32 activation codes).
-#include "wsg_common.hpp"
+#include "argmax.hpp"
 
 namespace wsg {
 namespace {
@@ -402,11 +402,22 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     }
 }
 
+// A finished unit's greedy-token keys (S = 1): one per output row m < M,
+// from the unit's rows of y[m].
+__device__ __forceinline__ void w4_publish(const W4Lin &L, int tile) {
+    const int64_t r0 = (int64_t)tile * L.tile_rtiles * 16;
+    const int64_t nrows = min((int64_t)L.tile_rtiles * 16, L.N - r0);
+    for (int m = 0; m < L.M; ++m)
+        publish_rows(L.arg, L.y + (int64_t)m * L.N, r0, nrows, tile, m);
+}
+
 template <int R, int B, bool NT, int MODE, bool TAIL>
 __global__ __launch_bounds__(kBlock) void w4_gemv_kernel(W4Lin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
     w4_unit<R, B, NT, MODE, TAIL>(L, u / L.S, u % L.S, xs_dyn);
+    if (L.arg.keys != nullptr && L.S == 1)
+        w4_publish(L, u);
 }
 
 template <int R, int B, bool NT, int MODE, bool TAIL>
@@ -416,18 +427,28 @@ __global__ __launch_bounds__(kBlock) void w4_grouped_kernel(const W4Lin *__restr
     const Unit u = units[blockIdx.x];
     const W4Lin L = lins[u.lin];
     w4_unit<R, B, NT, MODE, TAIL>(L, u.tile, u.s, xs_dyn);
+    if (L.arg.keys != nullptr && L.S == 1)
+        w4_publish(L, u.tile);
 }
 
-// y[m][n] = sum over slices s = 0..S-1, in that order, of part[s][m][n].
+// y[m][n] = sum over slices s = 0..S-1, in that order, of part[s][m][n];
+// and every row m's greedy-token key of this workgroup when taken.
 __global__ __launch_bounds__(kBlock) void w4_reduce_kernel(W4Lin L) {
     const int64_t total = (int64_t)L.M * L.N;
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i >= total)
-        return;
-    float a = L.part[i];
-    for (int s = 1; s < L.S; ++s)
-        a += L.part[(int64_t)s * total + i];
-    L.y[i] = a;
+    unsigned long long key = 0;
+    int m = -1;
+    if (i < total) {
+        float a = L.part[i];
+        for (int s = 1; s < L.S; ++s)
+            a += L.part[(int64_t)s * total + i];
+        L.y[i] = a;
+        m = (int)(i / L.N);
+        key = arg_key(a, i - (int64_t)m * L.N);
+    }
+    if (L.arg.keys != nullptr)
+        for (int mm = 0; mm < L.M; ++mm)
+            arg_publish(L.arg, mm == m ? key : 0ull, blockIdx.x, mm);
 }
 
 // One thread per packed word: tile t, block b, lane l, word i.
@@ -543,9 +564,10 @@ hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, 
                          : grp_mode<kA16>(lins, units, n_units, lds_bytes, c, s);
 }
 
+int w4_reduce_blocks(int64_t M, int64_t N) { return (int)((M * N + kBlock - 1) / kBlock); }
+
 hipError_t launch_w4_reduce(const W4Lin &L, hipStream_t s) {
-    const int64_t total = (int64_t)L.M * L.N;
-    hipLaunchKernelGGL(w4_reduce_kernel, dim3((unsigned)((total + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, L);
+    hipLaunchKernelGGL(w4_reduce_kernel, dim3((unsigned)w4_reduce_blocks(L.M, L.N)), dim3(kBlock), 0, s, L);
     return hipGetLastError();
 }
 

@@ -32,12 +32,16 @@ __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f
 // Fused greedy-token output of a linear (device functions in argmax.hpp).
 // keys == nullptr: no token is taken.
 struct ArgOut {
-    unsigned long long *keys;  // [n_keys] best key of each publishing workgroup
-    int32_t *idx;              // out: token (index of the largest logit)
-    float *val;                // out, optional: its logit
+    unsigned long long *keys;  // [M][stride] best key of each publishing workgroup, per position
+    int32_t *idx;              // out: [M] tokens (index of the largest logit of each output row)
+    float *val;                // out, optional: [M] their logits
     int32_t n_keys;            // workgroups that publish in one launch
+    int32_t stride;            // keys per position row (n_keys rounded up to 32)
+    int32_t M;                 // positions (output rows of a verify block); 1 otherwise
     int32_t pad;
 };
+
+inline int32_t arg_key_stride(int32_t n_keys) { return (n_keys + 31) / 32 * 32; }
 
 // Fused causal-conv1d decode step over a linear's output (conv1d.hpp).
 // out == nullptr: none.
@@ -89,6 +93,7 @@ struct W4Lin {
     int32_t kbs;           // k-blocks per slice, a multiple of 4 when S > 1
     int32_t tile_rtiles;   // 16-row tiles per work unit
     int32_t n_tiles;       // ceil(n_rtiles / tile_rtiles)
+    ArgOut arg;            // optional greedy token of each output row (S = 1: the units; S > 1: the reduce)
 };
 
 // One work unit of a grouped launch: linear `lin`, row tile `tile`, k-slice `s`.
@@ -136,6 +141,7 @@ hipError_t launch_w4(const W4Lin &L, int mode, const W4Cfg &c, hipStream_t s);
 hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes,
                              int mode, const W4Cfg &c, hipStream_t s);
 hipError_t launch_w4_reduce(const W4Lin &L, hipStream_t s);
+int w4_reduce_blocks(int64_t M, int64_t N);
 hipError_t launch_pack_w4(const uint32_t *Wc, const uint16_t *s4, u32x4 *Wp, u32x2 *Sp,
                           int64_t N, int32_t K, hipStream_t s);
 struct ProbeCfg {
