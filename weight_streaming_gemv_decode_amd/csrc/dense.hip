@@ -105,21 +105,17 @@ __device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
     return s;
 }
 
-// Writes row `row` (a partial when S > 1) and returns its y (S = 1).
+// Writes row `row`: y (S = 1) or its partial of slice s (S > 1).
 template <int KIND, typename Acc>
-__device__ __forceinline__ float store_row(const DenseLin &L, int s, int64_t row, Acc v) {
+__device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row, Acc v) {
     if (L.S > 1) {
         static_cast<Acc *>(L.part)[(int64_t)s * L.N + row] = v;
-        return 0.0f;
     } else if constexpr (KIND == kF16) {
         L.y[row] = v;
-        return v;
     } else {
         if (L.acc_out)
             L.acc_out[row] = v;
-        const float yv = ((float)v * L.w_scale[row]) * L.x_scale[0];
-        L.y[row] = yv;
-        return yv;
+        L.y[row] = ((float)v * L.w_scale[row]) * L.x_scale[0];
     }
 }
 
