@@ -60,7 +60,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.orc_argmax_f32.argtypes = [P, I64, P]
     lib.orc_round_f16.argtypes = [P, I64, P]
     lib.orc_causal_conv1d_step.argtypes = [P, P, P, P, I64, I64, ctypes.c_int, P, P]
-    for f in (lib.orc_causal_conv1d_step, lib.orc_f16_decode, lib.orc_gemv_f16, lib.orc_gemv_w8a8, lib.orc_gemv_w4a16,
+    lib.orc_topk_f32.argtypes = [P, I64, I64, P]
+    for f in (lib.orc_topk_f32, lib.orc_causal_conv1d_step, lib.orc_f16_decode, lib.orc_gemv_f16, lib.orc_gemv_w8a8, lib.orc_gemv_w4a16,
               lib.orc_quantize_x_i8, lib.orc_gemv_w4a8, lib.orc_argmax_f32, lib.orc_round_f16):
         f.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [ctypes.c_int]
@@ -260,6 +261,16 @@ def argmax_f32(y: np.ndarray, lib: Optional[ctypes.CDLL] = None) -> int:
     out = np.zeros(1, np.int64)
     _check((lib or load()).orc_argmax_f32(_ptr(y), y.size, _ptr(out)), "argmax_f32")
     return int(out[0])
+
+
+def topk_f32(y: np.ndarray, k: int, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """Indices of the k largest fp32 values in the greedy token's order
+    (larger first, NaN below every number, -0 == +0, lower index first
+    among equals), as int64 [k]."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.zeros(k, np.int64)
+    _check((lib or load()).orc_topk_f32(_ptr(y), y.size, int(k), _ptr(out)), "topk_f32")
+    return out
 
 
 def argmax_is_valid(idx: int, y_ref: np.ndarray, A: np.ndarray) -> bool:

@@ -377,6 +377,50 @@ int orc_argmax_f32(const float *y, int64_t n, int64_t *idx)
     return ORC_OK;
 }
 
+/* Top-k of the logits (the token choice of the same post's second change,
+ * widened from the single largest logit to the k largest, as samplers that
+ * draw from the best k candidates need).  The order is the greedy token's:
+ * larger values first (IEEE comparison, so -0 equals +0), a NaN below every
+ * number, and among equal values (or among NaNs) the lower index first.
+ * idx receives the first k indices of all n indices sorted by that order. */
+static const float *topk_values;
+
+static int topk_before(int64_t a, int64_t b)
+{
+    const float va = topk_values[a], vb = topk_values[b];
+    const int na = isnan(va), nb = isnan(vb);
+    if (na != nb)
+        return nb;                      /* the number comes before the NaN */
+    if (!na && va != vb)
+        return va > vb;
+    return a < b;
+}
+
+static int topk_compare(const void *pa, const void *pb)
+{
+    const int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    if (a == b)
+        return 0;
+    return topk_before(a, b) ? -1 : 1;
+}
+
+int orc_topk_f32(const float *y, int64_t n, int64_t k, int64_t *idx)
+{
+    if (n <= 0 || k <= 0 || k > n)
+        return ORC_ERR_SHAPE;
+    int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    if (!order)
+        return ORC_ERR_SHAPE;
+    for (int64_t i = 0; i < n; ++i)
+        order[i] = i;
+    topk_values = y;
+    qsort(order, (size_t)n, sizeof(int64_t), topk_compare);
+    for (int64_t i = 0; i < k; ++i)
+        idx[i] = order[i];
+    free(order);
+    return ORC_OK;
+}
+
 void orc_set_threads(int n)
 {
     if (n > 0)

@@ -319,6 +319,30 @@ def pin_argmax_numpy(lib, n=5000, seed=20):
     assert oracle.argmax_f32(y, lib=lib) == n - 1
 
 
+def pin_topk_golden(lib):
+    g = _golden("topk_order.json")
+    for c in g["cases"]:
+        y = np.array([int(v, 16) for v in c["bits"]], np.uint32).view(np.float32)
+        assert oracle.topk_f32(y, c["k"], lib=lib).tolist() == c["topk"], c["note"]
+
+
+def pin_topk_numpy(lib, n=3000, seed=25):
+    """numpy's stable lexicographic sort on (-value, index) puts NaN last and
+    keeps equal values (and -0 / +0) in index order: its first k entries are
+    the top-k; k = 1 is the greedy token."""
+    r = synth.rng(914, seed)
+    for trial in range(10):
+        y = np.round(r.normal(0, 4, n)).astype(np.float32)
+        y[r.integers(0, n, 40)] = -0.0
+        if trial % 2:
+            y[r.integers(0, n, 100)] = np.nan
+        want = np.lexsort((np.arange(n), -y))
+        for k in (1, 7, 64, n):
+            got = oracle.topk_f32(y, k, lib=lib)
+            assert np.array_equal(got, want[:k]), (trial, k)
+        assert int(oracle.topk_f32(y, 1, lib=lib)[0]) == oracle.argmax_f32(y, lib=lib)
+
+
 # ---------------------------------------------------------- fp16 chain ---
 
 def pin_round_f16_golden(lib):
@@ -421,5 +445,5 @@ ALL_PINS = [
     pin_w8a8_int32_range, pin_w4_golden, pin_w4_numpy_dequant, pin_w4_exact_rational,
     pin_quant_golden, pin_quant_properties, pin_w4a8_golden, pin_w4a8_integer_matmul,
     pin_argmax_golden, pin_argmax_numpy, pin_round_f16_golden, pin_round_f16_numpy, pin_chain_permutations,
-    pin_conv_golden, pin_conv_sequence_numpy, pin_conv_special_kernels,
+    pin_conv_golden, pin_conv_sequence_numpy, pin_conv_special_kernels, pin_topk_golden, pin_topk_numpy,
 ]

@@ -49,6 +49,10 @@ MUTANTS = [
     ("conv_no_bias", "double pre = bias ? (double)bias[c] : 0.0;", "double pre = 0.0;"),
     ("conv_silu_sign", "pre / (1.0 + exp(-pre))", "pre / (1.0 + exp(pre))"),
     ("conv_x_not_appended", "state[c * (W - 1) + W - 2] = x[c];", "state[c * (W - 1) + W - 2] = 0.0f;"),
+    ("topk_ties_reversed", "    return a < b;\n}", "    return a > b;\n}"),
+    ("topk_nan_first", "        return nb;                      /* the number comes before the NaN */",
+     "        return na;"),
+    ("topk_ascending", "        return va > vb;", "        return va < vb;"),
     ("argmax_signed_zero", "if (isnan(y[best]) || y[i] > y[best])",
      "if (isnan(y[best]) || y[i] > y[best] || (y[i] == y[best] && signbit(y[best]) && !signbit(y[i])))"),
 ]
