@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true", help="only the decode-step stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,conv,graph,probe,ordered)")
+    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,conv,graph,topk,probe,ordered)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB fp32 copy kernel (reads 1 GiB, writes 1 GiB) to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass")
@@ -417,6 +417,25 @@ def main():
                                                         "GBps": step_bytes / (s2["median_ms"] * 1e-3) / 1e9}
         st_.close()
         extras["conv1d"] = rec
+
+    if want("topk"):
+        # top-k over the lm_head's 248,320 fp32 logits (64 calls captured in one graph)
+        N = synth.LMHEAD[0]
+        r = synth.rng(7, 0)
+        ys = [torch.from_numpy(r.normal(0, 1, N).astype(np.float32)).to(dev) for _ in range(4)]
+        rec = {}
+        for k in (1, 8, 50):
+            idx = torch.empty(k, dtype=torch.int32, device=dev)
+            ws = torch.empty(max(256, wsgemv.lib().wsg_topk_ws_bytes(N, k)), dtype=torch.uint8, device=dev)
+            fn = lambda i: wsgemv.topk_f32(ys[i % 4], k, idx=idx, ws=ws, stream=stream)  # noqa: E731
+            s = summary(graph_times(torch, fn, 64, 10, stream))
+            rec[f"k={k}"] = {"median_us": round(s["median_ms"] * 1e3, 2)}
+        tok = torch.empty(1, dtype=torch.int32, device=dev)
+        aws = torch.empty(wsgemv.ARGMAX_WS_BYTES, dtype=torch.uint8, device=dev)
+        fn = lambda i: wsgemv.argmax_f32(ys[i % 4], token=tok, ws=aws, stream=stream)  # noqa: E731
+        s = summary(graph_times(torch, fn, 64, 10, stream))
+        rec["argmax_f32 (for comparison)"] = {"median_us": round(s["median_ms"] * 1e3, 2)}
+        extras["topk_248320_logits"] = rec
 
     if want("probe"):
         # attainable streaming-read rate against transfer size (back-to-back launches)

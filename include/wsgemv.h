@@ -180,6 +180,19 @@ wsg_status wsg_argmax_f32(const float *y, int64_t N, int32_t *token, float *toke
                           size_t ws_bytes, wsg_stream_t stream);
 
 /*
+ * wsg_topk_f32: the k largest values of fp32 y [N] in the same order (larger
+ * first, NaN below every number, -0 equal to +0, lower index first among
+ * equals): idx int32 [k] (out, in that order), val optional fp32 [k] (out).
+ * k = 1..WSG_TOPK_MAX and k <= N <= INT32_MAX.  Selection passes keep each
+ * workgroup's k best keys until one workgroup picks the final k; no atomics.
+ *   ws   wsg_topk_ws_bytes(N, k) bytes, 256-byte aligned (two key buffers)
+ */
+enum { WSG_TOPK_MAX = 64 };
+size_t wsg_topk_ws_bytes(int64_t N, int32_t k);
+wsg_status wsg_topk_f32(const float *y, int64_t N, int32_t k, int32_t *idx, float *val, void *ws,
+                        size_t ws_bytes, wsg_stream_t stream);
+
+/*
  * gemv_f16_argmax: gemv_f16 (y = W . x, fp32 logits, written in full) with
  * the greedy token over y fused into the kernel that writes y (the k-split
  * reduce when splits > 1).  This is the lm_head of a decode step.

@@ -23,7 +23,7 @@ def L():
 def test_exports_every_declared_function(L):
     names = wsgemv.header_functions()
     assert {"gemv_f16", "gemv_w8a8", "gemv_w4a16", "gemv_w4a8", "decode_step_linears", "wsg_pack_w4",
-            "gemv_f16_argmax", "wsg_argmax_f32", "causal_conv1d_step",
+            "gemv_f16_argmax", "wsg_argmax_f32", "causal_conv1d_step", "wsg_topk_f32", "wsg_topk_ws_bytes",
             "wsg_decode_step_create"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/wsgemv.h but not exported"
@@ -161,6 +161,22 @@ def _validate_only(L, arr):
     bad.conv_state = None
     return OK if L.wsg_decode_step_create((wsgemv.wsg_linear * 1)(bad), 1, 0x100, None,
                                           ctypes.byref(ctypes.c_void_p())) == NULL else -1
+
+
+def test_topk_validation(L):
+    f = L.wsg_topk_f32
+    need = L.wsg_topk_ws_bytes(1000, 8)
+    assert need > 0 and need % 256 == 0
+    assert L.wsg_topk_ws_bytes(1000, 0) == 0 and L.wsg_topk_ws_bytes(1000, 65) == 0 and L.wsg_topk_ws_bytes(5, 8) == 0
+    assert f(FAKE, 1000, 0, FAKE, None, FAKE, need, None) == SHAPE             # k >= 1
+    assert f(FAKE, 5, 8, FAKE, None, FAKE, need, None) == SHAPE                # k <= N
+    assert f(FAKE, 1000, 65, FAKE, None, FAKE, need, None) == UNSUP            # k <= 64
+    assert f(FAKE, 0, 1, FAKE, None, FAKE, need, None) == SHAPE
+    assert f(None, 1000, 8, FAKE, None, FAKE, need, None) == NULL
+    assert f(FAKE, 1000, 8, None, None, FAKE, need, None) == NULL
+    assert f(FAKE + 2, 1000, 8, FAKE, None, FAKE, need, None) == ALIGN
+    assert f(FAKE, 1000, 8, FAKE, None, FAKE, need - 1, None) == WS
+    assert f(FAKE, 1000, 8, FAKE, None, FAKE + 16, need, None) == ALIGN
 
 
 def test_launch_table(L):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(REPO, "include")
 LIB = os.path.join(HERE, "libwsgemv.so")
 BUILD_DIR = os.path.join(REPO, "_build")
 
-SOURCES = ["api.cpp", "dense.hip", "w4.hip", "conv1d.hip"]
+SOURCES = ["api.cpp", "dense.hip", "w4.hip", "conv1d.hip", "topk.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

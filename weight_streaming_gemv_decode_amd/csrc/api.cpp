@@ -520,6 +520,39 @@ wsg_status causal_conv1d_step(const float *x, const void *w, const float *bias, 
     });
 }
 
+size_t wsg_topk_ws_bytes(int64_t N, int32_t k) {
+    if (N < 1 || N > (int64_t)INT32_MAX || k < 1 || k > WSG_TOPK_MAX || k > N)
+        return 0;
+    int64_t max_keys = 0;
+    topk_plan(N, k, &max_keys, nullptr);
+    return 2 * align256((size_t)max_keys * 8);
+}
+
+wsg_status wsg_topk_f32(const float *y, int64_t N, int32_t k, int32_t *idx, float *val, void *ws, size_t ws_bytes,
+                        wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_token_args(N, idx, val);
+        if (st != WSG_OK)
+            return st;
+        if (k < 1 || k > N)
+            return WSG_ERR_SHAPE;
+        if (k > WSG_TOPK_MAX)
+            return WSG_ERR_UNSUPPORTED;
+        if (!y)
+            return WSG_ERR_NULL;
+        if (!aligned(y, 4))
+            return WSG_ERR_ALIGN;
+        const size_t need = wsg_topk_ws_bytes(N, k);
+        st = check_ws(ws, ws_bytes, need);
+        if (st != WSG_OK)
+            return st;
+        auto *a = static_cast<unsigned long long *>(ws);
+        auto *b = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + need / 2);
+        hipError_t e = launch_topk(y, N, k, idx, val, a, b, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? WSG_OK : hip_fail(e);
+    });
+}
+
 wsg_status gemv_f16_argmax(const void *W, const void *x, float *y, int32_t *token, float *token_logit,
                            int64_t N, int64_t K, int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream) {
     return guarded([&]() -> wsg_status {

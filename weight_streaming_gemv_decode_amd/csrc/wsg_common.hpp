@@ -154,6 +154,9 @@ hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int gri
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
 hipError_t launch_argmax_finish(const ArgOut &a, hipStream_t s);
 hipError_t launch_conv1d_step(const float *x, const ConvOut &cv, int64_t C, hipStream_t s);
+int64_t topk_plan(int64_t N, int k, int64_t *max_keys, int *passes);
+hipError_t launch_topk(const float *y, int64_t N, int k, int32_t *idx, float *val, unsigned long long *ws_a,
+                       unsigned long long *ws_b, hipStream_t s);
 hipError_t launch_argmax_f32(const float *y, int64_t N, ArgOut a, hipStream_t s);
 int argmax_f32_blocks(int64_t N);
 

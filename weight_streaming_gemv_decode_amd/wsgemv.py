@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libwsgemv.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "wsgemv.h")
 
 F16, W8A8, W4A16, W4A8 = 0, 1, 2, 3
-ARGMAX_WS_BYTES, WITH_ARGMAX = 8192, 0x100
+ARGMAX_WS_BYTES, WITH_ARGMAX, TOPK_MAX = 8192, 0x100, 64
 STEP_ORDERED, STEP_GROUPED, STEP_EAGER, STEP_FORCE_GRAPH = 0, 1, 0x100, 0x200
 STEP_GRAPH_MIN_LAUNCHES = 8
 STATUS = {0: "WSG_OK", 1: "WSG_ERR_NULL", 2: "WSG_ERR_SHAPE", 3: "WSG_ERR_ALIGN", 4: "WSG_ERR_UNSUPPORTED",
@@ -64,6 +64,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "wsg_argmax_f32": ([P, I64, P, P, P, SZ, P], I32),
         "gemv_f16_argmax": ([P, P, P, P, P, I64, I64, I32, P, SZ, P], I32),
         "causal_conv1d_step": ([P, P, P, P, P, I64, I32, I32, P], I32),
+        "wsg_topk_ws_bytes": ([I64, I32], SZ),
+        "wsg_topk_f32": ([P, I64, I32, P, P, P, SZ, P], I32),
         "wsg_decode_step_create": ([ctypes.POINTER(wsg_linear), I32, I32, P, ctypes.POINTER(P)], I32),
         "decode_step_linears": ([P, P], I32),
         "wsg_decode_step_destroy": ([P], I32),
@@ -176,6 +178,22 @@ def argmax_f32(y: torch.Tensor, token: Optional[torch.Tensor] = None, token_logi
     _check(lib().wsg_argmax_f32(_dev(y, torch.float32, "y", (N,)), N, _dev(token, torch.int32, "token", (1,)), tl,
                                 wp, wn, _stream(stream)), "wsg_argmax_f32")
     return token
+
+
+def topk_f32(y: torch.Tensor, k: int, idx: Optional[torch.Tensor] = None, val: Optional[torch.Tensor] = None,
+             ws: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """(idx int32 [k], val): the k largest of fp32 y [N], larger first, lower index first among equals."""
+    N = y.shape[0]
+    if idx is None:
+        idx = torch.empty(k, dtype=torch.int32, device=y.device)
+    if ws is None:
+        n = int(lib().wsg_topk_ws_bytes(N, k))
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=y.device)
+    wp, wn = _ws(ws)
+    vp = _dev(val, torch.float32, "val", (k,)) if val is not None else None
+    _check(lib().wsg_topk_f32(_dev(y, torch.float32, "y", (N,)), N, k, _dev(idx, torch.int32, "idx", (k,)), vp, wp, wn,
+                              _stream(stream)), "wsg_topk_f32")
+    return idx, val
 
 
 def gemv_f16_argmax(W: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
