@@ -525,7 +525,9 @@ size_t wsg_topk_ws_bytes(int64_t N, int32_t k) {
         return 0;
     int64_t max_keys = 0;
     topk_plan(N, k, &max_keys, nullptr);
-    return 2 * align256((size_t)max_keys * 8);
+    const size_t need = 2 * align256((size_t)max_keys * 8);
+    // k = 1 runs as the greedy token (its key array must fit too)
+    return k == 1 ? std::max(need, token_key_bytes(argmax_f32_blocks(N))) : need;
 }
 
 wsg_status wsg_topk_f32(const float *y, int64_t N, int32_t k, int32_t *idx, float *val, void *ws, size_t ws_bytes,
@@ -546,9 +548,17 @@ wsg_status wsg_topk_f32(const float *y, int64_t N, int32_t k, int32_t *idx, floa
         st = check_ws(ws, ws_bytes, need);
         if (st != WSG_OK)
             return st;
-        auto *a = static_cast<unsigned long long *>(ws);
-        auto *b = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + need / 2);
-        hipError_t e = launch_topk(y, N, k, idx, val, a, b, static_cast<hipStream_t>(stream));
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hipError_t e;
+        if (k == 1) {  // the greedy token: one reduce over y and the finish
+            e = launch_argmax_f32(y, N, arg_out(ws, argmax_f32_blocks(N), idx, val), s);
+        } else {
+            auto *a = static_cast<unsigned long long *>(ws);
+            int64_t max_keys = 0;
+            topk_plan(N, k, &max_keys, nullptr);
+            auto *b = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + align256((size_t)max_keys * 8));
+            e = launch_topk(y, N, k, idx, val, a, b, s);
+        }
         return e == hipSuccess ? WSG_OK : hip_fail(e);
     });
 }

@@ -4,22 +4,21 @@
 // lm_head results that picks the next token (MiniCPM-V 4.6 on Orange Pi
 // AIPro post, second change) to the k best candidates.
 //
-// Keys are unique (the index is part of the key), so "the next best" is the
-// largest key below the last one taken.  Each wave picks the k best of its
-// candidates (held in registers) by k rounds of a wavefront maximum under a
-// moving threshold, with no barrier between rounds; after one barrier, the
-// first wave picks the k best of the waves' results the same way.  A
-// selection pass gives every workgroup 2048 candidates and writes its k best
-// keys; passes repeat until one workgroup of 1024 threads (16 candidates per
-// thread) picks the final k in order.  No atomics; the result does not
-// depend on workgroup order.
+// Keys are unique (the index is part of the key), so the top k are exactly
+// the keys at or above the k-th largest.  A workgroup finds that key by a
+// radix select on its 64-bit keys, one byte at a time from the top: a
+// histogram of the current byte over the keys that share the bytes already
+// fixed (shared-memory atomic adds), then the bin that holds the k-th
+// largest; it stops early once that bin holds exactly the keys still
+// needed.  The keys at or above it are gathered and one wave sorts them
+// (bitonic, through lane exchanges).  A selection pass gives every
+// workgroup 2048 candidates and writes its k best keys; passes repeat until
+// one workgroup of 1024 threads (16 candidates per thread) picks the final
+// k in order.  No global atomics; the result does not depend on workgroup
+// order.
 #include <algorithm>
 
 #include "argmax.hpp"
-
-// Wavefront maximum from the ROCm device library (a DPP reduction over the
-// active lanes; the result is returned to every lane).
-extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_max_u64(unsigned long long);
 
 namespace wsg {
 namespace {
@@ -30,45 +29,99 @@ constexpr int kFinalThreads = 1024;
 constexpr int kFinalPerThread = 16;          // the final workgroup takes up to 16384 candidates
 constexpr int kMaxK = 64;
 
-// The k best of this wave's candidates c[0..E) per lane, in order, into
-// res[0..k) (lane 0 writes).  All 64 lanes must be active.
-template <int E>
-__device__ __forceinline__ void wave_topk(const unsigned long long (&c)[E], int k, unsigned long long *res) {
-    const int lane = threadIdx.x & (kWave - 1);
-    unsigned long long thr = ~0ull;
-    for (int r = 0; r < k; ++r) {
-        unsigned long long best = 0ull;
-#pragma unroll
-        for (int j = 0; j < E; ++j)
-            if (c[j] < thr)
-                best = max_u64(best, c[j]);
-        best = __ockl_wfred_max_u64(best);  // the wave's maximum, in every lane
-        if (lane == 0)
-            res[r] = best;
-        thr = best;  // 0 once exhausted: every later key is 0 too
+// The k largest of the workgroup's candidates (E per thread, 0 = none), in
+// descending order, into res[0..k) (shared memory; zeros when fewer than k
+// candidates are nonzero).  Every thread must call it.
+template <int THREADS, int E>
+__device__ __forceinline__ void block_select(const unsigned long long (&c)[E], int k, unsigned long long *res) {
+    __shared__ uint32_t hist[2][256];  // this round's histogram and the next one's, zeroed ahead
+    __shared__ unsigned long long s_prefix;
+    __shared__ int s_need, s_done, s_count;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    if (tid == 0) {
+        s_prefix = 0ull;
+        s_need = k;
+        s_done = 0;
+        s_count = 0;
     }
-}
-
-// Per workgroup of WAVES waves: every wave picks its k best of E candidates
-// per lane, then wave 0 picks the k best of the WAVES * k results (held as
-// WAVES * k / 64 per lane, at most 16) into res[0..k).
-template <int WAVES, int E>
-__device__ __forceinline__ bool block_topk(const unsigned long long (&c)[E], int k, unsigned long long *res) {
-    __shared__ unsigned long long wres[WAVES * kMaxK];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    wave_topk(c, k, wres + wave * kMaxK);
+    for (int i = tid; i < 2 * 256; i += THREADS)
+        hist[i >> 8][i & 255] = 0u;
     __syncthreads();
-    if (wave != 0)
-        return false;
-    constexpr int E2 = WAVES * kMaxK / kWave;
-    unsigned long long c2[E2];
+    for (int d = 7; d >= 0 && !s_done; --d) {
+        uint32_t *h_cur = hist[d & 1], *h_next = hist[(d + 1) & 1];
+        const unsigned long long prefix = s_prefix;
+        const int hi_shift = 8 * (d + 1);
 #pragma unroll
-    for (int j = 0; j < E2; ++j) {
-        const int i = lane + j * kWave;                // candidate i: wave i / k, rank i % k
-        c2[j] = i < WAVES * k ? wres[(i / k) * kMaxK + i % k] : 0ull;
+        for (int j = 0; j < E; ++j) {
+            const bool match = d == 7 || (c[j] >> hi_shift) == (prefix >> hi_shift);
+            if (match)
+                atomicAdd(&h_cur[(c[j] >> (8 * d)) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid < kWave) {
+            // lane l owns bins 255 - 4l .. 252 - 4l; find the bin holding the need-th largest
+            uint32_t h[4], t = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                h[q] = h_cur[255 - 4 * lane - q];
+                t += h[q];
+            }
+            uint32_t above = t;  // inclusive scan over lanes (higher bins first)
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t v = __shfl_up(above, o);
+                if (lane >= o)
+                    above += v;
+            }
+            above -= t;  // keys in bins above this lane's
+            const uint32_t need = (uint32_t)s_need;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (above < need && need <= above + h[q]) {
+                    const uint32_t bin = 255u - 4u * lane - q;
+                    s_prefix = prefix | ((unsigned long long)bin << (8 * d));
+                    s_need = (int)(need - above);
+                    s_done = h[q] == need - above;  // every key of the bin is needed
+                }
+                above += h[q];
+            }
+        } else {
+            for (int i = tid - kWave; i < 256; i += THREADS - kWave)
+                h_next[i] = 0u;
+        }
+        __syncthreads();
     }
-    wave_topk(c2, k, res);
-    return true;
+    // the threshold: s_prefix with the bytes below the last fixed one at zero
+    // (when the search ended early) is at or below exactly the k largest
+    const unsigned long long thr = s_prefix;
+    __shared__ unsigned long long sel[kMaxK];
+    if (tid < kMaxK)
+        sel[tid] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        if (c[j] != 0ull && c[j] >= thr) {
+            const int pos = atomicAdd(&s_count, 1);
+            if (pos < kMaxK)
+                sel[pos] = c[j];
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        // bitonic sort of the 64 gathered keys, descending, one per lane
+        unsigned long long v = sel[lane];
+        for (int size = 2; size <= kWave; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const unsigned long long o = shfl_xor_u64(v, stride);
+                const bool lower = (lane & stride) == 0;
+                const bool desc = (lane & size) == 0;   // direction of this lane's sequence
+                const bool take_max = lower == desc;
+                v = take_max ? max_u64(v, o) : (v < o ? v : o);
+            }
+        }
+        if (lane < k)
+            res[lane] = v;
+    }
+    __syncthreads();
 }
 
 // FROM_Y: candidates are y[0..count) (keys formed here); otherwise keys.
@@ -86,11 +139,9 @@ __global__ __launch_bounds__(kBlock) void topk_pass_kernel(const float *__restri
             c[j] = FROM_Y ? arg_key(y[i], i) : in[i];
     }
     __shared__ unsigned long long res[kMaxK];
-    if (block_topk<kWavesPerBlock>(c, k, res)) {
-        // wave 0 only: its lane-0 writes of res are visible to its own lanes
-        if ((int)threadIdx.x < k)
-            out[(int64_t)blockIdx.x * k + threadIdx.x] = res[threadIdx.x];
-    }
+    block_select<kBlock>(c, k, res);
+    if ((int)threadIdx.x < k)
+        out[(int64_t)blockIdx.x * k + threadIdx.x] = res[threadIdx.x];
 }
 
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const unsigned long long *__restrict__ in,
@@ -102,13 +153,12 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const unsigne
         c[j] = i < count ? in[i] : 0ull;
     }
     __shared__ unsigned long long res[kMaxK];
-    if (block_topk<kFinalThreads / kWave>(c, k, res)) {
-        if ((int)threadIdx.x < k) {
-            ArgOut a{};
-            a.idx = idx;
-            a.val = val;
-            arg_write(a, res[threadIdx.x], threadIdx.x);
-        }
+    block_select<kFinalThreads>(c, k, res);
+    if ((int)threadIdx.x < k) {
+        ArgOut a{};
+        a.idx = idx;
+        a.val = val;
+        arg_write(a, res[threadIdx.x], threadIdx.x);
     }
 }
 
