@@ -31,7 +31,8 @@ constexpr int kMaxK = 64;
 
 // The k largest of the workgroup's candidates (E per thread, 0 = none), in
 // descending order, into res[0..k) (shared memory; zeros when fewer than k
-// candidates are nonzero).  Every thread must call it.
+// candidates are nonzero).  Every thread must call it.  Zero keys never
+// enter a histogram, so padding costs nothing.
 template <int THREADS, int E>
 __device__ __forceinline__ void block_select(const unsigned long long (&c)[E], int k, unsigned long long *res) {
     __shared__ uint32_t hist[2][256];  // this round's histogram and the next one's, zeroed ahead
@@ -53,7 +54,8 @@ __device__ __forceinline__ void block_select(const unsigned long long (&c)[E], i
         const int hi_shift = 8 * (d + 1);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
-            const bool match = d == 7 || (c[j] >> hi_shift) == (prefix >> hi_shift);
+            // zero keys are padding (no candidate): they stay out of the histograms
+            const bool match = c[j] != 0ull && (d == 7 || (c[j] >> hi_shift) == (prefix >> hi_shift));
             if (match)
                 atomicAdd(&h_cur[(c[j] >> (8 * d)) & 255u], 1u);
         }
@@ -74,6 +76,11 @@ __device__ __forceinline__ void block_select(const unsigned long long (&c)[E], i
             }
             above -= t;  // keys in bins above this lane's
             const uint32_t need = (uint32_t)s_need;
+            if (d == 7 && lane == kWave - 1 && above + t < need) {
+                // fewer than k candidates in all: every one of them is taken
+                s_prefix = 0ull;
+                s_done = 1;
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (above < need && need <= above + h[q]) {
