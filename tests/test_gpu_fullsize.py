@@ -1,7 +1,7 @@
 """The full int4 decode steps at their real sizes, in the launch
 configuration the benchmark times (the GROUPED plan): 28 layers x {qkv,
-o, gate_up, down} + the 248320 x 1024 lm_head, at M = 1, at an M = 4
-verify block, and with int8 activations.  Every linear is checked against
+o, gate_up, down} + the 248320 x 1024 lm_head, at M = 1, at M = 4 and
+M = 8 verify blocks, and with int8 activations.  Every linear is checked against
 the oracle on sampled rows (the first and last rows and a seeded sample),
 which the oracle computes one by one on the same inputs."""
 import numpy as np
@@ -21,7 +21,7 @@ def _rows(N, name, k=48):
     return np.unique(np.concatenate([pick, [0, N - 1]]))
 
 
-@pytest.fixture(scope="module", params=[1, 4], ids=["M1", "M4"])
+@pytest.fixture(scope="module", params=[1, 4, 8], ids=["M1", "M4", "M8"])
 def w4_step(request):
     M = request.param
     return M, synth.decode_step_w4(workload=5, M=M)

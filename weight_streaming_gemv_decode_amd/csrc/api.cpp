@@ -1107,10 +1107,10 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     // fp16 activations, M = 1: 1 tile x 8 blocks per step, 4 tiles per unit;
                     // int8 activations: 1 tile x 4 blocks per step, 8 tiles per unit (the
                     // per-unit quantisation is amortised over more rows);
-                    // verify blocks: 2 tiles x 4 blocks per step, 16 tiles per unit
+                    // verify blocks: 2 tiles x 4 blocks per step, 8 tiles per unit
                     const bool a8 = wmode == kA8;
                     p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles
-                                                              : (l.M > 1 ? 16 : (a8 ? 8 : 4));
+                                                              : (l.M > 1 || a8 ? 8 : 4);
                     p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (l.M > 1 ? 2 : 1);
                     p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (l.M > 1 || a8 ? 4 : 8);
                     W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);

@@ -61,7 +61,7 @@ __device__ __forceinline__ unsigned long long block_max_key(unsigned long long b
 __device__ __forceinline__ void arg_publish(const ArgOut &a, unsigned long long best, int64_t k, int m = 0) {
     best = block_max_key(best);
     if (threadIdx.x == 0)
-        a.keys[(int64_t)m * a.stride + k] = best;
+        *glob(a.keys + (int64_t)m * a.stride + k) = best;
 }
 
 // After a work unit has written rows [r0, r0 + nrows) of output row y (one
@@ -73,7 +73,7 @@ __device__ __forceinline__ void publish_rows(const ArgOut &a, const float *y, in
     __syncthreads();  // the unit's stores of y are visible to the whole workgroup
     unsigned long long best = 0;
     for (int64_t i = threadIdx.x; i < nrows; i += kBlock)
-        best = max_u64(best, arg_key(y[r0 + i], r0 + i));
+        best = max_u64(best, arg_key(*glob(y + r0 + i), r0 + i));
     arg_publish(a, best, k, m);
 }
 

@@ -18,14 +18,14 @@ constexpr int kMaxConvWidth = 8;
 
 __device__ __forceinline__ void conv_step(const ConvOut &cv, int64_t c, float x) {
     const int W = cv.W;
-    float *st = cv.state + c * (W - 1);
-    const uint16_t *w = cv.w + c * W;
+    auto *st = glob(cv.state + c * (W - 1));
+    const auto *w = glob(cv.w + c * W);
     float win[kMaxConvWidth];
 #pragma unroll
     for (int j = 0; j < kMaxConvWidth - 1; ++j)
         if (j < W - 1)
             win[j] = st[j];
-    float pre = cv.bias ? cv.bias[c] : 0.0f;
+    float pre = cv.bias ? *glob(cv.bias + c) : 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxConvWidth; ++j) {
         if (j < W) {
@@ -37,7 +37,7 @@ __device__ __forceinline__ void conv_step(const ConvOut &cv, int64_t c, float x)
     for (int j = 0; j < kMaxConvWidth - 1; ++j)
         if (j < W - 1)
             st[j] = j + 1 < W - 1 ? win[j + 1] : x;
-    cv.out[c] = cv.silu ? pre / (1.0f + __expf(-pre)) : pre;
+    *glob(cv.out + c) = cv.silu ? pre / (1.0f + __expf(-pre)) : pre;
 }
 
 }  // namespace wsg

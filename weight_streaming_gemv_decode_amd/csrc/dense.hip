@@ -32,9 +32,9 @@ namespace {
 template <bool NT>
 __device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
     if constexpr (NT)
-        return __builtin_nontemporal_load(p);
+        return __builtin_nontemporal_load(glob(p));
     else
-        return *p;
+        return *glob(p);
 }
 
 template <int KIND>
@@ -109,13 +109,13 @@ __device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
 template <int KIND, typename Acc>
 __device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row, Acc v) {
     if (L.S > 1) {
-        static_cast<Acc *>(L.part)[(int64_t)s * L.N + row] = v;
+        *glob(static_cast<Acc *>(L.part) + (int64_t)s * L.N + row) = v;
     } else if constexpr (KIND == kF16) {
-        L.y[row] = v;
+        *glob(L.y + row) = v;
     } else {
         if (L.acc_out)
-            L.acc_out[row] = v;
-        L.y[row] = ((float)v * L.w_scale[row]) * L.x_scale[0];
+            *glob(L.acc_out + row) = v;
+        *glob(L.y + row) = ((float)v * *glob(L.w_scale + row)) * *glob(L.x_scale);
     }
 }
 
@@ -195,7 +195,7 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
 
     const u32x4 *xg = L.x + kv0;
     for (int i = tid; i < nchunk * CHUNK; i += kBlock)
-        xs[i] = i < nv ? xg[i] : u32x4{0u, 0u, 0u, 0u};
+        xs[i] = i < nv ? *glob(xg + i) : u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
 
     if (nsteps == 0)
@@ -242,7 +242,7 @@ __device__ __forceinline__ void dense_after_unit(const DenseLin &L, int tile) {
     if (L.conv.out != nullptr) {
         __syncthreads();  // the unit's stores of y are visible to the whole workgroup
         for (int64_t i = threadIdx.x; i < nrows; i += kBlock)
-            conv_step(L.conv, r0 + i, L.y[r0 + i]);
+            conv_step(L.conv, r0 + i, *glob(L.y + r0 + i));
     }
     if (L.arg.keys != nullptr)
         publish_rows(L.arg, L.y, r0, nrows, tile);

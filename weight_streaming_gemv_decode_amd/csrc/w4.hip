@@ -51,9 +51,9 @@ namespace {
 template <bool NT>
 __device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
     if constexpr (NT)
-        return __builtin_nontemporal_load(p);
+        return __builtin_nontemporal_load(glob(p));
     else
-        return *p;
+        return *glob(p);
 }
 
 // Constants of the unpack, pinned in registers once per kernel: gfx9 VOP3
@@ -141,7 +141,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             if (!TAIL || B * c + B <= nkb) {
 #pragma unroll
                 for (int qq = 0; qq < B / 4; ++qq)
-                    Bf.sc[r][qq] = q[qq * 16 + r16];
+                    Bf.sc[r][qq] = *glob(q + qq * 16 + r16);
 #pragma unroll
                 for (int b = 0; b < B; ++b)
                     Bf.w[r][b] = load_w<NT>(p + b * kWave + lane);
@@ -150,7 +150,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                 for (int qq = 0; qq < B / 4; ++qq) {
                     Bf.sc[r][qq] = u32x2{0u, 0u};
                     if (B * c + 4 * qq < nkb)
-                        Bf.sc[r][qq] = q[qq * 16 + r16];
+                        Bf.sc[r][qq] = *glob(q + qq * 16 + r16);
                 }
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
@@ -184,9 +184,9 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                 const int64_t n = rt * 16 + r16;
                 if (lane < 16 && rt <= last_rt && n < L.N) {
                     if (L.S > 1)
-                        L.part[(int64_t)s * L.N + n] = v;
+                        *glob(L.part + (int64_t)s * L.N + n) = v;
                     else
-                        L.y[n] = v;
+                        *glob(L.y + n) = v;
                 }
                 acc1[r] = 0.0f;
             } else {
@@ -199,9 +199,9 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                         const int m = 4 * g + i;
                         if (m < M) {
                             if (L.S > 1)
-                                L.part[((int64_t)s * M + m) * L.N + n] = accm[r][i];
+                                *glob(L.part + ((int64_t)s * M + m) * L.N + n) = accm[r][i];
                             else
-                                L.y[(int64_t)m * L.N + n] = accm[r][i];
+                                *glob(L.y + (int64_t)m * L.N + n) = accm[r][i];
                         }
                     }
                 }
@@ -258,16 +258,15 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                     acc1[r] += p * scale_of(Bf.sc[r][b / 4], b % 4);
                 }
             } else {
-                // A operand: lane l supplies row m = l % 16 of X (zero for m >= M),
-                // k = 32 i + 8 g .. + 7 of the block.
+                // A operand: lane l supplies row m = l % 16 of X, k = 32 i + 8 g
+                // .. + 7 of the block.  Result rows m >= M are never stored, so
+                // their lanes repeat row M - 1 instead of zeros: every lane reads
+                // LDS unconditionally, with no masking and no zero fill.
+                const int am = min(r16, M - 1);
                 f16x8 a[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-                    if (r16 < M)
-                        v = xs[r16 * nxv + xv0 + 4 * i];
-                    a[i] = __builtin_bit_cast(f16x8, v);
-                }
+                for (int i = 0; i < 4; ++i)
+                    a[i] = __builtin_bit_cast(f16x8, xs[am * nxv + xv0 + 4 * i]);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const uint32_t words[4] = {Bf.w[r][b].x, Bf.w[r][b].y, Bf.w[r][b].z, Bf.w[r][b].w};
@@ -296,7 +295,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
         // (1) max |x| over the whole row
         float amax = 0.0f;
         for (int v = tid; v < L.K / 8; v += kBlock) {
-            const u32x4 h = L.x[v];
+            const u32x4 h = *glob(L.x + v);
             const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -323,7 +322,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t v = (int64_t)(kb0 + b) * 16 + 4 * i + gg;   // k = 8 v .. 8 v + 7
-                const u32x4 h = L.x[v];
+                const u32x4 h = *glob(L.x + v);
                 const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
                 int e[8];
 #pragma unroll
@@ -350,20 +349,20 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                                         (uint32_t)(e[2] & 255) << 16 | (uint32_t)(e[3] & 255) << 24;
                     const uint32_t n1 = (uint32_t)(e[4] & 255) | (uint32_t)(e[5] & 255) << 8 |
                                         (uint32_t)(e[6] & 255) << 16 | (uint32_t)(e[7] & 255) << 24;
-                    reinterpret_cast<u32x2 *>(L.xq_out)[v] = u32x2{n0, n1};
+                    *glob(reinterpret_cast<u32x2 *>(L.xq_out) + v) = u32x2{n0, n1};
                 }
             }
             sumx[p] = sum;
         }
         if (L.sx_out != nullptr && tile == 0 && s == 0 && tid == 0)
-            *L.sx_out = sx;
+            *glob(L.sx_out) = sx;
         __syncthreads();
     } else {
         // Stage the activation slice of every row m < M: xs[m * nxv + v].
         const int64_t xrow = (int64_t)L.K / 8;
         for (int i = tid; i < M * nxv; i += kBlock) {
             const int m = i / nxv, v = i - m * nxv;
-            xs[i] = L.x[m * xrow + (int64_t)kb0 * 16 + v];
+            xs[i] = *glob(L.x + m * xrow + (int64_t)kb0 * 16 + v);
         }
         __syncthreads();
     }
@@ -411,8 +410,18 @@ __device__ __forceinline__ void w4_publish(const W4Lin &L, int tile) {
         publish_rows(L.arg, L.y + (int64_t)m * L.N, r0, nrows, tile, m);
 }
 
+// The matrix-core variant holds the A operands, the MFMA chains and two
+// steps of weights; left alone the compiler gives the 2-tile x 4-block shape
+// 196 VGPRs + 32 AGPRs, two waves per SIMD.  Capping it at three waves per
+// SIMD (168 registers) costs no spills and keeps more weight loads in
+// flight.  Steps of 16 blocks would spill under the cap and keep the default.
+template <int R, int B, int MODE>
+constexpr int w4_min_waves_per_simd() {
+    return MODE == kMfma && R * B <= 8 ? 3 : 1;
+}
+
 template <int R, int B, bool NT, int MODE, bool TAIL>
-__global__ __launch_bounds__(kBlock) void w4_gemv_kernel(W4Lin L) {
+__global__ __launch_bounds__(kBlock, (w4_min_waves_per_simd<R, B, MODE>())) void w4_gemv_kernel(W4Lin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
     w4_unit<R, B, NT, MODE, TAIL>(L, u / L.S, u % L.S, xs_dyn);
@@ -421,7 +430,7 @@ __global__ __launch_bounds__(kBlock) void w4_gemv_kernel(W4Lin L) {
 }
 
 template <int R, int B, bool NT, int MODE, bool TAIL>
-__global__ __launch_bounds__(kBlock) void w4_grouped_kernel(const W4Lin *__restrict__ lins,
+__global__ __launch_bounds__(kBlock, (w4_min_waves_per_simd<R, B, MODE>())) void w4_grouped_kernel(const W4Lin *__restrict__ lins,
                                                             const Unit *__restrict__ units) {
     extern __shared__ u32x4 xs_dyn[];
     const Unit u = units[blockIdx.x];

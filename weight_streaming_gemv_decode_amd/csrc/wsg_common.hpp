@@ -29,6 +29,18 @@ enum W4Mode : int32_t { kA16 = 0, kMfma = 1, kA8 = 2 };
 // element expression (v.y, v.z, ...) lowers to element 0 for every element.
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
+// The global-memory view of a device pointer.  The work-table kernels read
+// their tensor pointers from memory, where the compiler cannot see that they
+// point to global memory, and would access them with flat instructions.  A
+// flat access also counts against the LDS wait counter, so each wait for an
+// activation read from LDS would also wait for every weight load still in
+// flight, which serialises the stream inside a wave.  Every kernel access to
+// a tensor goes through glob(), which makes it a global load or store.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *glob(T *p) {
+    return (__attribute__((address_space(1))) T *)p;
+}
+
 // Fused greedy-token output of a linear (device functions in argmax.hpp).
 // keys == nullptr: no token is taken.
 struct ArgOut {
