@@ -266,8 +266,9 @@ typedef struct wsg_linear {
                             y[m] (the rule of wsg_argmax_f32; for a verify block, one
                             token per drafted position); N must be 1..INT32_MAX */
     float *argmax_val;   /* optional fp32 [M]: their logits; only with argmax_idx */
-    /* F16, W8A8 (M = 1): optional causal-conv1d decode step over y, fused where
-       y is final (see causal_conv1d_step; its C is N).  conv_out NULL = none. */
+    /* Any kind with M = 1: optional causal-conv1d decode step over y, fused
+       where y is final (see causal_conv1d_step; its C is N).  conv_out NULL =
+       none; set with M > 1: WSG_ERR_UNSUPPORTED. */
     const void *conv_w;  /* fp16 [N, conv_width] */
     const float *conv_bias; /* optional fp32 [N] */
     float *conv_state;   /* fp32 [N, conv_width - 1], updated */

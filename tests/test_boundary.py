@@ -145,7 +145,8 @@ def test_conv1d_validation(L):
     assert f(FAKE, FAKE, FAKE + 2, FAKE, FAKE, 10, 4, 0, None) == ALIGN
     assert f(None, FAKE, None, FAKE, FAKE, 0, 4, 0, None) == OK                 # no channels
     out = ctypes.c_void_p()
-    for kind, M, width, want in ((2, 1, 4, UNSUP), (0, 1, 9, UNSUP), (0, 1, 4, OK)):
+    for kind, M, width, want in ((2, 4, 4, UNSUP), (3, 2, 4, UNSUP), (0, 1, 9, UNSUP), (0, 1, 4, OK), (2, 1, 4, OK),
+                                 (3, 1, 4, OK)):
         l = wsgemv.wsg_linear(kind, M, 64, 256, FAKE, FAKE if kind >= 2 else None, FAKE, None, FAKE, None,
                               128 if kind >= 2 else 0, 0, None, None, FAKE, None, FAKE, FAKE, width, 0)
         arr = (wsgemv.wsg_linear * 1)(l)

@@ -156,3 +156,52 @@ def test_fused_into_w8a8_split_and_zero_k():
     _within(host(outz), want_z, oracle.conv_bound(A_z, want_z, False), "K=0 conv")
     assert_bits_equal(host(stz), st_z, "K=0 state")
     step.close()
+
+
+@pytest.mark.parametrize("kind,N,mode,splits", [
+    (wsgemv.W4A16, 2048, wsgemv.STEP_GROUPED, 0),
+    (wsgemv.W4A16, 1000, wsgemv.STEP_GROUPED | wsgemv.STEP_FORCE_GRAPH, 0),
+    (wsgemv.W4A16, 1000, wsgemv.STEP_ORDERED, 2),             # the conv runs in the k-split reduce
+    (wsgemv.W4A8, 1000, wsgemv.STEP_GROUPED, 0),
+    (wsgemv.W4A8, 2048, wsgemv.STEP_ORDERED | wsgemv.STEP_FORCE_GRAPH, 2),
+], ids=["w4a16-grouped", "w4a16-grouped-graph-ragged", "w4a16-ordered-split2", "w4a8-grouped-ragged",
+        "w4a8-ordered-split2"])
+def test_fused_into_int4_linear(kind, N, mode, splits):
+    """The conv step over an int4 linear's output (M = 1), in the work
+    unit's epilogue or in the k-split reduce; two replays with new
+    activations.  Bound as for the fp16 case: the conv rule plus, per tap,
+    the GEMV bound of the output that tap saw."""
+    say(f"conv1d fused int4 kind={kind} N={N} mode={mode:#x} splits={splits}")
+    K, W, silu = 1024, 4, True
+    Wc = synth.w4_words(136, 0, N, K)
+    s4 = synth.f16_uniform(136, 1, (N, K // 128), 0.002, 0.02)
+    Wp, Sp = wsgemv.pack_w4(dev(Wc.view(np.int32)), dev(s4))
+    cw, cb, st0 = _fused_case(kind, N, K, W, silu, 137)
+    x_buf = torch.empty(K, dtype=torch.float16, device="cuda")
+    y = torch.empty(N, device="cuda")
+    out = torch.empty(N, device="cuda")
+    st = dev(st0)
+    lin = wsgemv.Linear(kind, Wp, x_buf, y, N, K, scale=Sp, group=128, splits=splits, conv_w=dev(cw),
+                        conv_bias=dev(cb), conv_state=st, conv_out=out, conv_silu=silu)
+    step = wsgemv.DecodeStep([lin], mode)
+    st_ref = st0.copy()
+    taps = np.abs(cw.astype(np.float64))
+    gb_hist = [np.zeros(N)] * (W - 1)
+    for t in range(2):
+        x = synth.f16_normal(138, t, (K,), synth.X_SIGMA)
+        x_buf.copy_(dev(x))
+        step()
+        if kind == wsgemv.W4A16:
+            y_ref, A_y = oracle.gemv_w4a16(Wc, s4, x)
+        else:
+            xq, sx = oracle.quantize_x_i8(x)
+            y_ref, A_y = oracle.gemv_w4a8(Wc, s4, xq, sx)
+        y_ref, A_y = y_ref.reshape(N), A_y.reshape(N)
+        assert_within(host(y), y_ref, A_y, f"y step {t}")
+        want, A_c, st_ref = oracle.causal_conv1d_step(y_ref.astype(np.float32), cw, cb, st_ref, silu)
+        prop = sum(taps[:, j] * gb_hist[j] for j in range(W - 1)) + taps[:, W - 1] * oracle.bound(A_y)
+        gb_hist = gb_hist[1:] + [oracle.bound(A_y)]
+        _within(host(out), want, oracle.conv_bound(A_c, want, silu) + 1.1 * prop, f"conv step {t}")
+        # the newest state tap holds the kernel's own output of this step
+        assert_bits_equal(host(st)[:, W - 2], host(y), f"state tap {W - 2} after step {t}")
+    step.close()

@@ -815,7 +815,7 @@ int32_t w4_token_keys(const W4Lin &L) { return L.S > 1 ? w4_reduce_blocks(L.M, L
 
 wsg_status validate_linear(const wsg_linear &l) {
     if (l.conv_out || l.conv_w || l.conv_state || l.conv_bias || l.conv_width) {
-        if ((l.kind != kF16 && l.kind != kW8A8) || l.M != 1)
+        if (l.kind < kF16 || l.kind > kW4A8 || l.M != 1)
             return WSG_ERR_UNSUPPORTED;
         wsg_status st = check_conv(l.N, l.conv_width, l.conv_w, l.conv_bias, l.conv_state, l.conv_out);
         if (st != WSG_OK)
@@ -1088,6 +1088,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     o.wc = p.cfg;
                     o.w = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
                     o.wc.tail = w4_needs_tail(o.w, o.wc.B);
+                    if (l.conv_out)
+                        o.w.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
                     if (l.argmax_idx) {
                         o.w.arg = arg_out(nullptr, w4_token_keys(o.w), l.argmax_idx, l.argmax_val, l.M);
                         o.fix = new_keys(o.w.arg.n_keys, l.M);
@@ -1119,6 +1121,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                         return WSG_ERR_UNSUPPORTED;
                     }
                     const int li = (int)wl[wmode].size();
+                    if (l.conv_out)
+                        L.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
                     if (l.argmax_idx) {
                         L.arg = arg_out(nullptr, w4_token_keys(L), l.argmax_idx, l.argmax_val, l.M);
                         wsg_step::Op f{};

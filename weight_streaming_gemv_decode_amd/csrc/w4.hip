@@ -44,6 +44,7 @@
 // in that same order.  The zero-point enters exactly, in integers, as an
 // initial accumulator of -8 * (sum of the lane's 32 activation codes).
 #include "argmax.hpp"
+#include "conv1d.hpp"
 
 namespace wsg {
 namespace {
@@ -401,12 +402,18 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     }
 }
 
-// A finished unit's greedy-token keys (S = 1): one per output row m < M,
-// from the unit's rows of y[m].
-__device__ __forceinline__ void w4_publish(const W4Lin &L, int tile) {
+// The epilogues of a finished unit (S = 1) that read its rows of y back:
+// the causal-conv1d step of each row (M = 1), then the greedy-token key of
+// each output row m < M.
+__device__ __forceinline__ void w4_after_unit(const W4Lin &L, int tile) {
     const int64_t r0 = (int64_t)tile * L.tile_rtiles * 16;
     const int64_t nrows = min((int64_t)L.tile_rtiles * 16, L.N - r0);
-    for (int m = 0; m < L.M; ++m)
+    if (L.conv.out != nullptr) {
+        __syncthreads();  // the unit's stores of y are visible to the whole workgroup
+        for (int64_t i = threadIdx.x; i < nrows; i += kBlock)
+            conv_step(L.conv, r0 + i, *glob(L.y + r0 + i));
+    }
+    for (int m = 0; L.arg.keys != nullptr && m < L.M; ++m)
         publish_rows(L.arg, L.y + (int64_t)m * L.N, r0, nrows, tile, m);
 }
 
@@ -425,8 +432,8 @@ __global__ __launch_bounds__(kBlock, (w4_min_waves_per_simd<R, B, MODE>())) void
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
     w4_unit<R, B, NT, MODE, TAIL>(L, u / L.S, u % L.S, xs_dyn);
-    if (L.arg.keys != nullptr && L.S == 1)
-        w4_publish(L, u);
+    if (L.S == 1 && (L.arg.keys != nullptr || L.conv.out != nullptr))
+        w4_after_unit(L, u);
 }
 
 template <int R, int B, bool NT, int MODE, bool TAIL>
@@ -436,12 +443,13 @@ __global__ __launch_bounds__(kBlock, (w4_min_waves_per_simd<R, B, MODE>())) void
     const Unit u = units[blockIdx.x];
     const W4Lin L = lins[u.lin];
     w4_unit<R, B, NT, MODE, TAIL>(L, u.tile, u.s, xs_dyn);
-    if (L.arg.keys != nullptr && L.S == 1)
-        w4_publish(L, u.tile);
+    if (L.S == 1 && (L.arg.keys != nullptr || L.conv.out != nullptr))
+        w4_after_unit(L, u.tile);
 }
 
 // y[m][n] = sum over slices s = 0..S-1, in that order, of part[s][m][n];
-// and every row m's greedy-token key of this workgroup when taken.
+// every row m's greedy-token key of this workgroup when taken; and the
+// causal-conv1d step over y (M = 1) when taken.
 __global__ __launch_bounds__(kBlock) void w4_reduce_kernel(W4Lin L) {
     const int64_t total = (int64_t)L.M * L.N;
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
@@ -454,6 +462,8 @@ __global__ __launch_bounds__(kBlock) void w4_reduce_kernel(W4Lin L) {
         L.y[i] = a;
         m = (int)(i / L.N);
         key = arg_key(a, i - (int64_t)m * L.N);
+        if (L.conv.out != nullptr)  // M = 1
+            conv_step(L.conv, i, a);
     }
     if (L.arg.keys != nullptr)
         for (int mm = 0; mm < L.M; ++mm)

@@ -106,6 +106,7 @@ struct W4Lin {
     int32_t tile_rtiles;   // 16-row tiles per work unit
     int32_t n_tiles;       // ceil(n_rtiles / tile_rtiles)
     ArgOut arg;            // optional greedy token of each output row (S = 1: the units; S > 1: the reduce)
+    ConvOut conv;          // optional causal-conv1d step over y (M = 1; where y is final)
 };
 
 // One work unit of a grouped launch: linear `lin`, row tile `tile`, k-slice `s`.
