@@ -449,6 +449,16 @@ def main():
                "sample": f"{n_cpu} full decode steps (all 113 GEMVs, 1.22 GB each) through the fp64 C oracle, "
                          f"OpenMP over rows on {cores} threads ({platform.processor() or platform.machine()})"}
         log(f"oracle: {dt:.2f}s/step on {cores} threads over {n_cpu} steps")
+        # the same oracle on one thread: one whole step (a few seconds)
+        oracle.set_threads(1)
+        t1 = time.perf_counter()
+        for _, W, x in step_in:
+            oracle.gemv_f16(W, x)
+        dt1 = time.perf_counter() - t1
+        oracle.set_threads(cores)
+        cpu["single_thread"] = {"value": round(step_bytes / dt1 / 1e9, 3), "unit": "GB/s",
+                                "ms_per_step": round(dt1 * 1e3, 1), "sample": "1 full decode step on 1 thread"}
+        log(f"oracle: {dt1:.2f}s/step on 1 thread")
 
     line = {
         "metric": METRIC,

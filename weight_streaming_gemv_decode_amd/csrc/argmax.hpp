@@ -31,9 +31,10 @@ __device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsi
     return a > b ? a : b;
 }
 
+// The key of lane l ^ o (every lane of the wave active; o a power of two).
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o);
+    const uint32_t lo = xor_lane((uint32_t)v, o);
+    const uint32_t hi = xor_lane((uint32_t)(v >> 32), o);
     return ((unsigned long long)hi << 32) | lo;
 }
 

@@ -78,7 +78,7 @@ __device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
         for (int i = 0; i < 4; ++i) {
             T keep = up ? v[i + 4] : v[i];
             T send = up ? v[i] : v[i + 4];
-            v[i] = keep + __shfl_xor(send, 32);
+            v[i] = keep + xor_lane(send, 32);
         }
     }
     if constexpr (R >= 4) {
@@ -88,7 +88,7 @@ __device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
         for (int i = 0; i < 2; ++i) {
             T keep = up ? v[i + 2] : v[i];
             T send = up ? v[i] : v[i + 2];
-            v[i] = keep + __shfl_xor(send, o);
+            v[i] = keep + xor_lane(send, o);
         }
     }
     if constexpr (R >= 2) {
@@ -96,12 +96,12 @@ __device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
         const bool up = lane & o;
         T keep = up ? v[1] : v[0];
         T send = up ? v[0] : v[1];
-        v[0] = keep + __shfl_xor(send, o);
+        v[0] = keep + xor_lane(send, o);
     }
     T s = v[0];
 #pragma unroll
     for (int o = 32 / R; o >= 1; o >>= 1)
-        s += __shfl_xor(s, o);
+        s += xor_lane(s, o);
     return s;
 }
 

@@ -5,17 +5,19 @@
 // AIPro post, second change) to the k best candidates.
 //
 // Keys are unique (the index is part of the key), so the top k are exactly
-// the keys at or above the k-th largest.  A workgroup finds that key by a
-// radix select on its 64-bit keys, one byte at a time from the top: a
-// histogram of the current byte over the keys that share the bytes already
-// fixed (shared-memory atomic adds), then the bin that holds the k-th
-// largest; it stops early once that bin holds exactly the keys still
-// needed.  The keys at or above it are gathered and one wave sorts them
-// (bitonic, through lane exchanges).  A selection pass gives every
-// workgroup 2048 candidates and writes its k best keys; passes repeat until
-// one workgroup of 1024 threads (16 candidates per thread) picks the final
-// k in order.  No global atomics; the result does not depend on workgroup
-// order.
+// the keys at or above the k-th largest.  A selection pass gives every
+// workgroup 2048 candidates; the workgroup finds the k-th largest by a radix
+// select on the 64-bit keys, one byte at a time from the top (a histogram of
+// the current byte over the keys that share the bytes already fixed, in
+// shared memory, then the bin that holds the k-th largest; it stops early
+// once that bin holds exactly the keys still needed), gathers the keys at or
+// above it, and one wave sorts them (bitonic, through lane exchanges).  Each
+// workgroup writes its k best keys as a sorted list.  Passes repeat until at
+// most 256 lists remain; one workgroup then merges them: two sorted lists of
+// 64 merge in one wave as the lane-wise maximum of one list and the other
+// reversed (the 64 largest of both, in bitonic order) followed by six
+// exchange stages.  No global atomics; the result does not depend on
+// workgroup order.
 #include <algorithm>
 
 #include "argmax.hpp"
@@ -25,8 +27,9 @@ namespace {
 
 constexpr int kPerThread = 8;
 constexpr int kChunk = kBlock * kPerThread;  // candidates per workgroup of a pass
-constexpr int kFinalThreads = 1024;
-constexpr int kFinalPerThread = 16;          // the final workgroup takes up to 16384 candidates
+constexpr int kMergeWaves = 16;              // waves of the merging workgroup
+constexpr int kMergeLists = 256;             // most sorted lists the merge takes
+constexpr int kListsPerWave = kMergeLists / kMergeWaves;
 constexpr int kMaxK = 64;
 
 // The k largest of the workgroup's candidates (E per thread, 0 = none), in
@@ -116,7 +119,9 @@ __device__ __forceinline__ void block_select(const unsigned long long (&c)[E], i
     if (tid < kWave) {
         // bitonic sort of the 64 gathered keys, descending, one per lane
         unsigned long long v = sel[lane];
+#pragma unroll
         for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
                 const unsigned long long o = shfl_xor_u64(v, stride);
                 const bool lower = (lane & stride) == 0;
@@ -151,70 +156,112 @@ __global__ __launch_bounds__(kBlock) void topk_pass_kernel(const float *__restri
         out[(int64_t)blockIdx.x * k + threadIdx.x] = res[threadIdx.x];
 }
 
-__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(const unsigned long long *__restrict__ in,
-                                                                  int64_t count, int k, int32_t *idx, float *val) {
-    unsigned long long c[kFinalPerThread];
+// The key of lane 63 - l: reversed within each 16-lane row, then rows
+// swapped across (xor 48).
+__device__ __forceinline__ unsigned long long mirror_u64(unsigned long long v) {
+    uint32_t lo = __builtin_amdgcn_mov_dpp((uint32_t)v, 0x140, 0xF, 0xF, false);  // row_mirror
+    uint32_t hi = __builtin_amdgcn_mov_dpp((uint32_t)(v >> 32), 0x140, 0xF, 0xF, false);
+    lo = xor_lane(xor_lane(lo, 32), 16);
+    hi = xor_lane(xor_lane(hi, 32), 16);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Lane l's key of the 64 largest of two descending lists held one key per
+// lane (v, b), in descending order.  b reversed is ascending, so the
+// lane-wise maximum holds the 64 largest of both in bitonic order; a bitonic
+// merge (lower lane takes the larger) sorts it.
+__device__ __forceinline__ unsigned long long merge64(unsigned long long v, unsigned long long b, int lane) {
+    v = max_u64(v, mirror_u64(b));
 #pragma unroll
-    for (int j = 0; j < kFinalPerThread; ++j) {
-        const int64_t i = threadIdx.x + (int64_t)j * kFinalThreads;
-        c[j] = i < count ? in[i] : 0ull;
+    for (int stride = kWave / 2; stride > 0; stride >>= 1) {
+        const unsigned long long o = shfl_xor_u64(v, stride);
+        v = (lane & stride) ? (v < o ? v : o) : max_u64(v, o);
     }
-    __shared__ unsigned long long res[kMaxK];
-    block_select<kFinalThreads>(c, k, res);
-    if ((int)threadIdx.x < k) {
+    return v;
+}
+
+// The k largest keys of `lists` sorted lists (list l = in[l k .. l k + k),
+// descending, zero-padded), in descending order, as the token rule's
+// indices and values: every wave merges its share of the lists (all loaded
+// first), then the waves' results are merged pairwise through shared memory.
+__global__ __launch_bounds__(kMergeWaves * kWave) void topk_merge_kernel(const unsigned long long *__restrict__ in,
+                                                                        int lists, int k, int32_t *idx, float *val) {
+    __shared__ unsigned long long part[kMergeWaves][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    unsigned long long b[kListsPerWave];
+#pragma unroll
+    for (int j = 0; j < kListsPerWave; ++j) {
+        const int l = wave + j * kMergeWaves;
+        b[j] = (l < lists && lane < k) ? *glob(in + (int64_t)l * k + lane) : 0ull;
+    }
+    unsigned long long v = b[0];  // one list is sorted already
+#pragma unroll
+    for (int j = 1; j < kListsPerWave; ++j)
+        if (wave + j * kMergeWaves < lists)  // wave-uniform
+            v = merge64(v, b[j], lane);
+    part[wave][lane] = v;
+    for (int half = kMergeWaves / 2; half > 0; half >>= 1) {
+        __syncthreads();
+        if (wave < half)
+            v = merge64(part[wave][lane], part[wave + half][lane], lane);
+        __syncthreads();
+        if (wave < half)
+            part[wave][lane] = v;
+    }
+    if (wave == 0 && lane < k) {
         ArgOut a{};
         a.idx = idx;
         a.val = val;
-        arg_write(a, res[threadIdx.x], threadIdx.x);
+        arg_write(a, v, lane);
     }
 }
 
 }  // namespace
 
-// Candidate counts of the passes for (N, k): N, then ceil(count / 2048) * k
-// until at most 16384 remain for the final workgroup.  Returns the number of
-// keys the workspace must hold for the two ping-pong buffers.
+// The selection passes for (N, k): each turns `count` candidates into one
+// sorted list of k per 2048, until at most 256 lists remain for the merge.
+// Returns the number of lists left; *max_keys is the most keys one pass
+// writes (each of the two ping-pong buffers must hold that many).
 int64_t topk_plan(int64_t N, int k, int64_t *max_keys, int *passes) {
-    int64_t count = N, biggest = 0;
+    int64_t count = N, biggest = 0, lists = 0;
     int p = 0;
-    while (count > (int64_t)kFinalThreads * kFinalPerThread || p == 0) {
-        const int64_t next = (count + kChunk - 1) / kChunk * k;
-        biggest = std::max(biggest, next);
-        count = next;
+    do {
+        lists = (count + kChunk - 1) / kChunk;
+        count = lists * k;
+        biggest = std::max(biggest, count);
         ++p;
-        if (p > 8)
-            break;
-    }
+    } while (lists > kMergeLists && p < 8);
     if (max_keys)
         *max_keys = biggest;
     if (passes)
         *passes = p;
-    return count;
+    return lists;
 }
 
 hipError_t launch_topk(const float *y, int64_t N, int k, int32_t *idx, float *val, unsigned long long *ws_a,
                        unsigned long long *ws_b, hipStream_t s) {
-    int64_t count = N;
+    int passes = 0;
+    topk_plan(N, k, nullptr, &passes);
+    int64_t count = N, lists = 0;
     const unsigned long long *in = nullptr;
     unsigned long long *out = ws_a;
-    bool first = true;
-    do {
-        const int64_t blocks = (count + kChunk - 1) / kChunk;
-        if (first)
-            hipLaunchKernelGGL(topk_pass_kernel<true>, dim3((unsigned)blocks), dim3(kBlock), 0, s, y, nullptr, count, k,
-                               out);
-        else
-            hipLaunchKernelGGL(topk_pass_kernel<false>, dim3((unsigned)blocks), dim3(kBlock), 0, s, nullptr, in, count,
+    for (int p = 0; p < passes; ++p) {
+        lists = (count + kChunk - 1) / kChunk;
+        if (p == 0)
+            hipLaunchKernelGGL(topk_pass_kernel<true>, dim3((unsigned)lists), dim3(kBlock), 0, s, y, nullptr, count,
                                k, out);
+        else
+            hipLaunchKernelGGL(topk_pass_kernel<false>, dim3((unsigned)lists), dim3(kBlock), 0, s, nullptr, in,
+                               count, k, out);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        count = blocks * k;
+        count = lists * k;
         in = out;
         out = (out == ws_a) ? ws_b : ws_a;
-        first = false;
-    } while (count > (int64_t)kFinalThreads * kFinalPerThread);
-    hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kFinalThreads), 0, s, in, count, k, idx, val);
+    }
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(1), dim3(kMergeWaves * kWave), 0, s, in, (int)lists, k, idx, val);
     return hipGetLastError();
 }
 

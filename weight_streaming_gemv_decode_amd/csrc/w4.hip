@@ -178,8 +178,8 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             const int64_t rt = rtb + r;
             if constexpr (!MFMA) {
                 float v = acc1[r];
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
+                v += xor_lane(v, 16);
+                v += xor_lane(v, 32);
                 if constexpr (MODE == kA8)
                     v *= sx;
                 const int64_t n = rt * 16 + r16;
@@ -305,7 +305,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             }
         }
         for (int o = 32; o >= 1; o >>= 1)
-            amax = fmaxf(amax, __shfl_xor(amax, o));
+            amax = fmaxf(amax, xor_lane(amax, o));
         float *red = reinterpret_cast<float *>(reinterpret_cast<int *>(xs + 8 * nkb) + 4 * nkb);
         if (lane == 0)
             red[wave] = amax;

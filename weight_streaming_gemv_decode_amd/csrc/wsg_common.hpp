@@ -29,6 +29,46 @@ enum W4Mode : int32_t { kA16 = 0, kMfma = 1, kA8 = 2 };
 // element expression (v.y, v.z, ...) lowers to element 0 for every element.
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
+// The value that lane (l ^ stride) holds, for stride = 1, 2, 4, ..., 32, by
+// DPP row operations and the gfx950 lane-swap instructions: plain vector
+// instructions, where a generic shuffle goes through the LDS crossbar and
+// waits for it.  Every lane of the wave must be active.  The stride must be a
+// compile-time constant after unrolling (the switch then folds away).
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int stride) {
+    const int lane = __lane_id();
+    switch (stride) {
+    case 1:
+        return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    case 2:
+        return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    case 4: {
+        const uint32_t up = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0xF, false);  // row_shl:4, lane i reads i + 4
+        const uint32_t dn = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // row_shr:4, lane i reads i - 4
+        return (lane & 4) ? dn : up;
+    }
+    case 8:
+        return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    case 16: {
+        // swap(v, v): element 0 holds rows (0, 0, 2, 2), element 1 rows (1, 1, 3, 3)
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    }
+    default: {
+        // swap(v, v): element 0 holds halves (0, 0), element 1 halves (1, 1)
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+    }
+}
+
+__device__ __forceinline__ float xor_lane(float v, int stride) {
+    return __builtin_bit_cast(float, xor_lane(__builtin_bit_cast(uint32_t, v), stride));
+}
+
+__device__ __forceinline__ int32_t xor_lane(int32_t v, int stride) {
+    return (int32_t)xor_lane((uint32_t)v, stride);
+}
+
 // The global-memory view of a device pointer.  The work-table kernels read
 // their tensor pointers from memory, where the compiler cannot see that they
 // point to global memory, and would access them with flat instructions.  A
