@@ -309,8 +309,9 @@ int32_t wsg_read_probe_grid(size_t bytes);
  * (rows per work unit), "group_R"/"group_CH"/"group_unit_kb" (the same for
  * grouped decode-step launches), "w4_R" (16-row tiles per wave step), "w4_B" (128-k blocks per
  * wave step: 4, 8),
- * "w4_tiles" / "group_w4_tiles" (tiles per work unit), "probe_U" (loads in
- * flight per lane: 4, 8, 16), "probe_chunked" (0/1).  value < 0 restores the
+ * "w4_tiles" / "group_w4_tiles" (tiles per work unit), "w4_mfma_m1" (1: W4A16
+ * at M = 1 on the matrix-core kernel), "probe_U" (loads in flight per lane:
+ * 4, 8, 16), "probe_chunked" (0/1).  value < 0 restores the
  * table's choice.  Process-wide, not thread-safe; plans capture the values
  * in force when they are created.  No result depends on these settings
  * beyond the summation order.  Unknown keys and kernel shapes that are not

@@ -13,7 +13,7 @@ from weight_streaming_gemv_decode_amd import synth, wsgemv
 pytestmark = pytest.mark.gpu
 
 KEYS = ("nt", "dense_R", "dense_CH", "dense_rows", "group_R", "group_CH", "group_unit_kb", "w4_R", "w4_B",
-        "w4_tiles", "group_w4_tiles")
+        "w4_tiles", "group_w4_tiles", "w4_mfma_m1")
 
 
 def _pair(kr, kc, R, CH):
@@ -100,6 +100,27 @@ def test_w4_shapes(M, N, K):
                     wsgemv.tune_set("w4_tiles", tiles)
                     got = host(wsgemv.gemv_w4a16(Wp, Sp, Xd, N, splits=1))
                     assert_bits_equal(got, base, f"nt={nt} R={R} B={B} tiles={tiles}")
+
+
+@pytest.mark.parametrize("N,K", [(100, 1024), (17, 640)])
+def test_w4_m1_on_matrix_cores(N, K):
+    """M = 1 through the matrix-core kernel (a tuning switch): a different
+    summation order, so within the bound rather than bit-identical, and
+    every shape of that kernel bit-identical to its own default."""
+    say(f"tuning w4 M=1 on MFMA {N}x{K}")
+    Wc = synth.w4_words(83, N, N, K)
+    s4 = synth.f16_uniform(83, K, (N, K // 128), 0.002, 0.02)
+    x = synth.f16_normal(83, 1, (K,), synth.X_SIGMA)
+    y_ref, A = oracle.gemv_w4a16(Wc, s4, x)
+    Wp, Sp = wsgemv.pack_w4(dev(Wc), dev(s4))
+    wsgemv.tune_set("w4_mfma_m1", 1)
+    base = host(wsgemv.gemv_w4a16(Wp, Sp, dev(x), N, splits=1))
+    assert_within(base, y_ref.reshape(N), A.reshape(N), "mfma M=1")
+    for R, B in ((1, 4), (2, 4), (1, 8)):
+        wsgemv.tune_set("w4_R", R)
+        wsgemv.tune_set("w4_B", B)
+        got = host(wsgemv.gemv_w4a16(Wp, Sp, dev(x), N, splits=1))
+        assert_bits_equal(got, base, f"mfma M=1 R={R} B={B}")
 
 
 def test_grouped_shapes_bit_identical():

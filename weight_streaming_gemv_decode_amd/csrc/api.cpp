@@ -50,6 +50,7 @@ struct Tune {
     int64_t dense_R = -1, dense_CH = -1, dense_rows = -1;
     int64_t group_R = -1, group_CH = -1, group_unit_kb = -1;
     int64_t w4_R = -1, w4_B = -1, w4_tiles = -1, group_w4_tiles = -1;
+    int64_t w4_mfma_m1 = -1;     // 1: W4A16 at M = 1 on the matrix cores
     int64_t probe_U = -1, probe_chunked = -1;
 };
 Tune g_tune;
@@ -682,7 +683,7 @@ wsg_status gemv_w4a16(const void *Wp, const void *Sp, const void *x, float *y, i
             return st;
         W4Lin L = make_w4(Wp, Sp, x, y, static_cast<float *>(ws), M, N, K, p);
         p.cfg.tail = w4_needs_tail(L, p.cfg.B);
-        return enqueue_w4(L, M > 1 ? kMfma : kA16, p.cfg, s);
+        return enqueue_w4(L, (M > 1 || g_tune.w4_mfma_m1 == 1) ? kMfma : kA16, p.cfg, s);
     });
 }
 
@@ -703,6 +704,7 @@ wsg_status wsg_tune_set(const char *key, int64_t value) {
                  {"w4_B", &g_tune.w4_B},
                  {"w4_tiles", &g_tune.w4_tiles},
                  {"group_w4_tiles", &g_tune.group_w4_tiles},
+                 {"w4_mfma_m1", &g_tune.w4_mfma_m1},
                  {"probe_U", &g_tune.probe_U},
                  {"probe_chunked", &g_tune.probe_chunked}};
     for (auto &t : table) {
@@ -1078,7 +1080,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     dtail[ki] = dtail[ki] || dense_needs_tail(L, gcfg.CH);
                 }
             } else {
-                const int wmode = l.kind == kW4A8 ? kA8 : (l.M > 1 ? kMfma : kA16);
+                const int wmode = l.kind == kW4A8 ? kA8 : ((l.M > 1 || g_tune.w4_mfma_m1 == 1) ? kMfma : kA16);
                 if (base_mode == WSG_STEP_ORDERED) {
                     W4Plan p = plan_w4(l.M, l.N, l.K, l.splits);
                     part_bytes = std::max(part_bytes, w4_ws_bytes(p, l.M, l.N));
@@ -1111,10 +1113,11 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     // per-unit quantisation is amortised over more rows);
                     // verify blocks: 2 tiles x 4 blocks per step, 8 tiles per unit
                     const bool a8 = wmode == kA8;
+                    const bool mfma = wmode == kMfma;
                     p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles
-                                                              : (l.M > 1 || a8 ? 8 : 4);
-                    p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (l.M > 1 ? 2 : 1);
-                    p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (l.M > 1 || a8 ? 4 : 8);
+                                                              : (mfma || a8 ? 8 : 4);
+                    p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (mfma ? 2 : 1);
+                    p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (mfma || a8 ? 4 : 8);
                     W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
                     if (w4_lds_bytes(L, wmode) > 48 * 1024) {
                         free_step(st);
