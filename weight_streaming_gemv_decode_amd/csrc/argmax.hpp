@@ -42,8 +42,9 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
 template <int WAVES = kWavesPerBlock>
 __device__ __forceinline__ unsigned long long block_max_key(unsigned long long best) {
     __shared__ unsigned long long red[WAVES];
-    for (int o = kWave / 2; o >= 1; o >>= 1)
-        best = max_u64(best, shfl_xor_u64(best, o));
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+        best = max_u64(best, shfl_xor_u64(best, (kWave / 2) >> i));
     const int tid = threadIdx.x;
     if ((tid & (kWave - 1)) == 0)
         red[tid / kWave] = best;

@@ -99,9 +99,12 @@ __device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
         v[0] = keep + xor_lane(send, o);
     }
     T s = v[0];
+    // strides 32/R .. 1, counted by an affine index so the loop unrolls and
+    // every exchange gets a constant stride
+    constexpr int kSteps = R == 1 ? 6 : R == 2 ? 5 : R == 4 ? 4 : 3;
 #pragma unroll
-    for (int o = 32 / R; o >= 1; o >>= 1)
-        s += xor_lane(s, o);
+    for (int i = 0; i < kSteps; ++i)
+        s += xor_lane(s, (32 / R) >> i);
     return s;
 }
 

@@ -120,9 +120,11 @@ __device__ __forceinline__ void block_select(const unsigned long long (&c)[E], i
         // bitonic sort of the 64 gathered keys, descending, one per lane
         unsigned long long v = sel[lane];
 #pragma unroll
-        for (int size = 2; size <= kWave; size <<= 1) {
+        for (int ls = 1; ls <= 6; ++ls) {  // sequences of size 2^ls
+            const int size = 1 << ls;
 #pragma unroll
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int j = 1; j <= ls; ++j) {
+                const int stride = size >> j;
                 const unsigned long long o = shfl_xor_u64(v, stride);
                 const bool lower = (lane & stride) == 0;
                 const bool desc = (lane & size) == 0;   // direction of this lane's sequence
@@ -173,7 +175,8 @@ __device__ __forceinline__ unsigned long long mirror_u64(unsigned long long v) {
 __device__ __forceinline__ unsigned long long merge64(unsigned long long v, unsigned long long b, int lane) {
     v = max_u64(v, mirror_u64(b));
 #pragma unroll
-    for (int stride = kWave / 2; stride > 0; stride >>= 1) {
+    for (int i = 0; i < 6; ++i) {
+        const int stride = (kWave / 2) >> i;
         const unsigned long long o = shfl_xor_u64(v, stride);
         v = (lane & stride) ? (v < o ? v : o) : max_u64(v, o);
     }

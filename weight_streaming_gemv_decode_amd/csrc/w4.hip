@@ -304,8 +304,9 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                 amax = fmaxf(amax, fmaxf(fabsf((float)p[0]), fabsf((float)p[1])));
             }
         }
-        for (int o = 32; o >= 1; o >>= 1)
-            amax = fmaxf(amax, xor_lane(amax, o));
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            amax = fmaxf(amax, xor_lane(amax, 32 >> i));
         float *red = reinterpret_cast<float *>(reinterpret_cast<int *>(xs + 8 * nkb) + 4 * nkb);
         if (lane == 0)
             red[wave] = amax;
