@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true", help="only the decode-step stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,conv,graph,topk,probe,ordered)")
+    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,conv,graph,topk,probe,ordered,chain)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB fp32 copy kernel (reads 1 GiB, writes 1 GiB) to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass")
@@ -245,6 +245,29 @@ def main():
         extras["c3_ordered_graph"] = {"median_ms": s["median_ms"], "GBps": step_bytes / (s["median_ms"] * 1e-3) / 1e9,
                                       "launches": o.info()[0]}
         o.close()
+
+    if want("chain"):
+        # the same 113 linears as one dependent chain: every linear reads the
+        # leading K entries of the previous linear's fp16 output (y16), which
+        # stands in for the attention / activation glue between them; the
+        # ORDERED plan (one graph) runs them in order
+        y16s, cl = [], []
+        x = lins[0].x
+        for l in lins:
+            y16 = torch.empty(l.N, dtype=torch.float16, device=dev)
+            cl.append(wsgemv.Linear(l.kind, l.W, x[:l.K], torch.empty(l.N, device=dev), l.N, l.K, y16=y16))
+            y16s.append(y16)
+            x = y16
+        ch = wsgemv.DecodeStep(cl, wsgemv.STEP_ORDERED, stream=stream)
+        for _ in range(3):
+            ch(stream)
+        s = summary(event_times(torch, lambda i: ch(stream), 50, stream))
+        extras["c3_dependent_chain_ordered_graph"] = {
+            "median_ms": s["median_ms"], "GBps": step_bytes / (s["median_ms"] * 1e-3) / 1e9,
+            "launches": ch.info()[0],
+            "note": "each linear's x is the leading K entries of the previous linear's fp16 output"}
+        ch.close()
+        del y16s, cl
 
     if want("token"):
         # the timed step with the lm_head also taking the greedy token

@@ -245,7 +245,7 @@ wsg_status causal_conv1d_step(const float *x, const void *w, const float *bias, 
  *   mode WSG_STEP_GROUPED: the linears of each kind run as one launch over a
  *     work table of (linear, row tile, k-slice) units.  Valid because every
  *     linear of the list reads its own x and writes its own y; a list whose
- *     linears feed each other must use ORDERED.
+ *     linears feed each other (through y16) must use ORDERED.
  *   | WSG_STEP_EAGER: never capture; decode_step_linears launches directly.
  *   | WSG_STEP_FORCE_GRAPH: always capture, whatever the launch count.
  * decode_step_linears enqueues one step on `stream`.  A plan is not
@@ -276,6 +276,13 @@ typedef struct wsg_linear {
     float *conv_out;     /* fp32 [N] */
     int32_t conv_width;  /* 2..8 */
     int32_t conv_silu;   /* nonzero: SiLU on the conv output */
+    /* Optional fp16 [M,N] copy of y, rounded to nearest even (overflow to
+       inf), written where y is final.  It is how one linear feeds the next:
+       a later linear of an ORDERED plan may take it, or a contiguous part of
+       it, as its x.  A GROUPED plan rejects (WSG_ERR_UNSUPPORTED) a list in
+       which any linear's x overlaps any linear's y16, since its units run in
+       no fixed order.  2-byte aligned; must not alias any input. */
+    void *y16;
 } wsg_linear;
 
 typedef struct wsg_step wsg_step;

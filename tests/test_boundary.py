@@ -240,3 +240,23 @@ def test_tuning_overrides_validated():
     finally:
         for k in keys:
             wsgemv.tune_set(k, -1)
+
+
+def test_y16_validation(L):
+    """A linear's fp16 output copy: 2-byte aligned; a GROUPED plan rejects a
+    list in which one linear's x overlaps a y16 (the units run in no fixed
+    order), before any HIP call."""
+    out = ctypes.c_void_p()
+    y16 = FAKE + 0x100000                       # a.y16 spans 64 rows x 2 bytes = 128 bytes
+    a = wsgemv.wsg_linear(0, 1, 64, 64, FAKE, None, FAKE, None, FAKE + 0x10000, None, 0, 0)
+    a.y16 = y16 + 1
+    assert L.wsg_decode_step_create((wsgemv.wsg_linear * 1)(a), 1, 1, None, ctypes.byref(out)) == ALIGN
+    a.y16 = y16
+    # an int4 linear whose fp16 x (128 values, 256 bytes) starts inside, at, or ends inside a.y16
+    for x_at in (y16, y16 + 64, y16 + 112, y16 - 240):
+        b = wsgemv.wsg_linear(2, 1, 64, 128, FAKE, FAKE, x_at, None, FAKE + 0x20000, None, 128, 0)
+        got = L.wsg_decode_step_create((wsgemv.wsg_linear * 2)(a, b), 2, 1, None, ctypes.byref(out))
+        assert got == UNSUP, (hex(x_at), got)
+    # a W8A8 linear's int8 x is K bytes: 80 bytes from y16 - 64 reach into a.y16
+    c = wsgemv.wsg_linear(1, 1, 64, 80, FAKE, FAKE, y16 - 64, FAKE, FAKE + 0x30000, None, 0, 0)
+    assert L.wsg_decode_step_create((wsgemv.wsg_linear * 2)(c, a), 2, 1, None, ctypes.byref(out)) == UNSUP

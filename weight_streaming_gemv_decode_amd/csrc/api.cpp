@@ -788,7 +788,7 @@ struct wsg_step {
     void *dev = nullptr;  // one device allocation: partials, descriptor and unit tables
 
     struct Op {
-        enum Type { kDense, kDenseGroup, kW4, kW4Group, kZero, kArgmax, kArgFinish, kConv } type;
+        enum Type { kDense, kDenseGroup, kW4, kW4Group, kZero, kZero16, kArgmax, kArgFinish, kConv } type;
         int kind = 0;
         DenseLin d{};
         DenseCfg dc{};
@@ -800,6 +800,7 @@ struct wsg_step {
         int lds = 0;
         int mode = 0;                 // W4 kernel mode (kA16, kMfma, kA8)
         float *zero_p = nullptr;
+        uint16_t *zero16_p = nullptr;  // kZero16
         int64_t zero_n = 0;
         ArgOut arg{};                 // kArgmax: token over zero_p[0..zero_n); kArgFinish: token from keys
         ConvOut conv{};               // kConv: conv step over zero_p[0..zero_n)
@@ -815,7 +816,29 @@ namespace {
 // Workgroups that publish keys for an int4 linear's tokens.
 int32_t w4_token_keys(const W4Lin &L) { return L.S > 1 ? w4_reduce_blocks(L.M, L.N) : L.n_tiles; }
 
+// True when some linear's x overlaps some linear's y16: the list chains
+// linears, which only the ORDERED plan runs in order.
+bool feeds_another(const wsg_linear *L, int32_t n) {
+    for (int32_t j = 0; j < n; ++j) {
+        if (!L[j].y16 || L[j].N == 0)
+            continue;
+        const auto *y0 = static_cast<const char *>(L[j].y16);
+        const auto *y1 = y0 + (size_t)L[j].M * (size_t)L[j].N * 2;
+        for (int32_t i = 0; i < n; ++i) {
+            if (!L[i].x || L[i].K == 0)
+                continue;
+            const size_t xb = (size_t)L[i].M * (size_t)L[i].K * (L[i].kind == kW8A8 ? 1 : 2);
+            const auto *x0 = static_cast<const char *>(L[i].x);
+            if (x0 < y1 && y0 < x0 + xb)
+                return true;
+        }
+    }
+    return false;
+}
+
 wsg_status validate_linear(const wsg_linear &l) {
+    if (l.y16 && !aligned(l.y16, 2))
+        return WSG_ERR_ALIGN;
     if (l.conv_out || l.conv_w || l.conv_state || l.conv_bias || l.conv_width) {
         if (l.kind < kF16 || l.kind > kW4A8 || l.M != 1)
             return WSG_ERR_UNSUPPORTED;
@@ -884,6 +907,9 @@ hipError_t run_ops(const wsg_step *st, hipStream_t s) {
         case wsg_step::Op::kZero:
             e = launch_zero_f32(op.zero_p, op.zero_n, s);
             break;
+        case wsg_step::Op::kZero16:
+            e = launch_zero_u16(op.zero16_p, op.zero_n, s);
+            break;
         case wsg_step::Op::kArgmax:
             e = launch_argmax_f32(op.zero_p, op.zero_n, op.arg, s);
             break;
@@ -944,6 +970,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             if (base_mode == WSG_STEP_GROUPED && linears[i].splits > 1)
                 return WSG_ERR_UNSUPPORTED;
         }
+        if (base_mode == WSG_STEP_GROUPED && feeds_another(linears, n))
+            return WSG_ERR_UNSUPPORTED;
         hipStream_t s = static_cast<hipStream_t>(stream);
         wsg_step *st = new wsg_step();
         st->mode = mode;
@@ -999,6 +1027,13 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     z.zero_n = l.N;
                     st->ops.push_back(z);
                 }
+                if (l.y16) {
+                    wsg_step::Op z16{};
+                    z16.type = wsg_step::Op::kZero16;
+                    z16.zero16_p = static_cast<uint16_t *>(l.y16);
+                    z16.zero_n = (int64_t)l.M * l.N;
+                    st->ops.push_back(z16);
+                }
                 if (l.conv_out) {
                     wsg_step::Op c{};
                     c.type = wsg_step::Op::kConv;
@@ -1031,6 +1066,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     o.d = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale), l.x_scale,
                                      l.acc_out, l.N, l.K, p);
                     o.dc.tail = dense_needs_tail(o.d, o.dc.CH);
+                    o.d.y16 = static_cast<uint16_t *>(l.y16);
                     if (l.conv_out)
                         o.d.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
                     if (l.argmax_idx) {
@@ -1062,6 +1098,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     DenseLin L = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale),
                                             l.x_scale, l.acc_out, l.N, l.K, p);
                     const int li = (int)dl[ki].size();
+                    L.y16 = static_cast<uint16_t *>(l.y16);
                     if (l.conv_out)
                         L.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
                     if (l.argmax_idx) {
@@ -1090,6 +1127,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     o.wc = p.cfg;
                     o.w = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
                     o.wc.tail = w4_needs_tail(o.w, o.wc.B);
+                    o.w.y16 = static_cast<uint16_t *>(l.y16);
                     if (l.conv_out)
                         o.w.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
                     if (l.argmax_idx) {
@@ -1124,6 +1162,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                         return WSG_ERR_UNSUPPORTED;
                     }
                     const int li = (int)wl[wmode].size();
+                    L.y16 = static_cast<uint16_t *>(l.y16);
                     if (l.conv_out)
                         L.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
                     if (l.argmax_idx) {

@@ -113,12 +113,18 @@ template <int KIND, typename Acc>
 __device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row, Acc v) {
     if (L.S > 1) {
         *glob(static_cast<Acc *>(L.part) + (int64_t)s * L.N + row) = v;
-    } else if constexpr (KIND == kF16) {
-        *glob(L.y + row) = v;
     } else {
-        if (L.acc_out)
-            *glob(L.acc_out + row) = v;
-        *glob(L.y + row) = ((float)v * *glob(L.w_scale + row)) * *glob(L.x_scale);
+        float yv;
+        if constexpr (KIND == kF16) {
+            yv = v;
+        } else {
+            if (L.acc_out)
+                *glob(L.acc_out + row) = v;
+            yv = ((float)v * *glob(L.w_scale + row)) * *glob(L.x_scale);
+        }
+        *glob(L.y + row) = yv;
+        if (L.y16)
+            *glob(L.y16 + row) = f16_bits(yv);
     }
 }
 
@@ -295,6 +301,8 @@ __global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
             yv = ((float)a * L.w_scale[n]) * L.x_scale[0];
         }
         L.y[n] = yv;
+        if (L.y16)
+            L.y16[n] = f16_bits(yv);
         best = arg_key(yv, n);
         if (L.conv.out != nullptr)
             conv_step(L.conv, n, yv);
@@ -307,6 +315,12 @@ __global__ __launch_bounds__(kBlock) void zero_f32_kernel(float *p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i < n)
         p[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(kBlock) void zero_u16_kernel(uint16_t *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < n)
+        p[i] = 0;
 }
 
 // The token from the key array: one workgroup of 1024 threads reduces
@@ -515,6 +529,13 @@ hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s) {
     if (n <= 0)
         return hipSuccess;
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_u16(uint16_t *p, int64_t n, hipStream_t s) {
+    if (n <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(zero_u16_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, p, n);
     return hipGetLastError();
 }
 

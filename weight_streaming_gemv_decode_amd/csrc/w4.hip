@@ -184,10 +184,13 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                     v *= sx;
                 const int64_t n = rt * 16 + r16;
                 if (lane < 16 && rt <= last_rt && n < L.N) {
-                    if (L.S > 1)
+                    if (L.S > 1) {
                         *glob(L.part + (int64_t)s * L.N + n) = v;
-                    else
+                    } else {
                         *glob(L.y + n) = v;
+                        if (L.y16)
+                            *glob(L.y16 + n) = f16_bits(v);
+                    }
                 }
                 acc1[r] = 0.0f;
             } else {
@@ -199,10 +202,13 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                     for (int i = 0; i < 4; ++i) {
                         const int m = 4 * g + i;
                         if (m < M) {
-                            if (L.S > 1)
+                            if (L.S > 1) {
                                 *glob(L.part + ((int64_t)s * M + m) * L.N + n) = accm[r][i];
-                            else
+                            } else {
                                 *glob(L.y + (int64_t)m * L.N + n) = accm[r][i];
+                                if (L.y16)
+                                    *glob(L.y16 + (int64_t)m * L.N + n) = f16_bits(accm[r][i]);
+                            }
                         }
                     }
                 }
@@ -461,6 +467,8 @@ __global__ __launch_bounds__(kBlock) void w4_reduce_kernel(W4Lin L) {
         for (int s = 1; s < L.S; ++s)
             a += L.part[(int64_t)s * total + i];
         L.y[i] = a;
+        if (L.y16)
+            L.y16[i] = f16_bits(a);
         m = (int)(i / L.N);
         key = arg_key(a, i - (int64_t)m * L.N);
         if (L.conv.out != nullptr)  // M = 1

@@ -29,6 +29,9 @@ enum W4Mode : int32_t { kA16 = 0, kMfma = 1, kA8 = 2 };
 // element expression (v.y, v.z, ...) lowers to element 0 for every element.
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
+// fp32 -> fp16 bits, round to nearest even (overflow to inf).
+__device__ __forceinline__ uint16_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
 // The value that lane (l ^ stride) holds, for stride = 1, 2, 4, ..., 32, by
 // DPP row operations and the gfx950 lane-swap instructions: plain vector
 // instructions, where a generic shuffle goes through the LDS crossbar and
@@ -125,6 +128,7 @@ struct DenseLin {
     int32_t pad;
     ArgOut arg;            // optional greedy token over y (S = 1: the units; S > 1: the reduce)
     ConvOut conv;          // optional causal-conv1d step over y (same place as y is final)
+    uint16_t *y16;         // optional fp16 copy of y [N] (same place as y is final)
 };
 
 // One int4 linear in the packed tile layout (16 rows x 128 k per 1 KiB tile).
@@ -147,6 +151,7 @@ struct W4Lin {
     int32_t n_tiles;       // ceil(n_rtiles / tile_rtiles)
     ArgOut arg;            // optional greedy token of each output row (S = 1: the units; S > 1: the reduce)
     ConvOut conv;          // optional causal-conv1d step over y (M = 1; where y is final)
+    uint16_t *y16;         // optional fp16 copy of y [M][N] (where y is final)
 };
 
 // One work unit of a grouped launch: linear `lin`, row tile `tile`, k-slice `s`.
@@ -205,6 +210,7 @@ struct ProbeCfg {
 hipError_t launch_read_probe(const u32x4 *buf, int64_t nvec, float *out, int grid, const ProbeCfg &c,
                              hipStream_t s);
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t s);
+hipError_t launch_zero_u16(uint16_t *p, int64_t n, hipStream_t s);
 hipError_t launch_argmax_finish(const ArgOut &a, hipStream_t s);
 hipError_t launch_conv1d_step(const float *x, const ConvOut &cv, int64_t C, hipStream_t s);
 int64_t topk_plan(int64_t N, int k, int64_t *max_keys, int *passes);

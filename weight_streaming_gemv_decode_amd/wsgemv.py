@@ -40,7 +40,7 @@ class wsg_linear(ctypes.Structure):
                 ("group", ctypes.c_int32), ("splits", ctypes.c_int32), ("argmax_idx", ctypes.c_void_p),
                 ("argmax_val", ctypes.c_void_p), ("conv_w", ctypes.c_void_p), ("conv_bias", ctypes.c_void_p),
                 ("conv_state", ctypes.c_void_p), ("conv_out", ctypes.c_void_p), ("conv_width", ctypes.c_int32),
-                ("conv_silu", ctypes.c_int32)]
+                ("conv_silu", ctypes.c_int32), ("y16", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -336,20 +336,23 @@ class Linear:
                  argmax_idx: Optional[torch.Tensor] = None, argmax_val: Optional[torch.Tensor] = None,
                  conv_w: Optional[torch.Tensor] = None, conv_bias: Optional[torch.Tensor] = None,
                  conv_state: Optional[torch.Tensor] = None, conv_out: Optional[torch.Tensor] = None,
-                 conv_silu: bool = False):
+                 conv_silu: bool = False, y16: Optional[torch.Tensor] = None):
         self.kind, self.W, self.x, self.y, self.N, self.K, self.M = kind, W, x, y, N, K, M
         self.scale, self.x_scale, self.acc_out, self.group, self.splits = scale, x_scale, acc_out, group, splits
         self.argmax_idx, self.argmax_val = argmax_idx, argmax_val
         self.conv_w, self.conv_bias, self.conv_state, self.conv_out = conv_w, conv_bias, conv_state, conv_out
         self.conv_width = 0 if conv_w is None else int(conv_w.shape[1])
         self.conv_silu = int(bool(conv_silu))
+        if y16 is not None and (y16.dtype != torch.float16 or y16.numel() < M * N or not y16.is_contiguous()):
+            raise ValueError("y16 must be a contiguous fp16 tensor of at least M*N elements")
+        self.y16 = y16   # optional fp16 copy of y, rounded to nearest even
 
     def c(self) -> wsg_linear:
         p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         return wsg_linear(self.kind, self.M, self.N, self.K, p(self.W), p(self.scale), p(self.x), p(self.x_scale),
                           p(self.y), p(self.acc_out), self.group, self.splits, p(self.argmax_idx),
                           p(self.argmax_val), p(self.conv_w), p(self.conv_bias), p(self.conv_state),
-                          p(self.conv_out), self.conv_width, self.conv_silu)
+                          p(self.conv_out), self.conv_width, self.conv_silu, p(self.y16))
 
 
 class DecodeStep:
