@@ -352,6 +352,19 @@ def main():
                                           "rotation": "9 copies, 36 calls captured in one graph",
                                           "attainable_same_size": attainable(torch, wsgemv, b, s["median_ms"] * 1e3,
                                                                              stream, graph_inner=36)}
+            # the same weights with fp16 activations quantised per token in the kernel
+            xf = torch.from_numpy(synth.f16_normal(4, 3, (K,), synth.X_SIGMA)).to(dev)
+            wsd = wsgemv.workspace(wsgemv.W8A8_DYN, 1, N, K, 0, dev)
+            fn = lambda i: wsgemv.gemv_w8a8_dyn(copies[i % 9], sw, xf, y=y, acc_out=acc, ws=wsd,  # noqa: E731
+                                                stream=stream)
+            s = summary(graph_times(torch, fn, 36, 10, stream))
+            b = N * K + N * 4 + 2 * K + N * 4 + N * 4
+            extras[f"c4_w8a8_dyn_{N}x{K}"] = {"bytes_incl_acc_out": b, "median_us": s["median_ms"] * 1e3,
+                                              "GBps": b / (s["median_ms"] * 1e-3) / 1e9,
+                                              "note": "fp16 x quantised per token inside every work unit",
+                                              "attainable_same_size": attainable(torch, wsgemv, b,
+                                                                                 s["median_ms"] * 1e3, stream,
+                                                                                 graph_inner=36)}
             del copies
 
     def w4_step_extra(kind, M, label):

@@ -63,7 +63,7 @@ enum {
     WSG_ERR_STATE = 8        /* NULL or destroyed plan */
 };
 
-enum { WSG_F16 = 0, WSG_W8A8 = 1, WSG_W4A16 = 2, WSG_W4A8 = 3 }; /* wsg_linear.kind */
+enum { WSG_F16 = 0, WSG_W8A8 = 1, WSG_W4A16 = 2, WSG_W4A8 = 3, WSG_W8A8_DYN = 4 }; /* wsg_linear.kind */
 
 const char *wsg_status_string(wsg_status s);
 int32_t wsg_last_hip_error(void);
@@ -101,6 +101,24 @@ wsg_status gemv_f16(const void *W, const void *x, float *y, int64_t N, int64_t K
 wsg_status gemv_w8a8(const int8_t *Wq, const float *w_scale, const int8_t *xq,
                      const float *x_scale, float *y, int32_t *acc_out, int64_t N, int64_t K,
                      int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream);
+
+/*
+ * int8 weights x fp16 activations quantised per token inside the kernel, M = 1
+ * (vLLM Arm CPU optimisation post, INT8 W8A8 section: the activations are
+ * quantised to 8 bits at run time).  The quantiser is gemv_w4a8's:
+ *   Wq, w_scale  as for gemv_w8a8
+ *   x        fp16 [K], 16-byte aligned, K % 16 == 0
+ *   s_x      = fp32(max_k |x_k|) / 127; xq[k] = clamp(rint(x[k] / s_x), -127, 127)
+ *            (fp32 division, ties to even); max|x| == 0 gives s_x = 0, xq = 0
+ *   acc[n]   = sum_k Wq[n,k] * xq[k], exact int32
+ *   y[n]     = ((float)acc[n] * w_scale[n]) * s_x, fp32
+ *   acc_out  optional int32 [N]; xq_out optional int8 [K] (16-byte aligned);
+ *            sx_out optional fp32 [1].  ws as for gemv_w8a8 (WSG_W8A8_DYN in
+ *            wsg_workspace_bytes).
+ */
+wsg_status gemv_w8a8_dyn(const int8_t *Wq, const float *w_scale, const void *x, float *y,
+                         int32_t *acc_out, int8_t *xq_out, float *sx_out, int64_t N, int64_t K,
+                         int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream);
 
 /*
  * INT4 weights, load-time packing (vLLM Arm CPU optimisation post, dense
@@ -252,15 +270,15 @@ wsg_status causal_conv1d_step(const float *x, const void *w, const float *bias, 
  * thread-safe and one plan's steps must not overlap each other in time.
  */
 typedef struct wsg_linear {
-    int32_t kind;        /* WSG_F16, WSG_W8A8, WSG_W4A16 or WSG_W4A8 */
+    int32_t kind;        /* WSG_F16, WSG_W8A8, WSG_W4A16, WSG_W4A8 or WSG_W8A8_DYN */
     int32_t M;           /* 1; or 1..8 for WSG_W4A16 */
     int64_t N, K;
-    const void *W;       /* F16: fp16 [N,K]; W8A8: int8 [N,K]; W4A16, W4A8: packed Wp */
-    const void *scale;   /* W8A8: fp32 [N]; W4A16, W4A8: packed Sp; F16: NULL */
-    const void *x;       /* F16, W4A16, W4A8: fp16 [M,K]; W8A8: int8 [K] */
-    const float *x_scale;/* W8A8: fp32 [1]; otherwise NULL */
+    const void *W;       /* F16: fp16 [N,K]; W8A8, W8A8_DYN: int8 [N,K]; W4A16, W4A8: packed Wp */
+    const void *scale;   /* W8A8, W8A8_DYN: fp32 [N]; W4A16, W4A8: packed Sp; F16: NULL */
+    const void *x;       /* F16, W4A16, W4A8, W8A8_DYN: fp16 [M,K]; W8A8: int8 [K] */
+    const float *x_scale;/* W8A8: fp32 [1]; otherwise NULL (W8A8_DYN computes it) */
     float *y;            /* fp32 [M,N] */
-    int32_t *acc_out;    /* W8A8: optional int32 [N]; otherwise NULL */
+    int32_t *acc_out;    /* W8A8, W8A8_DYN: optional int32 [N]; otherwise NULL */
     int32_t group;       /* W4A16, W4A8: 128; otherwise 0 */
     int32_t splits;      /* 0 = table's choice; ORDERED mode only */
     int32_t *argmax_idx; /* optional int32 [M]: the greedy token of each output row

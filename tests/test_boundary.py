@@ -260,3 +260,33 @@ def test_y16_validation(L):
     # a W8A8 linear's int8 x is K bytes: 80 bytes from y16 - 64 reach into a.y16
     c = wsgemv.wsg_linear(1, 1, 64, 80, FAKE, FAKE, y16 - 64, FAKE, FAKE + 0x30000, None, 0, 0)
     assert L.wsg_decode_step_create((wsgemv.wsg_linear * 2)(c, a), 2, 1, None, ctypes.byref(out)) == UNSUP
+
+
+def test_w8a8_dyn_validation(L):
+    """int8 weights with fp16 activations quantised in the kernel: every
+    rejection returns before any HIP call."""
+    f = L.gemv_w8a8_dyn
+    args = lambda **kw: [kw.get(k, v) for k, v in (("Wq", FAKE), ("sw", FAKE), ("x", FAKE), ("y", FAKE),  # noqa: E731
+                                                  ("acc", None), ("xq", None), ("sx", None), ("N", 64),
+                                                  ("K", 128), ("S", 0), ("ws", None), ("wsb", 0), ("st", None))]
+    assert f(*args(K=100)) == SHAPE                   # K % 16
+    assert f(*args(N=-1)) == SHAPE
+    assert f(*args(Wq=None)) == NULL
+    assert f(*args(x=None)) == NULL
+    assert f(*args(y=None)) == NULL
+    assert f(*args(sw=None)) == NULL
+    assert f(*args(x=MIS)) == ALIGN
+    assert f(*args(acc=FAKE + 2)) == ALIGN
+    assert f(*args(xq=FAKE + 8)) == ALIGN             # codes are written 16 bytes at a time
+    assert f(*args(sx=FAKE + 2)) == ALIGN
+    assert f(*args(sw=FAKE + 2)) == ALIGN
+    assert f(*args(S=200)) == SHAPE                   # more slices than 16-byte vectors
+    assert f(*args(N=0)) == OK                        # nothing to do
+    assert L.wsg_workspace_bytes(4, 1, 4096, 14336, 2) == 2 * 4096 * 4
+    assert L.wsg_plan_splits(4, 1, 4096, 14336) == L.wsg_plan_splits(1, 1, 4096, 14336)
+    # in a decode step: M = 1 only, and the activation scale is computed, not given
+    out = ctypes.c_void_p()
+    for M, xs, want in ((2, None, UNSUP), (1, FAKE, UNSUP), (1, None, NULL)):
+        lin = wsgemv.wsg_linear(4, M, 64, 128, FAKE, None if want == NULL else FAKE, FAKE, xs, FAKE, None, 0, 0)
+        got = L.wsg_decode_step_create((wsgemv.wsg_linear * 1)(lin), 1, 1, None, ctypes.byref(out))
+        assert got == want, (M, xs, got)

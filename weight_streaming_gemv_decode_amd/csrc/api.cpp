@@ -427,7 +427,7 @@ const char *wsg_build_info(void) { return "wsgemv for gfx950"; }
 int32_t wsg_plan_splits(int32_t kind, int64_t M, int64_t N, int64_t K) {
     if (N <= 0 || K <= 0)
         return 1;
-    if (kind == kF16 || kind == kW8A8) {
+    if (kind == kF16 || kind == kW8A8 || kind == kW8A8D) {
         if (K % elem_per_vec(kind))
             return 1;
         return plan_dense(kind, N, K, 0).S;
@@ -452,7 +452,7 @@ size_t wsg_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K, int32_
     }
     if (N <= 0 || K <= 0 || splits < 0)
         return 0;
-    if (kind == kF16 || kind == kW8A8) {
+    if (kind == kF16 || kind == kW8A8 || kind == kW8A8D) {
         if (K % elem_per_vec(kind))
             return 0;
         return dense_ws_bytes(plan_dense(kind, N, K, splits), N);
@@ -628,6 +628,42 @@ wsg_status gemv_w8a8(const int8_t *Wq, const float *w_scale, const int8_t *xq, c
         DenseLin L = make_dense(kW8A8, Wq, xq, y, ws, w_scale, x_scale, acc_out, N, K, p);
         p.cfg.tail = dense_needs_tail(L, p.cfg.CH);
         return enqueue_dense(kW8A8, L, p.cfg, s);
+    });
+}
+
+wsg_status gemv_w8a8_dyn(const int8_t *Wq, const float *w_scale, const void *x, float *y, int32_t *acc_out,
+                         int8_t *xq_out, float *sx_out, int64_t N, int64_t K, int32_t splits, void *ws,
+                         size_t ws_bytes, wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_dense_args(kW8A8D, Wq, x, y, N, K, splits);
+        if (st != WSG_OK)
+            return st;
+        if ((acc_out && !aligned(acc_out, 4)) || (xq_out && !aligned(xq_out, 16)) || (sx_out && !aligned(sx_out, 4)))
+            return WSG_ERR_ALIGN;
+        if (N == 0)
+            return WSG_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (K == 0) {  // the empty sum, and s_x = max of nothing / 127 = 0
+            hipError_t e = launch_zero_f32(y, N, s);
+            if (e == hipSuccess && acc_out)
+                e = launch_zero_f32(reinterpret_cast<float *>(acc_out), N, s);
+            if (e == hipSuccess && sx_out)
+                e = launch_zero_f32(sx_out, 1, s);
+            return e == hipSuccess ? WSG_OK : hip_fail(e);
+        }
+        if (!w_scale)
+            return WSG_ERR_NULL;
+        if (!aligned(w_scale, 4))
+            return WSG_ERR_ALIGN;
+        DensePlan p = plan_dense(kW8A8D, N, K, splits);
+        st = check_ws(ws, ws_bytes, dense_ws_bytes(p, N));
+        if (st != WSG_OK)
+            return st;
+        DenseLin L = make_dense(kW8A8D, Wq, x, y, ws, w_scale, nullptr, acc_out, N, K, p);
+        L.xq_out = xq_out;
+        L.sx_out = sx_out;
+        p.cfg.tail = dense_needs_tail(L, p.cfg.CH);
+        return enqueue_dense(kW8A8D, L, p.cfg, s);
     });
 }
 
@@ -840,14 +876,14 @@ wsg_status validate_linear(const wsg_linear &l) {
     if (l.y16 && !aligned(l.y16, 2))
         return WSG_ERR_ALIGN;
     if (l.conv_out || l.conv_w || l.conv_state || l.conv_bias || l.conv_width) {
-        if (l.kind < kF16 || l.kind > kW4A8 || l.M != 1)
+        if (l.kind < kF16 || l.kind > kW8A8D || l.M != 1)
             return WSG_ERR_UNSUPPORTED;
         wsg_status st = check_conv(l.N, l.conv_width, l.conv_w, l.conv_bias, l.conv_state, l.conv_out);
         if (st != WSG_OK)
             return st;
     }
     if (l.argmax_idx || l.argmax_val) {
-        if (l.kind != kF16 && l.kind != kW8A8 && l.kind != kW4A16 && l.kind != kW4A8)
+        if (l.kind < kF16 || l.kind > kW8A8D)
             return WSG_ERR_UNSUPPORTED;
         wsg_status st = check_token_args(l.N, l.argmax_idx, l.argmax_val);
         if (st != WSG_OK)
@@ -868,6 +904,20 @@ wsg_status validate_linear(const wsg_linear &l) {
         if (!l.scale || !l.x_scale)
             return WSG_ERR_NULL;
         if (!aligned(l.scale, 4) || !aligned(l.x_scale, 4) || (l.acc_out && !aligned(l.acc_out, 4)))
+            return WSG_ERR_ALIGN;
+        return WSG_OK;
+    }
+    case kW8A8D: {
+        if (l.M != 1)
+            return WSG_ERR_UNSUPPORTED;
+        wsg_status st = check_dense_args(kW8A8D, l.W, l.x, l.y, l.N, l.K, l.splits);
+        if (st != WSG_OK || l.N == 0 || l.K == 0)
+            return st;
+        if (l.x_scale)
+            return WSG_ERR_UNSUPPORTED;  // the activation scale is computed, not given
+        if (!l.scale)
+            return WSG_ERR_NULL;
+        if (!aligned(l.scale, 4) || (l.acc_out && !aligned(l.acc_out, 4)))
             return WSG_ERR_ALIGN;
         return WSG_OK;
     }
@@ -978,10 +1028,10 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         st->use_graph = !(mode & WSG_STEP_EAGER);
 
         // Host-side plan: ops, plus the byte layout of the device block.
-        std::vector<DenseLin> dl[2];           // grouped dense linears per kind (F16, W8A8)
-        std::vector<Unit> du[2];
-        int dlds[2] = {0, 0};
-        bool dtail[2] = {false, false};
+        std::vector<DenseLin> dl[3];           // grouped dense linears per kind (F16, W8A8, W8A8D)
+        std::vector<Unit> du[3];
+        int dlds[3] = {0, 0, 0};
+        bool dtail[3] = {false, false, false};
         std::vector<W4Lin> wl[3];              // grouped int4 linears per kernel mode (kA16, kMfma, kA8)
         std::vector<Unit> wu[3];
         int wlds[3] = {0, 0, 0};
@@ -1022,7 +1072,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                 z.zero_p = l.y;
                 z.zero_n = (int64_t)l.M * l.N;
                 st->ops.push_back(z);
-                if (l.kind == kW8A8 && l.acc_out) {
+                if ((l.kind == kW8A8 || l.kind == kW8A8D) && l.acc_out) {
                     z.zero_p = reinterpret_cast<float *>(l.acc_out);
                     z.zero_n = l.N;
                     st->ops.push_back(z);
@@ -1054,8 +1104,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                 }
                 continue;
             }
-            if (l.kind == kF16 || l.kind == kW8A8) {
-                const int ki = l.kind == kF16 ? 0 : 1;
+            if (l.kind == kF16 || l.kind == kW8A8 || l.kind == kW8A8D) {
+                const int ki = l.kind == kF16 ? 0 : (l.kind == kW8A8 ? 1 : 2);
                 if (base_mode == WSG_STEP_ORDERED) {
                     DensePlan p = plan_dense(l.kind, l.N, l.K, l.splits);
                     part_bytes = std::max(part_bytes, dense_ws_bytes(p, l.N));
@@ -1190,8 +1240,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         off = align_up(off + keys_bytes, 256);
         const size_t part_off = off;
         off = align_up(off + part_bytes, 256);
-        size_t dl_off[2], du_off[2], wl_off[3], wu_off[3];
-        for (int k = 0; k < 2; ++k) {
+        size_t dl_off[3], du_off[3], wl_off[3], wu_off[3];
+        for (int k = 0; k < 3; ++k) {
             dl_off[k] = off;
             off = align_up(off + dl[k].size() * sizeof(DenseLin), 256);
             du_off[k] = off;
@@ -1234,7 +1284,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             if (bytes)
                 std::memcpy(host.data() + o, src, bytes);
         };
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < 3; ++k) {
             put(dl_off[k], dl[k].data(), dl[k].size() * sizeof(DenseLin));
             put(du_off[k], du[k].data(), du[k].size() * sizeof(Unit));
         }
@@ -1249,11 +1299,11 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             if (op.type == wsg_step::Op::kW4 && op.w.S > 1)
                 op.w.part = reinterpret_cast<float *>(base + part_off);
         }
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < 3; ++k) {
             if (!du[k].empty()) {
                 wsg_step::Op o{};
                 o.type = wsg_step::Op::kDenseGroup;
-                o.kind = k == 0 ? kF16 : kW8A8;
+                o.kind = k == 0 ? kF16 : (k == 1 ? kW8A8 : kW8A8D);
                 o.dc = gcfg;
                 o.dc.tail = dtail[k];
                 o.lins = base + dl_off[k];

@@ -64,6 +64,75 @@ struct DenseOps<kW8A8> {
     }
 };
 
+template <>
+struct DenseOps<kW8A8D> : DenseOps<kW8A8> {};
+
+// Per-token activation scale of fp16 x [nvec8 16-byte vectors]: s_x =
+// max|x| / 127 in fp32, over the whole vector, by the whole workgroup (the
+// same reading as the int4 W4A8 kernel: vLLM Arm CPU optimisation post,
+// INT8 sections).  A maximum is order-free, so every workgroup that
+// computes it gets the same bits.  Contains barriers.
+__device__ __forceinline__ float dyn_scale(const u32x4 *x, int64_t nvec8) {
+    __shared__ float red[kWavesPerBlock];
+    float amax = 0.0f;
+    constexpr int U = 4;  // loads in flight per thread
+    for (int64_t v0 = threadIdx.x; v0 < nvec8; v0 += (int64_t)kBlock * U) {
+        u32x4 h[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + (int64_t)u * kBlock;
+            h[u] = v < nvec8 ? *glob(x + v) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t hw[4] = {h[u].x, h[u].y, h[u].z, h[u].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f16x2 p = as_h2(hw[j]);
+                amax = fmaxf(amax, fmaxf(fabsf((float)p[0]), fabsf((float)p[1])));
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+        amax = fmaxf(amax, xor_lane(amax, 32 >> i));
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        red[threadIdx.x / kWave] = amax;
+    __syncthreads();
+    amax = red[0];
+#pragma unroll
+    for (int w = 1; w < kWavesPerBlock; ++w)
+        amax = fmaxf(amax, red[w]);
+    __syncthreads();  // red[] may be rewritten by the next call
+    return amax / 127.0f;
+}
+
+// The 16 int8 codes of fp16 x[16 v .. 16 v + 15] (vectors 2 v and 2 v + 1):
+// clamp(rint(x / s_x), -127, 127) with IEEE fp32 division, ties to even; all
+// zero when s_x = 0.  Byte b of the result is the code of element 16 v + b.
+__device__ __forceinline__ u32x4 quantize16(const u32x4 *x, int64_t v, float sx) {
+    uint32_t out[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const u32x4 q = *glob(x + 2 * v + h);
+        const uint32_t hw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f16x2 p = as_h2(hw[j + t / 2]);
+                float r = 0.0f;
+                if (sx != 0.0f)
+                    r = fminf(fmaxf(rintf((float)p[t & 1] / sx), -127.0f), 127.0f);
+                word |= ((uint32_t)(int)r & 255u) << (8 * t);
+            }
+            out[2 * h + j / 2] = word;
+        }
+    }
+    return u32x4{out[0], out[1], out[2], out[3]};
+}
+
 // Sum R per-lane values over the 64 lanes of a wave.  Stage o (o = 32, 16,
 // ...) pairs lane l with l^o: the lane with bit o set keeps the upper half
 // of its remaining values and receives its partner's upper half, the other
@@ -108,9 +177,10 @@ __device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
     return s;
 }
 
-// Writes row `row`: y (S = 1) or its partial of slice s (S > 1).
+// Writes row `row`: y (S = 1) or its partial of slice s (S > 1).  sx is the
+// activation scale of the dynamically quantised kind.
 template <int KIND, typename Acc>
-__device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row, Acc v) {
+__device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row, Acc v, float sx) {
     if (L.S > 1) {
         *glob(static_cast<Acc *>(L.part) + (int64_t)s * L.N + row) = v;
     } else {
@@ -120,7 +190,7 @@ __device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row,
         } else {
             if (L.acc_out)
                 *glob(L.acc_out + row) = v;
-            yv = ((float)v * *glob(L.w_scale + row)) * *glob(L.x_scale);
+            yv = ((float)v * *glob(L.w_scale + row)) * (KIND == kW8A8D ? sx : *glob(L.x_scale));
         }
         *glob(L.y + row) = yv;
         if (L.y16)
@@ -171,6 +241,7 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
 #pragma unroll
     for (int r = 0; r < R; ++r)
         acc[r] = 0;
+    float sx = 0.0f;  // kW8A8D: the activation scale
 
     auto consume = [&](const u32x4(&buf)[R][CH], int gi, int c) {
         u32x4 xv[CH];
@@ -188,7 +259,7 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
             if ((lane & (span - 1)) == 0) {
                 const int64_t row = row0 + (int64_t)(wave + gi * kWavesPerBlock) * R + lane / span;
                 if (row <= last_row) {
-                    store_row<KIND>(L, s, row, v);
+                    store_row<KIND>(L, s, row, v, sx);
                 }
             }
 #pragma unroll
@@ -202,9 +273,27 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
     if (nsteps > 0)
         load_step(bufA, 0, 0);
 
-    const u32x4 *xg = L.x + kv0;
-    for (int i = tid; i < nchunk * CHUNK; i += kBlock)
-        xs[i] = i < nv ? *glob(xg + i) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (KIND == kW8A8D) {
+        // fp16 x quantised per token: the scale over the whole row, then the
+        // codes of this slice into LDS (and to xq_out from the first row tile)
+        sx = dyn_scale(L.x, (int64_t)L.kvec * 2);
+        const bool write_codes = L.xq_out != nullptr && tile == 0;
+        for (int i = tid; i < nchunk * CHUNK; i += kBlock) {
+            u32x4 q = u32x4{0u, 0u, 0u, 0u};
+            if (i < nv) {
+                q = quantize16(L.x, kv0 + i, sx);
+                if (write_codes)
+                    *glob(reinterpret_cast<u32x4 *>(L.xq_out) + kv0 + i) = q;
+            }
+            xs[i] = q;
+        }
+        if (L.sx_out != nullptr && tile == 0 && s == 0 && tid == 0)
+            *glob(L.sx_out) = sx;
+    } else {
+        const u32x4 *xg = L.x + kv0;
+        for (int i = tid; i < nchunk * CHUNK; i += kBlock)
+            xs[i] = i < nv ? *glob(xg + i) : u32x4{0u, 0u, 0u, 0u};
+    }
     __syncthreads();
 
     if (nsteps == 0)
@@ -283,6 +372,9 @@ template <int KIND>
 __global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
     const int64_t n = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     unsigned long long best = 0;
+    float sx = 0.0f;
+    if constexpr (KIND == kW8A8D)
+        sx = dyn_scale(L.x, (int64_t)L.kvec * 2);  // the same bits as the units computed
     if (n < L.N) {
         float yv;
         if constexpr (KIND == kF16) {
@@ -298,7 +390,7 @@ __global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
                 a += p[(int64_t)s * L.N + n];
             if (L.acc_out)
                 L.acc_out[n] = a;
-            yv = ((float)a * L.w_scale[n]) * L.x_scale[0];
+            yv = ((float)a * L.w_scale[n]) * (KIND == kW8A8D ? sx : L.x_scale[0]);
         }
         L.y[n] = yv;
         if (L.y16)
@@ -483,6 +575,8 @@ hipError_t launch_dense(int kind, const DenseLin &L, const DenseCfg &c, hipStrea
         return single_kind<kF16>(L, c, s);
     if (kind == kW8A8)
         return single_kind<kW8A8>(L, c, s);
+    if (kind == kW8A8D)
+        return single_kind<kW8A8D>(L, c, s);
     return hipErrorInvalidValue;
 }
 
@@ -492,6 +586,8 @@ hipError_t launch_dense_grouped(int kind, const DenseLin *lins, const Unit *unit
         return group_kind<kF16>(lins, units, n_units, lds_bytes, c, s);
     if (kind == kW8A8)
         return group_kind<kW8A8>(lins, units, n_units, lds_bytes, c, s);
+    if (kind == kW8A8D)
+        return group_kind<kW8A8D>(lins, units, n_units, lds_bytes, c, s);
     return hipErrorInvalidValue;
 }
 
@@ -501,6 +597,8 @@ hipError_t launch_dense_reduce(int kind, const DenseLin &L, hipStream_t s) {
     const int grid = dense_reduce_blocks(L.N);
     if (kind == kF16)
         hipLaunchKernelGGL(dense_reduce_kernel<kF16>, dim3(grid), dim3(kBlock), 0, s, L);
+    else if (kind == kW8A8D)
+        hipLaunchKernelGGL(dense_reduce_kernel<kW8A8D>, dim3(grid), dim3(kBlock), 0, s, L);
     else
         hipLaunchKernelGGL(dense_reduce_kernel<kW8A8>, dim3(grid), dim3(kBlock), 0, s, L);
     return hipGetLastError();

@@ -18,7 +18,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum Kind : int32_t { kF16 = 0, kW8A8 = 1, kW4A16 = 2, kW4A8 = 3 };
+enum Kind : int32_t { kF16 = 0, kW8A8 = 1, kW4A16 = 2, kW4A8 = 3, kW8A8D = 4 };
 
 // int4-weight kernel modes: fp16 activations on the VALU (M = 1), fp16
 // activations on MFMA (M = 2..8), int8 activations quantised in-kernel (M = 1).
@@ -129,6 +129,8 @@ struct DenseLin {
     ArgOut arg;            // optional greedy token over y (S = 1: the units; S > 1: the reduce)
     ConvOut conv;          // optional causal-conv1d step over y (same place as y is final)
     uint16_t *y16;         // optional fp16 copy of y [N] (same place as y is final)
+    int8_t *xq_out;        // kW8A8D: optional int8 codes [K] (written by the first row tile)
+    float *sx_out;         // kW8A8D: optional activation scale [1]
 };
 
 // One int4 linear in the packed tile layout (16 rows x 128 k per 1 KiB tile).

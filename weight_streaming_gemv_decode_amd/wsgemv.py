@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwsgemv.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "wsgemv.h")
 
-F16, W8A8, W4A16, W4A8 = 0, 1, 2, 3
+F16, W8A8, W4A16, W4A8, W8A8_DYN = 0, 1, 2, 3, 4
 ARGMAX_WS_BYTES, WITH_ARGMAX, TOPK_MAX = 8192, 0x100, 64
 STEP_ORDERED, STEP_GROUPED, STEP_EAGER, STEP_FORCE_GRAPH = 0, 1, 0x100, 0x200
 STEP_GRAPH_MIN_LAUNCHES = 8
@@ -61,6 +61,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "wsg_pack_w4": ([P, P, P, P, I64, I64, I64, P], I32),
         "gemv_w4a16": ([P, P, P, P, I64, I64, I64, I64, I32, P, SZ, P], I32),
         "gemv_w4a8": ([P, P, P, P, P, P, I64, I64, I64, I32, P, SZ, P], I32),
+        "gemv_w8a8_dyn": ([P, P, P, P, P, P, P, I64, I64, I32, P, SZ, P], I32),
         "wsg_argmax_f32": ([P, I64, P, P, P, SZ, P], I32),
         "gemv_f16_argmax": ([P, P, P, P, P, I64, I64, I32, P, SZ, P], I32),
         "causal_conv1d_step": ([P, P, P, P, P, I64, I32, I32, P], I32),
@@ -248,6 +249,27 @@ def gemv_w8a8(Wq: torch.Tensor, w_scale: torch.Tensor, xq: torch.Tensor, x_scale
                            _dev(y, torch.float32, "y", (N,)), acc_p, N, K, splits, wp, wn, _stream(stream)),
            "gemv_w8a8")
     return y, acc_out
+
+
+def gemv_w8a8_dyn(Wq: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                  acc_out: Optional[torch.Tensor] = None, xq_out: Optional[torch.Tensor] = None,
+                  sx_out: Optional[torch.Tensor] = None, splits: int = 0, ws: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """y = acc * w_scale[n] * s_x with x fp16 [K] quantised per token in the
+    kernel (s_x = max|x| / 127, xq = clamp(rint(x / s_x), +-127)); acc int32."""
+    N, K = Wq.shape
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=Wq.device)
+    if ws is None:
+        ws = workspace(W8A8_DYN, 1, N, K, splits, Wq.device)
+    wp, wn = _ws(ws)
+    opt = lambda t, dt, name, shape: _dev(t, dt, name, shape) if t is not None else None  # noqa: E731
+    _check(lib().gemv_w8a8_dyn(_dev(Wq, torch.int8, "Wq"), _dev(w_scale, torch.float32, "w_scale", (N,)),
+                               _dev(x, torch.float16, "x", (K,)), _dev(y, torch.float32, "y", (N,)),
+                               opt(acc_out, torch.int32, "acc_out", (N,)), opt(xq_out, torch.int8, "xq_out", (K,)),
+                               opt(sx_out, torch.float32, "sx_out", (1,)), N, K, splits, wp, wn, _stream(stream)),
+           "gemv_w8a8_dyn")
+    return y
 
 
 def packed_w4_bytes(N: int, K: int, group: int = 128) -> Tuple[int, int]:
