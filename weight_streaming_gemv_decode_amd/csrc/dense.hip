@@ -1,6 +1,7 @@
 // Row-major weight streaming for M = 1: fp16 weights (fp32 accumulate via
-// v_dot2_f32_f16) and int8 weights x int8 activations (exact int32 via
-// v_dot4_i32_i8), the on-device split-K reduce, and the HBM read probe.
+// v_dot2_f32_f16), int8 weights x int8 activations (exact int32 via
+// v_dot4_i32_i8), the same with fp16 activations quantised per token in the
+// kernel, the on-device split-K reduce, and the HBM read probe.
 //
 // The product is the decode-step vector-matrix product of the MiniCPM-V 4.6
 // on Orange Pi AIPro (Ascend 310B) post (baseline paragraph: M = 1; closing
@@ -19,8 +20,9 @@
 // loads in flight.  The activation slice is staged once per unit in LDS
 // (read with ds_read_b128, shared by the R rows of a step).  Row sums are
 // reduced across the wave with a halving exchange (R values per lane become
-// one row per 64/R lanes in log2(64) shuffle stages), then written as y, or
-// as a partial that a second small kernel adds in slice order.
+// one row per 64/R lanes in log2(64) lane-exchange stages), then written as
+// y (and its fp16 copy), or as a partial that a second small kernel adds in
+// slice order.
 #include "argmax.hpp"
 #include "conv1d.hpp"
 
