@@ -74,27 +74,20 @@ struct DenseOps<kW8A8D> : DenseOps<kW8A8> {};
 // same reading as the int4 W4A8 kernel: vLLM Arm CPU optimisation post,
 // INT8 sections).  A maximum is order-free, so every workgroup that
 // computes it gets the same bits.  Contains barriers.
-__device__ __forceinline__ float dyn_scale(const u32x4 *x, int64_t nvec8) {
-    __shared__ float red[kWavesPerBlock];
-    float amax = 0.0f;
-    constexpr int U = 4;  // loads in flight per thread
-    for (int64_t v0 = threadIdx.x; v0 < nvec8; v0 += (int64_t)kBlock * U) {
-        u32x4 h[U];
+// The largest |value| of 8 fp16 values.
+__device__ __forceinline__ float absmax8(u32x4 h, float amax) {
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t v = v0 + (int64_t)u * kBlock;
-            h[u] = v < nvec8 ? *glob(x + v) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t hw[4] = {h[u].x, h[u].y, h[u].z, h[u].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f16x2 p = as_h2(hw[j]);
-                amax = fmaxf(amax, fmaxf(fabsf((float)p[0]), fabsf((float)p[1])));
-            }
-        }
+    for (int j = 0; j < 4; ++j) {
+        const f16x2 p = as_h2(hw[j]);
+        amax = fmaxf(amax, fmaxf(fabsf((float)p[0]), fabsf((float)p[1])));
     }
+    return amax;
+}
+
+// Maximum over the workgroup (contains barriers).
+__device__ __forceinline__ float block_max_f32(float amax) {
+    __shared__ float red[kWavesPerBlock];
 #pragma unroll
     for (int i = 0; i < 6; ++i)
         amax = fmaxf(amax, xor_lane(amax, 32 >> i));
@@ -106,17 +99,34 @@ __device__ __forceinline__ float dyn_scale(const u32x4 *x, int64_t nvec8) {
     for (int w = 1; w < kWavesPerBlock; ++w)
         amax = fmaxf(amax, red[w]);
     __syncthreads();  // red[] may be rewritten by the next call
-    return amax / 127.0f;
+    return amax;
 }
 
-// The 16 int8 codes of fp16 x[16 v .. 16 v + 15] (vectors 2 v and 2 v + 1):
+__device__ __forceinline__ float dyn_scale(const u32x4 *x, int64_t nvec8) {
+    float amax = 0.0f;
+    constexpr int U = 4;  // loads in flight per thread
+    for (int64_t v0 = threadIdx.x; v0 < nvec8; v0 += (int64_t)kBlock * U) {
+        u32x4 h[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + (int64_t)u * kBlock;
+            h[u] = v < nvec8 ? *glob(x + v) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            amax = absmax8(h[u], amax);
+    }
+    return block_max_f32(amax) / 127.0f;
+}
+
+// The 16 int8 codes of 16 fp16 values (lo: the first 8, hi: the next 8):
 // clamp(rint(x / s_x), -127, 127) with IEEE fp32 division, ties to even; all
 // zero when s_x = 0.  Byte b of the result is the code of element 16 v + b.
-__device__ __forceinline__ u32x4 quantize16(const u32x4 *x, int64_t v, float sx) {
+__device__ __forceinline__ u32x4 quantize16(u32x4 lo, u32x4 hi, float sx) {
     uint32_t out[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const u32x4 q = *glob(x + 2 * v + h);
+        const u32x4 q = h == 0 ? lo : hi;
         const uint32_t hw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {
@@ -278,16 +288,42 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
     if constexpr (KIND == kW8A8D) {
         // fp16 x quantised per token: the scale over the whole row, then the
         // codes of this slice into LDS (and to xq_out from the first row tile)
-        sx = dyn_scale(L.x, (int64_t)L.kvec * 2);
         const bool write_codes = L.xq_out != nullptr && tile == 0;
-        for (int i = tid; i < nchunk * CHUNK; i += kBlock) {
-            u32x4 q = u32x4{0u, 0u, 0u, 0u};
-            if (i < nv) {
-                q = quantize16(L.x, kv0 + i, sx);
-                if (write_codes)
-                    *glob(reinterpret_cast<u32x4 *>(L.xq_out) + kv0 + i) = q;
+        auto put = [&](int i, u32x4 q) {  // code vector i of the row
+            xs[i - kv0] = q;
+            if (write_codes)
+                *glob(reinterpret_cast<u32x4 *>(L.xq_out) + i) = q;
+        };
+        for (int i = nv + tid; i < nchunk * CHUNK; i += kBlock)
+            xs[i] = u32x4{0u, 0u, 0u, 0u};
+        constexpr int kHold = 4;  // code vectors per thread kept in registers
+        if (L.kvec <= kHold * kBlock) {
+            // one pass over x: each thread keeps its fp16 values for the codes
+            u32x4 h[kHold][2];
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kHold; ++j) {
+                const int i = tid + j * kBlock;
+                h[j][0] = h[j][1] = u32x4{0u, 0u, 0u, 0u};
+                if (i < L.kvec) {
+                    h[j][0] = *glob(L.x + 2 * i);
+                    h[j][1] = *glob(L.x + 2 * i + 1);
+                }
             }
-            xs[i] = q;
+#pragma unroll
+            for (int j = 0; j < kHold; ++j)
+                amax = absmax8(h[j][1], absmax8(h[j][0], amax));
+            sx = block_max_f32(amax) / 127.0f;
+#pragma unroll
+            for (int j = 0; j < kHold; ++j) {
+                const int i = tid + j * kBlock;
+                if (i >= kv0 && i < kv0 + nv)
+                    put(i, quantize16(h[j][0], h[j][1], sx));
+            }
+        } else {
+            sx = dyn_scale(L.x, (int64_t)L.kvec * 2);
+            for (int i = kv0 + tid; i < kv0 + nv; i += kBlock)
+                put(i, quantize16(*glob(L.x + 2 * i), *glob(L.x + 2 * i + 1), sx));
         }
         if (L.sx_out != nullptr && tile == 0 && s == 0 && tid == 0)
             *glob(L.sx_out) = sx;
