@@ -294,7 +294,77 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             finish_group(gi);
     };
 
+    // Steps are (row group gi, step c) in order, c fastest; a is the step
+    // in bufA.
+    int ga = 0, ca = 0;
+    auto next = [&](int &gg, int &cc) {
+        if (++cc == nquad) {
+            cc = 0;
+            ++gg;
+        }
+    };
     Buf bufA, bufB;
+
+    if constexpr (MFMA) {
+        // Verify blocks stage M rows of activations per unit.  Their first
+        // vectors are loaded into registers ahead of both weight steps:
+        // vector-memory loads retire in issue order, so writing them to LDS
+        // then waits for them alone, with both steps in flight across the
+        // barrier (M = 4: 71 vs 74 us per decode step, M = 8: 76 vs 81 us,
+        // on MI355X).  The M = 1 kernels keep the order below: holding these
+        // registers with both steps costs them a wave per SIMD, and they
+        // measured slower.
+        constexpr int kXHold = 4;
+        const int64_t xrow = (int64_t)L.K / 8;
+        const int nx = M * nxv;
+        auto xsrc = [&](int i) {
+            const int m = i / nxv, v = i - m * nxv;
+            return glob(L.x + m * xrow + (int64_t)kb0 * 16 + v);
+        };
+        u32x4 xh[kXHold];
+#pragma unroll
+        for (int j = 0; j < kXHold; ++j) {
+            const int i = tid + j * kBlock;
+            if (i < nx)
+                xh[j] = *xsrc(i);
+        }
+        int gb = 0, cb = 0;
+        next(gb, cb);
+        if (nsteps > 0)
+            load_step(bufA, 0, 0);
+        if (nsteps > 1)
+            load_step(bufB, gb, cb);
+#pragma unroll
+        for (int j = 0; j < kXHold; ++j) {
+            const int i = tid + j * kBlock;
+            if (i < nx)
+                xs[i] = xh[j];
+        }
+        for (int i = tid + kXHold * kBlock; i < nx; i += kBlock)
+            xs[i] = *xsrc(i);
+        __syncthreads();
+        // a buffer is refilled with the step after next once it is consumed
+        for (int st = 0; st < nsteps; st += 2) {
+            consume(bufA, ga, ca);
+            if (st + 2 < nsteps) {
+                next(ga, ca);
+                next(ga, ca);
+                load_step(bufA, ga, ca);
+            }
+            if (st + 1 >= nsteps)
+                break;
+            consume(bufB, gb, cb);
+            if (st + 3 < nsteps) {
+                next(gb, cb);
+                next(gb, cb);
+                load_step(bufB, gb, cb);
+            }
+        }
+        return;
+    }
+
+    // M = 1: the first weight step goes out before the activation staging
+    // and its barrier, the second behind the barrier.
     if (nsteps > 0)
         load_step(bufA, 0, 0);
 
@@ -366,24 +436,14 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             *glob(L.sx_out) = sx;
         __syncthreads();
     } else {
-        // Stage the activation slice of every row m < M: xs[m * nxv + v].
-        const int64_t xrow = (int64_t)L.K / 8;
-        for (int i = tid; i < M * nxv; i += kBlock) {
-            const int m = i / nxv, v = i - m * nxv;
-            xs[i] = *glob(L.x + m * xrow + (int64_t)kb0 * 16 + v);
-        }
+        // Stage the activation slice: xs[v].
+        for (int i = tid; i < nxv; i += kBlock)
+            xs[i] = *glob(L.x + (int64_t)kb0 * 16 + i);
         __syncthreads();
     }
 
     if (nsteps == 0)
         return;
-    int ga = 0, ca = 0;
-    auto next = [&](int &gg, int &cc) {
-        if (++cc == nquad) {
-            cc = 0;
-            ++gg;
-        }
-    };
     int st = 0;
     while (st + 2 < nsteps) {
         int gb = ga, cb = ca;
