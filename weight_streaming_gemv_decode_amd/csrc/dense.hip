@@ -288,8 +288,8 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
     // the plain kinds): the slice's first vectors are loaded into registers
     // ahead of both weight steps, so the staging waits for them alone and
     // both steps are in flight across the barrier.  Measured on MI355X, early
-    // makes the 2- and 4-row shapes faster (2048x2048: 3.6 vs 3.9 us; int8
-    // 14336x4096: 10.8 vs 10.9 us) and the 8-row shapes of the decode step
+    // makes the 2-row shapes faster (int8 4096x14336: 10.8 vs 11.4 us;
+    // 2048x2048: 3.6-3.9 vs 3.9 us) and the 8-row shapes of the decode step
     // and the lm_head about 2% slower.
     constexpr bool kEarly = KIND != kW8A8D && R * CH <= 4;
     // Steps are (row group gi, chunk c) in order; a is the step in bufA.

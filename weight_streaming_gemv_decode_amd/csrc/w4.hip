@@ -310,8 +310,8 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
         // vectors are loaded into registers ahead of both weight steps:
         // vector-memory loads retire in issue order, so writing them to LDS
         // then waits for them alone, with both steps in flight across the
-        // barrier (M = 4: 71 vs 74 us per decode step, M = 8: 76 vs 81 us,
-        // on MI355X).  The M = 1 kernels keep the order below: holding these
+        // barrier (decode step on MI355X, M = 4: 71-74 vs 74-75 us; M = 8:
+        // 75-79 vs 81-82 us).  The M = 1 kernels keep the order below: holding these
         // registers with both steps costs them a wave per SIMD, and they
         // measured slower.
         constexpr int kXHold = 4;
