@@ -288,9 +288,11 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
     // the plain kinds): the slice's first vectors are loaded into registers
     // ahead of both weight steps, so the staging waits for them alone and
     // both steps are in flight across the barrier.  Measured on MI355X, early
-    // makes the 2-row shapes faster (int8 4096x14336: 10.8 vs 11.4 us;
-    // 2048x2048: 3.6-3.9 vs 3.9 us) and the 8-row shapes of the decode step
-    // and the lm_head about 2% slower.
+    // makes the 2-row shapes faster when a row takes two or more steps (int8
+    // 4096x14336: 10.8 vs 11.4 us; 2048x2048: 3.6-3.9 vs 3.9 us), and
+    // slower where it does not (the dependent decode chain, whose linears
+    // mostly take one step per row: 484 vs 469 us) and for the 8-row shapes
+    // of the decode step and the lm_head (about 2%).
     constexpr bool kEarly = KIND != kW8A8D && R * CH <= 4;
     // Steps are (row group gi, chunk c) in order; a is the step in bufA.
     int ga = 0, ca = 0;
@@ -302,7 +304,7 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
     };
     u32x4 bufA[R][CH], bufB[R][CH];
 
-    if constexpr (kEarly) {
+    if (kEarly && nchunk >= 2) {
         constexpr int kXHold = 4;  // activation vectors per thread loaded ahead
         const u32x4 *xg = L.x + kv0;
         const int nx = nchunk * CHUNK;
