@@ -120,27 +120,21 @@ __device__ __forceinline__ float dyn_scale(const u32x4 *x, int64_t nvec8) {
 }
 
 // The 16 int8 codes of 16 fp16 values (lo: the first 8, hi: the next 8):
-// clamp(rint(x / s_x), -127, 127) with IEEE fp32 division, ties to even; all
-// zero when s_x = 0.  Byte b of the result is the code of element 16 v + b.
-__device__ __forceinline__ u32x4 quantize16(u32x4 lo, u32x4 hi, float sx) {
+// clamp(rint(x / s_x), -127, 127) with IEEE fp32 division, ties to even
+// (int8_codes; rsx = fp32(1 / s_x)); all zero when s_x = 0.  Byte b of the
+// result is the code of element 16 v + b.
+__device__ __forceinline__ u32x4 quantize16(u32x4 lo, u32x4 hi, float sx, float rsx) {
+    const uint32_t hw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     uint32_t out[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const u32x4 q = h == 0 ? lo : hi;
-        const uint32_t hw[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const f16x2 p = as_h2(hw[j + t / 2]);
-                float r = 0.0f;
-                if (sx != 0.0f)
-                    r = fminf(fmaxf(rintf((float)p[t & 1] / sx), -127.0f), 127.0f);
-                word |= ((uint32_t)(int)r & 255u) << (8 * t);
-            }
-            out[2 * h + j / 2] = word;
-        }
+    for (int w = 0; w < 4; ++w) {  // four codes per output word keep few registers live
+        const f16x2 p0 = as_h2(hw[2 * w]), p1 = as_h2(hw[2 * w + 1]);
+        const float v[4] = {(float)p0[0], (float)p0[1], (float)p1[0], (float)p1[1]};
+        int c[4] = {0, 0, 0, 0};
+        if (sx != 0.0f)
+            int8_codes(v, sx, rsx, c);
+        out[w] = ((uint32_t)c[0] & 255u) | ((uint32_t)c[1] & 255u) << 8 | ((uint32_t)c[2] & 255u) << 16 |
+                 ((uint32_t)c[3] & 255u) << 24;
     }
     return u32x4{out[0], out[1], out[2], out[3]};
 }
@@ -382,16 +376,18 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
             for (int j = 0; j < kHold; ++j)
                 amax = absmax8(h[j][1], absmax8(h[j][0], amax));
             sx = block_max_f32(amax) / 127.0f;
+            const float rsx = 1.0f / sx;
 #pragma unroll
             for (int j = 0; j < kHold; ++j) {
                 const int i = tid + j * kBlock;
                 if (i >= kv0 && i < kv0 + nv)
-                    put(i, quantize16(h[j][0], h[j][1], sx));
+                    put(i, quantize16(h[j][0], h[j][1], sx, rsx));
             }
         } else {
             sx = dyn_scale(L.x, (int64_t)L.kvec * 2);
+            const float rsx = 1.0f / sx;
             for (int i = kv0 + tid; i < kv0 + nv; i += kBlock)
-                put(i, quantize16(*glob(L.x + 2 * i), *glob(L.x + 2 * i + 1), sx));
+                put(i, quantize16(*glob(L.x + 2 * i), *glob(L.x + 2 * i + 1), sx, rsx));
         }
         if (L.sx_out != nullptr && tile == 0 && s == 0 && tid == 0)
             *glob(L.sx_out) = sx;

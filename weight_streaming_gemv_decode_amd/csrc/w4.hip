@@ -389,6 +389,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
         __syncthreads();
         amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
         sx = amax / 127.0f;
+        const float rsx = 1.0f / sx;
         // (2) codes of this slice, one (block, lane group) pair per thread:
         // 8 bytes per packed word in the order (e0,e4,e1,e5 | e2,e6,e3,e7)
         u32x2 *xq8 = reinterpret_cast<u32x2 *>(xs);
@@ -402,17 +403,17 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                 const int64_t v = (int64_t)(kb0 + b) * 16 + 4 * i + gg;   // k = 8 v .. 8 v + 7
                 const u32x4 h = *glob(L.x + v);
                 const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
-                int e[8];
+                int e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f16x2 pr = as_h2(hw[j]);
+                for (int j = 0; j < 4; j += 2) {  // four codes at a time keep few registers live
+                    const f16x2 p0 = as_h2(hw[j]), p1 = as_h2(hw[j + 1]);
+                    const float xv[4] = {(float)p0[0], (float)p0[1], (float)p1[0], (float)p1[1]};
+                    int c[4] = {0, 0, 0, 0};
+                    if (amax != 0.0f)
+                        int8_codes(xv, sx, rsx, c);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        float r = 0.0f;
-                        if (amax != 0.0f)
-                            r = fminf(fmaxf(rintf((float)pr[t] / sx), -127.0f), 127.0f);
-                        e[2 * j + t] = (int)r;
-                    }
+                    for (int t = 0; t < 4; ++t)
+                        e[2 * j + t] = c[t];
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j)

@@ -72,6 +72,34 @@ __device__ __forceinline__ int32_t xor_lane(int32_t v, int stride) {
     return (int32_t)xor_lane((uint32_t)v, stride);
 }
 
+// Per-token int8 activation codes c = clamp(rint(x / s), -127, 127), with the
+// quotient the IEEE fp32 division x / s (rounded to nearest) and rint ties to
+// even, for N values and s > 0; rs = fp32(1 / s).  The quotient is first
+// taken as t = fp32(x * rs): with unit roundoff u = 2^-24, t and fp32(x / s)
+// differ by at most about 3u|t|, so when t lies farther than 8u|t| from every
+// half-integer both round to the same integer.  Only a lane holding a value
+// inside that window (or a NaN) takes the exact division, for its N values.
+// The distance 0.5 - |t - rint(t)| is exact where it matters (t - rint(t) is
+// exact; the subtraction from 0.5 is exact once |t - rint(t)| >= 1/4), and
+// no step is contracted into a fused multiply-add.
+template <int N>
+__device__ __forceinline__ void int8_codes(const float (&x)[N], float s, float rs, int (&c)[N]) {
+#pragma clang fp contract(off)
+    bool exact = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float t = x[i] * rs;
+        const float r = rintf(t);
+        exact |= !(0.5f - fabsf(t - r) > fabsf(t) * 0x1p-21f);
+        c[i] = (int)fminf(fmaxf(r, -127.0f), 127.0f);
+    }
+    if (exact) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            c[i] = (int)fminf(fmaxf(rintf(x[i] / s), -127.0f), 127.0f);
+    }
+}
+
 // The global-memory view of a device pointer.  The work-table kernels read
 // their tensor pointers from memory, where the compiler cannot see that they
 // point to global memory, and would access them with flat instructions.  A
