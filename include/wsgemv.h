@@ -22,6 +22,10 @@
  *    ABI.  WSG_ERR_HIP keeps the hipError_t in wsg_last_hip_error() (per
  *    thread).
  *  - N == 0 is a no-op.  K == 0 writes y = 0 (the empty sum).
+ *  - A shape whose launch would need more than 2^32 - 1 work-items (HIP's
+ *    32-bit grid: beyond tens to hundreds of millions of rows, fewer with
+ *    many forced slices) returns WSG_ERR_UNSUPPORTED before anything is
+ *    launched, as do the per-call limits stated below.
  *  - Outputs must not alias inputs.  Inputs must stay alive until the
  *    stream has reached the work.
  *

@@ -290,3 +290,21 @@ def test_w8a8_dyn_validation(L):
         lin = wsgemv.wsg_linear(4, M, 64, 128, FAKE, None if want == NULL else FAKE, FAKE, xs, FAKE, None, 0, 0)
         got = L.wsg_decode_step_create((wsgemv.wsg_linear * 1)(lin), 1, 1, None, ctypes.byref(out))
         assert got == want, (M, xs, got)
+
+
+def test_launch_size_limits(L):
+    """Shapes whose launches would exceed HIP's 32-bit work-item count are
+    rejected before any size is narrowed or any kernel is launched; the
+    largest accepted ones still pass validation (checked with a NULL output,
+    so nothing is launched)."""
+    big = 1 << 33                      # rows: N / 4 units would not fit a launch
+    assert L.gemv_f16(FAKE, FAKE, FAKE, big, 64, 0, None, 0, None) == UNSUP
+    assert L.gemv_f16(FAKE, FAKE, FAKE, big, 0, 0, None, 0, None) == UNSUP       # K = 0 zero-fill launch too
+    assert L.gemv_f16(FAKE, FAKE, FAKE, 1 << 26, 4096, 16, FAKE, 1 << 40, None) == UNSUP  # forced splits
+    assert L.gemv_f16(FAKE, FAKE, None, 1 << 24, 64, 0, None, 0, None) == NULL   # 16M rows: fits
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, big, 64, 0, None, 0, None]
+    assert L.gemv_w8a8(*args) == UNSUP
+    assert L.gemv_w4a16(FAKE, FAKE, FAKE, FAKE, 8, big // 8, 256, 128, 0, None, 0, None) == UNSUP
+    assert L.gemv_w4a16(FAKE, FAKE, FAKE, None, 1, 1 << 24, 256, 128, 0, None, 0, None) == NULL
+    assert L.wsg_pack_w4(FAKE, FAKE, FAKE, FAKE, big, 1 << 14, 128, None) == UNSUP
+    assert L.causal_conv1d_step(FAKE, FAKE, None, FAKE, FAKE, 1 << 40, 4, 0, None) == UNSUP

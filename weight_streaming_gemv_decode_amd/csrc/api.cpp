@@ -32,6 +32,13 @@ wsg_status hip_fail(hipError_t e) {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// HIP takes a launch's grid as a 32-bit count of work-items, so a launch of
+// kBlock-thread workgroups holds at most this many workgroups.  Shapes whose
+// launches would need more are rejected (WSG_ERR_UNSUPPORTED) before any
+// size is narrowed to the kernels' 32-bit fields.
+constexpr int64_t kMaxBlocks = (int64_t)UINT32_MAX / kBlock;
+bool grid_ok(int64_t blocks) { return blocks <= kMaxBlocks; }
+
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest k-slice, in 16-byte vectors, a dense unit stages in LDS (32 KiB).
@@ -156,7 +163,7 @@ wsg_status check_dense_args(int kind, const void *W, const void *x, const float 
                             int32_t splits) {
     if (N < 0 || K < 0)
         return WSG_ERR_SHAPE;
-    if (N > (int64_t)INT32_MAX * 16 || K > (1LL << 28))
+    if (N > (int64_t)INT32_MAX * 16 || K > (1LL << 28) || !grid_ok(cdiv(N, kBlock)))
         return WSG_ERR_UNSUPPORTED;
     if (K % elem_per_vec(kind))
         return WSG_ERR_SHAPE;
@@ -178,6 +185,9 @@ wsg_status check_dense_args(int kind, const void *W, const void *x, const float 
     // every slice must hold at least one vector
     if (splits > 0 && (int64_t)(splits - 1) * cdiv(kvec, splits) >= kvec)
         return WSG_ERR_SHAPE;
+    const DensePlan p = plan_dense(kind, N, K, splits);
+    if (!grid_ok(cdiv(N, p.tile_rows) * p.S))
+        return WSG_ERR_UNSUPPORTED;
     return WSG_OK;
 }
 
@@ -234,7 +244,7 @@ wsg_status check_token_args(int64_t N, const int32_t *token, const float *token_
 wsg_status check_conv(int64_t C, int32_t W, const void *w, const float *bias, const float *state, const float *out) {
     if (C < 0)
         return WSG_ERR_SHAPE;
-    if (W < 2 || W > 8)
+    if (W < 2 || W > 8 || !grid_ok(cdiv(C, kBlock)))
         return WSG_ERR_UNSUPPORTED;
     if (C == 0)
         return WSG_OK;
@@ -343,7 +353,7 @@ wsg_status check_w4_args(const void *Wp, const void *Sp, const void *x, const fl
         return WSG_ERR_SHAPE;
     if (M < 1 || M > kMaxM)
         return M == 0 ? WSG_ERR_SHAPE : WSG_ERR_UNSUPPORTED;
-    if (N > (int64_t)INT32_MAX * 16 || K > (1LL << 24))
+    if (N > (int64_t)INT32_MAX * 16 || K > (1LL << 24) || !grid_ok(cdiv(M * N, kBlock)))
         return WSG_ERR_UNSUPPORTED;
     if (N == 0)
         return WSG_OK;
@@ -369,6 +379,9 @@ wsg_status check_w4_args(const void *Wp, const void *Sp, const void *x, const fl
     } else if (splits == 1 && (int64_t)M * kb * 256 > 48 * 1024) {
         return WSG_ERR_SHAPE;
     }
+    const W4Plan p = plan_w4(M, N, K, splits);
+    if (!grid_ok(cdiv(cdiv(N, 16), p.tile_rtiles) * p.S))
+        return WSG_ERR_UNSUPPORTED;
     return WSG_OK;
 }
 
@@ -688,7 +701,7 @@ wsg_status wsg_pack_w4(const uint32_t *Wc, const void *s4, void *Wp, void *Sp, i
             return WSG_ERR_UNSUPPORTED;
         if (K % 128)
             return WSG_ERR_SHAPE;
-        if (K > (1LL << 24) || N > (int64_t)INT32_MAX * 16)
+        if (K > (1LL << 24) || N > (int64_t)INT32_MAX * 16 || !grid_ok(cdiv(N, 16) * (K / 128)))
             return WSG_ERR_UNSUPPORTED;
         if (N == 0 || K == 0)
             return WSG_OK;
@@ -1231,6 +1244,14 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     wtail[wmode] = wtail[wmode] || w4_needs_tail(L, p.cfg.B);
                     wcfg[wmode] = p.cfg;
                 }
+            }
+        }
+
+        // a grouped launch covers every unit of its kind
+        for (int k = 0; k < 3; ++k) {
+            if (!grid_ok((int64_t)du[k].size()) || !grid_ok((int64_t)wu[k].size())) {
+                free_step(st);
+                return WSG_ERR_UNSUPPORTED;
             }
         }
 
