@@ -145,7 +145,7 @@ def summary(ts):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU: the batch-1 GEMV is measured on one "
+        print(json.dumps({"error": "the library runs on exactly one GPU: the batch-1 GEMV is measured on one "
                                    "MI355X and no multi-GPU path exists; rerun with --gpus 1"}))
         sys.exit(2)
 

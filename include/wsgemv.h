@@ -60,7 +60,7 @@ enum {
     WSG_ERR_NULL = 1,        /* a required pointer is NULL */
     WSG_ERR_SHAPE = 2,       /* negative or inconsistent sizes, K not a multiple of the vector width */
     WSG_ERR_ALIGN = 3,       /* a pointer is not aligned as stated */
-    WSG_ERR_UNSUPPORTED = 4, /* a valid request this build does not implement (e.g. M > 8) */
+    WSG_ERR_UNSUPPORTED = 4, /* a valid request the library does not implement (e.g. M > 8) */
     WSG_ERR_WORKSPACE = 5,   /* workspace missing or too small for the chosen split */
     WSG_ERR_HIP = 6,         /* a HIP runtime call failed; see wsg_last_hip_error() */
     WSG_ERR_NOMEM = 7,       /* host or device allocation failed (plan creation only) */
