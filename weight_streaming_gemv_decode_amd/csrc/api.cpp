@@ -95,7 +95,9 @@ int dense_tile_rows(int64_t slice_bytes_per_row, int R) {
     return (int)std::min<int64_t>(rows, 1 << 20);
 }
 
-DensePlan plan_dense(int kind, int64_t N, int64_t K, int splits) {
+// `token`: the linear also takes the greedy token, whose finish kernel reads
+// one key per work unit.
+DensePlan plan_dense(int kind, int64_t N, int64_t K, int splits, bool token = false) {
     const int64_t kvec = K / elem_per_vec(kind);
     DensePlan p;
     int S = splits > 0 ? splits : dense_min_splits(kvec);
@@ -120,6 +122,12 @@ DensePlan plan_dense(int kind, int64_t N, int64_t K, int splits) {
         // 64-vector slices (e.g. K = 1024 fp16 cut in two): 8 rows x 1 vector per step
         p.cfg = DenseCfg{8, 1, use_nt(), false};
         tr = 32;
+    } else if (cdiv(N, 16) * S >= 1024 && kind == kF16 && !token) {
+        // many rows: 4-row units (1 row per wave).  On the 248320x1024
+        // lm_head they measured 70.6 us against 73.7 us for 16-row units;
+        // with the token, 4x the units would be 4x the keys its finish reads.
+        p.cfg = DenseCfg{1, 2, use_nt(), false};
+        tr = 4;
     } else if (cdiv(N, 16) * S >= 1024) {
         p.cfg = DenseCfg{4, 2, use_nt(), false};
         tr = 16;
@@ -460,7 +468,7 @@ size_t wsg_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K, int32_
             return 0;
         if (K == 0 || K % elem_per_vec(base))
             return token_key_bytes(argmax_f32_blocks(N));
-        const DensePlan p = plan_dense(base, N, K, splits);
+        const DensePlan p = plan_dense(base, N, K, splits, true);
         return token_key_bytes(dense_token_keys(p, N)) + dense_ws_bytes(p, N);
     }
     if (N <= 0 || K <= 0 || splits < 0)
@@ -597,7 +605,7 @@ wsg_status gemv_f16_argmax(const void *W, const void *x, float *y, int32_t *toke
                 e = launch_argmax_f32(y, N, arg_out(ws, nk, token, token_logit), s);
             return e == hipSuccess ? WSG_OK : hip_fail(e);
         }
-        DensePlan p = plan_dense(kF16, N, K, splits);
+        DensePlan p = plan_dense(kF16, N, K, splits, true);
         const int32_t nk = dense_token_keys(p, N);
         const size_t kb = token_key_bytes(nk);
         st = check_ws(ws, ws_bytes, kb + dense_ws_bytes(p, N));
@@ -1120,7 +1128,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             if (l.kind == kF16 || l.kind == kW8A8 || l.kind == kW8A8D) {
                 const int ki = l.kind == kF16 ? 0 : (l.kind == kW8A8 ? 1 : 2);
                 if (base_mode == WSG_STEP_ORDERED) {
-                    DensePlan p = plan_dense(l.kind, l.N, l.K, l.splits);
+                    DensePlan p = plan_dense(l.kind, l.N, l.K, l.splits, l.argmax_idx != nullptr);
                     part_bytes = std::max(part_bytes, dense_ws_bytes(p, l.N));
                     wsg_step::Op o{};
                     o.type = wsg_step::Op::kDense;
