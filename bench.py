@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extras", action="store_true", help="only the decode-step stream")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,conv,graph,topk,probe,ordered,chain)")
+    ap.add_argument("--only", default="", help="comma list of extras to run (c1,c2,c4,c5,c6,token,conv,graph,topk,probe,ordered,chain,shard)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB fp32 copy kernel (reads 1 GiB, writes 1 GiB) to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass")
@@ -452,6 +452,66 @@ def main():
                                                         "GBps": step_bytes / (s2["median_ms"] * 1e-3) / 1e9}
         st_.close()
         extras["conv1d"] = rec
+
+    if want("shard"):
+        # One GPU's share of the step spread over G = 8 GPUs, timed like C3
+        # (GROUPED, one launch; three weight copies rotated past the 256 MB
+        # Infinity Cache), for two cuts of the decoder linears: Megatron
+        # pairs (qkv and gate+up over N, o and down over K, whose partial
+        # sums would be all-reduced), and every linear over N (outputs would
+        # be all-gathered).  The lm_head is cut over the vocabulary.
+        G = 8
+        cuts = {"pairs": {"qkv": (G, 1), "o": (1, G), "gate_up": (G, 1), "down": (1, G)},
+                "rows": {"qkv": (G, 1), "o": (G, 1), "gate_up": (G, 1), "down": (G, 1)}}
+        rec = {"G": G, "note": "per-GPU product only; the collectives are not run"}
+        for label, cut in cuts.items():
+            shapes = []
+            for name, N, K, wi, xi in synth.decode_step_shapes():
+                if name == "lm_head":
+                    shapes.append((name, N // G, K, wi, xi))
+                else:
+                    dn, dk = cut[name.split(".")[1]]
+                    shapes.append((name, N // dn, K // dk, wi, xi))
+            b = sum(N * K * 2 + K * 2 + N * 4 for _, N, K, _, _ in shapes)
+            sets = []
+            for c in range(3):
+                lins_g = []
+                for name, N, K, wi, xi in shapes:
+                    Wg = torch.from_numpy(synth.f16_normal(8, 4 * wi + c, (N, K), synth.W_SIGMA)).to(dev)
+                    xg = torch.from_numpy(synth.f16_normal(9, xi, (K,), synth.X_SIGMA)).to(dev)
+                    lins_g.append(wsgemv.Linear(wsgemv.F16, Wg, xg, torch.empty(N, device=dev), N, K))
+                sets.append(wsgemv.DecodeStep(lins_g, wsgemv.STEP_GROUPED, stream=stream))
+            for i in range(6):
+                sets[i % 3](stream)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                ev0.record(stream)
+                for i in range(60):
+                    sets[i % 3](stream)
+                ev1.record(stream)
+            stream.synchronize()
+            t = ev0.elapsed_time(ev1) * 1e3 / 60
+            layer = ", ".join(f"{n.split('.')[1]} {N}x{K}" for n, N, K, _, _ in shapes[:4])
+            rec[f"step_{label}"] = {"bytes_per_gpu": b, "step_us": round(t, 2),
+                                    "GBps": round(b / (t * 1e-6) / 1e9, 1),
+                                    "shapes": f"{layer} (x28), lm_head {shapes[-1][1]}x{shapes[-1][2]}"}
+            for st in sets:
+                st.close()
+            del sets
+        # the lm_head shard alone, 8 rotated copies in one graph
+        N, K = synth.LMHEAD[0] // G, synth.LMHEAD[1]
+        W = torch.from_numpy(synth.f16_normal(10, 0, (N, K), synth.W_SIGMA)).to(dev)
+        copies = [W] + [W.clone() for _ in range(7)]
+        x = torch.from_numpy(synth.f16_normal(10, 1, (K,), synth.X_SIGMA)).to(dev)
+        y = torch.empty(N, device=dev)
+        fn = lambda i: wsgemv.gemv_f16(copies[i % 8], x, y=y, stream=stream)  # noqa: E731
+        s = summary(graph_times(torch, fn, 32, 10, stream))
+        bl = N * K * 2 + K * 2 + N * 4
+        rec["lm_head_31040x1024"] = {"bytes": bl, "median_us": round(s["median_ms"] * 1e3, 2),
+                                     "GBps": round(bl / (s["median_ms"] * 1e-3) / 1e9, 1),
+                                     "rotation": "8 copies, 32 calls captured in one graph"}
+        extras["shard_8way_one_gpu"] = rec
+        del copies
 
     if want("topk"):
         # top-k over the lm_head's 248,320 fp32 logits (64 calls captured in one graph)
