@@ -615,8 +615,8 @@ def main():
         "data": "synthetic: seeded fp16 weights ~N(0,0.02), activations ~N(0,1); fp32 accumulate, fp32 outputs",
         "config": {"workload": "fp16 batch-1 decode-step linear stream: 28 x {qkv 2048x1024, o 1024x1024, "
                                "gate_up 6144x1024, down 1024x3072} + lm_head 248320x1024, GROUPED plan: "
-                               "one launch over a work table of 16,720 units (ORDERED, one node per linear, "
-                               "is the captured hipGraph in extras)",
+                               f"one launch over a work table of {units:,} units (ORDERED, one node per "
+                               "linear, is the captured hipGraph in extras)",
                    "bytes_per_step": step_bytes, "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
                    "launches_per_step": launches, "work_units": units},
         "roofline": roofline,

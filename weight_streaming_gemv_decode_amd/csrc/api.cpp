@@ -1059,14 +1059,35 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         bool wtail[3] = {false, false, false};
         W4Cfg wcfg[3] = {};
         size_t part_bytes = 0;
-        // Grouped launches: 8 rows x 1 vector per wave step, units of at least
-        // 32 rows (64 KiB at K = 1024 fp16).
-        DenseCfg gcfg{8, 1, use_nt(), false};
+        // Grouped launches, one per kind: 8 rows x 1 vector per wave step,
+        // units of at least 32 rows (64 KiB at K = 1024 fp16).  An fp16 launch
+        // whose linears run no epilogue (token, conv) takes 2 rows x 2 vectors
+        // per step instead, units of about 128 KiB (64 rows at K = 1024), and
+        // of 16 KiB (8 rows) for linears of 16384 rows or more (the lm_head):
+        // interleaved on MI355X the 113-linear step took 173.0-173.5 us
+        // against 174.0-174.8 us.  With the lm_head taking the token that
+        // shape measured 181-182 us against 178.6-179.3 us (at 8-, 32- and
+        // 64-row units), so plans with epilogues keep the 8 x 1 shape.
+        bool f16_epilogue = false;
+        for (int32_t i = 0; i < n; ++i)
+            f16_epilogue |= linears[i].kind == kF16 && (linears[i].argmax_idx || linears[i].conv_out);
+        const bool f16_hybrid = !f16_epilogue;
+        DenseCfg gcfg[3] = {{8, 1, use_nt(), false}, {8, 1, use_nt(), false}, {8, 1, use_nt(), false}};
+        if (f16_hybrid)
+            gcfg[0] = DenseCfg{2, 2, use_nt(), false};
         if (g_tune.group_R > 0 && g_tune.group_CH > 0) {
-            gcfg.R = (int)g_tune.group_R;
-            gcfg.CH = (int)g_tune.group_CH;
+            for (auto &c : gcfg) {
+                c.R = (int)g_tune.group_R;
+                c.CH = (int)g_tune.group_CH;
+            }
         }
-        const int64_t unit_bytes = g_tune.group_unit_kb > 0 ? g_tune.group_unit_kb * 1024 : 32 * 1024;
+        auto unit_bytes = [&](const wsg_linear &l) -> int64_t {
+            if (g_tune.group_unit_kb > 0)
+                return g_tune.group_unit_kb * 1024;
+            if (l.kind != kF16 || !f16_hybrid)
+                return 32 * 1024;
+            return l.N >= 16384 ? 16 * 1024 : 128 * 1024;
+        };
         // Greedy-token key arrays (one per linear that takes a token) open the
         // device block; descriptors get their addresses once it exists.
         std::vector<size_t> key_off;           // per key array: offset in the keys region
@@ -1154,7 +1175,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     }
                 } else {
                     DensePlan p{};
-                    p.cfg = gcfg;
+                    p.cfg = gcfg[ki];
                     p.S = 1;
                     p.kvs = (int)(l.K / elem_per_vec(l.kind));
                     if (p.kvs > kMaxSliceVec) {
@@ -1162,8 +1183,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                         return WSG_ERR_UNSUPPORTED;
                     }
                     {
-                        const int q = kWavesPerBlock * gcfg.R;
-                        int64_t rows = unit_bytes / ((int64_t)p.kvs * 16);
+                        const int q = kWavesPerBlock * gcfg[ki].R;
+                        int64_t rows = unit_bytes(l) / ((int64_t)p.kvs * 16);
                         p.tile_rows = (int)std::min<int64_t>(1 << 20, std::max<int64_t>(q, rows / q * q));
                     }
                     DenseLin L = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale),
@@ -1184,8 +1205,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     dl[ki].push_back(L);
                     for (int t = 0; t < L.n_tiles; ++t)
                         du[ki].push_back(Unit{li, t, 0, 0});
-                    dlds[ki] = std::max(dlds[ki], dense_lds_bytes(L, gcfg.CH));
-                    dtail[ki] = dtail[ki] || dense_needs_tail(L, gcfg.CH);
+                    dlds[ki] = std::max(dlds[ki], dense_lds_bytes(L, gcfg[ki].CH));
+                    dtail[ki] = dtail[ki] || dense_needs_tail(L, gcfg[ki].CH);
                 }
             } else {
                 const int wmode = l.kind == kW4A8 ? kA8 : ((l.M > 1 || g_tune.w4_mfma_m1 == 1) ? kMfma : kA16);
@@ -1333,7 +1354,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                 wsg_step::Op o{};
                 o.type = wsg_step::Op::kDenseGroup;
                 o.kind = k == 0 ? kF16 : (k == 1 ? kW8A8 : kW8A8D);
-                o.dc = gcfg;
+                o.dc = gcfg[k];
                 o.dc.tail = dtail[k];
                 o.lins = base + dl_off[k];
                 o.units = reinterpret_cast<const Unit *>(base + du_off[k]);
