@@ -363,23 +363,55 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
         return;
     }
 
-    // M = 1: the first weight step goes out before the activation staging
-    // and its barrier, the second behind the barrier.
-    if (nsteps > 0)
-        load_step(bufA, 0, 0);
-
     if constexpr (MODE == kA8) {
-        // (1) max |x| over the whole row
+        // The per-token scale needs max |x| over the whole fp16 row before
+        // any code.  A row of at most kA8HoldVec vectors per thread is loaded
+        // into registers ahead of the first weight step and stashed in LDS
+        // for the codes, so neither pass waits for weights (loads retire in
+        // issue order) and x is read from memory once; longer rows are read
+        // twice, behind the first weight step.  The second step goes out
+        // behind the barrier, as in the fp16 M = 1 kernel: issuing it earlier
+        // made the kernel hold 94 VGPRs instead of 72 (five waves per SIMD
+        // instead of seven).
+        const bool held = a8_row_held(L.K);
+        const int nxall = L.K / 8;
+        u32x4 *xraw = xs + 9 * L.kbs + 1;  // after the codes, sums and red[]
         float amax = 0.0f;
-        for (int v = tid; v < L.K / 8; v += kBlock) {
-            const u32x4 h = *glob(L.x + v);
+        auto absmax_vec = [&](u32x4 h) {
             const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const f16x2 p = as_h2(hw[j]);
                 amax = fmaxf(amax, fmaxf(fabsf((float)p[0]), fabsf((float)p[1])));
             }
+        };
+        if (held) {
+            u32x4 xh[kA8HoldVec];
+#pragma unroll
+            for (int j = 0; j < kA8HoldVec; ++j) {
+                const int i = tid + j * kBlock;
+                xh[j] = u32x4{0u, 0u, 0u, 0u};
+                if (i < nxall)
+                    xh[j] = *glob(L.x + i);
+            }
+            if (nsteps > 0)
+                load_step(bufA, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kA8HoldVec; ++j) {
+                const int i = tid + j * kBlock;
+                if (i < nxall) {
+                    xraw[i] = xh[j];
+                    absmax_vec(xh[j]);
+                }
+            }
+        } else {
+            // the first weight step goes out before the row is read
+            if (nsteps > 0)
+                load_step(bufA, 0, 0);
+            for (int v = tid; v < nxall; v += kBlock)
+                absmax_vec(*glob(L.x + v));
         }
+        // (1) max |x| over the whole row (the barrier also publishes xraw)
 #pragma unroll
         for (int i = 0; i < 6; ++i)
             amax = fmaxf(amax, xor_lane(amax, 32 >> i));
@@ -401,7 +433,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t v = (int64_t)(kb0 + b) * 16 + 4 * i + gg;   // k = 8 v .. 8 v + 7
-                const u32x4 h = *glob(L.x + v);
+                const u32x4 h = held ? xraw[v] : *glob(L.x + v);
                 const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
                 int e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
@@ -437,6 +469,10 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             *glob(L.sx_out) = sx;
         __syncthreads();
     } else {
+        // M = 1, fp16 activations: the first weight step goes out before the
+        // activation staging and its barrier, the second behind the barrier.
+        if (nsteps > 0)
+            load_step(bufA, 0, 0);
         // Stage the activation slice: xs[v].
         for (int i = tid; i < nxv; i += kBlock)
             xs[i] = *glob(L.x + (int64_t)kb0 * 16 + i);

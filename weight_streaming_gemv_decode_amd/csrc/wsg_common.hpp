@@ -256,9 +256,14 @@ inline int dense_lds_bytes(const DenseLin &L, int CH) {
     return nch * chunk * 16;
 }
 
+// int8-activation units whose fp16 row fits kA8HoldVec 16-byte vectors per
+// thread hold it in registers, and stash it in LDS for the codes.
+constexpr int kA8HoldVec = 2;
+__host__ __device__ inline bool a8_row_held(int64_t K) { return K / 8 <= (int64_t)kA8HoldVec * kBlock; }
+
 inline int w4_lds_bytes(const W4Lin &L, int mode) {
-    if (mode == kA8)  // int8 codes of the slice, one int sum per (block, lane group), 4 floats
-        return L.kbs * 128 + L.kbs * 4 * 4 + 16;
+    if (mode == kA8)  // int8 codes of the slice, one int sum per (block, lane group), 4 floats[, the fp16 row]
+        return L.kbs * 128 + L.kbs * 4 * 4 + 16 + (a8_row_held(L.K) ? L.K * 2 : 0);
     // x slice for all M rows: kbs blocks of 128 fp16 per row
     return L.M * L.kbs * 128 * 2;
 }
