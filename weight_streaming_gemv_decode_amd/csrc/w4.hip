@@ -469,12 +469,26 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             *glob(L.sx_out) = sx;
         __syncthreads();
     } else {
-        // M = 1, fp16 activations: the first weight step goes out before the
-        // activation staging and its barrier, the second behind the barrier.
+        // M = 1, fp16 activations: the first vectors of the activation slice
+        // are loaded ahead of the first weight step, so that staging them
+        // waits for them alone; the second step goes out behind the barrier.
+        constexpr int kXHold1 = 2;
+        u32x4 xh[kXHold1];
+#pragma unroll
+        for (int j = 0; j < kXHold1; ++j) {
+            const int i = tid + j * kBlock;
+            if (i < nxv)
+                xh[j] = *glob(L.x + (int64_t)kb0 * 16 + i);
+        }
         if (nsteps > 0)
             load_step(bufA, 0, 0);
-        // Stage the activation slice: xs[v].
-        for (int i = tid; i < nxv; i += kBlock)
+#pragma unroll
+        for (int j = 0; j < kXHold1; ++j) {
+            const int i = tid + j * kBlock;
+            if (i < nxv)
+                xs[i] = xh[j];
+        }
+        for (int i = tid + kXHold1 * kBlock; i < nxv; i += kBlock)
             xs[i] = *glob(L.x + (int64_t)kb0 * 16 + i);
         __syncthreads();
     }
