@@ -1185,6 +1185,10 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     {
                         const int q = kWavesPerBlock * gcfg[ki].R;
                         int64_t rows = unit_bytes(l) / ((int64_t)p.kvs * 16);
+                        // short rows do not fill a wave step: at most 64 rows
+                        // per unit keeps such linears spread over workgroups
+                        if (ki == 0 && f16_hybrid && g_tune.group_unit_kb <= 0)
+                            rows = std::min<int64_t>(rows, 64);
                         p.tile_rows = (int)std::min<int64_t>(1 << 20, std::max<int64_t>(q, rows / q * q));
                     }
                     DenseLin L = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale),
