@@ -43,8 +43,6 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest k-slice, in 16-byte vectors, a dense unit stages in LDS (32 KiB).
 constexpr int kMaxSliceVec = 2048;
-// Target weight bytes of one work unit.
-constexpr int64_t kUnitBytes = 128 * 1024;
 // Work units wanted per launch (4 per compute unit on 256 CUs).
 constexpr int64_t kWantUnits = 1024;
 constexpr int kMaxM = 8;
@@ -86,14 +84,6 @@ struct DensePlan {
 int elem_per_vec(int kind) { return kind == kF16 ? 8 : 16; }
 
 int dense_min_splits(int64_t kvec) { return (int)std::max<int64_t>(1, cdiv(kvec, kMaxSliceVec)); }
-
-// Rows per unit: a multiple of 4 waves x R rows, close to kUnitBytes.
-int dense_tile_rows(int64_t slice_bytes_per_row, int R) {
-    const int q = kWavesPerBlock * R;
-    int64_t rows = kUnitBytes / std::max<int64_t>(1, slice_bytes_per_row);
-    rows = std::max<int64_t>(q, rows / q * q);
-    return (int)std::min<int64_t>(rows, 1 << 20);
-}
 
 // `token`: the linear also takes the greedy token, whose finish kernel reads
 // one key per work unit.
