@@ -542,13 +542,25 @@ __global__ __launch_bounds__(kFinishThreads) void argmax_finish_kernel(ArgOut a)
 }
 
 // Greedy token over a given fp32 vector: at most kArgBlocks workgroups, each
-// striding over the vector in kBlock-wide rows, then the finish kernel.
+// striding over the vector in kBlock-wide rows, then the finish kernel.  A
+// thread issues the loads of kArgLoads rows before it folds any of them, so
+// their latencies overlap.
 constexpr int kArgBlocks = 1024;
+constexpr int kArgLoads = 8;
 
 __global__ __launch_bounds__(kBlock) void argmax_f32_kernel(const float *__restrict__ y, int64_t N, ArgOut a) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
     unsigned long long best = 0;
-    for (int64_t n = (int64_t)blockIdx.x * kBlock + threadIdx.x; n < N; n += (int64_t)gridDim.x * kBlock)
-        best = max_u64(best, arg_key(y[n], n));
+    for (int64_t n0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; n0 < N; n0 += kArgLoads * stride) {
+        float v[kArgLoads];
+#pragma unroll
+        for (int j = 0; j < kArgLoads; ++j)
+            v[j] = n0 + j * stride < N ? *glob(y + n0 + j * stride) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kArgLoads; ++j)
+            if (n0 + j * stride < N)
+                best = max_u64(best, arg_key(v[j], n0 + j * stride));
+    }
     arg_publish(a, best, blockIdx.x);
 }
 
