@@ -13,8 +13,10 @@
 // once that bin holds exactly the keys still needed), gathers the keys at or
 // above it, and one wave sorts them (bitonic, through lane exchanges).  Each
 // workgroup writes its k best keys as a sorted list.  Passes repeat until at
-// most 256 lists remain; one workgroup then merges them: two sorted lists of
-// 64 merge in one wave as the lane-wise maximum of one list and the other
+// most 256 lists remain.  The merge then runs in two launches when more than
+// 16 lists remain: workgroups of 16 waves merge 16 lists each on their own
+// compute units, and one workgroup merges their results.  Two sorted lists
+// of 64 merge in one wave as the lane-wise maximum of one list and the other
 // reversed (the 64 largest of both, in bitonic order) followed by six
 // exchange stages.  No global atomics; the result does not depend on
 // workgroup order.
@@ -183,25 +185,32 @@ __device__ __forceinline__ unsigned long long merge64(unsigned long long v, unsi
     return v;
 }
 
-// The k largest keys of `lists` sorted lists (list l = in[l k .. l k + k),
-// descending, zero-padded), in descending order, as the token rule's
-// indices and values: every wave merges its share of the lists (all loaded
-// first), then the waves' results are merged pairwise through shared memory.
+// The k largest keys of sorted lists (list l = in[l k .. l k + k),
+// descending, zero-padded), in descending order.  Workgroup g takes lists
+// [g per_wg, min(lists, (g + 1) per_wg)): every wave merges its share of them
+// (all loaded first), then the waves' results are merged pairwise through
+// shared memory.  The result goes to out[g k .. g k + k) as a sorted list
+// when out is given, else (one workgroup) as the token rule's indices and
+// values.
 __global__ __launch_bounds__(kMergeWaves * kWave) void topk_merge_kernel(const unsigned long long *__restrict__ in,
-                                                                        int lists, int k, int32_t *idx, float *val) {
+                                                                        int lists, int per_wg, int k,
+                                                                        unsigned long long *out, int32_t *idx,
+                                                                        float *val) {
     __shared__ unsigned long long part[kMergeWaves][kWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int first = blockIdx.x * per_wg;
+    const int last = min(lists, first + per_wg);
     unsigned long long b[kListsPerWave];
 #pragma unroll
     for (int j = 0; j < kListsPerWave; ++j) {
-        const int l = wave + j * kMergeWaves;
-        b[j] = (l < lists && lane < k) ? *glob(in + (int64_t)l * k + lane) : 0ull;
+        const int l = first + wave + j * kMergeWaves;
+        b[j] = (l < last && lane < k) ? *glob(in + (int64_t)l * k + lane) : 0ull;
     }
     unsigned long long v = b[0];  // one list is sorted already
 #pragma unroll
     for (int j = 1; j < kListsPerWave; ++j)
-        if (wave + j * kMergeWaves < lists)  // wave-uniform
+        if (first + wave + j * kMergeWaves < last)  // wave-uniform
             v = merge64(v, b[j], lane);
     part[wave][lane] = v;
     for (int half = kMergeWaves / 2; half > 0; half >>= 1) {
@@ -213,10 +222,14 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void topk_merge_kernel(const u
             part[wave][lane] = v;
     }
     if (wave == 0 && lane < k) {
-        ArgOut a{};
-        a.idx = idx;
-        a.val = val;
-        arg_write(a, v, lane);
+        if (out != nullptr) {
+            *glob(out + (int64_t)blockIdx.x * k + lane) = v;
+        } else {
+            ArgOut a{};
+            a.idx = idx;
+            a.val = val;
+            arg_write(a, v, lane);
+        }
     }
 }
 
@@ -264,7 +277,20 @@ hipError_t launch_topk(const float *y, int64_t N, int k, int32_t *idx, float *va
         in = out;
         out = (out == ws_a) ? ws_b : ws_a;
     }
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(1), dim3(kMergeWaves * kWave), 0, s, in, (int)lists, k, idx, val);
+    if (lists > kMergeWaves) {
+        // one list per wave on several compute units; the other ping-pong
+        // buffer (room for at least lists * k keys) takes the groups' lists
+        const int groups = (int)((lists + kMergeWaves - 1) / kMergeWaves);
+        hipLaunchKernelGGL(topk_merge_kernel, dim3(groups), dim3(kMergeWaves * kWave), 0, s, in, (int)lists,
+                           kMergeWaves, k, out, nullptr, nullptr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        in = out;
+        lists = groups;
+    }
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(1), dim3(kMergeWaves * kWave), 0, s, in, (int)lists, kMergeLists, k,
+                       nullptr, idx, val);
     return hipGetLastError();
 }
 
