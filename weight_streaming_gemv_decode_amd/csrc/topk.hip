@@ -212,8 +212,14 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void topk_merge_kernel(const u
     for (int j = 1; j < kListsPerWave; ++j)
         if (first + wave + j * kMergeWaves < last)  // wave-uniform
             v = merge64(v, b[j], lane);
+    // waves at or above `have` hold no list: the pairwise rounds start at the
+    // smallest power of two that covers the ones that do
+    const int have = min(last - first, kMergeWaves);
+    int top = 1;
+    while (top < have)
+        top <<= 1;
     part[wave][lane] = v;
-    for (int half = kMergeWaves / 2; half > 0; half >>= 1) {
+    for (int half = top / 2; half > 0; half >>= 1) {
         __syncthreads();
         if (wave < half)
             v = merge64(part[wave][lane], part[wave + half][lane], lane);
