@@ -42,7 +42,9 @@ def test_golden():
         assert got.tolist() == c["topk"], c["note"]
 
 
-@pytest.mark.parametrize("N", [1, 64, 2047, 2048, 2049, 248320, (1 << 20) + 7])
+# 16 / 17 / 256 lists of 2048 candidates: one merging workgroup; merging
+# groups of 16 with a last group of one list; sixteen full groups
+@pytest.mark.parametrize("N", [1, 64, 2047, 2048, 2049, 32768, 32769, 248320, 524288, (1 << 20) + 7])
 @pytest.mark.parametrize("k", [1, 2, 8, 50, 64])
 def test_random_with_ties_nan_and_signed_zero(N, k):
     if k > N:
