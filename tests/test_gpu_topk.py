@@ -42,9 +42,10 @@ def test_golden():
         assert got.tolist() == c["topk"], c["note"]
 
 
-# 16 / 17 / 256 lists of 2048 candidates: one merging workgroup; merging
-# groups of 16 with a last group of one list; sixteen full groups
-@pytest.mark.parametrize("N", [1, 64, 2047, 2048, 2049, 32768, 32769, 248320, 524288, (1 << 20) + 7])
+# 16 / 17 / 33 / 256 lists of 1024 candidates: one merging workgroup;
+# merging groups of 16 with a last group of one list; sixteen full groups
+@pytest.mark.parametrize("N", [1, 64, 1023, 1024, 1025, 2049, 16384, 16385, 32769, 248320, 262144,
+                               (1 << 20) + 7])
 @pytest.mark.parametrize("k", [1, 2, 8, 50, 64])
 def test_random_with_ties_nan_and_signed_zero(N, k):
     if k > N:
@@ -61,8 +62,9 @@ def test_random_with_ties_nan_and_signed_zero(N, k):
 
 
 def test_several_selection_passes():
-    """3,000,000 values with k = 64: the first pass leaves 93,760 candidates,
-    more than one workgroup takes, so a second pass runs before the last."""
+    """3,000,000 values with k = 64: the first pass leaves 2,930 lists
+    (187,520 candidates), more than the merge takes, so a second pass runs
+    before it."""
     say("topk multi-pass")
     N, k = 3_000_000, 64
     r = synth.rng(171, 0)

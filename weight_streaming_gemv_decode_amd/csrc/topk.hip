@@ -6,7 +6,7 @@
 //
 // Keys are unique (the index is part of the key), so the top k are exactly
 // the keys at or above the k-th largest.  A selection pass gives every
-// workgroup 2048 candidates; the workgroup finds the k-th largest by a radix
+// workgroup 1024 candidates; the workgroup finds the k-th largest by a radix
 // select on the 64-bit keys, one byte at a time from the top (a histogram of
 // the current byte over the keys that share the bytes already fixed, in
 // shared memory, then the bin that holds the k-th largest; it stops early
@@ -27,7 +27,7 @@
 namespace wsg {
 namespace {
 
-constexpr int kPerThread = 8;
+constexpr int kPerThread = 4;
 constexpr int kChunk = kBlock * kPerThread;  // candidates per workgroup of a pass
 constexpr int kMergeWaves = 16;              // waves of the merging workgroup
 constexpr int kMergeLists = 256;             // most sorted lists the merge takes
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void topk_merge_kernel(const u
 }  // namespace
 
 // The selection passes for (N, k): each turns `count` candidates into one
-// sorted list of k per 2048, until at most 256 lists remain for the merge.
+// sorted list of k per 1024, until at most 256 lists remain for the merge.
 // Returns the number of lists left; *max_keys is the most keys one pass
 // writes (each of the two ping-pong buffers must hold that many).
 int64_t topk_plan(int64_t N, int k, int64_t *max_keys, int *passes) {
