@@ -42,8 +42,9 @@ def test_golden():
         assert got.tolist() == c["topk"], c["note"]
 
 
-# 16 / 17 / 33 / 256 lists of 1024 candidates: one merging workgroup;
-# merging groups of 16 with a last group of one list; sixteen full groups
+# 16 / 17 / 33 / 256 lists of 1024 candidates: one merging workgroup; one
+# merging group of 17; groups of 32 with a last group of one list; eight
+# full groups
 @pytest.mark.parametrize("N", [1, 64, 1023, 1024, 1025, 2049, 16384, 16385, 32769, 248320, 262144,
                                (1 << 20) + 7])
 @pytest.mark.parametrize("k", [1, 2, 8, 50, 64])

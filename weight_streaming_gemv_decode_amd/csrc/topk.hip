@@ -14,8 +14,8 @@
 // above it, and one wave sorts them (bitonic, through lane exchanges).  Each
 // workgroup writes its k best keys as a sorted list.  Passes repeat until at
 // most 256 lists remain.  The merge then runs in two launches when more than
-// 16 lists remain: workgroups of 16 waves merge 16 lists each on their own
-// compute units, and one workgroup merges their results.  Two sorted lists
+// 16 lists remain: workgroups of 16 waves merge 32 lists each (two per wave)
+// on their own compute units, and one workgroup merges their results.  Two sorted lists
 // of 64 merge in one wave as the lane-wise maximum of one list and the other
 // reversed (the 64 largest of both, in bitonic order) followed by six
 // exchange stages.  No global atomics; the result does not depend on
@@ -32,6 +32,7 @@ constexpr int kChunk = kBlock * kPerThread;  // candidates per workgroup of a pa
 constexpr int kMergeWaves = 16;              // waves of the merging workgroup
 constexpr int kMergeLists = 256;             // most sorted lists the merge takes
 constexpr int kListsPerWave = kMergeLists / kMergeWaves;
+constexpr int kGroupLists = 2 * kMergeWaves;    // lists per workgroup of a first merge launch
 constexpr int kMaxK = 64;
 
 // The k largest of the workgroup's candidates (E per thread, 0 = none), in
@@ -284,11 +285,11 @@ hipError_t launch_topk(const float *y, int64_t N, int k, int32_t *idx, float *va
         out = (out == ws_a) ? ws_b : ws_a;
     }
     if (lists > kMergeWaves) {
-        // one list per wave on several compute units; the other ping-pong
+        // two lists per wave on several compute units; the other ping-pong
         // buffer (room for at least lists * k keys) takes the groups' lists
-        const int groups = (int)((lists + kMergeWaves - 1) / kMergeWaves);
+        const int groups = (int)((lists + kGroupLists - 1) / kGroupLists);
         hipLaunchKernelGGL(topk_merge_kernel, dim3(groups), dim3(kMergeWaves * kWave), 0, s, in, (int)lists,
-                           kMergeWaves, k, out, nullptr, nullptr);
+                           kGroupLists, k, out, nullptr, nullptr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
