@@ -2,8 +2,12 @@
 
 One step is the whole hot path once: 28 layers x {qkv 2048x1024, o
 1024x1024, gate+up 6144x1024, down 1024x3072} plus the 248320x1024 lm_head,
-each GEMV on its own seeded activation, replayed as a captured hipGraph.
-Inputs are resident in HBM before timing starts.  Prints one JSON line.
+each GEMV on its own seeded activation.  The timed plan is GROUPED: the 113
+GEMVs run as one kernel launch over a work table, enqueued directly each
+step (a one-launch plan is not captured into a graph: a graph launch costs
+more than the kernel launch it would replace; the ORDERED plan, one node per
+linear, is the captured hipGraph timed in the extras).  Inputs are resident
+in HBM before timing starts.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
 """

@@ -206,8 +206,10 @@ wsg_status wsg_argmax_f32(const float *y, int64_t N, int32_t *token, float *toke
  * first, NaN below every number, -0 equal to +0, lower index first among
  * equals): idx int32 [k] (out, in that order), val optional fp32 [k] (out).
  * k = 1..WSG_TOPK_MAX and k <= N <= INT32_MAX.  Selection passes keep each
- * workgroup's k best keys as a sorted list until at most 256 lists remain,
- * and one workgroup merges them; no atomics.
+ * workgroup's k best keys as a sorted list until at most 256 lists remain.
+ * Up to 16 lists are merged by one workgroup; more are first merged in
+ * groups of 32 by several workgroups (one launch), whose results one
+ * workgroup then merges (a second launch).  No atomics.
  *   ws   wsg_topk_ws_bytes(N, k) bytes, 256-byte aligned (two key buffers)
  */
 enum { WSG_TOPK_MAX = 64 };

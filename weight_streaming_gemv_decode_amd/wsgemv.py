@@ -117,17 +117,42 @@ def _stream(stream) -> int:
 
 
 def _dev(t: torch.Tensor, dtype, name: str, shape=None) -> int:
+    """Device pointer of t after checking its type, dtype, contiguity and
+    shape, and last that it lives on a GPU."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
     return t.data_ptr()
+
+
+def _check_tensor(t, dtypes, name: str, numel: Optional[int] = None, min_bytes: Optional[int] = None,
+                  optional: bool = False, device: bool = True) -> None:
+    """Checks a tensor handed to a decode-step linear, in the same order as
+    _dev: type, dtype, contiguity, size (an exact element count, or at least
+    min_bytes bytes), then (device=True) that it lives on a GPU."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()} (shape {tuple(t.shape)})")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} must hold at least {min_bytes} bytes, got {t.numel() * t.element_size()}")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
 
 
 def plan_splits(kind: int, M: int, N: int, K: int) -> int:
@@ -363,11 +388,44 @@ class Linear:
         self.scale, self.x_scale, self.acc_out, self.group, self.splits = scale, x_scale, acc_out, group, splits
         self.argmax_idx, self.argmax_val = argmax_idx, argmax_val
         self.conv_w, self.conv_bias, self.conv_state, self.conv_out = conv_w, conv_bias, conv_state, conv_out
-        self.conv_width = 0 if conv_w is None else int(conv_w.shape[1])
+        self.conv_width = 0 if conv_w is None or conv_w.dim() != 2 else int(conv_w.shape[1])
         self.conv_silu = int(bool(conv_silu))
-        if y16 is not None and (y16.dtype != torch.float16 or y16.numel() < M * N or not y16.is_contiguous()):
-            raise ValueError("y16 must be a contiguous fp16 tensor of at least M*N elements")
         self.y16 = y16   # optional fp16 copy of y, rounded to nearest even
+        self._check()
+
+    def _check(self) -> None:
+        """Every tensor against the sizes given beside it, before the plan
+        freezes their addresses: a mis-sized buffer would otherwise become an
+        out-of-bounds load or store inside a kernel."""
+        f16, i8, f32, i32 = (torch.float16,), (torch.int8,), (torch.float32,), (torch.int32,)
+        anyd = (torch.uint8, torch.int8, torch.int16, torch.int32, torch.uint32, torch.int64, torch.float16,
+                torch.float32)
+        M, N, K, kind = self.M, self.N, self.K, self.kind
+        req = []  # (tensor, dtypes, name, numel, min_bytes, optional)
+        req.append((self.y, f32, "y", M * N, None, False))
+        if kind == F16:
+            req += [(self.W, f16, "W", N * K, None, False), (self.x, f16, "x", M * K, None, False)]
+        elif kind in (W8A8, W8A8_DYN):
+            req += [(self.W, i8, "W", N * K, None, False),
+                    (self.x, i8 if kind == W8A8 else f16, "x", K, None, False),
+                    (self.scale, f32, "scale", N, None, True), (self.x_scale, f32, "x_scale", 1, None, True),
+                    (self.acc_out, i32, "acc_out", N, None, True)]
+        elif kind in (W4A16, W4A8):
+            wb, sb = packed_w4_bytes(N, K, self.group) if self.group > 0 else (0, 0)
+            req += [(self.W, anyd, "W (packed)", None, wb, False), (self.scale, anyd, "scale (packed)", None, sb, True),
+                    (self.x, f16, "x", M * K, None, False)]
+        req += [(self.argmax_idx, i32, "argmax_idx", M, None, True), (self.argmax_val, f32, "argmax_val", M, None, True)]
+        if self.conv_w is not None:
+            Wc = self.conv_width
+            req += [(self.conv_w, f16, "conv_w", N * Wc, None, False), (self.conv_bias, f32, "conv_bias", N, None, True),
+                    (self.conv_state, f32, "conv_state", N * max(Wc - 1, 0), None, False),
+                    (self.conv_out, f32, "conv_out", N, None, False)]
+        req.append((self.y16, f16, "y16", None, 2 * M * N, True))
+        # sizes of every tensor first, then where they live
+        for t, dt, name, numel, mb, opt in req:
+            _check_tensor(t, dt, name, numel=numel, min_bytes=mb, optional=opt, device=False)
+        for t, dt, name, numel, mb, opt in req:
+            _check_tensor(t, dt, name, numel=numel, min_bytes=mb, optional=opt)
 
     def c(self) -> wsg_linear:
         p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
