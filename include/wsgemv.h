@@ -90,6 +90,23 @@ wsg_status gemv_f16(const void *W, const void *x, float *y, int64_t N, int64_t K
                     int32_t splits, void *ws, size_t ws_bytes, wsg_stream_t stream);
 
 /*
+ * gemv_f16 for callers that cannot allocate device memory or pass a
+ * workspace: code under stream or graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments and result as gemv_f16
+ * without (ws, ws_bytes).  The split-K partials (S * N * 4 bytes when S > 1)
+ * live in a fixed device array of WSG_STATIC_SCRATCH_BYTES inside the library,
+ * one per GPU, held until the process ends; its address is looked up on the
+ * first call on each device.  A shape whose partials do not fit returns
+ * WSG_ERR_WORKSPACE before anything is launched.  The call allocates nothing
+ * (no hipMalloc, no hipFree).  Every call on one GPU uses that GPU's array:
+ * two calls whose work overlaps in time on one GPU (different streams, or
+ * different threads) race on it, so serialise them.
+ */
+enum { WSG_STATIC_SCRATCH_BYTES = 16 << 20 };
+wsg_status gemv_f16_static(const void *W, const void *x, float *y, int64_t N, int64_t K,
+                           int32_t splits, wsg_stream_t stream);
+
+/*
  * int8 weights x int8 activations, M = 1 (vLLM Arm CPU optimisation post,
  * INT8 W8A8 section: 8-bit weights and 8-bit activations multiplied with an
  * integer multiply-accumulate; same MiniCPM-V post, closing paragraph: INT8

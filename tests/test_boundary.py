@@ -56,6 +56,20 @@ def test_gemv_f16_validation(L):
     assert f(None, None, None, 0, 64, 0, None, 0, None) == OK               # N = 0: no-op, nothing launched
 
 
+def test_gemv_f16_static_validation(L):
+    f = L.gemv_f16_static
+    assert f(FAKE, FAKE, FAKE, -1, 64, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 12, 0, None) == SHAPE                   # K % 8
+    assert f(None, FAKE, FAKE, 4, 64, 0, None) == NULL
+    assert f(FAKE, FAKE, FAKE + 1, 4, 64, 0, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, 4, 64, 9, None) == SHAPE                   # more slices than vectors
+    # partials beyond the library's scratch array are refused before any HIP call
+    cap = wsgemv.STATIC_SCRATCH_BYTES
+    N = cap // 8 + 1
+    assert f(FAKE, FAKE, FAKE, N, 4096, 2, None) == WS
+    assert f(None, None, None, 0, 64, 0, None) == OK                      # N = 0: no-op
+
+
 def test_gemv_w8a8_validation(L):
     f = L.gemv_w8a8
     args = lambda **kw: [kw.get("W", FAKE), kw.get("ws_", FAKE), kw.get("x", FAKE), kw.get("xs", FAKE),  # noqa

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -276,6 +277,40 @@ wsg_status enqueue_dense(int kind, const DenseLin &L, const DenseCfg &cfg, hipSt
     return WSG_OK;
 }
 
+// ------------------------------------------------ allocation-free scratch --
+
+// Device scratch of gemv_f16_static: the split-K partials live in this
+// file-scope array instead of a caller workspace.  Each GPU holds its own
+// copy, at its own address, until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch_dev.
+__attribute__((used)) static __device__ __align__(256) unsigned char scratch[WSG_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use on
+// that device, with that device current).
+wsg_status static_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return WSG_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e);
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return WSG_OK;
+}
+
 // ------------------------------------------------------------------- w4 --
 
 struct W4Plan {
@@ -492,6 +527,33 @@ wsg_status gemv_f16(const void *W, const void *x, float *y, int64_t N, int64_t K
         if (st != WSG_OK)
             return st;
         DenseLin L = make_dense(kF16, W, x, y, ws, nullptr, nullptr, nullptr, N, K, p);
+        p.cfg.tail = dense_needs_tail(L, p.cfg.CH);
+        return enqueue_dense(kF16, L, p.cfg, s);
+    });
+}
+
+wsg_status gemv_f16_static(const void *W, const void *x, float *y, int64_t N, int64_t K, int32_t splits,
+                           wsg_stream_t stream) {
+    return guarded([&]() -> wsg_status {
+        wsg_status st = check_dense_args(kF16, W, x, y, N, K, splits);
+        if (st != WSG_OK || N == 0)
+            return st;
+        DensePlan p = plan_dense(kF16, N, K, splits);
+        const size_t need = K == 0 ? 0 : dense_ws_bytes(p, N);
+        if (need > (size_t)WSG_STATIC_SCRATCH_BYTES)
+            return WSG_ERR_WORKSPACE;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (K == 0) {
+            hipError_t e = launch_zero_f32(y, N, s);
+            return e == hipSuccess ? WSG_OK : hip_fail(e);
+        }
+        void *part = nullptr;
+        if (need > 0) {
+            st = static_scratch(&part);
+            if (st != WSG_OK)
+                return st;
+        }
+        DenseLin L = make_dense(kF16, W, x, y, part, nullptr, nullptr, nullptr, N, K, p);
         p.cfg.tail = dense_needs_tail(L, p.cfg.CH);
         return enqueue_dense(kF16, L, p.cfg, s);
     });

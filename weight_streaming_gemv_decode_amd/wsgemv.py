@@ -21,6 +21,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "wsgemv.h")
 
 F16, W8A8, W4A16, W4A8, W8A8_DYN = 0, 1, 2, 3, 4
 ARGMAX_WS_BYTES, WITH_ARGMAX, TOPK_MAX = 8192, 0x100, 64
+STATIC_SCRATCH_BYTES = 16 << 20
 STEP_ORDERED, STEP_GROUPED, STEP_EAGER, STEP_FORCE_GRAPH = 0, 1, 0x100, 0x200
 STEP_GRAPH_MIN_LAUNCHES = 8
 STATUS = {0: "WSG_OK", 1: "WSG_ERR_NULL", 2: "WSG_ERR_SHAPE", 3: "WSG_ERR_ALIGN", 4: "WSG_ERR_UNSUPPORTED",
@@ -55,6 +56,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "wsg_plan_splits": ([I32, I64, I64, I64], I32),
         "wsg_workspace_bytes": ([I32, I64, I64, I64, I32], SZ),
         "gemv_f16": ([P, P, P, I64, I64, I32, P, SZ, P], I32),
+        "gemv_f16_static": ([P, P, P, I64, I64, I32, P], I32),
         "gemv_w8a8": ([P, P, P, P, P, P, I64, I64, I32, P, SZ, P], I32),
         "wsg_w4_packed_weight_bytes": ([I64, I64], SZ),
         "wsg_w4_packed_scale_bytes": ([I64, I64, I64], SZ),
@@ -187,6 +189,16 @@ def gemv_f16(W: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
     wp, wn = _ws(ws)
     _check(lib().gemv_f16(_dev(W, torch.float16, "W"), _dev(x, torch.float16, "x", (K,)),
                           _dev(y, torch.float32, "y", (N,)), N, K, splits, wp, wn, _stream(stream)), "gemv_f16")
+    return y
+
+
+def gemv_f16_static(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor, splits: int = 0, stream=None) -> torch.Tensor:
+    """gemv_f16 with no workspace: the library's per-GPU scratch array holds
+    the split-K partials and the call allocates nothing.  Calls that overlap
+    in time on one GPU race on that array."""
+    N, K = W.shape
+    _check(lib().gemv_f16_static(_dev(W, torch.float16, "W"), _dev(x, torch.float16, "x", (K,)),
+                                 _dev(y, torch.float32, "y", (N,)), N, K, splits, _stream(stream)), "gemv_f16_static")
     return y
 
 
