@@ -289,6 +289,23 @@ wsg_status causal_conv1d_step(const float *x, const void *w, const float *bias, 
  *     linears feed each other (through y16) must use ORDERED.
  *   | WSG_STEP_EAGER: never capture; decode_step_linears launches directly.
  *   | WSG_STEP_FORCE_GRAPH: always capture, whatever the launch count.
+ *   mode WSG_STEP_PERSISTENT (no flags): the whole list, dependent linears
+ *     included, runs as ONE cooperative launch per step whose workgroups are
+ *     all resident at once.  A linear's input is either a buffer no linear of
+ *     the list writes, or lies wholly inside the fp16 output (y16) of one
+ *     EARLIER linear: the consumer starts its weight loads before that input
+ *     is ready and takes each input value once the producer has published it
+ *     for this step (the decode chain of the MiniCPM-V post's step, without a
+ *     launch per linear; EdgeFM summary, section 2C, one executable step per
+ *     decode iteration).  Supported: WSG_F16, M = 1, K <= 4096, splits 0 or 1,
+ *     no argmax/conv epilogue, K > 0; an input taken from a y16 must start
+ *     a multiple of 8 values into it; an input that overlaps any fp32 y, a
+ *     later or the same linear's y16, or two y16s returns
+ *     WSG_ERR_UNSUPPORTED.  Outputs are bit-identical from step to step.
+ *     Every wait inside the launch is bounded; a wait that gives up leaves
+ *     that step's results invalid and is counted (wsg_decode_step_status).
+ *     Creation allocates the plan's tables and a tagged copy (4 bytes per
+ *     output) of every y16 that feeds another linear.
  * decode_step_linears enqueues one step on `stream`.  A plan is not
  * thread-safe and one plan's steps must not overlap each other in time.
  */
@@ -328,8 +345,8 @@ typedef struct wsg_linear {
 
 typedef struct wsg_step wsg_step;
 
-enum { WSG_STEP_ORDERED = 0, WSG_STEP_GROUPED = 1, WSG_STEP_EAGER = 0x100, WSG_STEP_FORCE_GRAPH = 0x200,
-       WSG_STEP_GRAPH_MIN_LAUNCHES = 8 };
+enum { WSG_STEP_ORDERED = 0, WSG_STEP_GROUPED = 1, WSG_STEP_PERSISTENT = 2, WSG_STEP_EAGER = 0x100,
+       WSG_STEP_FORCE_GRAPH = 0x200, WSG_STEP_GRAPH_MIN_LAUNCHES = 8 };
 
 wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t mode,
                                   wsg_stream_t stream, wsg_step **out);
@@ -339,6 +356,22 @@ wsg_status wsg_decode_step_destroy(wsg_step *step);
  * step replays a captured graph (1) or launches directly (0).  Any output
  * pointer may be NULL. */
 wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t *units, int32_t *graph);
+
+/*
+ * Waits of a WSG_STEP_PERSISTENT plan that gave up since the last call
+ * (0 for other plans): synchronises `stream`, reads the plan's counter into
+ * *give_ups, then clears it.  A nonzero count means some step enqueued
+ * before this call produced invalid outputs.
+ */
+wsg_status wsg_decode_step_status(wsg_step *step, wsg_stream_t stream, uint32_t *give_ups);
+
+/*
+ * Grid of a persistent launch: min(units, min(blocks_per_cu, cap_per_cu) * cus),
+ * i.e. never more workgroups than the work units, nor than can be resident
+ * at once (blocks_per_cu from the occupancy of the kernel, cap_per_cu <= 0
+ * meaning no cap).  0 when any count is <= 0.  Pure function.
+ */
+int64_t wsg_chain_grid(int64_t units, int32_t blocks_per_cu, int32_t cus, int32_t cap_per_cu);
 
 /*
  * HBM read ceiling: every lane streams 16-byte loads over buf[0, bytes) and

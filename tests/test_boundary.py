@@ -322,3 +322,68 @@ def test_launch_size_limits(L):
     assert L.gemv_w4a16(FAKE, FAKE, FAKE, None, 1, 1 << 24, 256, 128, 0, None, 0, None) == NULL
     assert L.wsg_pack_w4(FAKE, FAKE, FAKE, FAKE, big, 1 << 14, 128, None) == UNSUP
     assert L.causal_conv1d_step(FAKE, FAKE, None, FAKE, FAKE, 1 << 40, 4, 0, None) == UNSUP
+
+
+def test_chain_grid_sizing(L):
+    """The persistent launch's grid: never more workgroups than units, nor
+    than can be resident at once (blocks per CU from the occupancy query,
+    optionally capped), and 0 for empty or invalid counts."""
+    g = L.wsg_chain_grid
+    assert g(10**9, 5, 256, 4) == 4 * 256      # capped below the resident count
+    assert g(10**9, 3, 256, 4) == 3 * 256      # the resident count is the limit
+    assert g(10**9, 5, 256, 0) == 5 * 256      # no cap
+    assert g(100, 5, 256, 4) == 100            # fewer units than slots
+    assert g(0, 5, 256, 4) == 0 and g(10, 0, 256, 4) == 0 and g(10, 5, 0, 4) == 0 and g(-1, 5, 256, 4) == 0
+    for units in (1, 255, 256, 1023, 1024, 1025, 36864):
+        for per in (1, 2, 5, 8):
+            for cap in (-1, 0, 1, 4, 16):
+                G = g(units, per, 256, cap)
+                assert 1 <= G <= units and G <= per * 256 and (cap <= 0 or G <= cap * 256)
+
+
+def test_persistent_validation(L):
+    """WSG_STEP_PERSISTENT accepts only fp16 M = 1 lists whose inputs are
+    plain buffers or lie wholly inside one earlier linear's y16; every
+    rejection returns before any HIP call."""
+    out = ctypes.c_void_p()
+    P = 2
+    y16 = FAKE + 0x100000                       # 64 outputs x 2 bytes
+
+    def lin(kind=0, N=64, K=64, x=FAKE, y=None, y16_=None, M=1, splits=0, **kw):
+        a = wsgemv.wsg_linear(kind, M, N, K, FAKE, kw.get("scale"), x, kw.get("xs"), y or FAKE + 0x10000 * (1 + N % 7),
+                              None, kw.get("group", 0), splits)
+        a.y16 = y16_
+        for k in ("argmax_idx",):
+            if k in kw:
+                setattr(a, k, kw[k])
+        return a
+
+    def create(*ls, mode=P):
+        return L.wsg_decode_step_create((wsgemv.wsg_linear * len(ls))(*ls), len(ls), mode, None, ctypes.byref(out))
+
+    a = lin(N=64, K=64, y=FAKE + 0x10000, y16_=y16)
+    assert create(a, mode=P | 0x100) == UNSUP                                     # no graph flags
+    assert create(a, mode=P | 0x200) == UNSUP
+    assert create(lin(kind=1, scale=FAKE, xs=FAKE)) == UNSUP                      # W8A8
+    assert create(lin(kind=2, K=128, scale=FAKE, group=128)) == UNSUP             # int4
+    assert create(lin(splits=2, K=4096)) == UNSUP                                 # forced split
+    assert create(lin(K=4104)) == UNSUP                                           # K > 4096
+    assert create(lin(argmax_idx=FAKE)) == UNSUP                                  # epilogue
+    # inputs against outputs: b reads 32 values (64 bytes) of a.y16 at various places
+    y_b = FAKE + 0x20000
+    for x_at, want in ((y16 + 64, "inside"), (y16 + 96, "straddles"), (y16 + 1, "odd")):
+        b = lin(N=64, K=32, x=x_at, y=y_b)
+        got = create(a, b)
+        if want == "inside":
+            assert got not in (UNSUP, SHAPE, NULL, ALIGN), got   # accepted by validation (fails later without a GPU)
+        else:
+            assert got in (UNSUP, ALIGN), (want, got)
+    b = lin(N=64, K=32, x=y16, y=y_b)
+    assert create(b, a) == UNSUP                                                  # reads a LATER linear's y16
+    c = lin(N=64, K=64, x=y16, y=FAKE + 0x30000, y16_=y16)
+    assert create(c) == UNSUP                                                     # reads its own y16
+    d = lin(N=64, K=32, x=FAKE + 0x10000, y=y_b)
+    assert create(a, d) == UNSUP                                                  # reads an fp32 y
+    e = lin(N=64, K=64, x=FAKE + 0x40000, y=FAKE + 0x50000, y16_=y16 + 64)        # its y16 overlaps a's
+    f = lin(N=64, K=64, x=y16 + 64, y=FAKE + 0x60000)                             # x inside both y16s
+    assert create(a, e, f) == UNSUP

@@ -58,6 +58,10 @@ struct Tune {
     int64_t w4_R = -1, w4_B = -1, w4_tiles = -1, group_w4_tiles = -1;
     int64_t w4_mfma_m1 = -1;     // 1: W4A16 at M = 1 on the matrix cores
     int64_t probe_U = -1, probe_chunked = -1;
+    int64_t chain_unit_kb = -1;       // persistent step: weight bytes per work unit (KiB)
+    int64_t chain_blocks_per_cu = -1; // persistent step: workgroups per compute unit (at most the resident count)
+    int64_t chain_spin_limit = -1;    // persistent step: polls before a wait gives up
+    int64_t chain_test_stale = -1;    // 1: consumers wait for a tag no producer writes (tests the give-up path)
 };
 Tune g_tune;
 
@@ -815,7 +819,11 @@ wsg_status wsg_tune_set(const char *key, int64_t value) {
                  {"group_w4_tiles", &g_tune.group_w4_tiles},
                  {"w4_mfma_m1", &g_tune.w4_mfma_m1},
                  {"probe_U", &g_tune.probe_U},
-                 {"probe_chunked", &g_tune.probe_chunked}};
+                 {"probe_chunked", &g_tune.probe_chunked},
+                 {"chain_unit_kb", &g_tune.chain_unit_kb},
+                 {"chain_blocks_per_cu", &g_tune.chain_blocks_per_cu},
+                 {"chain_spin_limit", &g_tune.chain_spin_limit},
+                 {"chain_test_stale", &g_tune.chain_test_stale}};
     for (auto &t : table) {
         if (std::strcmp(key, t.name) == 0) {
             *t.slot = value < 0 ? -1 : value;
@@ -918,6 +926,14 @@ struct wsg_step {
     std::vector<Op> ops;
     int32_t launches = 0;
     int64_t units = 0;
+
+    // persistent dependency-respecting plan (WSG_STEP_PERSISTENT)
+    bool chain = false;
+    ChainArgs chain_args{};
+    int chain_grid = 0;
+    int chain_lds = 0;
+    bool chain_tail = false;
+    uint32_t chain_epoch = 0;
 };
 
 namespace {
@@ -1065,6 +1081,200 @@ void free_step(wsg_step *st) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Owns a plan until it is handed to the caller.
+struct StepOwner {
+    wsg_step *p;
+    explicit StepOwner(wsg_step *s) : p(s) {}
+    ~StepOwner() { free_step(p); }
+    wsg_step *release() {
+        wsg_step *r = p;
+        p = nullptr;
+        return r;
+    }
+    StepOwner(const StepOwner &) = delete;
+    StepOwner &operator=(const StepOwner &) = delete;
+};
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const auto *p = static_cast<const char *>(a), *q = static_cast<const char *>(b);
+    return na > 0 && nb > 0 && p < q + nb && q < p + na;
+}
+
+// Largest input a persistent unit stages (16-byte vectors): K <= 4096.
+constexpr int kChainMaxVec = 512;
+constexpr uint32_t kChainSpinLimit = 1u << 18;
+constexpr int kChainBlocksPerCu = 4;
+
+// The persistent dependency-respecting plan: see WSG_STEP_PERSISTENT.
+wsg_status create_chain(const wsg_linear *L, int32_t n, hipStream_t s, wsg_step **out) {
+    // every linear: fp16, M = 1, whole k, no epilogue, K <= 4096
+    for (int32_t i = 0; i < n; ++i) {
+        const wsg_linear &l = L[i];
+        if (l.kind != kF16 || l.M != 1 || l.splits > 1 || l.argmax_idx || l.argmax_val || l.conv_out)
+            return WSG_ERR_UNSUPPORTED;
+        if (l.N > 0 && (l.K == 0 || l.K / 8 > kChainMaxVec))
+            return WSG_ERR_UNSUPPORTED;
+    }
+    // where each input comes from: nowhere in the list (a plain input), or
+    // wholly inside the fp16 output of one earlier linear
+    std::vector<int> prod(n, -1);
+    std::vector<int64_t> prod_off(n, 0);
+    std::vector<char> feeds(n, 0);
+    for (int32_t i = 0; i < n; ++i) {
+        const wsg_linear &l = L[i];
+        if (l.N == 0)
+            continue;
+        const size_t xb = (size_t)l.K * 2;
+        for (int32_t j = 0; j < n; ++j) {
+            if (L[j].N == 0)
+                continue;
+            if (overlaps(l.x, xb, L[j].y, (size_t)L[j].N * 4))
+                return WSG_ERR_UNSUPPORTED;  // fp32 outputs never feed, and are never overwritten while read
+            if (!L[j].y16 || !overlaps(l.x, xb, L[j].y16, (size_t)L[j].N * 2))
+                continue;
+            const auto *x0 = static_cast<const char *>(l.x), *y0 = static_cast<const char *>(L[j].y16);
+            // whole 8-value groups of the producer's outputs (aligned 64-bit tagged loads)
+            const bool inside = x0 >= y0 && x0 + xb <= y0 + (size_t)L[j].N * 2 && (x0 - y0) % 16 == 0;
+            if (j >= i || !inside || prod[i] >= 0)
+                return WSG_ERR_UNSUPPORTED;
+            prod[i] = j;
+            prod_off[i] = (x0 - y0) / 2;
+            feeds[j] = 1;
+        }
+    }
+
+    constexpr int chunk = kWave * 2;  // the kernel's vectors per row step
+    int max_nx = 0;
+    bool tail = false;
+    for (int32_t i = 0; i < n; ++i) {
+        if (L[i].N == 0)
+            continue;
+        const int kvec = (int)(L[i].K / 8);
+        max_nx = std::max(max_nx, (kvec + chunk - 1) / chunk * chunk);
+        tail = tail || kvec % chunk != 0;
+    }
+    const int lds = 2 * max_nx * 16;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = chain_blocks_per_cu(lds, tail, &per_cu);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    const int cap = g_tune.chain_blocks_per_cu > 0 ? (int)g_tune.chain_blocks_per_cu : kChainBlocksPerCu;
+    const int64_t resident = wsg_chain_grid(INT64_MAX, per_cu, cus, cap);
+    if (resident < 1)
+        return WSG_ERR_UNSUPPORTED;
+
+    // units: whole rows, sized so that each linear spreads over the grid
+    std::vector<ChainLin> lins;
+    std::vector<Unit> units;
+    std::vector<int> lin_of(n, -1);
+    for (int32_t i = 0; i < n; ++i) {
+        const wsg_linear &l = L[i];
+        if (l.N == 0)
+            continue;
+        const int64_t row_bytes = l.K * 2;
+        int64_t want = g_tune.chain_unit_kb > 0
+                           ? g_tune.chain_unit_kb * 1024
+                           : std::min<int64_t>(128 * 1024, std::max<int64_t>(16 * 1024, l.N * row_bytes / resident));
+        int64_t rows = std::max<int64_t>(8, want / row_bytes / 8 * 8);
+        rows = std::min<int64_t>(rows, cdiv(l.N, 8) * 8);
+        ChainLin c{};
+        c.W = static_cast<const u32x4 *>(l.W);
+        c.x = static_cast<const u32x4 *>(l.x);
+        c.y = l.y;
+        c.y16 = static_cast<uint16_t *>(l.y16);
+        c.N = l.N;
+        c.kvec = (int32_t)(l.K / 8);
+        c.tile_rows = (int32_t)rows;
+        c.n_tiles = (int32_t)cdiv(l.N, rows);
+        lin_of[i] = (int)lins.size();
+        for (int t = 0; t < c.n_tiles; ++t)
+            units.push_back(Unit{lin_of[i], t, 0, 0});
+        lins.push_back(c);
+    }
+    if (!grid_ok((int64_t)units.size()))
+        return WSG_ERR_UNSUPPORTED;
+
+    // device block: [control][tagged outputs][linears][units]
+    size_t off = 0;
+    const size_t ctl_off = off;
+    off = align_up(off + sizeof(ChainCtl), 256);
+    std::vector<size_t> tag_off(n, 0);
+    for (int32_t i = 0; i < n; ++i) {
+        if (!feeds[i])
+            continue;
+        tag_off[i] = off;
+        off = align_up(off + (size_t)L[i].N * 4, 256);
+    }
+    const size_t lin_off = off;
+    off = align_up(off + lins.size() * sizeof(ChainLin), 256);
+    const size_t unit_off = off;
+    off = align_up(off + units.size() * sizeof(Unit), 256);
+
+    StepOwner st(new wsg_step());
+    st.p->mode = WSG_STEP_PERSISTENT;
+    st.p->use_graph = false;
+    st.p->chain = true;
+    e = hipMalloc(&st.p->dev, off);
+    if (e != hipSuccess) {
+        st.p->dev = nullptr;
+        return e == hipErrorOutOfMemory ? WSG_ERR_NOMEM : hip_fail(e);
+    }
+    char *base = static_cast<char *>(st.p->dev);
+    for (int32_t i = 0; i < n; ++i) {
+        if (lin_of[i] < 0)
+            continue;
+        ChainLin &c = lins[lin_of[i]];
+        if (feeds[i])
+            c.tag_out = reinterpret_cast<uint32_t *>(base + tag_off[i]);
+        if (prod[i] >= 0) {
+            c.x_tag = reinterpret_cast<const uint32_t *>(base + tag_off[prod[i]]) + prod_off[i];
+            c.x = nullptr;
+        }
+    }
+    std::vector<char> host(off, 0);  // the control block and every tag start at zero
+    if (!lins.empty())
+        std::memcpy(host.data() + lin_off, lins.data(), lins.size() * sizeof(ChainLin));
+    if (!units.empty())
+        std::memcpy(host.data() + unit_off, units.data(), units.size() * sizeof(Unit));
+    e = hipMemcpyAsync(st.p->dev, host.data(), off, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+        return hip_fail(e);
+
+    ChainArgs &a = st.p->chain_args;
+    a.lins = reinterpret_cast<const ChainLin *>(base + lin_off);
+    a.units = reinterpret_cast<const Unit *>(base + unit_off);
+    a.ctl = reinterpret_cast<ChainCtl *>(base + ctl_off);
+    a.n_units = (int32_t)units.size();
+    a.xs_vecs = max_nx;
+    st.p->chain_grid = (int)wsg_chain_grid((int64_t)units.size(), per_cu, cus, cap);
+    st.p->chain_lds = lds;
+    st.p->chain_tail = tail;
+    st.p->units = (int64_t)units.size();
+    st.p->launches = units.empty() ? 0 : 1;
+    *out = st.release();
+    return WSG_OK;
+}
+
+hipError_t run_chain(wsg_step *st, hipStream_t s) {
+    if (st->chain_args.n_units == 0)
+        return hipSuccess;
+    if (++st->chain_epoch == 0)
+        st->chain_epoch = 1;
+    ChainArgs &a = st->chain_args;
+    a.epoch = st->chain_epoch;
+    a.tag = (st->chain_epoch - 1) % 65535u + 1u;
+    a.want = g_tune.chain_test_stale == 1 ? a.tag % 65535u + 1u : a.tag;
+    a.spin_limit = g_tune.chain_spin_limit >= 0 ? (uint32_t)std::min<int64_t>(g_tune.chain_spin_limit, UINT32_MAX)
+                                                : kChainSpinLimit;
+    return launch_chain(a, st->chain_grid, st->chain_lds, st->chain_tail, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1080,12 +1290,14 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
         if (n > 0 && !linears)
             return WSG_ERR_NULL;
         const int base_mode = mode & 0xFF;
-        if (base_mode != WSG_STEP_ORDERED && base_mode != WSG_STEP_GROUPED)
+        if (base_mode != WSG_STEP_ORDERED && base_mode != WSG_STEP_GROUPED && base_mode != WSG_STEP_PERSISTENT)
             return WSG_ERR_UNSUPPORTED;
         if (mode & ~(0xFF | WSG_STEP_EAGER | WSG_STEP_FORCE_GRAPH))
             return WSG_ERR_UNSUPPORTED;
         if ((mode & WSG_STEP_EAGER) && (mode & WSG_STEP_FORCE_GRAPH))
             return WSG_ERR_UNSUPPORTED;
+        if (base_mode == WSG_STEP_PERSISTENT && mode != WSG_STEP_PERSISTENT)
+            return WSG_ERR_UNSUPPORTED;  // one direct launch per step: no graph flags
         for (int32_t i = 0; i < n; ++i) {
             wsg_status v = validate_linear(linears[i]);
             if (v != WSG_OK)
@@ -1093,6 +1305,8 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             if (base_mode == WSG_STEP_GROUPED && linears[i].splits > 1)
                 return WSG_ERR_UNSUPPORTED;
         }
+        if (base_mode == WSG_STEP_PERSISTENT)
+            return create_chain(linears, n, static_cast<hipStream_t>(stream), out);
         if (base_mode == WSG_STEP_GROUPED && feeds_another(linears, n))
             return WSG_ERR_UNSUPPORTED;
         hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1489,7 +1703,9 @@ wsg_status decode_step_linears(wsg_step *step, wsg_stream_t stream) {
             return WSG_ERR_STATE;
         hipStream_t s = static_cast<hipStream_t>(stream);
         hipError_t e = hipSuccess;
-        if (step->exec)
+        if (step->chain)
+            e = run_chain(step, s);
+        else if (step->exec)
             e = hipGraphLaunch(step->exec, s);
         else
             e = run_ops(step, s);
@@ -1504,6 +1720,37 @@ wsg_status wsg_decode_step_destroy(wsg_step *step) {
         free_step(step);
         return WSG_OK;
     });
+}
+
+wsg_status wsg_decode_step_status(wsg_step *step, wsg_stream_t stream, uint32_t *give_ups) {
+    return guarded([&]() -> wsg_status {
+        if (!step)
+            return WSG_ERR_STATE;
+        if (!give_ups)
+            return WSG_ERR_NULL;
+        *give_ups = 0;
+        if (!step->chain)
+            return WSG_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        ChainCtl *ctl = step->chain_args.ctl;
+        uint32_t v = 0;
+        hipError_t e = hipStreamSynchronize(s);
+        if (e == hipSuccess)
+            e = hipMemcpy(&v, &ctl->give_ups, sizeof(v), hipMemcpyDeviceToHost);
+        if (e == hipSuccess && v != 0)
+            e = hipMemset(&ctl->give_ups, 0, sizeof(v));
+        if (e != hipSuccess)
+            return hip_fail(e);
+        *give_ups = v;
+        return WSG_OK;
+    });
+}
+
+int64_t wsg_chain_grid(int64_t units, int32_t blocks_per_cu, int32_t cus, int32_t cap_per_cu) {
+    if (units <= 0 || blocks_per_cu <= 0 || cus <= 0)
+        return 0;
+    const int64_t per = cap_per_cu > 0 ? std::min(blocks_per_cu, cap_per_cu) : blocks_per_cu;
+    return std::min(units, per * (int64_t)cus);
 }
 
 wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t *units, int32_t *graph) {

@@ -497,6 +497,221 @@ __global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
         arg_publish(L.arg, best, blockIdx.x);
 }
 
+// ------------------------------------------------- persistent chain step --
+//
+// One cooperative launch runs a whole list of fp16 linears in which a linear
+// may read (part of) an earlier linear's fp16 output.  Workgroup g runs work
+// units g, g + G, ... (G = the grid) in list order, so a unit only ever waits
+// for units of smaller index, all of which belong to resident workgroups.  A
+// unit issues its first two weight steps, then waits for its input, stages it
+// in LDS and streams the rest of its rows.  A producer publishes each output
+// as the 32-bit word (tag << 16) | fp16 with an agent-scope atomic store; a
+// consumer reads its input words with agent-scope atomic loads and takes a
+// word only when its tag is the step's, polling again (after a short sleep)
+// for the ones that are not yet current.  Every wait ends: after spin_limit
+// polls, or once another workgroup has given up in this step, the unit goes
+// on without its input and the give-up is counted for the host.
+
+constexpr int kMaxChainVec = 512;  // largest input staged per unit, in 16-byte vectors (K <= 4096)
+
+// 8 tagged words -> 8 fp16 (one LDS vector); true when every tag is `want`.
+__device__ __forceinline__ bool poll_vec(const uint32_t *p, uint32_t want, u32x4 &out) {
+    const auto *q = reinterpret_cast<const uint64_t *>(p);
+    uint64_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = __hip_atomic_load(glob(q + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+    uint32_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (uint32_t)w[i], hi = (uint32_t)(w[i] >> 32);
+        ok = ok && (lo >> 16) == want && (hi >> 16) == want;
+        v[i] = (lo & 0xFFFFu) | (hi << 16);
+    }
+    out = u32x4{v[0], v[1], v[2], v[3]};
+    return ok;
+}
+
+// The unit's input, vectors [0, nv) of L's input, into xs (zero up to nx).
+// Contains barriers; on return xs is visible to the whole workgroup.
+__device__ __forceinline__ void chain_stage(const ChainLin &L, const ChainArgs &a, int nv, int nx, u32x4 *xs) {
+    const int tid = threadIdx.x;
+    if (L.x_tag == nullptr) {
+        for (int i = tid; i < nx; i += kBlock)
+            xs[i] = i < nv ? *glob(L.x + i) : u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+        return;
+    }
+    constexpr int kPer = kMaxChainVec / kBlock;
+    __shared__ uint32_t s_stop[2];
+    uint32_t pend = 0;  // bit j: vector tid + j * kBlock is not current yet
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * kBlock;
+        if (i < nv) {
+            u32x4 v;
+            if (poll_vec(L.x_tag + 8 * (int64_t)i, a.want, v))
+                xs[i] = v;
+            else
+                pend |= 1u << j;
+        } else if (i < nx) {
+            xs[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    for (uint32_t it = 0;; ++it) {
+        // thread 0 decides for the workgroup whether to stop waiting; the
+        // decision is read by all after the barrier (two slots, so the next
+        // round's write cannot overtake a slow reader of this one)
+        if (tid == 0)
+            s_stop[it & 1] = it == 0 ? 0u
+                             : (it >= a.spin_limit ||
+                                __hip_atomic_load(&a.ctl->abort_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                                    a.epoch)
+                                 ? 1u
+                                 : 0u;
+        if (!__syncthreads_or(pend != 0))
+            return;
+        if (s_stop[it & 1]) {
+            if (tid == 0) {
+                __hip_atomic_fetch_add(&a.ctl->give_ups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.ctl->abort_epoch, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            return;
+        }
+        __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (pend & (1u << j)) {
+                const int i = tid + j * kBlock;
+                u32x4 v;
+                if (poll_vec(L.x_tag + 8 * (int64_t)i, a.want, v)) {
+                    xs[i] = v;
+                    pend &= ~(1u << j);
+                }
+            }
+        }
+    }
+}
+
+template <int R, int CH, bool TAIL>
+__device__ __forceinline__ void chain_unit(const ChainLin &L, int tile, const ChainArgs &a, u32x4 *xs) {
+    using Ops = DenseOps<kF16>;
+    constexpr int CHUNK = kWave * CH;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int nv = L.kvec;
+    const int nchunk = (nv + CHUNK - 1) / CHUNK;
+    const int64_t row0 = (int64_t)tile * L.tile_rows;
+    const int rows = (int)min((int64_t)L.tile_rows, L.N - row0);
+    const int64_t last_row = row0 + rows - 1;
+    const int ngroups = (rows + R - 1) / R;
+    const int mygroups = wave < ngroups ? (ngroups - 1 - wave) / kWavesPerBlock + 1 : 0;
+    const int nsteps = mygroups * nchunk;
+
+    auto load_step = [&](u32x4(&buf)[R][CH], int gi, int c) {
+        const int64_t rbase = row0 + (int64_t)(wave + gi * kWavesPerBlock) * R;
+        const int v0 = c * CHUNK;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x4 *p = L.W + (min(rbase + r, last_row) * L.kvec + v0);
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                if constexpr (TAIL) {
+                    buf[r][j] = u32x4{0u, 0u, 0u, 0u};
+                    if (v0 + j * kWave + lane < nv)
+                        buf[r][j] = load_w<true>(p + j * kWave + lane);
+                } else {
+                    buf[r][j] = load_w<true>(p + j * kWave + lane);
+                }
+            }
+        }
+    };
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = 0.0f;
+
+    auto consume = [&](const u32x4(&buf)[R][CH], int gi, int c) {
+        u32x4 xv[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            xv[j] = xs[c * CHUNK + j * kWave + lane];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                acc[r] = Ops::dot(buf[r][j], xv[j], acc[r]);
+        if (c == nchunk - 1) {
+            const float v = reduce_rows<R>(acc, lane);
+            constexpr int span = kWave / R;
+            if ((lane & (span - 1)) == 0) {
+                const int64_t row = row0 + (int64_t)(wave + gi * kWavesPerBlock) * R + lane / span;
+                if (row <= last_row) {
+                    const uint16_t h = f16_bits(v);
+                    *glob(L.y + row) = v;
+                    if (L.y16)
+                        *glob(L.y16 + row) = h;
+                    if (L.tag_out)
+                        __hip_atomic_store(glob(L.tag_out + row), (a.tag << 16) | h, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[r] = 0.0f;
+        }
+    };
+
+    int ga = 0, ca = 0;
+    auto next = [&](int &g, int &c) {
+        if (++c == nchunk) {
+            c = 0;
+            ++g;
+        }
+    };
+    u32x4 bufA[R][CH], bufB[R][CH];
+    int gb = 0, cb = 0;
+    next(gb, cb);
+    // the weight loads go out before the wait for the input
+    if (nsteps > 0)
+        load_step(bufA, 0, 0);
+    if (nsteps > 1)
+        load_step(bufB, gb, cb);
+    chain_stage(L, a, nv, nchunk * CHUNK, xs);
+    // a buffer is refilled with the step after next once it is consumed
+    for (int st = 0; st < nsteps; st += 2) {
+        consume(bufA, ga, ca);
+        if (st + 2 < nsteps) {
+            next(ga, ca);
+            next(ga, ca);
+            load_step(bufA, ga, ca);
+        }
+        if (st + 1 >= nsteps)
+            break;
+        consume(bufB, gb, cb);
+        if (st + 3 < nsteps) {
+            next(gb, cb);
+            next(gb, cb);
+            load_step(bufB, gb, cb);
+        }
+    }
+}
+
+template <int R, int CH, bool TAIL>
+__global__ __launch_bounds__(kBlock) void chain_kernel(ChainArgs a) {
+    extern __shared__ u32x4 xs_dyn[];
+    int k = 0;
+    for (int u = blockIdx.x; u < a.n_units; u += gridDim.x, ++k) {
+        const Unit un = a.units[u];
+        const ChainLin L = a.lins[un.lin];
+        chain_unit<R, CH, TAIL>(L, un.tile, a, xs_dyn + (k & 1) * a.xs_vecs);
+    }
+}
+
+constexpr int kChainR = 2, kChainCH = 2;
+
 __global__ __launch_bounds__(kBlock) void zero_f32_kernel(float *p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i < n)
@@ -695,6 +910,20 @@ hipError_t launch_dense_grouped(int kind, const DenseLin *lins, const Unit *unit
     if (kind == kW8A8D)
         return group_kind<kW8A8D>(lins, units, n_units, lds_bytes, c, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_chain(const ChainArgs &a, int grid, int lds_bytes, bool tail, hipStream_t s) {
+    ChainArgs args = a;
+    void *kargs[] = {&args};
+    const void *f = tail ? reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, true>)
+                         : reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, false>);
+    return hipLaunchCooperativeKernel(f, dim3(grid), dim3(kBlock), kargs, (unsigned)lds_bytes, s);
+}
+
+hipError_t chain_blocks_per_cu(int lds_bytes, bool tail, int *blocks) {
+    const void *f = tail ? reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, true>)
+                         : reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, false>);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, f, kBlock, (size_t)lds_bytes);
 }
 
 int dense_reduce_blocks(int64_t N) { return (int)((N + kBlock - 1) / kBlock); }

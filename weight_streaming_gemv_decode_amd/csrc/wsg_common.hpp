@@ -192,6 +192,44 @@ struct Unit {
     int32_t pad;
 };
 
+// One fp16 linear of a persistent dependency-respecting step (M = 1, whole
+// k per unit).  Its input is either a plain fp16 vector (x) or the tagged
+// output words of an earlier linear (x_tag): word k = (tag << 16) | fp16
+// bits of input k, current when its tag is the step's.
+struct ChainLin {
+    const u32x4 *W;          // [N][kvec]
+    const u32x4 *x;          // plain input [kvec] (x_tag == nullptr)
+    const uint32_t *x_tag;   // tagged input words [8 * kvec], or nullptr
+    float *y;                // [N]
+    uint16_t *y16;           // optional fp16 copy of y [N]
+    uint32_t *tag_out;       // optional tagged copy of y16 for later linears [N]
+    int64_t N;
+    int32_t kvec;            // 16-byte vectors per row
+    int32_t tile_rows;       // rows per work unit
+    int32_t n_tiles;
+    int32_t pad;
+};
+
+// Control block of a persistent step (its own 256-byte line).
+struct ChainCtl {
+    uint32_t give_ups;       // waits that gave up (cumulative until the host clears it)
+    uint32_t abort_epoch;    // epoch of the last step in which a wait gave up
+    uint32_t pad[62];
+};
+
+// Per-launch arguments of the persistent step kernel.
+struct ChainArgs {
+    const ChainLin *lins;
+    const Unit *units;
+    ChainCtl *ctl;
+    int32_t n_units;
+    int32_t xs_vecs;         // 16-byte vectors of one LDS input buffer (two alternate)
+    uint32_t epoch;          // step number (never 0)
+    uint32_t tag;            // written with this step's outputs (1..65535)
+    uint32_t want;           // inputs are current with this tag (== tag; tests may differ)
+    uint32_t spin_limit;     // polls before a wait gives up
+};
+
 struct DenseCfg {
     int R;        // rows per wave step
     int CH;       // 16-byte vectors per lane per row per step
@@ -225,6 +263,8 @@ hipError_t launch_dense_grouped(int kind, const DenseLin *lins, const Unit *unit
                                 int lds_bytes, const DenseCfg &c, hipStream_t s);
 hipError_t launch_dense_reduce(int kind, const DenseLin &L, hipStream_t s);
 int dense_reduce_blocks(int64_t N);
+hipError_t launch_chain(const ChainArgs &a, int grid, int lds_bytes, bool tail, hipStream_t s);
+hipError_t chain_blocks_per_cu(int lds_bytes, bool tail, int *blocks);
 hipError_t launch_w4(const W4Lin &L, int mode, const W4Cfg &c, hipStream_t s);
 hipError_t launch_w4_grouped(const W4Lin *lins, const Unit *units, int n_units, int lds_bytes,
                              int mode, const W4Cfg &c, hipStream_t s);

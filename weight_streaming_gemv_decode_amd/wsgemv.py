@@ -22,7 +22,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "wsgemv.h")
 F16, W8A8, W4A16, W4A8, W8A8_DYN = 0, 1, 2, 3, 4
 ARGMAX_WS_BYTES, WITH_ARGMAX, TOPK_MAX = 8192, 0x100, 64
 STATIC_SCRATCH_BYTES = 16 << 20
-STEP_ORDERED, STEP_GROUPED, STEP_EAGER, STEP_FORCE_GRAPH = 0, 1, 0x100, 0x200
+STEP_ORDERED, STEP_GROUPED, STEP_PERSISTENT, STEP_EAGER, STEP_FORCE_GRAPH = 0, 1, 2, 0x100, 0x200
 STEP_GRAPH_MIN_LAUNCHES = 8
 STATUS = {0: "WSG_OK", 1: "WSG_ERR_NULL", 2: "WSG_ERR_SHAPE", 3: "WSG_ERR_ALIGN", 4: "WSG_ERR_UNSUPPORTED",
           5: "WSG_ERR_WORKSPACE", 6: "WSG_ERR_HIP", 7: "WSG_ERR_NOMEM", 8: "WSG_ERR_STATE"}
@@ -73,6 +73,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "decode_step_linears": ([P, P], I32),
         "wsg_decode_step_destroy": ([P], I32),
         "wsg_decode_step_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I64), ctypes.POINTER(I32)], I32),
+        "wsg_decode_step_status": ([P, P, ctypes.POINTER(ctypes.c_uint32)], I32),
+        "wsg_chain_grid": ([I64, I32, I32, I32], I64),
         "wsg_read_probe": ([P, SZ, P, I32, P], I32),
         "wsg_read_probe_grid": ([SZ], I32),
         "wsg_tune_set": ([ctypes.c_char_p, I64], I32),
@@ -471,6 +473,12 @@ class DecodeStep:
         a, b = ctypes.c_int32(), ctypes.c_int64()
         _check(lib().wsg_decode_step_info(self._h, ctypes.byref(a), ctypes.byref(b), None), "wsg_decode_step_info")
         return a.value, b.value
+
+    def give_ups(self, stream=None) -> int:
+        """Waits of a persistent plan that gave up since the last call (synchronises the stream)."""
+        g = ctypes.c_uint32()
+        _check(lib().wsg_decode_step_status(self._h, _stream(stream), ctypes.byref(g)), "wsg_decode_step_status")
+        return int(g.value)
 
     def uses_graph(self) -> bool:
         g = ctypes.c_int32()
