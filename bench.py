@@ -303,6 +303,19 @@ def main():
             "launches": ch.info()[0],
             "note": "each linear's x is the leading K entries of the previous linear's fp16 output"}
         ch.close()
+        # the same chain as one persistent cooperative launch per step: each
+        # unit's weight loads go out before its input is ready, inputs are
+        # handed over as tagged fp16 words
+        pc = wsgemv.DecodeStep(cl, wsgemv.STEP_PERSISTENT, stream=stream)
+        for _ in range(3):
+            pc(stream)
+        s = summary(event_times(torch, lambda i: pc(stream), 50, stream))
+        t = region_time(torch, lambda i: pc(stream), 50, stream)
+        extras["c3_dependent_chain_persistent"] = {
+            "us": t * 1e3, "GBps": step_bytes / (t * 1e-3) / 1e9, "single_launch_median_us": s["median_ms"] * 1e3,
+            "launches": pc.info()[0], "work_units": pc.info()[1], "give_ups": pc.give_ups(stream),
+            "note": "the same dependent chain, one cooperative launch per step (WSG_STEP_PERSISTENT)"}
+        pc.close()
         del y16s, cl
 
     if want("token"):

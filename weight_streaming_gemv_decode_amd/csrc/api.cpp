@@ -1103,6 +1103,8 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 // Largest input a persistent unit stages (16-byte vectors): K <= 4096.
 constexpr int kChainMaxVec = 512;
 constexpr uint32_t kChainSpinLimit = 1u << 18;
+// Workgroups per compute unit (at most the resident count): on MI355X the C3
+// chain took 568-571 us with 3 or 4, 580-595 with 1 or 2.
 constexpr int kChainBlocksPerCu = 4;
 
 // The persistent dependency-respecting plan: see WSG_STEP_PERSISTENT.
@@ -1163,8 +1165,7 @@ wsg_status create_chain(const wsg_linear *L, int32_t n, hipStream_t s, wsg_step 
     if (e != hipSuccess)
         return hip_fail(e);
     const int cap = g_tune.chain_blocks_per_cu > 0 ? (int)g_tune.chain_blocks_per_cu : kChainBlocksPerCu;
-    const int64_t resident = wsg_chain_grid(INT64_MAX, per_cu, cus, cap);
-    if (resident < 1)
+    if (wsg_chain_grid(INT64_MAX, per_cu, cus, cap) < 1)
         return WSG_ERR_UNSUPPORTED;
 
     // units: whole rows, sized so that each linear spreads over the grid
@@ -1175,10 +1176,13 @@ wsg_status create_chain(const wsg_linear *L, int32_t n, hipStream_t s, wsg_step 
         const wsg_linear &l = L[i];
         if (l.N == 0)
             continue;
+        // about 32 KiB of weights per unit: both of a unit's first weight
+        // steps cover most of it, so little streaming is left once its input
+        // arrives; on MI355X the C3 chain took 568 us with 32 KiB units
+        // against 588 with units of the linear's bytes over the grid (16 to
+        // 128 KiB), 680 with 64 KiB and 896 with 128 KiB
         const int64_t row_bytes = l.K * 2;
-        int64_t want = g_tune.chain_unit_kb > 0
-                           ? g_tune.chain_unit_kb * 1024
-                           : std::min<int64_t>(128 * 1024, std::max<int64_t>(16 * 1024, l.N * row_bytes / resident));
+        const int64_t want = g_tune.chain_unit_kb > 0 ? g_tune.chain_unit_kb * 1024 : 32 * 1024;
         int64_t rows = std::max<int64_t>(8, want / row_bytes / 8 * 8);
         rows = std::min<int64_t>(rows, cdiv(l.N, 8) * 8);
         ChainLin c{};
@@ -1519,7 +1523,7 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
                     p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (mfma ? 2 : 1);
                     p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (mfma || a8 ? 4 : 8);
                     W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
-                    if (w4_lds_bytes(L, wmode) > 48 * 1024) {
+                    if (w4_lds_bytes(L, wmode) > 64 * 1024) {
                         free_step(st);
                         return WSG_ERR_UNSUPPORTED;
                     }

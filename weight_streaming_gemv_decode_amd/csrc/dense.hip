@@ -559,20 +559,30 @@ __device__ __forceinline__ void chain_stage(const ChainLin &L, const ChainArgs &
             xs[i] = u32x4{0u, 0u, 0u, 0u};
         }
     }
+    // While inputs are missing, only thread 0 polls: one input vector (a
+    // different one per workgroup, so the pollers of one input spread over
+    // its cache lines); the workgroup re-reads its missing vectors once that
+    // probe is current.  Thread 0 also decides whether to stop waiting; its
+    // decisions are read by all after the barrier (two slots, so the next
+    // round's write cannot overtake a slow reader of this one).
+    const int probe = (int)(((uint32_t)blockIdx.x * 2654435761u) % (uint32_t)nv);
     for (uint32_t it = 0;; ++it) {
-        // thread 0 decides for the workgroup whether to stop waiting; the
-        // decision is read by all after the barrier (two slots, so the next
-        // round's write cannot overtake a slow reader of this one)
-        if (tid == 0)
-            s_stop[it & 1] = it == 0 ? 0u
-                             : (it >= a.spin_limit ||
-                                __hip_atomic_load(&a.ctl->abort_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                                    a.epoch)
-                                 ? 1u
-                                 : 0u;
+        if (tid == 0) {
+            uint32_t d = 0;
+            if (it > 0) {
+                u32x4 v;
+                if (poll_vec(L.x_tag + 8 * (int64_t)probe, a.want, v))
+                    d |= 2u;
+                if (it >= a.spin_limit ||
+                    __hip_atomic_load(&a.ctl->abort_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch)
+                    d |= 1u;
+            }
+            s_stop[it & 1] = d;
+        }
         if (!__syncthreads_or(pend != 0))
             return;
-        if (s_stop[it & 1]) {
+        const uint32_t d = s_stop[it & 1];
+        if (d & 1u) {
             if (tid == 0) {
                 __hip_atomic_fetch_add(&a.ctl->give_ups, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(&a.ctl->abort_epoch, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -580,6 +590,8 @@ __device__ __forceinline__ void chain_stage(const ChainLin &L, const ChainArgs &
             return;
         }
         __builtin_amdgcn_s_sleep(8);
+        if (!(d & 2u))
+            continue;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             if (pend & (1u << j)) {

@@ -114,6 +114,10 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     const int nkb = min(L.kbs, L.kb - kb0);        // blocks in the slice
     const int nquad = (nkb + B - 1) / B;   // steps per row group
     const int nxv = nkb * 16;                      // 16-byte x vectors per row in the slice
+    // LDS row stride of the verify block's activations: a row is padded by
+    // 64 bytes, so the A-fragment reads of one instruction (rows 0..M-1, the
+    // same k) fall in different LDS banks instead of all in the same ones
+    const int xstride = nxv + kW4XRowPad;
     const int64_t n_rtiles = (L.N + 15) / 16;
     const int64_t rt0 = (int64_t)tile * L.tile_rtiles;
     const int nrt = (int)min((int64_t)L.tile_rtiles, n_rtiles - rt0);
@@ -273,7 +277,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                 f16x8 a[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    a[i] = __builtin_bit_cast(f16x8, xs[am * nxv + xv0 + 4 * i]);
+                    a[i] = __builtin_bit_cast(f16x8, xs[am * xstride + xv0 + 4 * i]);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const uint32_t words[4] = {Bf.w[r][b].x, Bf.w[r][b].y, Bf.w[r][b].z, Bf.w[r][b].w};
@@ -321,6 +325,10 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             const int m = i / nxv, v = i - m * nxv;
             return glob(L.x + m * xrow + (int64_t)kb0 * 16 + v);
         };
+        auto xdst = [&](int i) {
+            const int m = i / nxv;
+            return i + m * kW4XRowPad;
+        };
         u32x4 xh[kXHold];
 #pragma unroll
         for (int j = 0; j < kXHold; ++j) {
@@ -338,10 +346,10 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
         for (int j = 0; j < kXHold; ++j) {
             const int i = tid + j * kBlock;
             if (i < nx)
-                xs[i] = xh[j];
+                xs[xdst(i)] = xh[j];
         }
         for (int i = tid + kXHold * kBlock; i < nx; i += kBlock)
-            xs[i] = *xsrc(i);
+            xs[xdst(i)] = *xsrc(i);
         __syncthreads();
         // a buffer is refilled with the step after next once it is consumed
         for (int st = 0; st < nsteps; st += 2) {

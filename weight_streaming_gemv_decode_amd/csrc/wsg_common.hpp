@@ -301,10 +301,15 @@ inline int dense_lds_bytes(const DenseLin &L, int CH) {
 constexpr int kA8HoldVec = 2;
 __host__ __device__ inline bool a8_row_held(int64_t K) { return K / 8 <= (int64_t)kA8HoldVec * kBlock; }
 
+// Padding of each activation row of a verify block in LDS, in 16-byte vectors.
+constexpr int kW4XRowPad = 4;
+
 inline int w4_lds_bytes(const W4Lin &L, int mode) {
     if (mode == kA8)  // int8 codes of the slice, one int sum per (block, lane group), 4 floats[, the fp16 row]
         return L.kbs * 128 + L.kbs * 4 * 4 + 16 + (a8_row_held(L.K) ? L.K * 2 : 0);
-    // x slice for all M rows: kbs blocks of 128 fp16 per row
+    if (mode == kMfma)  // x slice for all M rows, each row padded
+        return L.M * (L.kbs * 16 + kW4XRowPad) * 16;
+    // x slice: kbs blocks of 128 fp16
     return L.M * L.kbs * 128 * 2;
 }
 
