@@ -23,31 +23,11 @@ import time
 
 import numpy as np
 
-PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["weight_streaming_gemv_decode_amd/csrc/dense.hip", "weight_streaming_gemv_decode_amd/csrc/wsg_common.hpp",
-                  "weight_streaming_gemv_decode_amd/csrc/argmax.hpp", "weight_streaming_gemv_decode_amd/csrc/conv1d.hpp",
-                  "weight_streaming_gemv_decode_amd/csrc/api.cpp"]
-
-
-def measured_traffic(path):
-    """Counter-measured traffic of the grouped kernel, or None when the
-    summary is missing or the kernel sources changed since it was taken."""
-    import hashlib
-    if not path or not os.path.exists(path):
-        return None
-    rec = None
-    for line in open(path):
-        if line.startswith("traffic-json: "):
-            rec = json.loads(line[len("traffic-json: "):])
-    if rec is None:
-        return None
-    h = hashlib.sha256()
-    for s in KERNEL_SOURCES:
-        h.update(open(os.path.join(HERE, s), "rb").read())
-    if h.hexdigest() != rec.get("source_sha256"):
-        return None
-    return rec
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+from weight_streaming_gemv_decode_amd.profsum import measured_traffic, measured_traffic_all  # noqa: E402
 METRIC = "achieved HBM GB/s (% of peak) for batch-1 GEMV; ms per decode-step stream"
 
 
@@ -62,9 +42,13 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB fp32 copy kernel (reads 1 GiB, writes 1 GiB) to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiler pass")
-    ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic_decode_step_f16_grouped.md"),
-                    help="profile summary holding the counter-measured per-launch HBM traffic of the grouped "
-                         "kernel; used only while the kernel sources still hash to the measured ones")
+    ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic_hbm_counters_per_config.md"),
+                    help="profile summary holding the counter-measured per-launch HBM traffic of every config; "
+                         "used only while the kernel sources still hash to the measured ones")
+    ap.add_argument("--counter-pass", default="", metavar="MANIFEST",
+                    help="run every config a few times for a rocprofv3 counter pass (FETCH_SIZE, WRITE_SIZE), "
+                         "after a copy kernel of known size, and write which launches belong to which config "
+                         "to MANIFEST (JSON); no timing, no JSON line")
     return ap.parse_args()
 
 
@@ -159,6 +143,113 @@ def summary(ts):
             "mean_ms": sum(ts) / len(ts)}
 
 
+def counter_pass(args, torch, synth, wsgemv, dev, stream):
+    """Every config a few steps, for a FETCH_SIZE or WRITE_SIZE pass; the
+    manifest says which launches belong to which config (in launch order)."""
+    configs = []
+
+    def run(label, workload, kernels, steps, nbytes, fn):
+        for i in range(steps):
+            fn(i)
+        stream.synchronize()
+        configs.append({"label": label, "workload": workload, "kernels": kernels, "steps": steps,
+                        "algorithmic_bytes": int(nbytes)})
+        log(f"counter pass: {label} ({steps} steps)")
+
+    with torch.cuda.stream(stream):
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        run("calibration", "plain fp32 copy of 1 GiB", ["AUnaryFunctor"], 3, 2 << 30,
+            lambda i: torch.mul(src, 1.0, out=dst))
+        del src, dst
+
+        step_in = synth.decode_step_f16(workload=3)
+        lins = [wsgemv.Linear(wsgemv.F16, torch.from_numpy(W).to(dev), torch.from_numpy(x).to(dev),
+                              torch.empty(W.shape[0], device=dev), W.shape[0], W.shape[1]) for _, W, x in step_in]
+        step_bytes = sum(W.nbytes + x.nbytes + W.shape[0] * 4 for _, W, x in step_in)
+        g = wsgemv.DecodeStep(lins, wsgemv.STEP_GROUPED, stream=stream)
+        run("c3_grouped", "C3 fp16 decode step, GROUPED", ["dense_grouped_kernel<0, 2, 2"], 6, step_bytes,
+            lambda i: g(stream))
+        g.close()
+        y16s, cl = [], []
+        x = lins[0].x
+        for l in lins:
+            y16 = torch.empty(l.N, dtype=torch.float16, device=dev)
+            cl.append(wsgemv.Linear(l.kind, l.W, x[:l.K], torch.empty(l.N, device=dev), l.N, l.K, y16=y16))
+            y16s.append(y16)
+            x = y16
+        pc = wsgemv.DecodeStep(cl, wsgemv.STEP_PERSISTENT, stream=stream)
+        run("c3_chain_persistent", "C3 as one dependent chain, persistent launch", ["chain_kernel<"], 6, step_bytes,
+            lambda i: pc(stream))
+        pc.close()
+        del cl, y16s
+
+        lm = lins[-1]
+        Ws = [lm.W, lm.W.clone()]
+        b = lm.N * lm.K * 2 + lm.K * 2 + lm.N * 4
+        y = torch.empty(lm.N, device=dev)
+        for S, ks in ((1, ["dense_gemv_kernel<0, 1, 2"]), (2, ["dense_gemv_kernel<0, 8, 1", "dense_reduce_kernel<0>"])):
+            ws = wsgemv.workspace(wsgemv.F16, 1, lm.N, lm.K, S, dev)
+            run(f"c2_S{S}", f"C2 lm_head 248320x1024, S = {S}", ks, 6, b,
+                lambda i: wsgemv.gemv_f16(Ws[i % 2], lm.x, y=y, splits=S, ws=ws, stream=stream))
+        del Ws, lins, step_in
+
+        N, K = synth.C1_SHAPE
+        W = torch.from_numpy(synth.f16_normal(1, 0, (N, K), synth.W_SIGMA)).to(dev)
+        xs1 = torch.from_numpy(synth.f16_normal(1, 1, (K,), synth.X_SIGMA)).to(dev)
+        copies = [W] + [W.clone() for _ in range(63)]
+        y1 = torch.empty(N, device=dev)
+        run("c1", "C1 fp16 2048x2048 (64 copies)", ["dense_gemv_kernel<0, 2, 2"], 128, N * K * 2 + K * 2 + N * 4,
+            lambda i: wsgemv.gemv_f16(copies[i % 64], xs1, y=y1, stream=stream))
+        del copies, W
+
+        for tag, (N, K) in zip("ab", synth.C4_SHAPES):
+            Wq = torch.from_numpy(synth.int8_uniform(4, 0, (N, K))).to(dev)
+            xq = torch.from_numpy(synth.int8_uniform(4, 1, (K,))).to(dev)
+            sw = torch.from_numpy(synth.f32_uniform(4, 2, (N,), 0.001, 0.01)).to(dev)
+            xsc = torch.tensor([synth.X_SCALE_W8A8], device=dev)
+            xf = torch.from_numpy(synth.f16_normal(4, 3, (K,), synth.X_SIGMA)).to(dev)
+            copies = [Wq] + [Wq.clone() for _ in range(8)]
+            y4 = torch.empty(N, device=dev)
+            acc = torch.empty(N, dtype=torch.int32, device=dev)
+            run(f"c4{tag}_w8a8", f"C4{tag} W8A8 {N}x{K} (9 copies)", ["dense_gemv_kernel<1, "], 18,
+                N * K + N * 4 + K + N * 4 + N * 4,
+                lambda i: wsgemv.gemv_w8a8(copies[i % 9], sw, xq, xsc, y=y4, acc_out=acc, stream=stream))
+            run(f"c4{tag}_w8a8_dyn", f"C4{tag} W8A8_DYN {N}x{K} (9 copies)", ["dense_gemv_kernel<4, "], 18,
+                N * K + N * 4 + 2 * K + N * 4 + N * 4,
+                lambda i: wsgemv.gemv_w8a8_dyn(copies[i % 9], sw, xf, y=y4, acc_out=acc, stream=stream))
+            del copies, Wq
+
+        for kind, M, label, kern in ((wsgemv.W4A16, 1, "c5_M1", "w4_grouped_kernel<1, 8, true, 0"),
+                                     (wsgemv.W4A16, 4, "c5_M4", "w4_grouped_kernel<2, 4, true, 1"),
+                                     (wsgemv.W4A16, 8, "c5_M8", "w4_grouped_kernel<2, 4, true, 1"),
+                                     (wsgemv.W4A8, 1, "c6", "w4_grouped_kernel<1, 4, true, 2")):
+            w4 = synth.decode_step_w4(workload=5, M=M)
+            sets = [[], []]
+            b = 0
+            for name, Wc, s4, X in w4:
+                N, K = Wc.shape[0], Wc.shape[1] * 8
+                Xd = torch.from_numpy(X if kind == wsgemv.W4A16 else X.reshape(K)).to(dev)
+                yw = torch.empty((M, N) if kind == wsgemv.W4A16 else (N,), device=dev)
+                for c in sets:
+                    Wp, Sp = wsgemv.pack_w4(torch.from_numpy(Wc.view(np.int32)).to(dev), torch.from_numpy(s4).to(dev),
+                                            stream=stream)
+                    c.append(wsgemv.Linear(kind, Wp, Xd, yw, N, K, M=M, scale=Sp, group=128))
+                b += Wc.nbytes + s4.nbytes + X.nbytes + M * N * 4
+            del w4
+            sts = [wsgemv.DecodeStep(c, wsgemv.STEP_GROUPED, stream=stream) for c in sets]
+            what = f"C5 W4A16 step, M = {M}" if kind == wsgemv.W4A16 else "C6 W4A8 step, M = 1"
+            run(label, what + " (2 packed copies)", [kern], 6, b, lambda i: sts[i % 2](stream))
+            for st in sts:
+                st.close()
+            del sets
+    torch.cuda.synchronize()
+    with open(args.counter_pass, "w") as f:
+        json.dump({"calibration": {"label": "calibration", "read_bytes": 1 << 30, "write_bytes": 1 << 30},
+                   "configs": configs}, f, indent=1)
+    log(f"manifest written: {args.counter_pass}")
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -171,6 +262,10 @@ def main():
     wsgemv.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
+
+    if args.counter_pass:
+        counter_pass(args, torch, synth, wsgemv, dev, stream)
+        return
 
     if args.calib_copy:
         # plain copy of known size for the profiler's byte counters
@@ -586,6 +681,26 @@ def main():
             t = probe_same_size(torch, wsgemv, mb << 20, stream, reps=20)
             rec[f"{mb}MiB"] = {"median_us": round(t, 2), "GBps": round((mb << 20) / (t * 1e-6) / 1e9, 1)}
         extras["hbm_read_probe"] = rec
+
+    # ---- counter-measured HBM traffic of each extra (while its kernel sources are unchanged) ----
+    recs = measured_traffic_all(args.traffic) or {}
+
+    def attach(entry, label):
+        r = recs.get(label)
+        if entry is not None and r is not None:
+            entry["traffic"] = {"bytes_per_step": r["bytes"], "ratio_to_algorithmic": r["ratio_to_algorithmic"],
+                                "read_bytes": r["read_bytes"], "write_bytes": r["write_bytes"]}
+    c2 = extras.get("c2_lm_head_248320x1024", {})
+    attach(c2.get("S=1") or c2.get("S=1 (auto)"), "c2_S1")
+    attach(c2.get("S=2"), "c2_S2")
+    attach(extras.get("c1_2048x2048"), "c1")
+    for tag, (N, K) in zip("ab", synth.C4_SHAPES):
+        attach(extras.get(f"c4_w8a8_{N}x{K}"), f"c4{tag}_w8a8")
+        attach(extras.get(f"c4_w8a8_dyn_{N}x{K}"), f"c4{tag}_w8a8_dyn")
+    for M in (1, 4, 8):
+        attach(extras.get(f"c5_w4a16_step_M{M}"), f"c5_M{M}")
+    attach(extras.get("c6_w4a8_step_M1"), "c6")
+    attach(extras.get("c3_dependent_chain_persistent"), "c3_chain_persistent")
 
     # ---- CPU oracle on the host cores, same step inputs ----
     cpu = None

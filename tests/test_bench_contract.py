@@ -21,18 +21,21 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in json.loads(line)["error"]
 
 
-def _summary(tmp_path, sha):
-    rec = {"kernel": "k", "bytes": 123, "read_bytes": 100, "write_bytes": 23, "ratio_to_algorithmic": 1.0,
-           "source_sha256": sha}
-    p = tmp_path / "traffic.md"
+def _summary(tmp_path, sha, label="c3_grouped"):
+    rec = {"label": label, "kernel": "k", "bytes": 123, "read_bytes": 100, "write_bytes": 23,
+           "ratio_to_algorithmic": 1.0, "source_sha256": sha}
+    p = tmp_path / f"traffic_{label}.md"
     p.write_text("# summary\n\ntraffic-json: " + json.dumps(rec) + "\n")
     return str(p)
 
 
 def test_traffic_only_for_the_measured_sources(tmp_path):
+    from weight_streaming_gemv_decode_amd import profsum
     h = hashlib.sha256()
-    for s in bench.KERNEL_SOURCES:
+    for s in profsum.SOURCES:
         h.update(open(os.path.join(REPO, s), "rb").read())
     assert bench.measured_traffic(_summary(tmp_path, h.hexdigest()))["bytes"] == 123
+    assert bench.measured_traffic(_summary(tmp_path, h.hexdigest(), "c1")) is None          # another config
+    assert bench.measured_traffic(_summary(tmp_path, h.hexdigest(), "c1"), "c1")["bytes"] == 123
     assert bench.measured_traffic(_summary(tmp_path, "0" * 64)) is None
     assert bench.measured_traffic(str(tmp_path / "missing.md")) is None

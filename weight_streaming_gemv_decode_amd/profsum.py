@@ -1,0 +1,176 @@
+"""Per-config HBM traffic from two rocprofv3 counter passes.
+
+A ``bench.py --counter-pass MANIFEST`` run launches a plain copy kernel of
+known size, then every config a few times over rotated weight copies, and
+writes MANIFEST: for each config, in launch order, the kernels one step of
+it launches and how many steps it ran.  Run it twice under rocprofv3, once
+with ``--pmc FETCH_SIZE`` and once with ``--pmc WRITE_SIZE`` (they cannot
+share a pass), then::
+
+    python -m weight_streaming_gemv_decode_amd.profsum --fetch F.csv --write W.csv \\
+        --manifest MANIFEST --out profiles/traffic_hbm_counters_per_config.md
+
+Each counter is scaled by what it reads for the copy kernel (which reads
+and writes a known number of bytes), dispatches are assigned to configs in
+launch order (the dispatches of other kernels, such as input set-up, are
+skipped), and every config's bytes per step are compared with its
+algorithmic bytes.  The summary ends with one ``traffic-json:`` line per
+config that bench.py attaches to its results while the kernel sources still
+hash to the ones measured.  Pure Python: no torch, no GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+from typing import Dict, List, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+REPO = os.path.dirname(HERE)
+# device code and launch planning of every measured kernel
+SOURCES = ["weight_streaming_gemv_decode_amd/csrc/dense.hip", "weight_streaming_gemv_decode_amd/csrc/w4.hip",
+           "weight_streaming_gemv_decode_amd/csrc/wsg_common.hpp", "weight_streaming_gemv_decode_amd/csrc/argmax.hpp",
+           "weight_streaming_gemv_decode_amd/csrc/conv1d.hpp", "weight_streaming_gemv_decode_amd/csrc/api.cpp"]
+COPY_KERNEL = "AUnaryFunctor"   # torch's elementwise multiply, the calibration copy
+JSON_TAG = "traffic-json: "
+
+
+def source_sha256(repo: str = REPO) -> str:
+    h = hashlib.sha256()
+    for s in SOURCES:
+        with open(os.path.join(repo, s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path: str, label: str = "c3_grouped") -> Optional[dict]:
+    """The counter record of one config from a summary, or None when the
+    summary or the config is missing or the kernel sources changed since
+    the counters were taken."""
+    recs = measured_traffic_all(path)
+    return None if recs is None else recs.get(label)
+
+
+def measured_traffic_all(path: str) -> Optional[Dict[str, dict]]:
+    if not path or not os.path.exists(path):
+        return None
+    recs = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith(JSON_TAG):
+                r = json.loads(line[len(JSON_TAG):])
+                recs[r.get("label", "c3_grouped")] = r
+    if not recs:
+        return None
+    sha = source_sha256()
+    return {k: v for k, v in recs.items() if v.get("source_sha256") == sha} or None
+
+
+def _dispatches(path: str, counter: str) -> List[tuple]:
+    """(dispatch id, kernel name, value) of one counter, in dispatch order."""
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = rows.get(d, (r["Kernel_Name"], 0.0))
+            rows[d] = (name, v + float(r["Counter_Value"]))
+    return [(d, n, v) for d, (n, v) in sorted(rows.items())]
+
+
+def per_config(path: str, counter: str, manifest: List[dict]) -> Dict[str, dict]:
+    """Average counter value per step of every manifest entry, plus the
+    copy kernel's average (entry label 'calibration')."""
+    disp = _dispatches(path, counter)
+    out = {}
+    i = 0
+    for e in manifest:
+        kernels = e["kernels"]
+        need = e["steps"] * len(kernels)
+        vals, names = [], collections.Counter()
+        while len(vals) < need and i < len(disp):
+            _, name, v = disp[i]
+            i += 1
+            hit = [k for k in kernels if k in name]
+            if hit:
+                vals.append(v)
+                names[hit[0]] += 1
+        if len(vals) < need:
+            raise ValueError(f"{e['label']}: found {len(vals)} of {need} dispatches of {kernels} in {path}")
+        out[e["label"]] = {"per_step": sum(vals) / e["steps"], "dispatches": len(vals), "kernels": dict(names)}
+    return out
+
+
+def summarize(fetch_csv: str, write_csv: str, manifest_path: str) -> List[dict]:
+    with open(manifest_path) as f:
+        man = json.load(f)
+    entries = man["configs"]
+    fetch = per_config(fetch_csv, "FETCH_SIZE", entries)
+    write = per_config(write_csv, "WRITE_SIZE", entries)
+    cal = man["calibration"]
+    fs = cal["read_bytes"] / 1024.0 / fetch[cal["label"]]["per_step"]
+    ws = cal["write_bytes"] / 1024.0 / write[cal["label"]]["per_step"]
+    sha = source_sha256()
+    recs = []
+    for e in entries:
+        if e["label"] == cal["label"]:
+            continue
+        fk, wk = fetch[e["label"]]["per_step"], write[e["label"]]["per_step"]
+        rb, wb = round(fk * 1024 * fs), round(wk * 1024 * ws)
+        recs.append({"label": e["label"], "workload": e["workload"], "kernels": e["kernels"],
+                     "steps_sampled": e["steps"], "fetch_kib_per_step": round(fk, 1), "write_kib_per_step": round(wk, 1),
+                     "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "read_bytes": rb, "write_bytes": wb,
+                     "bytes": rb + wb, "algorithmic_bytes": e["algorithmic_bytes"],
+                     "ratio_to_algorithmic": round((rb + wb) / e["algorithmic_bytes"], 4), "source_sha256": sha})
+    return recs, {"fetch_scale": fs, "write_scale": ws, "label": cal["label"],
+                  "fetch_kib": fetch[cal["label"]]["per_step"], "write_kib": write[cal["label"]]["per_step"],
+                  "read_bytes": cal["read_bytes"], "write_bytes": cal["write_bytes"]}
+
+
+def render(recs: List[dict], cal: dict, commands: List[str], notes: List[str] = ()) -> str:
+    lines = ["# HBM traffic per config: FETCH_SIZE and WRITE_SIZE counter passes", "",
+             "Two counter passes on one MI355X (one counter each), over the same `bench.py --counter-pass` run: "
+             "a plain fp32 copy of known size first, then every config over rotated weight copies (more bytes "
+             "than the 256 MB Infinity Cache), a few steps each. Commands (repository root as `$REPO`, run "
+             "from `/tmp`):", "", "```"] + commands + ["```", "",
+             f"Calibration: the copy kernel reads {cal['read_bytes']:,} B and writes {cal['write_bytes']:,} B; "
+             f"FETCH_SIZE reads {cal['fetch_kib']:.1f} KiB for it (scale {cal['fetch_scale']:.4f}) and WRITE_SIZE "
+             f"{cal['write_kib']:.1f} KiB (scale {cal['write_scale']:.4f}). Every config's counters are scaled by "
+             "these factors.", "",
+             "| Config | Kernels of one step | Steps | Read (B/step) | Written (B/step) | Algorithmic (B/step) "
+             "| Traffic / algorithmic |", "|---|---|---|---|---|---|---|"]
+    for r in recs:
+        ks = ", ".join(f"`{k}`" for k in r["kernels"])
+        lines.append(f"| {r['workload']} | {ks} | {r['steps_sampled']} | {r['read_bytes']:,} | {r['write_bytes']:,} "
+                     f"| {r['algorithmic_bytes']:,} | {r['ratio_to_algorithmic']:.4f} |")
+    lines += ["", "Algorithmic bytes are weights + scales + activations + outputs that a step needs; split-K "
+              "partials and re-read activations are excess and show up above 1.0. `source_sha256` hashes the "
+              "measured kernel sources; bench.py attaches a record to its results only while they are unchanged.",
+              ""]
+    lines += [n + "\n" for n in notes]
+    lines += [JSON_TAG + json.dumps(r) for r in recs]
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--manifest", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", action="append", default=[], help="a command line that produced the passes")
+    ap.add_argument("--note", action="append", default=[], help="a paragraph to add under the table")
+    a = ap.parse_args(argv)
+    recs, cal = summarize(a.fetch, a.write, a.manifest)
+    with open(a.out, "w") as f:
+        f.write(render(recs, cal, a.command, a.note))
+    for r in recs:
+        print(f"{r['label']:28s} {r['ratio_to_algorithmic']:.4f}")
+
+
+if __name__ == "__main__":
+    main()
