@@ -64,7 +64,8 @@ enum {
     WSG_ERR_WORKSPACE = 5,   /* workspace missing or too small for the chosen split */
     WSG_ERR_HIP = 6,         /* a HIP runtime call failed; see wsg_last_hip_error() */
     WSG_ERR_NOMEM = 7,       /* host or device allocation failed (plan creation only) */
-    WSG_ERR_STATE = 8        /* NULL or destroyed plan */
+    WSG_ERR_STATE = 8        /* NULL, destroyed or unknown plan handle (a new plan may later reuse a
+                                destroyed one's address, so do not keep destroyed handles) */
 };
 
 enum { WSG_F16 = 0, WSG_W8A8 = 1, WSG_W4A16 = 2, WSG_W4A8 = 3, WSG_W8A8_DYN = 4 }; /* wsg_linear.kind */
@@ -364,6 +365,20 @@ wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t
  * before this call produced invalid outputs.
  */
 wsg_status wsg_decode_step_status(wsg_step *step, wsg_stream_t stream, uint32_t *give_ups);
+
+/*
+ * Test hooks for plan creation on a machine without a GPU.  They only work
+ * when the environment variable WSG_ENABLE_TEST_HOOKS is "1" (otherwise
+ * WSG_ERR_UNSUPPORTED).  wsg_test_set_fault(mode): mode >= 0 makes
+ * wsg_decode_step_create build plans in host memory (such a plan cannot be
+ * launched: decode_step_linears returns WSG_ERR_STATE) and, for mode 1, 2 or
+ * 3, makes its device allocation, upload or graph capture fail (creation
+ * then returns WSG_ERR_NOMEM, WSG_ERR_HIP, WSG_ERR_HIP and frees what it
+ * made); mode -1 restores normal creation.  wsg_test_live_blocks(): host
+ * blocks of such plans not yet freed.
+ */
+wsg_status wsg_test_set_fault(int32_t mode);
+int64_t wsg_test_live_blocks(void);
 
 /*
  * Grid of a persistent launch: min(units, min(blocks_per_cu, cap_per_cu) * cus),

@@ -38,11 +38,12 @@ class OracleError(RuntimeError):
     pass
 
 
-def build(out_path: str = _LIB_PATH, defines: Sequence[str] = ()) -> str:
-    """Compile oracle.c with gcc (no fused multiply-add, no fast-math)."""
+def build(out_path: str = _LIB_PATH, defines: Sequence[str] = (), extra: Sequence[str] = ()) -> str:
+    """Compile oracle.c with gcc (no fused multiply-add, no fast-math);
+    `extra` adds compiler flags (the tests' sanitizer build)."""
     tmp = out_path + ".tmp"
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c99",
-           "-Wall", "-shared", "-fPIC", *[f"-D{d}" for d in defines], _SRC, "-o", tmp, "-lm"]
+           "-Wall", "-shared", "-fPIC", *extra, *[f"-D{d}" for d in defines], _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out_path)
     return out_path
@@ -80,6 +81,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     if path is not None:
         return _bind(ctypes.CDLL(path))
     if _lib is None:
+        alt = os.environ.get("WSG_ORACLE_LIB")  # another build of the same source (the tests' sanitizer build)
+        if alt:
+            _lib = _bind(ctypes.CDLL(alt))
+            return _lib
         if not os.path.exists(_LIB_PATH):
             build()
         _lib = _bind(ctypes.CDLL(_LIB_PATH))

@@ -57,6 +57,39 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host code checked by AddressSanitizer and UndefinedBehaviorSanitizer (the
+# device code is unchanged).  Each -fsanitize flag applies to the host pass only.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime, to preload into a
+    process that loads the sanitizer build."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_sanitized(out_dir: str) -> str:
+    """libwsgemv.so in out_dir with the host code (the C ABI, argument
+    validation, launch planning, plan creation) built under the sanitizers;
+    kernels as in build().  CPU tests load it through WSGEMV_LIB."""
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *SANITIZE_HOST, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        return obj
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, "libwsgemv.so")
+    subprocess.run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *SANITIZE_HOST, *objs, "-o", lib], check=True)
+    return lib
+
+
 def clean() -> None:
     if os.path.isdir(BUILD_DIR):
         shutil.rmtree(BUILD_DIR)

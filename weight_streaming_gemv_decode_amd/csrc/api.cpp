@@ -10,11 +10,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <unordered_set>
 #include <vector>
 
 #include "wsgemv.h"
@@ -899,6 +901,7 @@ wsg_status wsg_read_probe(const void *buf, size_t bytes, float *out, int32_t gri
 struct wsg_step {
     int32_t mode = 0;
     bool use_graph = true;
+    bool fake = false;    // built in host memory by the test mode: never launched
     hipStream_t cap = nullptr;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
@@ -937,6 +940,77 @@ struct wsg_step {
 };
 
 namespace {
+
+// ------------------------------------------------------ live plans --
+// Handles of plans that exist: calls on a NULL, destroyed or foreign handle
+// return WSG_ERR_STATE instead of touching freed memory.  (A new plan may
+// later be allocated at the address of a destroyed one.)
+std::mutex g_plans_mu;
+std::unordered_set<const wsg_step *> g_plans;
+
+void plan_register(const wsg_step *st) {
+    std::lock_guard<std::mutex> lock(g_plans_mu);
+    g_plans.insert(st);
+}
+
+bool plan_live(const wsg_step *st) {
+    std::lock_guard<std::mutex> lock(g_plans_mu);
+    return st != nullptr && g_plans.count(st) != 0;
+}
+
+bool plan_unregister(const wsg_step *st) {
+    std::lock_guard<std::mutex> lock(g_plans_mu);
+    return st != nullptr && g_plans.erase(st) != 0;
+}
+
+// ------------------------------------- device actions of plan creation --
+// Plan creation allocates one device block, uploads its tables and may
+// capture a graph.  The test mode (wsg_test_set_fault, enabled by the
+// environment) builds plans in host memory instead and can make one of these
+// actions fail, so that every failure path of creation runs on the CPU.
+enum Fault : int { kFaultNone = 0, kFaultAlloc = 1, kFaultUpload = 2, kFaultCapture = 3 };
+std::atomic<int> g_fake{0};            // 1: plans are built in host memory
+std::atomic<int> g_fault{kFaultNone};  // the action that fails in the test mode
+std::atomic<int64_t> g_fake_live{0};   // host blocks of test-mode plans not yet freed
+
+hipError_t dev_alloc(wsg_step *st, size_t bytes) {
+    if (st->fake) {
+        if (g_fault.load() == kFaultAlloc)
+            return hipErrorOutOfMemory;
+        st->dev = std::malloc(std::max<size_t>(bytes, 1));
+        if (!st->dev)
+            return hipErrorOutOfMemory;
+        ++g_fake_live;
+        return hipSuccess;
+    }
+    hipError_t e = hipMalloc(&st->dev, bytes);
+    if (e != hipSuccess)
+        st->dev = nullptr;
+    return e;
+}
+
+hipError_t dev_upload(wsg_step *st, const void *src, size_t bytes, hipStream_t s) {
+    if (st->fake) {
+        if (g_fault.load() == kFaultUpload)
+            return hipErrorInvalidValue;
+        std::memcpy(st->dev, src, bytes);
+        return hipSuccess;
+    }
+    hipError_t e = hipMemcpyAsync(st->dev, src, bytes, hipMemcpyHostToDevice, s);
+    return e == hipSuccess ? hipStreamSynchronize(s) : e;
+}
+
+void dev_free(wsg_step *st) {
+    if (!st->dev)
+        return;
+    if (st->fake) {
+        std::free(st->dev);
+        --g_fake_live;
+    } else {
+        (void)hipFree(st->dev);
+    }
+    st->dev = nullptr;
+}
 
 // Workgroups that publish keys for an int4 linear's tokens.
 int32_t w4_token_keys(const W4Lin &L) { return L.S > 1 ? w4_reduce_blocks(L.M, L.N) : L.n_tiles; }
@@ -1074,8 +1148,7 @@ void free_step(wsg_step *st) {
         (void)hipGraphDestroy(st->graph);
     if (st->cap)
         (void)hipStreamDestroy(st->cap);
-    if (st->dev)
-        (void)hipFree(st->dev);
+    dev_free(st);
     delete st;
 }
 
@@ -1086,14 +1159,458 @@ struct StepOwner {
     wsg_step *p;
     explicit StepOwner(wsg_step *s) : p(s) {}
     ~StepOwner() { free_step(p); }
-    wsg_step *release() {
-        wsg_step *r = p;
+    // hand the plan to the caller: it becomes a live handle
+    wsg_status give(wsg_step **out) {
+        plan_register(p);
+        *out = p;
         p = nullptr;
-        return r;
+        return WSG_OK;
     }
     StepOwner(const StepOwner &) = delete;
     StepOwner &operator=(const StepOwner &) = delete;
 };
+
+// The step's launch count and work units (graph or not).
+void count_launches(wsg_step &st) {
+    for (const auto &op : st.ops) {
+        st.launches += 1;
+        if (op.type == wsg_step::Op::kDense) {
+            st.units += (int64_t)op.d.n_tiles * op.d.S;
+            st.launches += op.d.S > 1;
+        } else if (op.type == wsg_step::Op::kW4) {
+            st.units += (int64_t)op.w.n_tiles * op.w.S;
+            st.launches += op.w.S > 1;
+        } else if (op.type == wsg_step::Op::kDenseGroup || op.type == wsg_step::Op::kW4Group) {
+            st.units += op.n_units;
+        } else if (op.type == wsg_step::Op::kArgmax) {
+            st.launches += 1;  // the reduce over y, then the finish kernel
+        }
+    }
+}
+
+// Captures the step's launches into a graph on an internal stream, when the
+// plan uses one.
+hipError_t capture_graph(wsg_step &st) {
+    if (!st.use_graph || st.ops.empty())
+        return hipSuccess;
+    if (st.fake) {  // the test mode never launches: the capture only fails on request
+        st.use_graph = false;
+        return g_fault.load() == kFaultCapture ? hipErrorStreamCaptureInvalidated : hipSuccess;
+    }
+    hipError_t e = hipStreamCreateWithFlags(&st.cap, hipStreamNonBlocking);
+    if (e == hipSuccess)
+        e = hipStreamBeginCapture(st.cap, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        hipError_t le = run_ops(&st, st.cap);
+        e = hipStreamEndCapture(st.cap, &st.graph);
+        if (le != hipSuccess)
+            e = le;
+    }
+    if (e == hipSuccess)
+        e = hipGraphInstantiate(&st.exec, st.graph, nullptr, nullptr, 0);
+    return e;
+}
+
+wsg_status alloc_status(hipError_t e) { return e == hipErrorOutOfMemory ? WSG_ERR_NOMEM : hip_fail(e); }
+
+// ------------------------------------------- ORDERED and GROUPED plans --
+
+// Host-side plan of an ORDERED or GROUPED step: its launches, and for a
+// GROUPED plan the work tables of each kernel kind, before the device block
+// exists; then the layout of that block.
+struct PlanBuild {
+    int base_mode = 0;
+    std::vector<DenseLin> dl[3];   // grouped dense linears per kind (F16, W8A8, W8A8D)
+    std::vector<Unit> du[3];
+    int dlds[3] = {0, 0, 0};
+    bool dtail[3] = {false, false, false};
+    std::vector<W4Lin> wl[3];      // grouped int4 linears per kernel mode (kA16, kMfma, kA8)
+    std::vector<Unit> wu[3];
+    int wlds[3] = {0, 0, 0};
+    bool wtail[3] = {false, false, false};
+    W4Cfg wcfg[3] = {};
+    DenseCfg gcfg[3] = {};
+    bool f16_hybrid = true;
+    size_t part_bytes = 0;         // split-K partials shared by the ORDERED linears (they run in order)
+    // Greedy-token key arrays (one per linear that takes a token) open the
+    // device block; descriptors get their addresses once it exists.
+    std::vector<size_t> key_off;   // per key array: offset in the keys region
+    size_t keys_bytes = 0;
+    struct TableFix {
+        bool w4;                   // false: dl[ki][li]; true: wl[ki][li]
+        int ki, li, keys;
+    };
+    std::vector<TableFix> table_fix;         // grouped descriptors that take a token
+    std::vector<wsg_step::Op> finish_after;  // their finish kernels, after the grouped launches
+    // the device block: [token keys][partials][dense tables x3][int4 tables x3]
+    size_t keys_off = 0, part_off = 0, dl_off[3] = {}, du_off[3] = {}, wl_off[3] = {}, wu_off[3] = {};
+    size_t bytes = 0;
+
+    int new_keys(int32_t n_keys, int32_t M = 1) {
+        key_off.push_back(keys_bytes);
+        keys_bytes += token_key_bytes(n_keys, M);
+        return (int)key_off.size() - 1;
+    }
+};
+
+// Grouped launches, one per kind: 8 rows x 1 vector per wave step, units of
+// at least 32 rows (64 KiB at K = 1024 fp16).  An fp16 launch whose linears
+// run no epilogue (token, conv) takes 2 rows x 2 vectors per step instead,
+// units of about 128 KiB (64 rows at K = 1024), and of 16 KiB (8 rows) for
+// linears of 16384 rows or more (the lm_head): interleaved on MI355X the
+// 113-linear step took 173.0-173.5 us against 174.0-174.8 us.  With the
+// lm_head taking the token that shape measured 181-182 us against
+// 178.6-179.3 us (at 8-, 32- and 64-row units), so plans with epilogues keep
+// the 8 x 1 shape.
+void plan_config(PlanBuild &pb, const wsg_linear *L, int32_t n) {
+    bool f16_epilogue = false;
+    for (int32_t i = 0; i < n; ++i)
+        f16_epilogue |= L[i].kind == kF16 && (L[i].argmax_idx || L[i].conv_out);
+    pb.f16_hybrid = !f16_epilogue;
+    for (auto &c : pb.gcfg)
+        c = DenseCfg{8, 1, use_nt(), false};
+    if (pb.f16_hybrid)
+        pb.gcfg[0] = DenseCfg{2, 2, use_nt(), false};
+    if (g_tune.group_R > 0 && g_tune.group_CH > 0) {
+        for (auto &c : pb.gcfg) {
+            c.R = (int)g_tune.group_R;
+            c.CH = (int)g_tune.group_CH;
+        }
+    }
+}
+
+// A linear with K = 0: y = 0 (and its copies and epilogues) by small kernels.
+void plan_k_zero(wsg_step &st, PlanBuild &pb, const wsg_linear &l) {
+    wsg_step::Op z{};
+    z.type = wsg_step::Op::kZero;
+    z.zero_p = l.y;
+    z.zero_n = (int64_t)l.M * l.N;
+    st.ops.push_back(z);
+    if ((l.kind == kW8A8 || l.kind == kW8A8D) && l.acc_out) {
+        z.zero_p = reinterpret_cast<float *>(l.acc_out);
+        z.zero_n = l.N;
+        st.ops.push_back(z);
+    }
+    if (l.y16) {
+        wsg_step::Op z16{};
+        z16.type = wsg_step::Op::kZero16;
+        z16.zero16_p = static_cast<uint16_t *>(l.y16);
+        z16.zero_n = (int64_t)l.M * l.N;
+        st.ops.push_back(z16);
+    }
+    if (l.conv_out) {
+        wsg_step::Op c{};
+        c.type = wsg_step::Op::kConv;
+        c.zero_p = l.y;
+        c.zero_n = l.N;
+        c.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
+        st.ops.push_back(c);
+    }
+    for (int32_t m = 0; l.argmax_idx && m < l.M; ++m) {
+        wsg_step::Op g{};
+        g.type = wsg_step::Op::kArgmax;
+        g.zero_p = l.y + (int64_t)m * l.N;
+        g.zero_n = l.N;
+        g.arg = arg_out(nullptr, argmax_f32_blocks(l.N), l.argmax_idx + m, l.argmax_val ? l.argmax_val + m : nullptr);
+        g.fix = pb.new_keys(g.arg.n_keys);
+        st.ops.push_back(g);
+    }
+}
+
+// An fp16 or int8-weight linear: its own launch (ORDERED) or units of the
+// kind's grouped launch (GROUPED).
+wsg_status plan_dense_linear(wsg_step &st, PlanBuild &pb, const wsg_linear &l) {
+    const int ki = l.kind == kF16 ? 0 : (l.kind == kW8A8 ? 1 : 2);
+    if (pb.base_mode == WSG_STEP_ORDERED) {
+        DensePlan p = plan_dense(l.kind, l.N, l.K, l.splits, l.argmax_idx != nullptr);
+        pb.part_bytes = std::max(pb.part_bytes, dense_ws_bytes(p, l.N));
+        wsg_step::Op o{};
+        o.type = wsg_step::Op::kDense;
+        o.kind = l.kind;
+        o.dc = p.cfg;
+        o.d = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale), l.x_scale, l.acc_out,
+                         l.N, l.K, p);
+        o.dc.tail = dense_needs_tail(o.d, o.dc.CH);
+        o.d.y16 = static_cast<uint16_t *>(l.y16);
+        if (l.conv_out)
+            o.d.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
+        if (l.argmax_idx) {
+            o.d.arg = arg_out(nullptr, dense_token_keys(o.d), l.argmax_idx, l.argmax_val);
+            o.fix = pb.new_keys(o.d.arg.n_keys);
+        }
+        st.ops.push_back(o);
+        if (l.argmax_idx) {
+            wsg_step::Op f{};
+            f.type = wsg_step::Op::kArgFinish;
+            f.arg = o.d.arg;
+            f.fix = o.fix;
+            st.ops.push_back(f);
+        }
+        return WSG_OK;
+    }
+    DensePlan p{};
+    p.cfg = pb.gcfg[ki];
+    p.S = 1;
+    p.kvs = (int)(l.K / elem_per_vec(l.kind));
+    if (p.kvs > kMaxSliceVec)
+        return WSG_ERR_UNSUPPORTED;
+    {
+        const int q = kWavesPerBlock * pb.gcfg[ki].R;
+        int64_t unit_bytes;
+        if (g_tune.group_unit_kb > 0)
+            unit_bytes = g_tune.group_unit_kb * 1024;
+        else if (l.kind != kF16 || !pb.f16_hybrid)
+            unit_bytes = 32 * 1024;
+        else
+            unit_bytes = l.N >= 16384 ? 16 * 1024 : 128 * 1024;
+        int64_t rows = unit_bytes / ((int64_t)p.kvs * 16);
+        // short rows do not fill a wave step: at most 64 rows per unit keeps
+        // such linears spread over workgroups
+        if (ki == 0 && pb.f16_hybrid && g_tune.group_unit_kb <= 0)
+            rows = std::min<int64_t>(rows, 64);
+        p.tile_rows = (int)std::min<int64_t>(1 << 20, std::max<int64_t>(q, rows / q * q));
+    }
+    DenseLin L = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale), l.x_scale, l.acc_out,
+                            l.N, l.K, p);
+    const int li = (int)pb.dl[ki].size();
+    L.y16 = static_cast<uint16_t *>(l.y16);
+    if (l.conv_out)
+        L.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
+    if (l.argmax_idx) {
+        L.arg = arg_out(nullptr, dense_token_keys(L), l.argmax_idx, l.argmax_val);
+        wsg_step::Op f{};
+        f.type = wsg_step::Op::kArgFinish;
+        f.arg = L.arg;
+        f.fix = pb.new_keys(L.arg.n_keys);
+        pb.table_fix.push_back(PlanBuild::TableFix{false, ki, li, f.fix});
+        pb.finish_after.push_back(f);
+    }
+    pb.dl[ki].push_back(L);
+    for (int t = 0; t < L.n_tiles; ++t)
+        pb.du[ki].push_back(Unit{li, t, 0, 0});
+    pb.dlds[ki] = std::max(pb.dlds[ki], dense_lds_bytes(L, pb.gcfg[ki].CH));
+    pb.dtail[ki] = pb.dtail[ki] || dense_needs_tail(L, pb.gcfg[ki].CH);
+    return WSG_OK;
+}
+
+// An int4-weight linear: its own launch (ORDERED) or units of its kernel
+// mode's grouped launch (GROUPED).
+wsg_status plan_w4_linear(wsg_step &st, PlanBuild &pb, const wsg_linear &l) {
+    const int wmode = l.kind == kW4A8 ? kA8 : ((l.M > 1 || g_tune.w4_mfma_m1 == 1) ? kMfma : kA16);
+    if (pb.base_mode == WSG_STEP_ORDERED) {
+        W4Plan p = plan_w4(l.M, l.N, l.K, l.splits);
+        pb.part_bytes = std::max(pb.part_bytes, w4_ws_bytes(p, l.M, l.N));
+        wsg_step::Op o{};
+        o.type = wsg_step::Op::kW4;
+        o.mode = wmode;
+        o.wc = p.cfg;
+        o.w = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
+        o.wc.tail = w4_needs_tail(o.w, o.wc.B);
+        o.w.y16 = static_cast<uint16_t *>(l.y16);
+        if (l.conv_out)
+            o.w.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
+        if (l.argmax_idx) {
+            o.w.arg = arg_out(nullptr, w4_token_keys(o.w), l.argmax_idx, l.argmax_val, l.M);
+            o.fix = pb.new_keys(o.w.arg.n_keys, l.M);
+        }
+        st.ops.push_back(o);
+        if (l.argmax_idx) {
+            wsg_step::Op f{};
+            f.type = wsg_step::Op::kArgFinish;
+            f.arg = o.w.arg;
+            f.fix = o.fix;
+            st.ops.push_back(f);
+        }
+        return WSG_OK;
+    }
+    W4Plan p = plan_w4(l.M, l.N, l.K, 1);
+    p.S = 1;
+    p.kbs = (int)(l.K / 128);
+    // fp16 activations, M = 1: 1 tile x 8 blocks per step, 4 tiles per unit;
+    // int8 activations: 1 tile x 4 blocks per step, 8 tiles per unit (the
+    // per-unit quantisation is amortised over more rows); verify blocks: 2
+    // tiles x 4 blocks per step, 8 tiles per unit
+    const bool a8 = wmode == kA8;
+    const bool mfma = wmode == kMfma;
+    p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles : (mfma || a8 ? 8 : 4);
+    p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (mfma ? 2 : 1);
+    p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (mfma || a8 ? 4 : 8);
+    W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
+    if (w4_lds_bytes(L, wmode) > 64 * 1024)
+        return WSG_ERR_UNSUPPORTED;
+    const int li = (int)pb.wl[wmode].size();
+    L.y16 = static_cast<uint16_t *>(l.y16);
+    if (l.conv_out)
+        L.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
+    if (l.argmax_idx) {
+        L.arg = arg_out(nullptr, w4_token_keys(L), l.argmax_idx, l.argmax_val, l.M);
+        wsg_step::Op f{};
+        f.type = wsg_step::Op::kArgFinish;
+        f.arg = L.arg;
+        f.fix = pb.new_keys(L.arg.n_keys, l.M);
+        pb.table_fix.push_back(PlanBuild::TableFix{true, wmode, li, f.fix});
+        pb.finish_after.push_back(f);
+    }
+    pb.wl[wmode].push_back(L);
+    for (int t = 0; t < L.n_tiles; ++t)
+        pb.wu[wmode].push_back(Unit{li, t, 0, 0});
+    pb.wlds[wmode] = std::max(pb.wlds[wmode], w4_lds_bytes(L, wmode));
+    pb.wtail[wmode] = pb.wtail[wmode] || w4_needs_tail(L, p.cfg.B);
+    pb.wcfg[wmode] = p.cfg;
+    return WSG_OK;
+}
+
+// Every linear of the list, in order.
+wsg_status plan_linears(wsg_step &st, PlanBuild &pb, const wsg_linear *L, int32_t n) {
+    for (int32_t i = 0; i < n; ++i) {
+        const wsg_linear &l = L[i];
+        if (l.N == 0)
+            continue;
+        wsg_status v = WSG_OK;
+        if (l.K == 0)
+            plan_k_zero(st, pb, l);
+        else if (l.kind == kF16 || l.kind == kW8A8 || l.kind == kW8A8D)
+            v = plan_dense_linear(st, pb, l);
+        else
+            v = plan_w4_linear(st, pb, l);
+        if (v != WSG_OK)
+            return v;
+    }
+    // a grouped launch covers every unit of its kind
+    for (int k = 0; k < 3; ++k)
+        if (!grid_ok((int64_t)pb.du[k].size()) || !grid_ok((int64_t)pb.wu[k].size()))
+            return WSG_ERR_UNSUPPORTED;
+    return WSG_OK;
+}
+
+// Offsets of the device block's parts and its size.
+void layout_block(PlanBuild &pb) {
+    size_t off = 0;
+    pb.keys_off = off;
+    off = align_up(off + pb.keys_bytes, 256);
+    pb.part_off = off;
+    off = align_up(off + pb.part_bytes, 256);
+    for (int k = 0; k < 3; ++k) {
+        pb.dl_off[k] = off;
+        off = align_up(off + pb.dl[k].size() * sizeof(DenseLin), 256);
+        pb.du_off[k] = off;
+        off = align_up(off + pb.du[k].size() * sizeof(Unit), 256);
+    }
+    for (int k = 0; k < 3; ++k) {
+        pb.wl_off[k] = off;
+        off = align_up(off + pb.wl[k].size() * sizeof(W4Lin), 256);
+        pb.wu_off[k] = off;
+        off = align_up(off + pb.wu[k].size() * sizeof(Unit), 256);
+    }
+    pb.bytes = off;
+}
+
+// With the device block at st.dev: the addresses of key arrays and
+// partials in every descriptor, the block's host image, and the grouped
+// launches (then the token finish kernels that follow them).
+void fill_block(wsg_step &st, PlanBuild &pb, std::vector<char> &host) {
+    char *base = static_cast<char *>(st.dev);
+    auto keys_at = [&](int fix) {
+        return reinterpret_cast<unsigned long long *>(base + pb.keys_off + pb.key_off[fix]);
+    };
+    for (const PlanBuild::TableFix &t : pb.table_fix)
+        (t.w4 ? pb.wl[t.ki][t.li].arg : pb.dl[t.ki][t.li].arg).keys = keys_at(t.keys);
+    for (auto &op : st.ops) {
+        if (op.fix < 0)
+            continue;
+        if (op.type == wsg_step::Op::kDense)
+            op.d.arg.keys = keys_at(op.fix);
+        else if (op.type == wsg_step::Op::kW4)
+            op.w.arg.keys = keys_at(op.fix);
+        else
+            op.arg.keys = keys_at(op.fix);
+    }
+    for (auto &op : pb.finish_after)
+        op.arg.keys = keys_at(op.fix);
+    auto put = [&](size_t o, const void *src, size_t bytes) {
+        if (bytes)
+            std::memcpy(host.data() + o, src, bytes);
+    };
+    for (int k = 0; k < 3; ++k) {
+        put(pb.dl_off[k], pb.dl[k].data(), pb.dl[k].size() * sizeof(DenseLin));
+        put(pb.du_off[k], pb.du[k].data(), pb.du[k].size() * sizeof(Unit));
+        put(pb.wl_off[k], pb.wl[k].data(), pb.wl[k].size() * sizeof(W4Lin));
+        put(pb.wu_off[k], pb.wu[k].data(), pb.wu[k].size() * sizeof(Unit));
+    }
+    // partials of ORDERED linears share one buffer (the ops run in order)
+    for (auto &op : st.ops) {
+        if (op.type == wsg_step::Op::kDense && op.d.S > 1)
+            op.d.part = base + pb.part_off;
+        if (op.type == wsg_step::Op::kW4 && op.w.S > 1)
+            op.w.part = reinterpret_cast<float *>(base + pb.part_off);
+    }
+    for (int k = 0; k < 3; ++k) {
+        if (pb.du[k].empty())
+            continue;
+        wsg_step::Op o{};
+        o.type = wsg_step::Op::kDenseGroup;
+        o.kind = k == 0 ? kF16 : (k == 1 ? kW8A8 : kW8A8D);
+        o.dc = pb.gcfg[k];
+        o.dc.tail = pb.dtail[k];
+        o.lins = base + pb.dl_off[k];
+        o.units = reinterpret_cast<const Unit *>(base + pb.du_off[k]);
+        o.n_units = (int)pb.du[k].size();
+        o.lds = pb.dlds[k];
+        st.ops.push_back(o);
+    }
+    for (int k = 0; k < 3; ++k) {
+        if (pb.wu[k].empty())
+            continue;
+        wsg_step::Op o{};
+        o.type = wsg_step::Op::kW4Group;
+        o.wc = pb.wcfg[k];
+        o.wc.tail = pb.wtail[k];
+        o.lins = base + pb.wl_off[k];
+        o.units = reinterpret_cast<const Unit *>(base + pb.wu_off[k]);
+        o.n_units = (int)pb.wu[k].size();
+        o.lds = pb.wlds[k];
+        o.mode = k;
+        st.ops.push_back(o);
+    }
+    for (const auto &op : pb.finish_after)
+        st.ops.push_back(op);
+}
+
+// An ORDERED or GROUPED plan: plan, lay out and allocate the device block,
+// upload it, count the launches and capture them when a graph pays off.
+wsg_status create_list(const wsg_linear *L, int32_t n, int32_t mode, hipStream_t s, wsg_step **out) {
+    StepOwner st(new wsg_step());
+    st.p->fake = g_fake.load() != 0;
+    st.p->mode = mode;
+    st.p->use_graph = !(mode & WSG_STEP_EAGER);
+    PlanBuild pb;
+    pb.base_mode = mode & 0xFF;
+    plan_config(pb, L, n);
+    wsg_status v = plan_linears(*st.p, pb, L, n);
+    if (v != WSG_OK)
+        return v;
+    layout_block(pb);
+    std::vector<char> host(pb.bytes);
+    if (pb.bytes > 0) {
+        hipError_t e = dev_alloc(st.p, pb.bytes);
+        if (e != hipSuccess)
+            return alloc_status(e);
+    }
+    fill_block(*st.p, pb, host);
+    if (pb.bytes > 0) {
+        hipError_t e = dev_upload(st.p, host.data(), pb.bytes, s);
+        if (e != hipSuccess)
+            return hip_fail(e);
+    }
+    count_launches(*st.p);
+    // a graph pays off only when it replaces enough direct launches
+    if (!(mode & WSG_STEP_FORCE_GRAPH) && st.p->launches < WSG_STEP_GRAPH_MIN_LAUNCHES)
+        st.p->use_graph = false;
+    hipError_t e = capture_graph(*st.p);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    return st.give(out);
+}
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     const auto *p = static_cast<const char *>(a), *q = static_cast<const char *>(b);
@@ -1156,14 +1673,16 @@ wsg_status create_chain(const wsg_linear *L, int32_t n, hipStream_t s, wsg_step 
         tail = tail || kvec % chunk != 0;
     }
     const int lds = 2 * max_nx * 16;
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess)
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = chain_blocks_per_cu(lds, tail, &per_cu);
-    if (e != hipSuccess)
-        return hip_fail(e);
+    int dev = 0, cus = 256, per_cu = kChainBlocksPerCu;  // the test mode's stand-in device
+    if (!g_fake.load()) {
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = chain_blocks_per_cu(lds, tail, &per_cu);
+        if (e != hipSuccess)
+            return hip_fail(e);
+    }
     const int cap = g_tune.chain_blocks_per_cu > 0 ? (int)g_tune.chain_blocks_per_cu : kChainBlocksPerCu;
     if (wsg_chain_grid(INT64_MAX, per_cu, cus, cap) < 1)
         return WSG_ERR_UNSUPPORTED;
@@ -1219,14 +1738,13 @@ wsg_status create_chain(const wsg_linear *L, int32_t n, hipStream_t s, wsg_step 
     off = align_up(off + units.size() * sizeof(Unit), 256);
 
     StepOwner st(new wsg_step());
+    st.p->fake = g_fake.load() != 0;
     st.p->mode = WSG_STEP_PERSISTENT;
     st.p->use_graph = false;
     st.p->chain = true;
-    e = hipMalloc(&st.p->dev, off);
-    if (e != hipSuccess) {
-        st.p->dev = nullptr;
-        return e == hipErrorOutOfMemory ? WSG_ERR_NOMEM : hip_fail(e);
-    }
+    hipError_t e = dev_alloc(st.p, off);
+    if (e != hipSuccess)
+        return alloc_status(e);
     char *base = static_cast<char *>(st.p->dev);
     for (int32_t i = 0; i < n; ++i) {
         if (lin_of[i] < 0)
@@ -1244,9 +1762,7 @@ wsg_status create_chain(const wsg_linear *L, int32_t n, hipStream_t s, wsg_step 
         std::memcpy(host.data() + lin_off, lins.data(), lins.size() * sizeof(ChainLin));
     if (!units.empty())
         std::memcpy(host.data() + unit_off, units.data(), units.size() * sizeof(Unit));
-    e = hipMemcpyAsync(st.p->dev, host.data(), off, hipMemcpyHostToDevice, s);
-    if (e == hipSuccess)
-        e = hipStreamSynchronize(s);
+    e = dev_upload(st.p, host.data(), off, s);
     if (e != hipSuccess)
         return hip_fail(e);
 
@@ -1261,8 +1777,7 @@ wsg_status create_chain(const wsg_linear *L, int32_t n, hipStream_t s, wsg_step 
     st.p->chain_tail = tail;
     st.p->units = (int64_t)units.size();
     st.p->launches = units.empty() ? 0 : 1;
-    *out = st.release();
-    return WSG_OK;
+    return st.give(out);
 }
 
 hipError_t run_chain(wsg_step *st, hipStream_t s) {
@@ -1309,401 +1824,18 @@ wsg_status wsg_decode_step_create(const wsg_linear *linears, int32_t n, int32_t 
             if (base_mode == WSG_STEP_GROUPED && linears[i].splits > 1)
                 return WSG_ERR_UNSUPPORTED;
         }
+        hipStream_t s = static_cast<hipStream_t>(stream);
         if (base_mode == WSG_STEP_PERSISTENT)
-            return create_chain(linears, n, static_cast<hipStream_t>(stream), out);
+            return create_chain(linears, n, s, out);
         if (base_mode == WSG_STEP_GROUPED && feeds_another(linears, n))
             return WSG_ERR_UNSUPPORTED;
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        wsg_step *st = new wsg_step();
-        st->mode = mode;
-        st->use_graph = !(mode & WSG_STEP_EAGER);
-
-        // Host-side plan: ops, plus the byte layout of the device block.
-        std::vector<DenseLin> dl[3];           // grouped dense linears per kind (F16, W8A8, W8A8D)
-        std::vector<Unit> du[3];
-        int dlds[3] = {0, 0, 0};
-        bool dtail[3] = {false, false, false};
-        std::vector<W4Lin> wl[3];              // grouped int4 linears per kernel mode (kA16, kMfma, kA8)
-        std::vector<Unit> wu[3];
-        int wlds[3] = {0, 0, 0};
-        bool wtail[3] = {false, false, false};
-        W4Cfg wcfg[3] = {};
-        size_t part_bytes = 0;
-        // Grouped launches, one per kind: 8 rows x 1 vector per wave step,
-        // units of at least 32 rows (64 KiB at K = 1024 fp16).  An fp16 launch
-        // whose linears run no epilogue (token, conv) takes 2 rows x 2 vectors
-        // per step instead, units of about 128 KiB (64 rows at K = 1024), and
-        // of 16 KiB (8 rows) for linears of 16384 rows or more (the lm_head):
-        // interleaved on MI355X the 113-linear step took 173.0-173.5 us
-        // against 174.0-174.8 us.  With the lm_head taking the token that
-        // shape measured 181-182 us against 178.6-179.3 us (at 8-, 32- and
-        // 64-row units), so plans with epilogues keep the 8 x 1 shape.
-        bool f16_epilogue = false;
-        for (int32_t i = 0; i < n; ++i)
-            f16_epilogue |= linears[i].kind == kF16 && (linears[i].argmax_idx || linears[i].conv_out);
-        const bool f16_hybrid = !f16_epilogue;
-        DenseCfg gcfg[3] = {{8, 1, use_nt(), false}, {8, 1, use_nt(), false}, {8, 1, use_nt(), false}};
-        if (f16_hybrid)
-            gcfg[0] = DenseCfg{2, 2, use_nt(), false};
-        if (g_tune.group_R > 0 && g_tune.group_CH > 0) {
-            for (auto &c : gcfg) {
-                c.R = (int)g_tune.group_R;
-                c.CH = (int)g_tune.group_CH;
-            }
-        }
-        auto unit_bytes = [&](const wsg_linear &l) -> int64_t {
-            if (g_tune.group_unit_kb > 0)
-                return g_tune.group_unit_kb * 1024;
-            if (l.kind != kF16 || !f16_hybrid)
-                return 32 * 1024;
-            return l.N >= 16384 ? 16 * 1024 : 128 * 1024;
-        };
-        // Greedy-token key arrays (one per linear that takes a token) open the
-        // device block; descriptors get their addresses once it exists.
-        std::vector<size_t> key_off;           // per key array: offset in the keys region
-        size_t keys_bytes = 0;
-        auto new_keys = [&](int32_t n_keys, int32_t M = 1) {
-            key_off.push_back(keys_bytes);
-            keys_bytes += token_key_bytes(n_keys, M);
-            return (int)key_off.size() - 1;
-        };
-        struct TableFix {
-            bool w4;      // false: dl[ki][li]; true: wl[ki][li]
-            int ki, li, keys;
-        };
-        std::vector<TableFix> table_fix;       // grouped dense descriptors that take a token
-        std::vector<wsg_step::Op> finish_after;  // their finish kernels, after the grouped launches
-
-        for (int32_t i = 0; i < n; ++i) {
-            const wsg_linear &l = linears[i];
-            if (l.N == 0)
-                continue;
-            if (l.K == 0) {
-                wsg_step::Op z{};
-                z.type = wsg_step::Op::kZero;
-                z.zero_p = l.y;
-                z.zero_n = (int64_t)l.M * l.N;
-                st->ops.push_back(z);
-                if ((l.kind == kW8A8 || l.kind == kW8A8D) && l.acc_out) {
-                    z.zero_p = reinterpret_cast<float *>(l.acc_out);
-                    z.zero_n = l.N;
-                    st->ops.push_back(z);
-                }
-                if (l.y16) {
-                    wsg_step::Op z16{};
-                    z16.type = wsg_step::Op::kZero16;
-                    z16.zero16_p = static_cast<uint16_t *>(l.y16);
-                    z16.zero_n = (int64_t)l.M * l.N;
-                    st->ops.push_back(z16);
-                }
-                if (l.conv_out) {
-                    wsg_step::Op c{};
-                    c.type = wsg_step::Op::kConv;
-                    c.zero_p = l.y;
-                    c.zero_n = l.N;
-                    c.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
-                    st->ops.push_back(c);
-                }
-                for (int32_t m = 0; l.argmax_idx && m < l.M; ++m) {
-                    wsg_step::Op g{};
-                    g.type = wsg_step::Op::kArgmax;
-                    g.zero_p = l.y + (int64_t)m * l.N;
-                    g.zero_n = l.N;
-                    g.arg = arg_out(nullptr, argmax_f32_blocks(l.N), l.argmax_idx + m,
-                                    l.argmax_val ? l.argmax_val + m : nullptr);
-                    g.fix = new_keys(g.arg.n_keys);
-                    st->ops.push_back(g);
-                }
-                continue;
-            }
-            if (l.kind == kF16 || l.kind == kW8A8 || l.kind == kW8A8D) {
-                const int ki = l.kind == kF16 ? 0 : (l.kind == kW8A8 ? 1 : 2);
-                if (base_mode == WSG_STEP_ORDERED) {
-                    DensePlan p = plan_dense(l.kind, l.N, l.K, l.splits, l.argmax_idx != nullptr);
-                    part_bytes = std::max(part_bytes, dense_ws_bytes(p, l.N));
-                    wsg_step::Op o{};
-                    o.type = wsg_step::Op::kDense;
-                    o.kind = l.kind;
-                    o.dc = p.cfg;
-                    o.d = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale), l.x_scale,
-                                     l.acc_out, l.N, l.K, p);
-                    o.dc.tail = dense_needs_tail(o.d, o.dc.CH);
-                    o.d.y16 = static_cast<uint16_t *>(l.y16);
-                    if (l.conv_out)
-                        o.d.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
-                    if (l.argmax_idx) {
-                        o.d.arg = arg_out(nullptr, dense_token_keys(o.d), l.argmax_idx, l.argmax_val);
-                        o.fix = new_keys(o.d.arg.n_keys);
-                    }
-                    st->ops.push_back(o);
-                    if (l.argmax_idx) {
-                        wsg_step::Op f{};
-                        f.type = wsg_step::Op::kArgFinish;
-                        f.arg = o.d.arg;
-                        f.fix = o.fix;
-                        st->ops.push_back(f);
-                    }
-                } else {
-                    DensePlan p{};
-                    p.cfg = gcfg[ki];
-                    p.S = 1;
-                    p.kvs = (int)(l.K / elem_per_vec(l.kind));
-                    if (p.kvs > kMaxSliceVec) {
-                        free_step(st);
-                        return WSG_ERR_UNSUPPORTED;
-                    }
-                    {
-                        const int q = kWavesPerBlock * gcfg[ki].R;
-                        int64_t rows = unit_bytes(l) / ((int64_t)p.kvs * 16);
-                        // short rows do not fill a wave step: at most 64 rows
-                        // per unit keeps such linears spread over workgroups
-                        if (ki == 0 && f16_hybrid && g_tune.group_unit_kb <= 0)
-                            rows = std::min<int64_t>(rows, 64);
-                        p.tile_rows = (int)std::min<int64_t>(1 << 20, std::max<int64_t>(q, rows / q * q));
-                    }
-                    DenseLin L = make_dense(l.kind, l.W, l.x, l.y, nullptr, static_cast<const float *>(l.scale),
-                                            l.x_scale, l.acc_out, l.N, l.K, p);
-                    const int li = (int)dl[ki].size();
-                    L.y16 = static_cast<uint16_t *>(l.y16);
-                    if (l.conv_out)
-                        L.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
-                    if (l.argmax_idx) {
-                        L.arg = arg_out(nullptr, dense_token_keys(L), l.argmax_idx, l.argmax_val);
-                        wsg_step::Op f{};
-                        f.type = wsg_step::Op::kArgFinish;
-                        f.arg = L.arg;
-                        f.fix = new_keys(L.arg.n_keys);
-                        table_fix.push_back(TableFix{false, ki, li, f.fix});
-                        finish_after.push_back(f);
-                    }
-                    dl[ki].push_back(L);
-                    for (int t = 0; t < L.n_tiles; ++t)
-                        du[ki].push_back(Unit{li, t, 0, 0});
-                    dlds[ki] = std::max(dlds[ki], dense_lds_bytes(L, gcfg[ki].CH));
-                    dtail[ki] = dtail[ki] || dense_needs_tail(L, gcfg[ki].CH);
-                }
-            } else {
-                const int wmode = l.kind == kW4A8 ? kA8 : ((l.M > 1 || g_tune.w4_mfma_m1 == 1) ? kMfma : kA16);
-                if (base_mode == WSG_STEP_ORDERED) {
-                    W4Plan p = plan_w4(l.M, l.N, l.K, l.splits);
-                    part_bytes = std::max(part_bytes, w4_ws_bytes(p, l.M, l.N));
-                    wsg_step::Op o{};
-                    o.type = wsg_step::Op::kW4;
-                    o.mode = wmode;
-                    o.wc = p.cfg;
-                    o.w = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
-                    o.wc.tail = w4_needs_tail(o.w, o.wc.B);
-                    o.w.y16 = static_cast<uint16_t *>(l.y16);
-                    if (l.conv_out)
-                        o.w.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
-                    if (l.argmax_idx) {
-                        o.w.arg = arg_out(nullptr, w4_token_keys(o.w), l.argmax_idx, l.argmax_val, l.M);
-                        o.fix = new_keys(o.w.arg.n_keys, l.M);
-                    }
-                    st->ops.push_back(o);
-                    if (l.argmax_idx) {
-                        wsg_step::Op f{};
-                        f.type = wsg_step::Op::kArgFinish;
-                        f.arg = o.w.arg;
-                        f.fix = o.fix;
-                        st->ops.push_back(f);
-                    }
-                } else {
-                    W4Plan p = plan_w4(l.M, l.N, l.K, 1);
-                    p.S = 1;
-                    p.kbs = (int)(l.K / 128);
-                    // fp16 activations, M = 1: 1 tile x 8 blocks per step, 4 tiles per unit;
-                    // int8 activations: 1 tile x 4 blocks per step, 8 tiles per unit (the
-                    // per-unit quantisation is amortised over more rows);
-                    // verify blocks: 2 tiles x 4 blocks per step, 8 tiles per unit
-                    const bool a8 = wmode == kA8;
-                    const bool mfma = wmode == kMfma;
-                    p.tile_rtiles = g_tune.group_w4_tiles > 0 ? (int)g_tune.group_w4_tiles
-                                                              : (mfma || a8 ? 8 : 4);
-                    p.cfg.R = g_tune.w4_R > 0 ? (int)g_tune.w4_R : (mfma ? 2 : 1);
-                    p.cfg.B = g_tune.w4_B > 0 ? (int)g_tune.w4_B : (mfma || a8 ? 4 : 8);
-                    W4Lin L = make_w4(l.W, l.scale, l.x, l.y, nullptr, l.M, l.N, l.K, p);
-                    if (w4_lds_bytes(L, wmode) > 64 * 1024) {
-                        free_step(st);
-                        return WSG_ERR_UNSUPPORTED;
-                    }
-                    const int li = (int)wl[wmode].size();
-                    L.y16 = static_cast<uint16_t *>(l.y16);
-                    if (l.conv_out)
-                        L.conv = conv_out(l.conv_w, l.conv_bias, l.conv_state, l.conv_out, l.conv_width, l.conv_silu);
-                    if (l.argmax_idx) {
-                        L.arg = arg_out(nullptr, w4_token_keys(L), l.argmax_idx, l.argmax_val, l.M);
-                        wsg_step::Op f{};
-                        f.type = wsg_step::Op::kArgFinish;
-                        f.arg = L.arg;
-                        f.fix = new_keys(L.arg.n_keys, l.M);
-                        table_fix.push_back(TableFix{true, wmode, li, f.fix});
-                        finish_after.push_back(f);
-                    }
-                    wl[wmode].push_back(L);
-                    for (int t = 0; t < L.n_tiles; ++t)
-                        wu[wmode].push_back(Unit{li, t, 0, 0});
-                    wlds[wmode] = std::max(wlds[wmode], w4_lds_bytes(L, wmode));
-                    wtail[wmode] = wtail[wmode] || w4_needs_tail(L, p.cfg.B);
-                    wcfg[wmode] = p.cfg;
-                }
-            }
-        }
-
-        // a grouped launch covers every unit of its kind
-        for (int k = 0; k < 3; ++k) {
-            if (!grid_ok((int64_t)du[k].size()) || !grid_ok((int64_t)wu[k].size())) {
-                free_step(st);
-                return WSG_ERR_UNSUPPORTED;
-            }
-        }
-
-        // Device block: [token keys][partials][dense tables x2][int4 tables x3]
-        size_t off = 0;
-        const size_t keys_off = off;
-        off = align_up(off + keys_bytes, 256);
-        const size_t part_off = off;
-        off = align_up(off + part_bytes, 256);
-        size_t dl_off[3], du_off[3], wl_off[3], wu_off[3];
-        for (int k = 0; k < 3; ++k) {
-            dl_off[k] = off;
-            off = align_up(off + dl[k].size() * sizeof(DenseLin), 256);
-            du_off[k] = off;
-            off = align_up(off + du[k].size() * sizeof(Unit), 256);
-        }
-        for (int k = 0; k < 3; ++k) {
-            wl_off[k] = off;
-            off = align_up(off + wl[k].size() * sizeof(W4Lin), 256);
-            wu_off[k] = off;
-            off = align_up(off + wu[k].size() * sizeof(Unit), 256);
-        }
-        if (off > 0) {
-            hipError_t e = hipMalloc(&st->dev, off);
-            if (e != hipSuccess) {
-                st->dev = nullptr;
-                free_step(st);
-                return e == hipErrorOutOfMemory ? WSG_ERR_NOMEM : hip_fail(e);
-            }
-        }
-        char *base = static_cast<char *>(st->dev);
-        std::vector<char> host(off);
-        auto keys_at = [&](int fix) {
-            return reinterpret_cast<unsigned long long *>(base + keys_off + key_off[fix]);
-        };
-        for (const TableFix &t : table_fix)
-            (t.w4 ? wl[t.ki][t.li].arg : dl[t.ki][t.li].arg).keys = keys_at(t.keys);
-        for (auto &op : st->ops) {
-            if (op.fix < 0)
-                continue;
-            if (op.type == wsg_step::Op::kDense)
-                op.d.arg.keys = keys_at(op.fix);
-            else if (op.type == wsg_step::Op::kW4)
-                op.w.arg.keys = keys_at(op.fix);
-            else
-                op.arg.keys = keys_at(op.fix);
-        }
-        for (auto &op : finish_after)
-            op.arg.keys = keys_at(op.fix);
-        auto put = [&](size_t o, const void *src, size_t bytes) {
-            if (bytes)
-                std::memcpy(host.data() + o, src, bytes);
-        };
-        for (int k = 0; k < 3; ++k) {
-            put(dl_off[k], dl[k].data(), dl[k].size() * sizeof(DenseLin));
-            put(du_off[k], du[k].data(), du[k].size() * sizeof(Unit));
-        }
-        for (int k = 0; k < 3; ++k) {
-            put(wl_off[k], wl[k].data(), wl[k].size() * sizeof(W4Lin));
-            put(wu_off[k], wu[k].data(), wu[k].size() * sizeof(Unit));
-        }
-        // partials of ORDERED linears share one buffer (the ops run in order)
-        for (auto &op : st->ops) {
-            if (op.type == wsg_step::Op::kDense && op.d.S > 1)
-                op.d.part = base + part_off;
-            if (op.type == wsg_step::Op::kW4 && op.w.S > 1)
-                op.w.part = reinterpret_cast<float *>(base + part_off);
-        }
-        for (int k = 0; k < 3; ++k) {
-            if (!du[k].empty()) {
-                wsg_step::Op o{};
-                o.type = wsg_step::Op::kDenseGroup;
-                o.kind = k == 0 ? kF16 : (k == 1 ? kW8A8 : kW8A8D);
-                o.dc = gcfg[k];
-                o.dc.tail = dtail[k];
-                o.lins = base + dl_off[k];
-                o.units = reinterpret_cast<const Unit *>(base + du_off[k]);
-                o.n_units = (int)du[k].size();
-                o.lds = dlds[k];
-                st->ops.push_back(o);
-            }
-        }
-        for (int k = 0; k < 3; ++k) {
-            if (!wu[k].empty()) {
-                wsg_step::Op o{};
-                o.type = wsg_step::Op::kW4Group;
-                o.wc = wcfg[k];
-                o.wc.tail = wtail[k];
-                o.lins = base + wl_off[k];
-                o.units = reinterpret_cast<const Unit *>(base + wu_off[k]);
-                o.n_units = (int)wu[k].size();
-                o.lds = wlds[k];
-                o.mode = k;
-                st->ops.push_back(o);
-            }
-        }
-        for (const auto &op : finish_after)
-            st->ops.push_back(op);
-        if (off > 0) {
-            hipError_t e = hipMemcpyAsync(st->dev, host.data(), off, hipMemcpyHostToDevice, s);
-            if (e == hipSuccess)
-                e = hipStreamSynchronize(s);
-            if (e != hipSuccess) {
-                free_step(st);
-                return hip_fail(e);
-            }
-        }
-        for (const auto &op : st->ops) {
-            st->launches += 1;
-            if (op.type == wsg_step::Op::kDense) {
-                st->units += (int64_t)op.d.n_tiles * op.d.S;
-                st->launches += op.d.S > 1;
-            } else if (op.type == wsg_step::Op::kW4) {
-                st->units += (int64_t)op.w.n_tiles * op.w.S;
-                st->launches += op.w.S > 1;
-            } else if (op.type == wsg_step::Op::kDenseGroup || op.type == wsg_step::Op::kW4Group) {
-                st->units += op.n_units;
-            } else if (op.type == wsg_step::Op::kArgmax) {
-                st->launches += 1;  // the reduce over y, then the finish kernel
-            }
-        }
-        // A graph pays off only when it replaces enough direct launches.
-        if (!(mode & WSG_STEP_FORCE_GRAPH) && st->launches < WSG_STEP_GRAPH_MIN_LAUNCHES)
-            st->use_graph = false;
-        if (st->use_graph && !st->ops.empty()) {
-            hipError_t e = hipStreamCreateWithFlags(&st->cap, hipStreamNonBlocking);
-            if (e == hipSuccess)
-                e = hipStreamBeginCapture(st->cap, hipStreamCaptureModeThreadLocal);
-            if (e == hipSuccess) {
-                hipError_t le = run_ops(st, st->cap);
-                e = hipStreamEndCapture(st->cap, &st->graph);
-                if (le != hipSuccess)
-                    e = le;
-            }
-            if (e == hipSuccess)
-                e = hipGraphInstantiate(&st->exec, st->graph, nullptr, nullptr, 0);
-            if (e != hipSuccess) {
-                free_step(st);
-                return hip_fail(e);
-            }
-        }
-        *out = st;
-        return WSG_OK;
+        return create_list(linears, n, mode, s, out);
     });
 }
 
 wsg_status decode_step_linears(wsg_step *step, wsg_stream_t stream) {
     return guarded([&]() -> wsg_status {
-        if (!step)
+        if (!plan_live(step) || step->fake)
             return WSG_ERR_STATE;
         hipStream_t s = static_cast<hipStream_t>(stream);
         hipError_t e = hipSuccess;
@@ -1719,7 +1851,7 @@ wsg_status decode_step_linears(wsg_step *step, wsg_stream_t stream) {
 
 wsg_status wsg_decode_step_destroy(wsg_step *step) {
     return guarded([&]() -> wsg_status {
-        if (!step)
+        if (!plan_unregister(step))
             return WSG_ERR_STATE;
         free_step(step);
         return WSG_OK;
@@ -1728,12 +1860,12 @@ wsg_status wsg_decode_step_destroy(wsg_step *step) {
 
 wsg_status wsg_decode_step_status(wsg_step *step, wsg_stream_t stream, uint32_t *give_ups) {
     return guarded([&]() -> wsg_status {
-        if (!step)
+        if (!plan_live(step))
             return WSG_ERR_STATE;
         if (!give_ups)
             return WSG_ERR_NULL;
         *give_ups = 0;
-        if (!step->chain)
+        if (!step->chain || step->fake)
             return WSG_OK;
         hipStream_t s = static_cast<hipStream_t>(stream);
         ChainCtl *ctl = step->chain_args.ctl;
@@ -1758,7 +1890,7 @@ int64_t wsg_chain_grid(int64_t units, int32_t blocks_per_cu, int32_t cus, int32_
 }
 
 wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t *units, int32_t *graph) {
-    if (!step)
+    if (!plan_live(step))
         return WSG_ERR_STATE;
     if (launches)
         *launches = step->launches;
@@ -1768,5 +1900,18 @@ wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t
         *graph = step->exec != nullptr;
     return WSG_OK;
 }
+
+wsg_status wsg_test_set_fault(int32_t mode) {
+    const char *env = std::getenv("WSG_ENABLE_TEST_HOOKS");
+    if (!env || std::strcmp(env, "1") != 0)
+        return WSG_ERR_UNSUPPORTED;
+    if (mode < -1 || mode > kFaultCapture)
+        return WSG_ERR_SHAPE;
+    g_fake.store(mode >= 0 ? 1 : 0);
+    g_fault.store(mode >= 0 ? mode : kFaultNone);
+    return WSG_OK;
+}
+
+int64_t wsg_test_live_blocks(void) { return g_fake_live.load(); }
 
 }  // extern "C"

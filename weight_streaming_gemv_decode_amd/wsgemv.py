@@ -16,7 +16,8 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwsgemv.so")
+# another build of the same sources may be named by WSGEMV_LIB (the tests' host-sanitizer build)
+LIB_PATH = os.environ.get("WSGEMV_LIB") or os.path.join(_HERE, "libwsgemv.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "wsgemv.h")
 
 F16, W8A8, W4A16, W4A8, W8A8_DYN = 0, 1, 2, 3, 4
@@ -75,6 +76,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "wsg_decode_step_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I64), ctypes.POINTER(I32)], I32),
         "wsg_decode_step_status": ([P, P, ctypes.POINTER(ctypes.c_uint32)], I32),
         "wsg_chain_grid": ([I64, I32, I32, I32], I64),
+        "wsg_test_set_fault": ([I32], I32),
+        "wsg_test_live_blocks": ([], I64),
         "wsg_read_probe": ([P, SZ, P, I32, P], I32),
         "wsg_read_probe_grid": ([SZ], I32),
         "wsg_tune_set": ([ctypes.c_char_p, I64], I32),
