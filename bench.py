@@ -143,6 +143,71 @@ def summary(ts):
             "mean_ms": sum(ts) / len(ts)}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def oracle_per_config(oracle, synth, step_in, cores):
+    """The oracle on one call of each config (one whole int4 step), on 1
+    thread and on `cores` threads: ms and GB/s over the config's
+    algorithmic bytes."""
+    out = {}
+
+    def timed(label, nbytes, fn, fn1=None, bytes1=None, sample1=None):
+        """fn on 1 and on `cores` threads (fn1 over bytes1 on 1 thread, when
+        the whole config would take too long there)."""
+        rec = {"bytes": int(nbytes)}
+        for n in (1, cores):
+            oracle.set_threads(n)
+            f, b = (fn1, bytes1) if (n == 1 and fn1 is not None) else (fn, nbytes)
+            t0 = time.perf_counter()
+            f()
+            dt = time.perf_counter() - t0
+            rec[f"threads_{n}"] = {"ms": round(dt * 1e3, 1), "GBps": round(b / dt / 1e9, 3)}
+            if n == 1 and fn1 is not None:
+                rec["threads_1"]["sample"] = sample1
+        out[label] = rec
+        log(f"oracle {label}: {rec}")
+
+    N, K = synth.C1_SHAPE
+    W = synth.f16_normal(1, 0, (N, K), synth.W_SIGMA)
+    x = synth.f16_normal(1, 1, (K,), synth.X_SIGMA)
+    timed("c1_2048x2048", N * K * 2 + K * 2 + N * 4, lambda: oracle.gemv_f16(W, x))
+    _, W, x = step_in[-1]
+    N, K = W.shape
+    timed("c2_lm_head_248320x1024", N * K * 2 + K * 2 + N * 4, lambda: oracle.gemv_f16(W, x))
+    for (N, K) in synth.C4_SHAPES:
+        Wq = synth.int8_uniform(4, 0, (N, K))
+        xq = synth.int8_uniform(4, 1, (K,))
+        sw = synth.f32_uniform(4, 2, (N,), 0.001, 0.01)
+        timed(f"c4_w8a8_{N}x{K}", N * K + N * 4 + K + N * 4 + N * 4,
+              lambda: oracle.gemv_w8a8(Wq, sw, xq, synth.X_SCALE_W8A8))
+    for M in (1, 4):
+        w4 = synth.decode_step_w4(workload=5, M=M)
+        nbytes = lambda ls: sum(Wc.nbytes + s4.nbytes + X.nbytes + M * Wc.shape[0] * 4  # noqa: E731
+                                for _, Wc, s4, X in ls)
+        step = lambda ls: [oracle.gemv_w4a16(Wc, s4, X) for _, Wc, s4, X in ls]  # noqa: E731
+        few = w4[:28] if M > 1 else None
+        timed(f"c5_w4a16_step_M{M}", nbytes(w4), lambda: step(w4),
+              (lambda: step(few)) if few else None, nbytes(few) if few else None,
+              "the first 7 decoder layers (28 linears) on 1 thread" if few else None)
+        nb = nbytes(w4)
+        if M == 1:
+            def w4a8():
+                for _, Wc, s4, X in w4:
+                    xq, sx = oracle.quantize_x_i8(X.reshape(-1))
+                    oracle.gemv_w4a8(Wc, s4, xq, sx)
+            timed("c6_w4a8_step_M1", nb, w4a8)
+        del w4
+    return out
+
+
 def counter_pass(args, torch, synth, wsgemv, dev, stream):
     """Every config a few steps, for a FETCH_SIZE or WRITE_SIZE pass; the
     manifest says which launches belong to which config (in launch order)."""
@@ -731,6 +796,12 @@ def main():
         cpu["single_thread"] = {"value": round(step_bytes / dt1 / 1e9, 3), "unit": "GB/s",
                                 "ms_per_step": round(dt1 * 1e3, 1), "sample": "1 full decode step on 1 thread"}
         log(f"oracle: {dt1:.2f}s/step on 1 thread")
+        cpu["cpu_model"] = cpu_model()
+        cpu["sample"] = cpu["sample"].replace(f"({platform.processor() or platform.machine()})",
+                                              f"({cpu['cpu_model']})")
+        if not args.no_extras:
+            cpu["per_config"] = oracle_per_config(oracle, synth, step_in, cores)
+        oracle.set_threads(cores)
 
     line = {
         "metric": METRIC,

@@ -136,7 +136,9 @@ wsg_status gemv_w8a8(const int8_t *Wq, const float *w_scale, const int8_t *xq,
  *   y[n]     = ((float)acc[n] * w_scale[n]) * s_x, fp32
  *   acc_out  optional int32 [N]; xq_out optional int8 [K] (16-byte aligned);
  *            sx_out optional fp32 [1].  ws as for gemv_w8a8 (WSG_W8A8_DYN in
- *            wsg_workspace_bytes).
+ *            wsg_workspace_bytes): with splits > 1 it holds the split
+ *            partials and, after them, the s_x that the first work unit
+ *            publishes for the reduce; it needs no initialisation.
  */
 wsg_status gemv_w8a8_dyn(const int8_t *Wq, const float *w_scale, const void *x, float *y,
                          int32_t *acc_out, int8_t *xq_out, float *sx_out, int64_t N, int64_t K,

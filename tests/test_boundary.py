@@ -296,7 +296,9 @@ def test_w8a8_dyn_validation(L):
     assert f(*args(sw=FAKE + 2)) == ALIGN
     assert f(*args(S=200)) == SHAPE                   # more slices than 16-byte vectors
     assert f(*args(N=0)) == OK                        # nothing to do
-    assert L.wsg_workspace_bytes(4, 1, 4096, 14336, 2) == 2 * 4096 * 4
+    # split partials, then 256 bytes for the activation scale the first work unit publishes
+    assert L.wsg_workspace_bytes(4, 1, 4096, 14336, 2) == 2 * 4096 * 4 + 256
+    assert L.wsg_workspace_bytes(4, 1, 4096, 14336, 1) == 0
     assert L.wsg_plan_splits(4, 1, 4096, 14336) == L.wsg_plan_splits(1, 1, 4096, 14336)
     # in a decode step: M = 1 only, and the activation scale is computed, not given
     out = ctypes.c_void_p()

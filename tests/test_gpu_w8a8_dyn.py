@@ -21,13 +21,16 @@ def _case(N, K, workload=140, x_sigma=synth.X_SIGMA):
     return Wq, sw, x
 
 
-def _check(Wq, sw, x, splits=0, what=""):
+def _check(Wq, sw, x, splits=0, what="", dirty_ws=False):
     N, K = Wq.shape
     acc = torch.full((N,), -7, dtype=torch.int32, device="cuda")
     xq = torch.full((max(K, 1),), 99, dtype=torch.int8, device="cuda")
     sx = torch.full((1,), float("nan"), device="cuda")
+    ws = wsgemv.workspace(wsgemv.W8A8_DYN, 1, N, K, splits)
+    if dirty_ws and ws is not None:
+        ws.fill_(0xFF)  # NaN bits everywhere: the partials and the published scale must be written before use
     y = wsgemv.gemv_w8a8_dyn(dev(Wq), dev(sw), dev(x), acc_out=acc, xq_out=xq[:K] if K else None, sx_out=sx,
-                             splits=splits)
+                             splits=splits, ws=ws)
     xq_ref, sx_ref = oracle.quantize_x_i8(x)
     assert_bits_equal(host(sx), np.array([sx_ref], np.float32), f"{what} scale")
     if K:
@@ -44,11 +47,13 @@ def test_shapes(N, K):
 
 
 @pytest.mark.parametrize("S", [1, 2, 7])
-def test_splits(S):
+@pytest.mark.parametrize("dirty", [False, True])
+def test_splits(S, dirty):
     """k split across workgroups: every slice quantises its own codes with
-    the same scale, and the reduce recomputes that scale."""
-    say(f"w8a8 dyn splits={S}")
-    _check(*_case(300, 7168, workload=141), splits=S, what=f"S={S}")
+    the same scale, which the first work unit also publishes in the
+    workspace for the reduce (a workspace full of NaN bits changes nothing)."""
+    say(f"w8a8 dyn splits={S} dirty={dirty}")
+    _check(*_case(300, 7168, workload=141), splits=S, what=f"S={S}", dirty_ws=dirty)
 
 
 def test_ties_to_even_and_clamp():

@@ -64,6 +64,7 @@ struct Tune {
     int64_t chain_blocks_per_cu = -1; // persistent step: workgroups per compute unit (at most the resident count)
     int64_t chain_spin_limit = -1;    // persistent step: polls before a wait gives up
     int64_t chain_test_stale = -1;    // 1: consumers wait for a tag no producer writes (tests the give-up path)
+    int64_t chain_sleep = -1;         // s_sleep(1) calls between polls of a waiting workgroup
 };
 Tune g_tune;
 
@@ -145,13 +146,20 @@ DensePlan plan_dense(int kind, int64_t N, int64_t K, int splits, bool token = fa
     return p;
 }
 
+// The partials of a split linear (and, for W8A8_DYN, the scale after them).
+void set_part(DenseLin &L, int kind, void *part) {
+    L.part = part;
+    L.sx_part = (kind == kW8A8D && part) ? reinterpret_cast<float *>(static_cast<char *>(part) +
+                                                                      (size_t)L.S * (size_t)L.N * 4)
+                                         : nullptr;
+}
+
 DenseLin make_dense(int kind, const void *W, const void *x, float *y, void *part, const float *w_scale,
                     const float *x_scale, int32_t *acc_out, int64_t N, int64_t K, const DensePlan &p) {
     DenseLin L{};
     L.W = static_cast<const u32x4 *>(W);
     L.x = static_cast<const u32x4 *>(x);
     L.y = y;
-    L.part = part;
     L.w_scale = w_scale;
     L.x_scale = x_scale;
     L.acc_out = acc_out;
@@ -161,6 +169,7 @@ DenseLin make_dense(int kind, const void *W, const void *x, float *y, void *part
     L.kvs = p.kvs;
     L.tile_rows = p.tile_rows;
     L.n_tiles = (int32_t)cdiv(N, p.tile_rows);
+    set_part(L, kind, part);
     return L;
 }
 
@@ -196,7 +205,12 @@ wsg_status check_dense_args(int kind, const void *W, const void *x, const float 
     return WSG_OK;
 }
 
-size_t dense_ws_bytes(const DensePlan &p, int64_t N) { return p.S > 1 ? (size_t)p.S * (size_t)N * 4 : 0; }
+// Split-K workspace: S partial rows, and for fp16 activations quantised in
+// the kernel one more float, the scale, which the reduce reads.
+size_t dense_ws_bytes(int kind, const DensePlan &p, int64_t N) {
+    return p.S > 1 ? (size_t)p.S * (size_t)N * 4 + (kind == kW8A8D ? 256 : 0) : 0;
+}
+
 
 wsg_status check_ws(const void *ws, size_t ws_bytes, size_t need) {
     if (need == 0)
@@ -500,14 +514,14 @@ size_t wsg_workspace_bytes(int32_t kind, int64_t M, int64_t N, int64_t K, int32_
         if (K == 0 || K % elem_per_vec(base))
             return token_key_bytes(argmax_f32_blocks(N));
         const DensePlan p = plan_dense(base, N, K, splits, true);
-        return token_key_bytes(dense_token_keys(p, N)) + dense_ws_bytes(p, N);
+        return token_key_bytes(dense_token_keys(p, N)) + dense_ws_bytes(base, p, N);
     }
     if (N <= 0 || K <= 0 || splits < 0)
         return 0;
     if (kind == kF16 || kind == kW8A8 || kind == kW8A8D) {
         if (K % elem_per_vec(kind))
             return 0;
-        return dense_ws_bytes(plan_dense(kind, N, K, splits), N);
+        return dense_ws_bytes(kind, plan_dense(kind, N, K, splits), N);
     }
     if (kind == kW4A16 || kind == kW4A8) {
         if (K % 128 || M < 1)
@@ -529,7 +543,7 @@ wsg_status gemv_f16(const void *W, const void *x, float *y, int64_t N, int64_t K
             return e == hipSuccess ? WSG_OK : hip_fail(e);
         }
         DensePlan p = plan_dense(kF16, N, K, splits);
-        st = check_ws(ws, ws_bytes, dense_ws_bytes(p, N));
+        st = check_ws(ws, ws_bytes, dense_ws_bytes(kF16, p, N));
         if (st != WSG_OK)
             return st;
         DenseLin L = make_dense(kF16, W, x, y, ws, nullptr, nullptr, nullptr, N, K, p);
@@ -545,7 +559,7 @@ wsg_status gemv_f16_static(const void *W, const void *x, float *y, int64_t N, in
         if (st != WSG_OK || N == 0)
             return st;
         DensePlan p = plan_dense(kF16, N, K, splits);
-        const size_t need = K == 0 ? 0 : dense_ws_bytes(p, N);
+        const size_t need = K == 0 ? 0 : dense_ws_bytes(kF16, p, N);
         if (need > (size_t)WSG_STATIC_SCRATCH_BYTES)
             return WSG_ERR_WORKSPACE;
         hipStream_t s = static_cast<hipStream_t>(stream);
@@ -666,7 +680,7 @@ wsg_status gemv_f16_argmax(const void *W, const void *x, float *y, int32_t *toke
         DensePlan p = plan_dense(kF16, N, K, splits, true);
         const int32_t nk = dense_token_keys(p, N);
         const size_t kb = token_key_bytes(nk);
-        st = check_ws(ws, ws_bytes, kb + dense_ws_bytes(p, N));
+        st = check_ws(ws, ws_bytes, kb + dense_ws_bytes(kF16, p, N));
         if (st != WSG_OK)
             return st;
         DenseLin L = make_dense(kF16, W, x, y, static_cast<char *>(ws) + kb, nullptr, nullptr, nullptr, N, K, p);
@@ -701,7 +715,7 @@ wsg_status gemv_w8a8(const int8_t *Wq, const float *w_scale, const int8_t *xq, c
         if (!aligned(w_scale, 4) || !aligned(x_scale, 4))
             return WSG_ERR_ALIGN;
         DensePlan p = plan_dense(kW8A8, N, K, splits);
-        st = check_ws(ws, ws_bytes, dense_ws_bytes(p, N));
+        st = check_ws(ws, ws_bytes, dense_ws_bytes(kW8A8, p, N));
         if (st != WSG_OK)
             return st;
         DenseLin L = make_dense(kW8A8, Wq, xq, y, ws, w_scale, x_scale, acc_out, N, K, p);
@@ -735,7 +749,7 @@ wsg_status gemv_w8a8_dyn(const int8_t *Wq, const float *w_scale, const void *x, 
         if (!aligned(w_scale, 4))
             return WSG_ERR_ALIGN;
         DensePlan p = plan_dense(kW8A8D, N, K, splits);
-        st = check_ws(ws, ws_bytes, dense_ws_bytes(p, N));
+        st = check_ws(ws, ws_bytes, dense_ws_bytes(kW8A8D, p, N));
         if (st != WSG_OK)
             return st;
         DenseLin L = make_dense(kW8A8D, Wq, x, y, ws, w_scale, nullptr, acc_out, N, K, p);
@@ -825,7 +839,8 @@ wsg_status wsg_tune_set(const char *key, int64_t value) {
                  {"chain_unit_kb", &g_tune.chain_unit_kb},
                  {"chain_blocks_per_cu", &g_tune.chain_blocks_per_cu},
                  {"chain_spin_limit", &g_tune.chain_spin_limit},
-                 {"chain_test_stale", &g_tune.chain_test_stale}};
+                 {"chain_test_stale", &g_tune.chain_test_stale},
+                 {"chain_sleep", &g_tune.chain_sleep}};
     for (auto &t : table) {
         if (std::strcmp(key, t.name) == 0) {
             *t.slot = value < 0 ? -1 : value;
@@ -1323,7 +1338,7 @@ wsg_status plan_dense_linear(wsg_step &st, PlanBuild &pb, const wsg_linear &l) {
     const int ki = l.kind == kF16 ? 0 : (l.kind == kW8A8 ? 1 : 2);
     if (pb.base_mode == WSG_STEP_ORDERED) {
         DensePlan p = plan_dense(l.kind, l.N, l.K, l.splits, l.argmax_idx != nullptr);
-        pb.part_bytes = std::max(pb.part_bytes, dense_ws_bytes(p, l.N));
+        pb.part_bytes = std::max(pb.part_bytes, dense_ws_bytes(l.kind, p, l.N));
         wsg_step::Op o{};
         o.type = wsg_step::Op::kDense;
         o.kind = l.kind;
@@ -1540,7 +1555,7 @@ void fill_block(wsg_step &st, PlanBuild &pb, std::vector<char> &host) {
     // partials of ORDERED linears share one buffer (the ops run in order)
     for (auto &op : st.ops) {
         if (op.type == wsg_step::Op::kDense && op.d.S > 1)
-            op.d.part = base + pb.part_off;
+            set_part(op.d, op.kind, base + pb.part_off);
         if (op.type == wsg_step::Op::kW4 && op.w.S > 1)
             op.w.part = reinterpret_cast<float *>(base + pb.part_off);
     }
@@ -1791,6 +1806,9 @@ hipError_t run_chain(wsg_step *st, hipStream_t s) {
     a.want = g_tune.chain_test_stale == 1 ? a.tag % 65535u + 1u : a.tag;
     a.spin_limit = g_tune.chain_spin_limit >= 0 ? (uint32_t)std::min<int64_t>(g_tune.chain_spin_limit, UINT32_MAX)
                                                 : kChainSpinLimit;
+    // polling again at once measured fastest on the C3 chain (sleeps of 2, 8
+    // and 16 between polls cost 1, 3 and 7 %)
+    a.sleep = g_tune.chain_sleep >= 0 ? (int)std::min<int64_t>(g_tune.chain_sleep, 64) : 0;
     return launch_chain(a, st->chain_grid, st->chain_lds, st->chain_tail, s);
 }
 

@@ -389,8 +389,12 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
             for (int i = kv0 + tid; i < kv0 + nv; i += kBlock)
                 put(i, quantize16(*glob(L.x + 2 * i), *glob(L.x + 2 * i + 1), sx, rsx));
         }
-        if (L.sx_out != nullptr && tile == 0 && s == 0 && tid == 0)
-            *glob(L.sx_out) = sx;
+        if (tile == 0 && s == 0 && tid == 0) {
+            if (L.sx_out != nullptr)
+                *glob(L.sx_out) = sx;
+            if (L.sx_part != nullptr)
+                *glob(L.sx_part) = sx;
+        }
     } else {
         const u32x4 *xg = L.x + kv0;
         for (int i = tid; i < nchunk * CHUNK; i += kBlock)
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
     unsigned long long best = 0;
     float sx = 0.0f;
     if constexpr (KIND == kW8A8D)
-        sx = dyn_scale(L.x, (int64_t)L.kvec * 2);  // the same bits as the units computed
+        sx = *L.sx_part;  // published by the first work unit of the launch
     if (n < L.N) {
         float yv;
         if constexpr (KIND == kF16) {
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
 // in LDS and streams the rest of its rows.  A producer publishes each output
 // as the 32-bit word (tag << 16) | fp16 with an agent-scope atomic store; a
 // consumer reads its input words with agent-scope atomic loads and takes a
-// word only when its tag is the step's, polling again (after a short sleep)
+// word only when its tag is the step's, polling again (after a tunable sleep)
 // for the ones that are not yet current.  Every wait ends: after spin_limit
 // polls, or once another workgroup has given up in this step, the unit goes
 // on without its input and the give-up is counted for the host.
@@ -589,7 +593,8 @@ __device__ __forceinline__ void chain_stage(const ChainLin &L, const ChainArgs &
             }
             return;
         }
-        __builtin_amdgcn_s_sleep(8);
+        for (int z = 0; z < a.sleep; ++z)
+            __builtin_amdgcn_s_sleep(1);
         if (!(d & 2u))
             continue;
 #pragma unroll

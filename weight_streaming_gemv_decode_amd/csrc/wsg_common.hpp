@@ -159,6 +159,7 @@ struct DenseLin {
     uint16_t *y16;         // optional fp16 copy of y [N] (same place as y is final)
     int8_t *xq_out;        // kW8A8D: optional int8 codes [K] (written by the first row tile)
     float *sx_out;         // kW8A8D: optional activation scale [1]
+    float *sx_part;        // kW8A8D with S > 1: the activation scale, after the partials (for the reduce)
 };
 
 // One int4 linear in the packed tile layout (16 rows x 128 k per 1 KiB tile).
@@ -228,6 +229,7 @@ struct ChainArgs {
     uint32_t tag;            // written with this step's outputs (1..65535)
     uint32_t want;           // inputs are current with this tag (== tag; tests may differ)
     uint32_t spin_limit;     // polls before a wait gives up
+    int32_t sleep;           // s_sleep(1) calls between polls (0: poll again at once)
 };
 
 struct DenseCfg {
