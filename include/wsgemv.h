@@ -41,6 +41,14 @@
  * workspace must hold wsg_workspace_bytes(...) bytes, 256-byte aligned; it
  * may be NULL when that size is 0.  One workspace must not serve two calls
  * that are in flight at the same time.
+ *
+ * For the fp16 and int8-weight kinds the last workgroup to finish a row
+ * tile adds that tile's partials (no second kernel); it finds out through
+ * one arrival counter per row tile, kept in the workspace after the
+ * partials.  So a split workspace must be zero-filled before its first use
+ * (hipMemset, torch.zeros); every call leaves the counters zero again, so
+ * one zero fill serves every later call.  The int4 kinds add their partials
+ * in a second kernel and need no initialisation.
  */
 #ifndef WSGEMV_H
 #define WSGEMV_H
@@ -97,8 +105,9 @@ wsg_status gemv_f16(const void *W, const void *x, float *y, int64_t N, int64_t K
  * without (ws, ws_bytes).  The split-K partials (S * N * 4 bytes when S > 1)
  * live in a fixed device array of WSG_STATIC_SCRATCH_BYTES inside the library,
  * one per GPU, held until the process ends; its address is looked up on the
- * first call on each device.  A shape whose partials do not fit returns
- * WSG_ERR_WORKSPACE before anything is launched.  The call allocates nothing
+ * first call on each device; a second kernel adds them (the array keeps no
+ * arrival counters, so nothing in it needs to start at zero).  A shape whose
+ * partials do not fit returns WSG_ERR_WORKSPACE before anything is launched.  The call allocates nothing
  * (no hipMalloc, no hipFree).  Every call on one GPU uses that GPU's array:
  * two calls whose work overlaps in time on one GPU (different streams, or
  * different threads) race on it, so serialise them.
@@ -137,8 +146,8 @@ wsg_status gemv_w8a8(const int8_t *Wq, const float *w_scale, const int8_t *xq,
  *   acc_out  optional int32 [N]; xq_out optional int8 [K] (16-byte aligned);
  *            sx_out optional fp32 [1].  ws as for gemv_w8a8 (WSG_W8A8_DYN in
  *            wsg_workspace_bytes): with splits > 1 it holds the split
- *            partials and, after them, the s_x that the first work unit
- *            publishes for the reduce; it needs no initialisation.
+ *            partials, the s_x that the first work unit publishes, and the
+ *            arrival counters (zero before the first use, see Split-K).
  */
 wsg_status gemv_w8a8_dyn(const int8_t *Wq, const float *w_scale, const void *x, float *y,
                          int32_t *acc_out, int8_t *xq_out, float *sx_out, int64_t N, int64_t K,
@@ -243,8 +252,9 @@ wsg_status wsg_topk_f32(const float *y, int64_t N, int32_t k, int32_t *idx, floa
  * reduce when splits > 1).  This is the lm_head of a decode step.
  *   N = 1..INT32_MAX; token int32 [1]; token_logit optional fp32 [1]
  *   ws           wsg_workspace_bytes(WSG_F16 | WSG_WITH_ARGMAX, 1, N, K,
- *                splits) bytes (the key array, then the split-K partials),
- *                256-byte aligned
+ *                splits) bytes (the key array, then the split-K partials
+ *                and counters), 256-byte aligned; zero before the first use
+ *                when the call splits k (see Split-K)
  */
 wsg_status gemv_f16_argmax(const void *W, const void *x, float *y, int32_t *token, float *token_logit,
                            int64_t N, int64_t K, int32_t splits, void *ws, size_t ws_bytes,

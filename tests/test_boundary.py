@@ -15,6 +15,14 @@ MIS = FAKE + 2                 # misaligned
 OK, NULL, SHAPE, ALIGN, UNSUP, WS, HIP, NOMEM, STATE = range(9)
 
 
+def split_ws(S, N, tile_rows, dyn=False):
+    """Workspace of a split fp16/int8 linear: S rows of 4-byte partials (and
+    for W8A8_DYN 256 bytes for the published scale), then, from the next
+    256-byte boundary, one 4-byte arrival counter per row tile."""
+    part = S * N * 4 + (256 if dyn else 0)
+    return (part + 255) // 256 * 256 + (N + tile_rows - 1) // tile_rows * 4
+
+
 @pytest.fixture(scope="module")
 def L():
     return wsgemv.lib()
@@ -50,7 +58,7 @@ def test_gemv_f16_validation(L):
     assert f(FAKE, FAKE, FAKE, 4, 64, 9, None, 0, None) == SHAPE           # more slices than vectors
     assert f(FAKE, FAKE, FAKE, 4, 1024, 2, None, 0, None) == WS            # split needs workspace
     need = L.wsg_workspace_bytes(0, 1, 4, 1024, 2)
-    assert need == 2 * 4 * 4
+    assert need == split_ws(2, 4, 32)
     assert f(FAKE, FAKE, FAKE, 4, 1024, 2, FAKE, need - 1, None) == WS
     assert f(FAKE, FAKE, FAKE, 4, 1024, 2, FAKE + 16, need, None) == ALIGN
     assert f(None, None, None, 0, 64, 0, None, 0, None) == OK               # N = 0: no-op, nothing launched
@@ -134,7 +142,7 @@ def test_argmax_validation(L):
     assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 60, 0, FAKE, 256, None) == SHAPE   # K % 8
     assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 64, 0, FAKE, 128, None) == WS
     need = L.wsg_workspace_bytes(0 | 0x100, 1, 4, 1024, 2)
-    assert need == 256 + 2 * 4 * 4
+    assert need == 256 + split_ws(2, 4, 32)                                   # one key, then the split
     assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 1024, 2, FAKE, need - 1, None) == WS
     assert L.wsg_workspace_bytes(2 | 0x100, 1, 16, 256, 0) == 0                  # int4: no fused token
     out = ctypes.c_void_p()
@@ -202,9 +210,12 @@ def test_launch_table(L):
     assert L.wsg_plan_splits(1, 1, 4096, 14336) == 1     # enough rows: no split
     assert L.wsg_plan_splits(0, 1, 248320, 1024) * 248320 * 4 == L.wsg_workspace_bytes(0, 1, 248320, 1024, 0) \
         or L.wsg_plan_splits(0, 1, 248320, 1024) == 1
-    for S in (1, 2, 3, 4):
-        want = 0 if S == 1 else S * 2048 * 4
-        assert L.wsg_workspace_bytes(0, 1, 2048, 2048, S) == want
+    # 2048x2048 fp16 (256 vectors a row): slices of 128 and 86 vectors take
+    # 8-row tiles, slices of 64 vectors 32-row tiles
+    for S, rows in ((2, 8), (3, 8), (4, 32)):
+        assert L.wsg_workspace_bytes(0, 1, 2048, 2048, S) == split_ws(S, 2048, rows)
+    assert L.wsg_workspace_bytes(0, 1, 2048, 2048, 1) == 0
+    assert L.wsg_workspace_bytes(0, 1, 248320, 1024, 2) == split_ws(2, 248320, 32)
 
 
 def test_decode_step_validation(L):
@@ -296,8 +307,9 @@ def test_w8a8_dyn_validation(L):
     assert f(*args(sw=FAKE + 2)) == ALIGN
     assert f(*args(S=200)) == SHAPE                   # more slices than 16-byte vectors
     assert f(*args(N=0)) == OK                        # nothing to do
-    # split partials, then 256 bytes for the activation scale the first work unit publishes
-    assert L.wsg_workspace_bytes(4, 1, 4096, 14336, 2) == 2 * 4096 * 4 + 256
+    # split partials, 256 bytes for the activation scale the first work unit
+    # publishes, then the counters (448-vector slices: 32-row tiles)
+    assert L.wsg_workspace_bytes(4, 1, 4096, 14336, 2) == split_ws(2, 4096, 32, dyn=True)
     assert L.wsg_workspace_bytes(4, 1, 4096, 14336, 1) == 0
     assert L.wsg_plan_splits(4, 1, 4096, 14336) == L.wsg_plan_splits(1, 1, 4096, 14336)
     # in a decode step: M = 1 only, and the activation scale is computed, not given

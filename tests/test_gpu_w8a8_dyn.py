@@ -28,7 +28,10 @@ def _check(Wq, sw, x, splits=0, what="", dirty_ws=False):
     sx = torch.full((1,), float("nan"), device="cuda")
     ws = wsgemv.workspace(wsgemv.W8A8_DYN, 1, N, K, splits)
     if dirty_ws and ws is not None:
-        ws.fill_(0xFF)  # NaN bits everywhere: the partials and the published scale must be written before use
+        # NaN bits over the partials and the published scale (everything before
+        # the arrival counters, which start at zero): both must be written before use
+        S = splits or wsgemv.plan_splits(wsgemv.W8A8_DYN, 1, N, K)
+        ws[:(S * N * 4 + 256 + 255) // 256 * 256].fill_(0xFF)
     y = wsgemv.gemv_w8a8_dyn(dev(Wq), dev(sw), dev(x), acc_out=acc, xq_out=xq[:K] if K else None, sx_out=sx,
                              splits=splits, ws=ws)
     xq_ref, sx_ref = oracle.quantize_x_i8(x)
@@ -51,7 +54,7 @@ def test_shapes(N, K):
 def test_splits(S, dirty):
     """k split across workgroups: every slice quantises its own codes with
     the same scale, which the first work unit also publishes in the
-    workspace for the reduce (a workspace full of NaN bits changes nothing)."""
+    workspace (partials and scale slots full of NaN bits change nothing)."""
     say(f"w8a8 dyn splits={S} dirty={dirty}")
     _check(*_case(300, 7168, workload=141), splits=S, what=f"S={S}", dirty_ws=dirty)
 

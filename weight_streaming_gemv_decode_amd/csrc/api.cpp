@@ -65,6 +65,7 @@ struct Tune {
     int64_t chain_spin_limit = -1;    // persistent step: polls before a wait gives up
     int64_t chain_test_stale = -1;    // 1: consumers wait for a tag no producer writes (tests the give-up path)
     int64_t chain_sleep = -1;         // s_sleep(1) calls between polls of a waiting workgroup
+    int64_t dense_fuse = -1;          // split-K sum: 0 reduce kernel, 1 last unit of each row tile
 };
 Tune g_tune;
 
@@ -87,7 +88,15 @@ struct DensePlan {
     int S;
     int kvs;
     int tile_rows;
+    int fuse;       // S > 1: how the partials are summed (DenseLin::fuse)
 };
+
+// How a split linear sums its partials (DenseLin::fuse): by default the last
+// unit of each row tile does.  Measured on MI355X against the reduce kernel
+// (bit-identical results): 6.7-7.1 against 9.3-9.7 us on fp16 linears of
+// 128-896 rows that the launch table splits, 7.7-8.7 against 10.1 us on the
+// int8 ones, and 76.9 against 77.0 us on the 248320x1024 lm_head at S = 2.
+int dense_fuse_mode() { return g_tune.dense_fuse >= 0 ? (int)std::min<int64_t>(g_tune.dense_fuse, 1) : 1; }
 
 int elem_per_vec(int kind) { return kind == kF16 ? 8 : 16; }
 
@@ -143,15 +152,41 @@ DensePlan plan_dense(int kind, int64_t N, int64_t K, int splits, bool token = fa
     if (g_tune.dense_rows > 0)
         tr = (int)g_tune.dense_rows;
     p.tile_rows = tr;
+    p.fuse = p.S > 1 ? dense_fuse_mode() : 0;
     return p;
 }
 
-// The partials of a split linear (and, for W8A8_DYN, the scale after them).
-void set_part(DenseLin &L, int kind, void *part) {
+// The partials of a split linear (and, for W8A8_DYN, the scale after them),
+// and the arrival counters of a fused one.
+void set_part(DenseLin &L, int kind, void *part, uint32_t *ctr) {
     L.part = part;
     L.sx_part = (kind == kW8A8D && part) ? reinterpret_cast<float *>(static_cast<char *>(part) +
                                                                       (size_t)L.S * (size_t)L.N * 4)
                                          : nullptr;
+    L.ctr = L.fuse ? ctr : nullptr;
+}
+
+// Split-K workspace: S partial rows, and for fp16 activations quantised in
+// the kernel one more float, the scale, which the reduce reads; a fused
+// linear's arrival counters follow (zero before the first call, and every
+// call leaves them zero).
+size_t dense_part_bytes(int kind, const DensePlan &p, int64_t N) {
+    return p.S > 1 ? (size_t)p.S * (size_t)N * 4 + (kind == kW8A8D ? 256 : 0) : 0;
+}
+
+size_t dense_ctr_bytes(const DensePlan &p, int64_t N) {
+    return p.S > 1 && p.fuse ? (size_t)cdiv(N, p.tile_rows) * 4 : 0;
+}
+
+size_t dense_ws_bytes(int kind, const DensePlan &p, int64_t N) {
+    const size_t pb = dense_part_bytes(kind, p, N), cb = dense_ctr_bytes(p, N);
+    return cb ? (pb + 255) / 256 * 256 + cb : pb;
+}
+
+uint32_t *dense_ws_ctr(int kind, const DensePlan &p, int64_t N, void *ws) {
+    if (!ws || !dense_ctr_bytes(p, N))
+        return nullptr;
+    return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + (dense_part_bytes(kind, p, N) + 255) / 256 * 256);
 }
 
 DenseLin make_dense(int kind, const void *W, const void *x, float *y, void *part, const float *w_scale,
@@ -169,7 +204,8 @@ DenseLin make_dense(int kind, const void *W, const void *x, float *y, void *part
     L.kvs = p.kvs;
     L.tile_rows = p.tile_rows;
     L.n_tiles = (int32_t)cdiv(N, p.tile_rows);
-    set_part(L, kind, part);
+    L.fuse = p.fuse;
+    set_part(L, kind, part, dense_ws_ctr(kind, p, N, part));
     return L;
 }
 
@@ -205,11 +241,6 @@ wsg_status check_dense_args(int kind, const void *W, const void *x, const float 
     return WSG_OK;
 }
 
-// Split-K workspace: S partial rows, and for fp16 activations quantised in
-// the kernel one more float, the scale, which the reduce reads.
-size_t dense_ws_bytes(int kind, const DensePlan &p, int64_t N) {
-    return p.S > 1 ? (size_t)p.S * (size_t)N * 4 + (kind == kW8A8D ? 256 : 0) : 0;
-}
 
 
 wsg_status check_ws(const void *ws, size_t ws_bytes, size_t need) {
@@ -235,12 +266,13 @@ ArgOut arg_out(void *keys, int32_t n_keys, int32_t *token, float *token_logit, i
     return a;
 }
 
-// Workgroups that publish a key for a dense linear's token: its units, or
-// the reduce's workgroups when k is split.
-int32_t dense_token_keys(const DenseLin &L) { return L.S > 1 ? dense_reduce_blocks(L.N) : L.n_tiles; }
+// Workgroups that publish a key for a dense linear's token: its units (or
+// the last unit of each row tile), or the reduce's workgroups when a reduce
+// kernel sums the split partials.
+int32_t dense_token_keys(const DenseLin &L) { return L.S > 1 && !L.fuse ? dense_reduce_blocks(L.N) : L.n_tiles; }
 
 int32_t dense_token_keys(const DensePlan &p, int64_t N) {
-    return p.S > 1 ? dense_reduce_blocks(N) : (int32_t)cdiv(N, p.tile_rows);
+    return p.S > 1 && !p.fuse ? dense_reduce_blocks(N) : (int32_t)cdiv(N, p.tile_rows);
 }
 
 // Key array bytes (M rows of keys) at the start of a token-taking workspace.
@@ -289,7 +321,7 @@ wsg_status enqueue_dense(int kind, const DenseLin &L, const DenseCfg &cfg, hipSt
     hipError_t e = launch_dense(kind, L, cfg, s);
     if (e != hipSuccess)
         return hip_fail(e);
-    if (L.S > 1) {
+    if (L.S > 1 && !L.fuse) {
         e = launch_dense_reduce(kind, L, s);
         if (e != hipSuccess)
             return hip_fail(e);
@@ -559,6 +591,7 @@ wsg_status gemv_f16_static(const void *W, const void *x, float *y, int64_t N, in
         if (st != WSG_OK || N == 0)
             return st;
         DensePlan p = plan_dense(kF16, N, K, splits);
+        p.fuse = 0;  // the shared array keeps no counters: a reduce kernel sums the partials
         const size_t need = K == 0 ? 0 : dense_ws_bytes(kF16, p, N);
         if (need > (size_t)WSG_STATIC_SCRATCH_BYTES)
             return WSG_ERR_WORKSPACE;
@@ -840,7 +873,8 @@ wsg_status wsg_tune_set(const char *key, int64_t value) {
                  {"chain_blocks_per_cu", &g_tune.chain_blocks_per_cu},
                  {"chain_spin_limit", &g_tune.chain_spin_limit},
                  {"chain_test_stale", &g_tune.chain_test_stale},
-                 {"chain_sleep", &g_tune.chain_sleep}};
+                 {"chain_sleep", &g_tune.chain_sleep},
+                 {"dense_fuse", &g_tune.dense_fuse}};
     for (auto &t : table) {
         if (std::strcmp(key, t.name) == 0) {
             *t.slot = value < 0 ? -1 : value;
@@ -1116,7 +1150,7 @@ hipError_t run_ops(const wsg_step *st, hipStream_t s) {
         switch (op.type) {
         case wsg_step::Op::kDense:
             e = launch_dense(op.kind, op.d, op.dc, s);
-            if (e == hipSuccess && op.d.S > 1)
+            if (e == hipSuccess && op.d.S > 1 && !op.d.fuse)
                 e = launch_dense_reduce(op.kind, op.d, s);
             break;
         case wsg_step::Op::kDenseGroup:
@@ -1191,7 +1225,7 @@ void count_launches(wsg_step &st) {
         st.launches += 1;
         if (op.type == wsg_step::Op::kDense) {
             st.units += (int64_t)op.d.n_tiles * op.d.S;
-            st.launches += op.d.S > 1;
+            st.launches += op.d.S > 1 && !op.d.fuse;
         } else if (op.type == wsg_step::Op::kW4) {
             st.units += (int64_t)op.w.n_tiles * op.w.S;
             st.launches += op.w.S > 1;
@@ -1247,6 +1281,7 @@ struct PlanBuild {
     DenseCfg gcfg[3] = {};
     bool f16_hybrid = true;
     size_t part_bytes = 0;         // split-K partials shared by the ORDERED linears (they run in order)
+    size_t ctr_bytes = 0;          // their arrival counters (fused sums), zero between linears
     // Greedy-token key arrays (one per linear that takes a token) open the
     // device block; descriptors get their addresses once it exists.
     std::vector<size_t> key_off;   // per key array: offset in the keys region
@@ -1257,8 +1292,8 @@ struct PlanBuild {
     };
     std::vector<TableFix> table_fix;         // grouped descriptors that take a token
     std::vector<wsg_step::Op> finish_after;  // their finish kernels, after the grouped launches
-    // the device block: [token keys][partials][dense tables x3][int4 tables x3]
-    size_t keys_off = 0, part_off = 0, dl_off[3] = {}, du_off[3] = {}, wl_off[3] = {}, wu_off[3] = {};
+    // the device block: [token keys][partials][counters][dense tables x3][int4 tables x3]
+    size_t keys_off = 0, part_off = 0, ctr_off = 0, dl_off[3] = {}, du_off[3] = {}, wl_off[3] = {}, wu_off[3] = {};
     size_t bytes = 0;
 
     int new_keys(int32_t n_keys, int32_t M = 1) {
@@ -1338,7 +1373,8 @@ wsg_status plan_dense_linear(wsg_step &st, PlanBuild &pb, const wsg_linear &l) {
     const int ki = l.kind == kF16 ? 0 : (l.kind == kW8A8 ? 1 : 2);
     if (pb.base_mode == WSG_STEP_ORDERED) {
         DensePlan p = plan_dense(l.kind, l.N, l.K, l.splits, l.argmax_idx != nullptr);
-        pb.part_bytes = std::max(pb.part_bytes, dense_ws_bytes(l.kind, p, l.N));
+        pb.part_bytes = std::max(pb.part_bytes, dense_part_bytes(l.kind, p, l.N));
+        pb.ctr_bytes = std::max(pb.ctr_bytes, dense_ctr_bytes(p, l.N));
         wsg_step::Op o{};
         o.type = wsg_step::Op::kDense;
         o.kind = l.kind;
@@ -1505,6 +1541,8 @@ void layout_block(PlanBuild &pb) {
     off = align_up(off + pb.keys_bytes, 256);
     pb.part_off = off;
     off = align_up(off + pb.part_bytes, 256);
+    pb.ctr_off = off;  // zero in the uploaded image
+    off = align_up(off + pb.ctr_bytes, 256);
     for (int k = 0; k < 3; ++k) {
         pb.dl_off[k] = off;
         off = align_up(off + pb.dl[k].size() * sizeof(DenseLin), 256);
@@ -1555,7 +1593,7 @@ void fill_block(wsg_step &st, PlanBuild &pb, std::vector<char> &host) {
     // partials of ORDERED linears share one buffer (the ops run in order)
     for (auto &op : st.ops) {
         if (op.type == wsg_step::Op::kDense && op.d.S > 1)
-            set_part(op.d, op.kind, base + pb.part_off);
+            set_part(op.d, op.kind, base + pb.part_off, reinterpret_cast<uint32_t *>(base + pb.ctr_off));
         if (op.type == wsg_step::Op::kW4 && op.w.S > 1)
             op.w.part = reinterpret_cast<float *>(base + pb.part_off);
     }

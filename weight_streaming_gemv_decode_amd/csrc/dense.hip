@@ -183,29 +183,44 @@ __device__ __forceinline__ T reduce_rows(T (&v)[R], int lane) {
     return s;
 }
 
-// Writes row `row`: y (S = 1) or its partial of slice s (S > 1).  sx is the
-// activation scale of the dynamically quantised kind.
+// Row `row` of y from its whole sum v (and acc_out, y16); sx is the
+// activation scale of the dynamically quantised kind.  Returns y[row].
 template <int KIND, typename Acc>
+__device__ __forceinline__ float finish_row(const DenseLin &L, int64_t row, Acc v, float sx) {
+    float yv;
+    if constexpr (KIND == kF16) {
+        yv = v;
+    } else {
+        if (L.acc_out)
+            *glob(L.acc_out + row) = v;
+        yv = ((float)v * *glob(L.w_scale + row)) * (KIND == kW8A8D ? sx : *glob(L.x_scale));
+    }
+    *glob(L.y + row) = yv;
+    if (L.y16)
+        *glob(L.y16 + row) = f16_bits(yv);
+    return yv;
+}
+
+// Writes row `row`: y (S = 1) or its partial of slice s (S > 1; written
+// through to the device's coherence point when the last unit of the row
+// tile sums them, FUSED).
+template <int KIND, bool FUSED, typename Acc>
 __device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row, Acc v, float sx) {
     if (L.S > 1) {
-        *glob(static_cast<Acc *>(L.part) + (int64_t)s * L.N + row) = v;
+        auto *p = glob(static_cast<Acc *>(L.part) + (int64_t)s * L.N + row);
+        if constexpr (FUSED)
+            __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            *p = v;
     } else {
-        float yv;
-        if constexpr (KIND == kF16) {
-            yv = v;
-        } else {
-            if (L.acc_out)
-                *glob(L.acc_out + row) = v;
-            yv = ((float)v * *glob(L.w_scale + row)) * (KIND == kW8A8D ? sx : *glob(L.x_scale));
-        }
-        *glob(L.y + row) = yv;
-        if (L.y16)
-            *glob(L.y16 + row) = f16_bits(yv);
+        finish_row<KIND>(L, row, v, sx);
     }
 }
 
-template <int KIND, int R, int CH, bool NT, bool TAIL>
-__device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u32x4 *xs) {
+// One work unit: rows of row tile `tile` over k slice s.  Returns the
+// activation scale of the dynamically quantised kind (0 for the others).
+template <int KIND, int R, int CH, bool NT, bool TAIL, bool FUSED = false>
+__device__ __forceinline__ float dense_unit(const DenseLin &L, int tile, int s, u32x4 *xs) {
     using Ops = DenseOps<KIND>;
     using Acc = typename Ops::Acc;
     constexpr int CHUNK = kWave * CH;
@@ -265,7 +280,7 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
             if ((lane & (span - 1)) == 0) {
                 const int64_t row = row0 + (int64_t)(wave + gi * kWavesPerBlock) * R + lane / span;
                 if (row <= last_row) {
-                    store_row<KIND>(L, s, row, v, sx);
+                    store_row<KIND, FUSED>(L, s, row, v, sx);
                 }
             }
 #pragma unroll
@@ -342,7 +357,7 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
                 load_step(bufB, gb, cb);
             }
         }
-        return;
+        return sx;
     }
 
     if (nsteps > 0)
@@ -403,7 +418,7 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
     __syncthreads();
 
     if (nsteps == 0)
-        return;
+        return sx;
     int st = 0;
     while (st + 2 < nsteps) {
         int gb = ga, cb = ca;
@@ -427,6 +442,7 @@ __device__ __forceinline__ void dense_unit(const DenseLin &L, int tile, int s, u
     } else {
         consume(bufA, ga, ca);
     }
+    return sx;
 }
 
 // The epilogues of a finished unit (S = 1) that read its rows of y back:
@@ -444,13 +460,59 @@ __device__ __forceinline__ void dense_after_unit(const DenseLin &L, int tile) {
         publish_rows(L.arg, L.y, r0, nrows, tile);
 }
 
-template <int KIND, int R, int CH, bool NT, bool TAIL>
+// Split k summed by the last unit of each row tile to finish: every unit
+// writes its partials with agent-scope stores (written through to the
+// device's coherence point, where the other compute dies' L2 caches read
+// them), waits until they are complete, then counts itself in on the
+// tile's counter; the unit that counts last reads the S partials back with
+// agent-scope loads and sums them in slice order (the reduce kernel's
+// order, so the result is the same bits), then runs the epilogues.  The
+// counter wraps to zero on the last arrival, ready for the next launch.
+// (Ordering plain stores by agent-scope release and acquire fences instead
+// writes back and invalidates the whole L2 per wave: 2.4 ms on the
+// 248320x1024 lm_head, against 77 us.)
+template <int KIND>
+__device__ __forceinline__ void dense_last_arriver(const DenseLin &L, int tile, float sx) {
+    using Acc = typename DenseOps<KIND>::Acc;
+    __shared__ uint32_t s_old;
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint32_t last = (uint32_t)L.S - 1u;
+    if (threadIdx.x == 0)
+        s_old = __builtin_amdgcn_atomic_inc32(glob(L.ctr + tile), last, __ATOMIC_RELAXED, "agent");
+    __syncthreads();
+    if (s_old != last)
+        return;
+    const int64_t r0 = (int64_t)tile * L.tile_rows;
+    const int nrows = (int)min((int64_t)L.tile_rows, L.N - r0);
+    const Acc *p = static_cast<const Acc *>(L.part);
+    for (int i = threadIdx.x; i < nrows; i += kBlock) {
+        const int64_t n = r0 + i;
+        Acc a = 0;
+        for (int s = 0; s < L.S; ++s) {
+            const auto *q = glob(p + (int64_t)s * L.N + n);
+            const Acc v = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a = s == 0 ? v : a + v;
+        }
+        finish_row<KIND>(L, n, a, sx);
+    }
+    if (L.arg.keys != nullptr || L.conv.out != nullptr)
+        dense_after_unit(L, tile);
+}
+
+// FUSED (split linears whose last unit per row tile sums the partials) is
+// a kernel of its own: the arrival code costs registers, and fewer resident
+// waves make the plain kernel slower (82 against 71.5 us on the lm_head).
+template <int KIND, int R, int CH, bool NT, bool TAIL, bool FUSED>
 __global__ __launch_bounds__(kBlock) void dense_gemv_kernel(DenseLin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
-    dense_unit<KIND, R, CH, NT, TAIL>(L, u / L.S, u % L.S, xs_dyn);
-    if (L.S == 1 && (L.arg.keys != nullptr || L.conv.out != nullptr))
+    const float sx = dense_unit<KIND, R, CH, NT, TAIL, FUSED>(L, u / L.S, u % L.S, xs_dyn);
+    if constexpr (FUSED) {
+        dense_last_arriver<KIND>(L, u / L.S, sx);
+    } else if (L.S == 1 && (L.arg.keys != nullptr || L.conv.out != nullptr)) {
         dense_after_unit(L, u);
+    }
 }
 
 template <int KIND, int R, int CH, bool NT, bool TAIL>
@@ -474,25 +536,12 @@ __global__ __launch_bounds__(kBlock) void dense_reduce_kernel(DenseLin L) {
     if constexpr (KIND == kW8A8D)
         sx = *L.sx_part;  // published by the first work unit of the launch
     if (n < L.N) {
-        float yv;
-        if constexpr (KIND == kF16) {
-            const float *p = static_cast<const float *>(L.part);
-            float a = p[n];
-            for (int s = 1; s < L.S; ++s)
-                a += p[(int64_t)s * L.N + n];
-            yv = a;
-        } else {
-            const int32_t *p = static_cast<const int32_t *>(L.part);
-            int32_t a = p[n];
-            for (int s = 1; s < L.S; ++s)
-                a += p[(int64_t)s * L.N + n];
-            if (L.acc_out)
-                L.acc_out[n] = a;
-            yv = ((float)a * L.w_scale[n]) * (KIND == kW8A8D ? sx : L.x_scale[0]);
-        }
-        L.y[n] = yv;
-        if (L.y16)
-            L.y16[n] = f16_bits(yv);
+        using Acc = typename DenseOps<KIND>::Acc;
+        const Acc *p = static_cast<const Acc *>(L.part);
+        Acc a = p[n];
+        for (int s = 1; s < L.S; ++s)
+            a += p[(int64_t)s * L.N + n];
+        const float yv = finish_row<KIND>(L, n, a, sx);
         best = arg_key(yv, n);
         if (L.conv.out != nullptr)
             conv_step(L.conv, n, yv);
@@ -852,7 +901,10 @@ template <int KIND, int R, int CH, bool NT, bool TAIL>
 hipError_t launch_single(const DenseLin &L, hipStream_t s) {
     const int units = L.n_tiles * L.S;
     const int lds = dense_lds_bytes(L, CH);
-    hipLaunchKernelGGL((dense_gemv_kernel<KIND, R, CH, NT, TAIL>), dim3(units), dim3(kBlock), lds, s, L);
+    if (L.S > 1 && L.fuse)
+        hipLaunchKernelGGL((dense_gemv_kernel<KIND, R, CH, NT, TAIL, true>), dim3(units), dim3(kBlock), lds, s, L);
+    else
+        hipLaunchKernelGGL((dense_gemv_kernel<KIND, R, CH, NT, TAIL, false>), dim3(units), dim3(kBlock), lds, s, L);
     return hipGetLastError();
 }
 

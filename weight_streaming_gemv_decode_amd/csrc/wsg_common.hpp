@@ -153,13 +153,15 @@ struct DenseLin {
     int32_t kvs;           // vectors per slice (the last slice may be shorter)
     int32_t tile_rows;     // rows per work unit
     int32_t n_tiles;       // ceil(N / tile_rows)
-    int32_t pad;
-    ArgOut arg;            // optional greedy token over y (S = 1: the units; S > 1: the reduce)
+    int32_t fuse;          // S > 1: 0 = a reduce kernel sums the partials; 1 = the last unit of each
+                           // row tile does (partials written through at agent scope)
+    ArgOut arg;            // optional greedy token over y (S = 1 or fused: the units; else the reduce)
     ConvOut conv;          // optional causal-conv1d step over y (same place as y is final)
     uint16_t *y16;         // optional fp16 copy of y [N] (same place as y is final)
     int8_t *xq_out;        // kW8A8D: optional int8 codes [K] (written by the first row tile)
     float *sx_out;         // kW8A8D: optional activation scale [1]
     float *sx_part;        // kW8A8D with S > 1: the activation scale, after the partials (for the reduce)
+    uint32_t *ctr;         // fuse != 0: [n_tiles] arrival counters, zero between launches
 };
 
 // One int4 linear in the packed tile layout (16 rows x 128 k per 1 KiB tile).

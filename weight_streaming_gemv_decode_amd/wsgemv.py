@@ -249,7 +249,7 @@ def gemv_f16_argmax(W: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] 
     if token is None:
         token = torch.empty(1, dtype=torch.int32, device=W.device)
     if ws is None:
-        ws = torch.empty(workspace_bytes(F16 | WITH_ARGMAX, 1, N, K, splits), dtype=torch.uint8, device=W.device)
+        ws = workspace(F16 | WITH_ARGMAX, 1, N, K, splits, W.device)
     wp, wn = _ws(ws)
     tl = _dev(token_logit, torch.float32, "token_logit", (1,)) if token_logit is not None else None
     _check(lib().gemv_f16_argmax(_dev(W, torch.float16, "W"), _dev(x, torch.float16, "x", (K,)),
