@@ -253,7 +253,7 @@ def counter_pass(args, torch, synth, wsgemv, dev, stream):
         Ws = [lm.W, lm.W.clone()]
         b = lm.N * lm.K * 2 + lm.K * 2 + lm.N * 4
         y = torch.empty(lm.N, device=dev)
-        for S, ks in ((1, ["dense_gemv_kernel<0, 1, 2"]), (2, ["dense_gemv_kernel<0, 8, 1", "dense_reduce_kernel<0>"])):
+        for S, ks in ((1, ["dense_gemv_kernel<0, 1, 2"]), (2, ["dense_gemv_kernel<0, 8, 1"])):
             ws = wsgemv.workspace(wsgemv.F16, 1, lm.N, lm.K, S, dev)
             run(f"c2_S{S}", f"C2 lm_head 248320x1024, S = {S}", ks, 6, b,
                 lambda i: wsgemv.gemv_f16(Ws[i % 2], lm.x, y=y, splits=S, ws=ws, stream=stream))
@@ -510,10 +510,23 @@ def main():
             res[f"S={S if S else wsgemv.plan_splits(0, 1, lm.N, lm.K)}{' (auto)' if S == 0 else ''}"] = {
                 "us": t * 1e3, "GBps": b / (t * 1e-3) / 1e9, "pct_peak": 100 * b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "single_launch_median_us": s["median_ms"] * 1e3}
+        res["S=2"]["note"] = "split-K; the last workgroup of each row tile adds the two partials (no reduce kernel)"
+        # ablation: the same split summed by a second, reduce kernel (same bits)
+        wsgemv.tune_set("dense_fuse", 0)
+        try:
+            ws = wsgemv.workspace(wsgemv.F16, 1, lm.N, lm.K, 2, dev)
+            y = torch.empty(lm.N, device=dev)
+            fn = lambda i: wsgemv.gemv_f16(Ws[i % 2], lm.x, y=y, splits=2, ws=ws, stream=stream)  # noqa: E731
+            for i in range(10):
+                fn(i)
+            t = region_time(torch, fn, 100, stream)
+        finally:
+            wsgemv.tune_set("dense_fuse", -1)
+        res["S=2 reduce kernel"] = {"us": t * 1e3, "GBps": b / (t * 1e-3) / 1e9,
+                                    "pct_peak": 100 * b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
         # the same lm_head with the greedy token fused into the kernel that writes the logits
         tok = torch.empty(1, dtype=torch.int32, device=dev)
-        ws = torch.empty(wsgemv.workspace_bytes(wsgemv.F16 | wsgemv.WITH_ARGMAX, 1, lm.N, lm.K), dtype=torch.uint8,
-                         device=dev)
+        ws = wsgemv.workspace(wsgemv.F16 | wsgemv.WITH_ARGMAX, 1, lm.N, lm.K, 0, dev)
         y = torch.empty(lm.N, device=dev)
         fn = lambda i: wsgemv.gemv_f16_argmax(Ws[i % 2], lm.x, y=y, token=tok, ws=ws, stream=stream)  # noqa: E731
         for i in range(10):

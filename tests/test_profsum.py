@@ -50,3 +50,43 @@ def test_summary(tmp_path):
     assert c2["read_bytes"] == round(311 * 1024 * 2.0) and c2["write_bytes"] == 9 * 1024
     text = profsum.render(recs, calrec, ["cmd"])
     assert text.count(profsum.JSON_TAG) == 2
+
+
+def test_shader_counter_summary(tmp_path):
+    """SQ pass: counters summed over a dispatch's rows, dispatches of other
+    kernels skipped, averages per (config, kernel), and the derived
+    occupancy and busy fractions from hand-computed values."""
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp",
+            "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size"]
+    # one die busy g = 8000 cycles; 1024 SIMDs; 10 us dispatch
+    g = 8000.0
+    want = {"GRBM_GUI_ACTIVE": 8 * g, "SQ_WAVE_CYCLES": 2.5 * g * 1024 / 4, "SQ_ACTIVE_INST_VALU": 0.4 * g * 1024 / 4,
+            "SQ_VALU_MFMA_BUSY_CYCLES": 0.1 * g * 1024, "SQ_WAVES": 1000.0, "SQ_INSTS_VALU": 50000.0,
+            "SQ_INSTS_MFMA": 3000.0, "SQ_INSTS_LDS": 7000.0}
+    with open(tmp_path / "sq.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, cols)
+        w.writeheader()
+        disp = [("noise_kernel", 0.5), ("w4_grouped_kernel<2, 4, true, 1, false>", 1.0),
+                ("w4_grouped_kernel<2, 4, true, 1, false>", 1.0), ("noise_kernel", 3.0)]
+        for d, (name, f_) in enumerate(disp, 1):
+            for c, v in want.items():
+                for half in (0, 1):   # two rows per counter, added
+                    w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": c,
+                                "Counter_Value": f_ * v / 2, "Start_Timestamp": 1000, "End_Timestamp": 11000,
+                                "VGPR_Count": 152, "Accum_VGPR_Count": 0, "SGPR_Count": 96, "LDS_Block_Size": 25088})
+    man = {"configs": [{"label": "c5_M4", "workload": "W4A16 step, M = 4", "kernels": ["w4_grouped_kernel<2, 4"],
+                        "steps": 2, "algorithmic_bytes": 1}]}
+    with open(tmp_path / "man.json", "w") as f:
+        json.dump(man, f)
+    recs = profsum.sq_per_config(str(tmp_path / "sq.csv"), man["configs"])
+    assert len(recs) == 1 and recs[0]["dispatches"] == 2 and recs[0]["vgpr"] == 152
+    d = profsum.sq_derived(recs[0])
+    assert abs(d["waves_per_simd"] - 2.5) < 1e-9
+    assert abs(d["valu_busy"] - 0.4) < 1e-9 and abs(d["mfma_busy"] - 0.1) < 1e-9
+    assert abs(d["valu_per_wave"] - 50.0) < 1e-9 and abs(d["mfma_per_wave"] - 3.0) < 1e-9
+    assert abs(d["grbm_per_ns"] - 6.4) < 1e-9          # 64000 cycles over 10000 ns
+    profsum.main(["--sq", str(tmp_path / "sq.csv"), "--manifest", str(tmp_path / "man.json"),
+                  "--out", str(tmp_path / "out.md"), "--command", "rocprofv3 ..."])
+    text = (tmp_path / "out.md").read_text()
+    assert "| W4A16 step, M = 4 | `w4_grouped_kernel<2, 4` | 2 | 10.0 | 6.4 | 152/0/96 | 25088 | 2.50 | 40% | 10% " \
+           "| 50 | 3 | 7 |" in text

@@ -49,6 +49,17 @@
 namespace wsg {
 namespace {
 
+// An LDS pointer for the direct-to-LDS load builtin.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T *lds(T *p) {
+    return (__attribute__((address_space(3))) T *)p;
+}
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory
+// operations and nothing else (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maximum).
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <bool NT>
 __device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
     if constexpr (NT)
@@ -310,31 +321,33 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
     Buf bufA, bufB;
 
     if constexpr (MFMA) {
-        // Verify blocks stage M rows of activations per unit.  Their first
-        // vectors are loaded into registers ahead of both weight steps:
-        // vector-memory loads retire in issue order, so writing them to LDS
-        // then waits for them alone, with both steps in flight across the
-        // barrier (decode step on MI355X, M = 4: 71-74 vs 74-75 us; M = 8:
-        // 75-79 vs 81-82 us).  The M = 1 kernels keep the order below: holding these
-        // registers with both steps costs them a wave per SIMD, and they
-        // measured slower.
-        constexpr int kXHold = 4;
+        // Verify blocks stage M rows of activations per unit.  Where a row
+        // of the slice is whole 64-vector chunks (no tail), each chunk goes
+        // straight from memory to LDS (gfx950 direct-to-LDS 16-byte loads,
+        // one chunk per wave instruction) ahead of both weight steps: no
+        // registers hold it, and since vector-memory loads retire in issue
+        // order, a wait for all but the weight loads issued after them
+        // leaves both weight steps in flight across the barrier.  Other
+        // slices stage through registers behind the weight steps.
         const int64_t xrow = (int64_t)L.K / 8;
-        const int nx = M * nxv;
-        auto xsrc = [&](int i) {
-            const int m = i / nxv, v = i - m * nxv;
-            return glob(L.x + m * xrow + (int64_t)kb0 * 16 + v);
-        };
-        auto xdst = [&](int i) {
-            const int m = i / nxv;
-            return i + m * kW4XRowPad;
-        };
-        u32x4 xh[kXHold];
-#pragma unroll
-        for (int j = 0; j < kXHold; ++j) {
-            const int i = tid + j * kBlock;
-            if (i < nx)
-                xh[j] = *xsrc(i);
+        const bool dma = !TAIL && nxv % kWave == 0;
+        if (dma) {
+            // chunks c = wave, wave + 4, ... of the M rows: row m, vectors v0 .. v0 + 63
+            int m = 0, v0 = wave * kWave;
+            while (v0 >= nxv) {
+                v0 -= nxv;
+                ++m;
+            }
+            for (; m < M;) {
+                __builtin_amdgcn_global_load_lds(glob(L.x + m * xrow + (int64_t)kb0 * 16 + v0 + lane),
+                                                 lds(xs + m * xstride + v0), 16, 0, 0);
+                v0 += kWavesPerBlock * kWave;
+                while (v0 >= nxv) {
+                    v0 -= nxv;
+                    ++m;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         int gb = 0, cb = 0;
         next(gb, cb);
@@ -342,15 +355,25 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
             load_step(bufA, 0, 0);
         if (nsteps > 1)
             load_step(bufB, gb, cb);
-#pragma unroll
-        for (int j = 0; j < kXHold; ++j) {
-            const int i = tid + j * kBlock;
-            if (i < nx)
-                xs[xdst(i)] = xh[j];
+        if (dma) {
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int kStepLoads = R * (B + B / 4);  // weight and scale loads of one step
+            if (nsteps > 1)
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kStepLoads));
+            else if (nsteps == 1)
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(kStepLoads));
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            const int nx = M * nxv;
+            for (int i = tid; i < nx; i += kBlock) {
+                const int m = i / nxv, v = i - m * nxv;
+                xs[i + m * kW4XRowPad] = *glob(L.x + m * xrow + (int64_t)kb0 * 16 + v);
+            }
+            __syncthreads();
         }
-        for (int i = tid + kXHold * kBlock; i < nx; i += kBlock)
-            xs[xdst(i)] = *xsrc(i);
-        __syncthreads();
         // a buffer is refilled with the step after next once it is consumed
         for (int st = 0; st < nsteps; st += 2) {
             consume(bufA, ga, ca);

@@ -17,6 +17,12 @@ skipped), and every config's bytes per step are compared with its
 algorithmic bytes.  The summary ends with one ``traffic-json:`` line per
 config that bench.py attaches to its results while the kernel sources still
 hash to the ones measured.  Pure Python: no torch, no GPU.
+
+The same run under one pass of shader counters (``--pmc`` with the SQ_ and
+GRBM_ counters of SQ_COUNTERS) is summarised per config and kernel with
+``--sq CSV`` instead of ``--fetch/--write``: resident waves per SIMD, the
+vector ALU's and the matrix cores' busy fractions, and instructions per
+wave.
 """
 from __future__ import annotations
 
@@ -105,6 +111,92 @@ def per_config(path: str, counter: str, manifest: List[dict]) -> Dict[str, dict]
     return out
 
 
+# One counter pass on MI355X: at most 8 SQ_ and 2 GRBM_ counters.
+SQ_COUNTERS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_MFMA",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
+XCDS, SIMDS = 8, 1024   # MI355X: 8 compute dies, 256 CUs of 4 SIMDs
+
+
+def _sq_dispatches(path: str) -> List[dict]:
+    """Per dispatch, in order: kernel name, duration (ns), registers, LDS
+    bytes and the sum of each counter over its rows."""
+    rows: Dict[int, dict] = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            e = rows.setdefault(d, {"name": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                                    "vgpr": int(r["VGPR_Count"]), "agpr": int(r["Accum_VGPR_Count"]),
+                                    "sgpr": int(r["SGPR_Count"]), "lds": int(r["LDS_Block_Size"]), "c": {}})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [rows[d] for d in sorted(rows)]
+
+
+def sq_per_config(path: str, manifest: List[dict]) -> List[dict]:
+    """Average counters per dispatch of every (config, kernel), dispatches
+    assigned to configs in launch order as in per_config."""
+    disp = _sq_dispatches(path)
+    out, i = [], 0
+    for e in manifest:
+        kernels = e["kernels"]
+        need = e["steps"] * len(kernels)
+        got: Dict[str, List[dict]] = collections.defaultdict(list)
+        n = 0
+        while n < need and i < len(disp):
+            d = disp[i]
+            i += 1
+            hit = [k for k in kernels if k in d["name"]]
+            if hit:
+                got[hit[0]].append(d)
+                n += 1
+        if n < need:
+            raise ValueError(f"{e['label']}: found {n} of {need} dispatches of {kernels} in {path}")
+        for k, ds in got.items():
+            avg = {c: sum(d["c"].get(c, 0.0) for d in ds) / len(ds) for c in SQ_COUNTERS}
+            out.append({"label": e["label"], "workload": e["workload"], "kernel": k, "dispatches": len(ds),
+                        "ns": sum(d["ns"] for d in ds) / len(ds), "vgpr": ds[0]["vgpr"], "agpr": ds[0]["agpr"],
+                        "sgpr": ds[0]["sgpr"], "lds": ds[0]["lds"], **avg})
+    return out
+
+
+def sq_derived(r: dict) -> dict:
+    """GRBM_GUI_ACTIVE adds the busy cycles of the 8 compute dies (about 20
+    per ns of kernel time on MI355X, 8 dies at ~2.5 GHz: grbm_per_ns shows
+    it), so one die was busy g = GRBM_GUI_ACTIVE / 8 cycles.  SQ_WAVE_CYCLES
+    and SQ_ACTIVE_INST_VALU count quad-cycles summed over all SIMDs;
+    SQ_VALU_MFMA_BUSY_CYCLES counts cycles."""
+    g = r["GRBM_GUI_ACTIVE"] / XCDS
+    return {"grbm_per_ns": r["GRBM_GUI_ACTIVE"] / r["ns"] if r["ns"] else 0.0,
+            "waves_per_simd": 4 * r["SQ_WAVE_CYCLES"] / (g * SIMDS) if g else 0.0,
+            "valu_busy": 4 * r["SQ_ACTIVE_INST_VALU"] / (g * SIMDS) if g else 0.0,
+            "mfma_busy": r["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * SIMDS) if g else 0.0,
+            "valu_per_wave": r["SQ_INSTS_VALU"] / r["SQ_WAVES"] if r["SQ_WAVES"] else 0.0,
+            "mfma_per_wave": r["SQ_INSTS_MFMA"] / r["SQ_WAVES"] if r["SQ_WAVES"] else 0.0,
+            "lds_per_wave": r["SQ_INSTS_LDS"] / r["SQ_WAVES"] if r["SQ_WAVES"] else 0.0}
+
+
+def render_sq(recs: List[dict], commands: List[str], notes: List[str] = ()) -> str:
+    lines = ["# Shader counters per config and kernel", "",
+             "One counter pass on one MI355X over a `bench.py --counter-pass` run (every config a few steps, "
+             f"in launch order), counters {', '.join(SQ_COUNTERS)}. Commands (repository root as `$REPO`, run "
+             "from `/tmp`):", "", "```"] + commands + ["```", "",
+             "Derived: one compute die was busy g = GRBM_GUI_ACTIVE / 8 cycles (GRBM_GUI_ACTIVE adds the 8 dies; "
+             "the `GRBM/ns` column, about 20 = 8 dies at ~2.5 GHz, checks it against the dispatch timestamps); "
+             "waves/SIMD = 4 SQ_WAVE_CYCLES / (g x 1024 SIMDs) (quad-cycles), VALU busy = 4 SQ_ACTIVE_INST_VALU "
+             "/ (g x 1024), MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (g x 1024). VGPR, AGPR and SGPR counts and "
+             "LDS bytes per workgroup are as the profiler reports them.", "",
+             "| Config | Kernel | Dispatches | us | GRBM/ns | VGPR/AGPR/SGPR | LDS B | waves/SIMD | VALU busy "
+             "| MFMA busy | VALU/wave | MFMA/wave | LDS/wave |", "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in recs:
+        d = sq_derived(r)
+        lines.append(f"| {r['workload']} | `{r['kernel']}` | {r['dispatches']} | {r['ns'] / 1e3:.1f} "
+                     f"| {d['grbm_per_ns']:.1f} | {r['vgpr']}/{r['agpr']}/{r['sgpr']} | {r['lds']} "
+                     f"| {d['waves_per_simd']:.2f} | {100 * d['valu_busy']:.0f}% | {100 * d['mfma_busy']:.0f}% "
+                     f"| {d['valu_per_wave']:.0f} | {d['mfma_per_wave']:.0f} | {d['lds_per_wave']:.0f} |")
+    lines.append("")
+    lines += [n + "\n" for n in notes]
+    return "\n".join(lines) + "\n"
+
+
 def summarize(fetch_csv: str, write_csv: str, manifest_path: str) -> List[dict]:
     with open(manifest_path) as f:
         man = json.load(f)
@@ -158,13 +250,26 @@ def render(recs: List[dict], cal: dict, commands: List[str], notes: List[str] = 
 
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--sq", help="a shader-counter pass (SQ_COUNTERS) instead of --fetch/--write")
     ap.add_argument("--manifest", required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--command", action="append", default=[], help="a command line that produced the passes")
     ap.add_argument("--note", action="append", default=[], help="a paragraph to add under the table")
     a = ap.parse_args(argv)
+    if a.sq:
+        with open(a.manifest) as f:
+            recs = sq_per_config(a.sq, json.load(f)["configs"])
+        with open(a.out, "w") as f:
+            f.write(render_sq(recs, a.command, a.note))
+        for r in recs:
+            d = sq_derived(r)
+            print(f"{r['label']:24s} {r['kernel']:34s} waves/SIMD {d['waves_per_simd']:.2f} "
+                  f"VALU {d['valu_busy']:.2f} MFMA {d['mfma_busy']:.2f}")
+        return
+    if not (a.fetch and a.write):
+        ap.error("--fetch and --write (or --sq) are required")
     recs, cal = summarize(a.fetch, a.write, a.manifest)
     with open(a.out, "w") as f:
         f.write(render(recs, cal, a.command, a.note))
