@@ -42,13 +42,12 @@
  * may be NULL when that size is 0.  One workspace must not serve two calls
  * that are in flight at the same time.
  *
- * For the fp16 and int8-weight kinds the last workgroup to finish a row
- * tile adds that tile's partials (no second kernel); it finds out through
- * one arrival counter per row tile, kept in the workspace after the
- * partials.  So a split workspace must be zero-filled before its first use
+ * The last workgroup to finish a row tile adds that tile's partials (no
+ * second kernel); it finds out through one arrival counter per row tile,
+ * kept in the workspace after the partials (from the next 256-byte
+ * boundary).  So a split workspace must be zero-filled before its first use
  * (hipMemset, torch.zeros); every call leaves the counters zero again, so
- * one zero fill serves every later call.  The int4 kinds add their partials
- * in a second kernel and need no initialisation.
+ * one zero fill serves every later call.
  */
 #ifndef WSGEMV_H
 #define WSGEMV_H

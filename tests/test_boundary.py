@@ -120,7 +120,8 @@ def test_w4_validation_and_sizes(L):
     assert g(*a8(sx=FAKE + 2)) == ALIGN
     assert g(*a8(S=3)) == SHAPE                                                 # slice past K
     assert g(*a8(N=16, K=1024, S=2)) == WS
-    assert L.wsg_workspace_bytes(3, 1, 16, 1024, 2) == 2 * 16 * 4
+    # 2 x 16 partials, then one counter (16 rows: a single 16-row tile)
+    assert L.wsg_workspace_bytes(3, 1, 16, 1024, 2) == 256 + 4
     assert g(*a8(N=0)) == OK                                                    # nothing to do
 
 

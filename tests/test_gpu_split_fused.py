@@ -1,6 +1,6 @@
-"""Split-K summed by the last unit of each row tile, the default for the
-fp16 and int8-weight kinds, checked against the same split summed by the
-reduce kernel and against the oracle.
+"""Split-K summed by the last unit of each row tile, the default for every
+kind (fp16, int8 and int4 weights), checked against the same split summed
+by the reduce kernel and against the oracle.
 
 Both paths add the S partials in slice order 0..S-1, so they must agree bit
 for bit; each is also within the oracle's GEMV bound (int8 accumulators
@@ -183,5 +183,88 @@ def test_ordered_step_with_fused_splits_replayed():
         assert_bits_equal(host(ys[-1]), host(ys_r[-1]), f"replay {rep} int8: fused vs reduce kernel")
         assert int(host(tok)[0]) == oracle.argmax_f32(host(ys[2]))
         assert int(host(tok)[0]) == int(host(tok_r)[0])
+    fused.close()
+    red.close()
+
+
+def _w4(seed, N, K):
+    Wc = synth.w4_words(seed, 0, N, K)
+    s4 = synth.f16_uniform(seed, 1, (N, K // 128), 0.002, 0.02)
+    Wp, Sp = wsgemv.pack_w4(dev(Wc), dev(s4))
+    return Wc, s4, Wp, Sp
+
+
+def _w4_ctr_off(M, N, S):
+    return (S * M * N * 4 + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(1, 700, 4096, 2), (1, 64, 8192, 0), (4, 300, 3072, 3), (8, 1000, 2048, 2),
+                                          (4, 40, 4096, 0)])
+def test_w4a16_fused_equals_reduce(M, N, K, splits):
+    S = splits or wsgemv.plan_splits(wsgemv.W4A16, M, N, K)
+    assert S > 1
+    say(f"fused split w4a16 M={M} {N}x{K} S={S}")
+    Wc, s4, Wp, Sp = _w4(199, N, K)
+    ws = wsgemv.workspace(wsgemv.W4A16, M, N, K, splits)
+    for rep in range(2):
+        X = synth.f16_normal(200, rep, (M, K), 1.0)
+        y = wsgemv.gemv_w4a16(Wp, Sp, dev(X), N, splits=splits, ws=ws)
+        c = host(ws[_w4_ctr_off(M, N, S):])
+        assert not c.any(), "arrival counters not zero after the call"
+        with _Reduce():
+            y_r = wsgemv.gemv_w4a16(Wp, Sp, dev(X), N, splits=splits)
+        assert_bits_equal(host(y), host(y_r), f"w4a16 M={M} S={S} rep {rep}: fused vs reduce kernel")
+        Y, A = oracle.gemv_w4a16(Wc, s4, X)
+        assert_within(host(y).reshape(M, N), Y, A, f"w4a16 M={M} S={S} rep {rep}")
+
+
+@pytest.mark.parametrize("N,K,splits", [(500, 4096, 2), (48, 8192, 0)])
+def test_w4a8_fused_equals_reduce(N, K, splits):
+    S = splits or wsgemv.plan_splits(wsgemv.W4A8, 1, N, K)
+    assert S > 1
+    say(f"fused split w4a8 {N}x{K} S={S}")
+    Wc, s4, Wp, Sp = _w4(201, N, K)
+    ws = wsgemv.workspace(wsgemv.W4A8, 1, N, K, splits)
+    x = synth.f16_normal(202, 0, (K,), 1.0)
+    y = wsgemv.gemv_w4a8(Wp, Sp, dev(x), N, splits=splits, ws=ws)
+    assert not host(ws[_w4_ctr_off(1, N, S):]).any()
+    with _Reduce():
+        y_r = wsgemv.gemv_w4a8(Wp, Sp, dev(x), N, splits=splits)
+    assert_bits_equal(host(y), host(y_r), "w4a8: fused vs reduce kernel")
+    xq, sx = oracle.quantize_x_i8(x)
+    assert_within(host(y), *oracle.gemv_w4a8(Wc, s4, xq, sx), "w4a8")
+
+
+def test_ordered_step_with_fused_w4_split_and_token():
+    """An ORDERED step with a split int4 verify block (M = 4) that takes the
+    greedy token of every row, replayed: tokens from the tile keys the last
+    units publish, equal to the reduce plan's."""
+    say("ordered step with a fused int4 split and tokens")
+    M, N, K = 4, 5000, 2048
+    Wc, s4, Wp, Sp = _w4(203, N, K)
+    X = torch.empty((M, K), dtype=torch.float16, device="cuda")
+
+    def plan():
+        y = torch.empty((M, N), device="cuda")
+        tok = torch.empty(M, dtype=torch.int32, device="cuda")
+        lin = wsgemv.Linear(wsgemv.W4A16, Wp, X, y, N, K, M=M, scale=Sp, group=128, splits=2, argmax_idx=tok)
+        return wsgemv.DecodeStep([lin], wsgemv.STEP_ORDERED | wsgemv.STEP_FORCE_GRAPH), y, tok
+
+    fused, y, tok = plan()
+    with _Reduce():
+        red, y_r, tok_r = plan()
+    for rep in range(3):
+        Xh = synth.f16_normal(204, rep, (M, K), 1.0)
+        X.copy_(torch.from_numpy(Xh))
+        fused()
+        red()
+        torch.cuda.synchronize()
+        assert_bits_equal(host(y), host(y_r), f"replay {rep}: fused vs reduce kernel")
+        Y, A = oracle.gemv_w4a16(Wc, s4, Xh)
+        assert_within(host(y), Y, A, f"replay {rep}")
+        yh = host(y)
+        for m in range(M):
+            assert int(host(tok)[m]) == oracle.argmax_f32(yh[m]), f"replay {rep} row {m}"
+        assert_bits_equal(host(tok), host(tok_r), f"replay {rep} tokens")
     fused.close()
     red.close()

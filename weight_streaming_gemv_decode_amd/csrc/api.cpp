@@ -370,6 +370,7 @@ struct W4Plan {
     int S;
     int kbs;
     int tile_rtiles;
+    int fuse;       // S > 1: how the partials are summed (W4Lin::fuse)
 };
 
 W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
@@ -401,11 +402,22 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
     if (g_tune.w4_tiles > 0)
         tt = g_tune.w4_tiles;
     p.tile_rtiles = (int)tt;
+    p.fuse = p.S > 1 ? dense_fuse_mode() : 0;
     if (g_tune.w4_R > 0)
         p.cfg.R = (int)g_tune.w4_R;
     if (g_tune.w4_B > 0)
         p.cfg.B = (int)g_tune.w4_B;
     return p;
+}
+
+// Split-K workspace of an int4 linear: S x M x N partials, then (fused)
+// one arrival counter per row tile from the next 256-byte boundary.
+size_t w4_part_bytes(const W4Plan &p, int64_t M, int64_t N) {
+    return p.S > 1 ? (size_t)p.S * (size_t)M * (size_t)N * 4 : 0;
+}
+
+size_t w4_ctr_bytes(const W4Plan &p, int64_t N) {
+    return p.S > 1 && p.fuse ? (size_t)cdiv(cdiv(N, 16), p.tile_rtiles) * 4 : 0;
 }
 
 W4Lin make_w4(const void *Wp, const void *Sp, const void *x, float *y, float *part, int64_t M, int64_t N,
@@ -425,6 +437,10 @@ W4Lin make_w4(const void *Wp, const void *Sp, const void *x, float *y, float *pa
     L.kbs = p.kbs;
     L.tile_rtiles = p.tile_rtiles;
     L.n_tiles = (int32_t)cdiv(cdiv(N, 16), p.tile_rtiles);
+    L.fuse = p.fuse;
+    const size_t pb = w4_part_bytes(p, M, N);
+    L.ctr = (p.fuse && part) ? reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(part) + (pb + 255) / 256 * 256)
+                             : nullptr;
     return L;
 }
 
@@ -471,14 +487,15 @@ wsg_status check_w4_args(const void *Wp, const void *Sp, const void *x, const fl
 }
 
 size_t w4_ws_bytes(const W4Plan &p, int64_t M, int64_t N) {
-    return p.S > 1 ? (size_t)p.S * (size_t)M * (size_t)N * 4 : 0;
+    const size_t pb = w4_part_bytes(p, M, N), cb = w4_ctr_bytes(p, N);
+    return cb ? (pb + 255) / 256 * 256 + cb : pb;
 }
 
 wsg_status enqueue_w4(const W4Lin &L, int mode, const W4Cfg &cfg, hipStream_t s) {
     hipError_t e = launch_w4(L, mode, cfg, s);
     if (e != hipSuccess)
         return hip_fail(e);
-    if (L.S > 1) {
+    if (L.S > 1 && !L.fuse) {
         e = launch_w4_reduce(L, s);
         if (e != hipSuccess)
             return hip_fail(e);
@@ -1062,7 +1079,7 @@ void dev_free(wsg_step *st) {
 }
 
 // Workgroups that publish keys for an int4 linear's tokens.
-int32_t w4_token_keys(const W4Lin &L) { return L.S > 1 ? w4_reduce_blocks(L.M, L.N) : L.n_tiles; }
+int32_t w4_token_keys(const W4Lin &L) { return L.S > 1 && !L.fuse ? w4_reduce_blocks(L.M, L.N) : L.n_tiles; }
 
 // True when some linear's x overlaps some linear's y16: the list chains
 // linears, which only the ORDERED plan runs in order.
@@ -1159,7 +1176,7 @@ hipError_t run_ops(const wsg_step *st, hipStream_t s) {
             break;
         case wsg_step::Op::kW4:
             e = launch_w4(op.w, op.mode, op.wc, s);
-            if (e == hipSuccess && op.w.S > 1)
+            if (e == hipSuccess && op.w.S > 1 && !op.w.fuse)
                 e = launch_w4_reduce(op.w, s);
             break;
         case wsg_step::Op::kW4Group:
@@ -1228,7 +1245,7 @@ void count_launches(wsg_step &st) {
             st.launches += op.d.S > 1 && !op.d.fuse;
         } else if (op.type == wsg_step::Op::kW4) {
             st.units += (int64_t)op.w.n_tiles * op.w.S;
-            st.launches += op.w.S > 1;
+            st.launches += op.w.S > 1 && !op.w.fuse;
         } else if (op.type == wsg_step::Op::kDenseGroup || op.type == wsg_step::Op::kW4Group) {
             st.units += op.n_units;
         } else if (op.type == wsg_step::Op::kArgmax) {
@@ -1450,7 +1467,8 @@ wsg_status plan_w4_linear(wsg_step &st, PlanBuild &pb, const wsg_linear &l) {
     const int wmode = l.kind == kW4A8 ? kA8 : ((l.M > 1 || g_tune.w4_mfma_m1 == 1) ? kMfma : kA16);
     if (pb.base_mode == WSG_STEP_ORDERED) {
         W4Plan p = plan_w4(l.M, l.N, l.K, l.splits);
-        pb.part_bytes = std::max(pb.part_bytes, w4_ws_bytes(p, l.M, l.N));
+        pb.part_bytes = std::max(pb.part_bytes, w4_part_bytes(p, l.M, l.N));
+        pb.ctr_bytes = std::max(pb.ctr_bytes, w4_ctr_bytes(p, l.N));
         wsg_step::Op o{};
         o.type = wsg_step::Op::kW4;
         o.mode = wmode;
@@ -1594,8 +1612,10 @@ void fill_block(wsg_step &st, PlanBuild &pb, std::vector<char> &host) {
     for (auto &op : st.ops) {
         if (op.type == wsg_step::Op::kDense && op.d.S > 1)
             set_part(op.d, op.kind, base + pb.part_off, reinterpret_cast<uint32_t *>(base + pb.ctr_off));
-        if (op.type == wsg_step::Op::kW4 && op.w.S > 1)
+        if (op.type == wsg_step::Op::kW4 && op.w.S > 1) {
             op.w.part = reinterpret_cast<float *>(base + pb.part_off);
+            op.w.ctr = op.w.fuse ? reinterpret_cast<uint32_t *>(base + pb.ctr_off) : nullptr;
+        }
     }
     for (int k = 0; k < 3; ++k) {
         if (pb.du[k].empty())

@@ -60,6 +60,17 @@ __device__ __forceinline__ __attribute__((address_space(3))) T *lds(T *p) {
 // expcnt 6:4 and lgkmcnt 11:8 left at their maximum).
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// A split-K partial: written through at agent scope when the last unit of
+// the row tile sums the partials (FUSED), else a plain store for the reduce
+// kernel.
+template <bool FUSED>
+__device__ __forceinline__ void store_part(float *p, float v) {
+    if constexpr (FUSED)
+        __hip_atomic_store(glob(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *glob(p) = v;
+}
+
 template <bool NT>
 __device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
     if constexpr (NT)
@@ -114,7 +125,7 @@ __device__ __forceinline__ float scale_of(u32x2 sc, int b) {
 // blocks of a slice are a multiple of B): then the step loads carry no
 // guards, and the compiler can keep the next step's loads in flight while
 // the current step is consumed (a guarded load path makes it wait for all).
-template <int R, int B, bool NT, int MODE, bool TAIL>
+template <int R, int B, bool NT, int MODE, bool TAIL, bool FUSED = false>
 __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *xs) {
     static_assert(B % 4 == 0, "steps are whole 4-block scale quads");
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -200,7 +211,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                 const int64_t n = rt * 16 + r16;
                 if (lane < 16 && rt <= last_rt && n < L.N) {
                     if (L.S > 1) {
-                        *glob(L.part + (int64_t)s * L.N + n) = v;
+                        store_part<FUSED>(L.part + (int64_t)s * L.N + n, v);
                     } else {
                         *glob(L.y + n) = v;
                         if (L.y16)
@@ -218,7 +229,7 @@ __device__ __forceinline__ void w4_unit(const W4Lin &L, int tile, int s, u32x4 *
                         const int m = 4 * g + i;
                         if (m < M) {
                             if (L.S > 1) {
-                                *glob(L.part + ((int64_t)s * M + m) * L.N + n) = accm[r][i];
+                                store_part<FUSED>(L.part + ((int64_t)s * M + m) * L.N + n, accm[r][i]);
                             } else {
                                 *glob(L.y + (int64_t)m * L.N + n) = accm[r][i];
                                 if (L.y16)
@@ -576,12 +587,52 @@ constexpr int w4_min_waves_per_simd() {
     return MODE == kMfma && R * B <= 8 ? 3 : 1;
 }
 
-template <int R, int B, bool NT, int MODE, bool TAIL>
+// Split k summed by the last unit of each row tile (the dense kinds' scheme:
+// written-through partials, the wave's stores complete before it counts in
+// on the tile's counter, which wraps to zero on the last arrival; the last
+// unit reads the S partials back with agent-scope loads and adds them in
+// slice order, the reduce kernel's order), then the epilogues.
+__device__ __forceinline__ void w4_last_arriver(const W4Lin &L, int tile) {
+    __shared__ uint32_t s_old;
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint32_t last = (uint32_t)L.S - 1u;
+    if (threadIdx.x == 0)
+        s_old = __builtin_amdgcn_atomic_inc32(glob(L.ctr + tile), last, __ATOMIC_RELAXED, "agent");
+    __syncthreads();
+    if (s_old != last)
+        return;
+    const int64_t r0 = (int64_t)tile * L.tile_rtiles * 16;
+    const int nrows = (int)min((int64_t)L.tile_rtiles * 16, L.N - r0);
+    const int64_t total = (int64_t)L.M * L.N;
+    for (int m = 0; m < L.M; ++m) {
+        for (int i = threadIdx.x; i < nrows; i += kBlock) {
+            const int64_t j = (int64_t)m * L.N + r0 + i;
+            float a = 0.0f;
+            for (int sl = 0; sl < L.S; ++sl) {
+                const float v = __hip_atomic_load(glob(L.part + (int64_t)sl * total + j), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                a = sl == 0 ? v : a + v;
+            }
+            *glob(L.y + j) = a;
+            if (L.y16)
+                *glob(L.y16 + j) = f16_bits(a);
+        }
+    }
+    if (L.arg.keys != nullptr || L.conv.out != nullptr)
+        w4_after_unit(L, tile);
+}
+
+// FUSED is a kernel of its own, so that the arrival code leaves the plain
+// kernel's registers (and resident waves) as they are.
+template <int R, int B, bool NT, int MODE, bool TAIL, bool FUSED>
 __global__ __launch_bounds__(kBlock, (w4_min_waves_per_simd<R, B, MODE>())) void w4_gemv_kernel(W4Lin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
-    w4_unit<R, B, NT, MODE, TAIL>(L, u / L.S, u % L.S, xs_dyn);
-    if (L.S == 1 && (L.arg.keys != nullptr || L.conv.out != nullptr))
+    w4_unit<R, B, NT, MODE, TAIL, FUSED>(L, u / L.S, u % L.S, xs_dyn);
+    if constexpr (FUSED)
+        w4_last_arriver(L, u / L.S);
+    else if (L.S == 1 && (L.arg.keys != nullptr || L.conv.out != nullptr))
         w4_after_unit(L, u);
 }
 
@@ -672,8 +723,12 @@ __global__ __launch_bounds__(kBlock) void pack_s4_kernel(const uint16_t *__restr
 template <int R, int B, bool NT, int MODE, bool TAIL>
 hipError_t launch_one(const W4Lin &L, hipStream_t s) {
     const int units = L.n_tiles * L.S;
-    hipLaunchKernelGGL((w4_gemv_kernel<R, B, NT, MODE, TAIL>), dim3(units), dim3(kBlock), w4_lds_bytes(L, MODE), s,
-                       L);
+    if (L.S > 1 && L.fuse)
+        hipLaunchKernelGGL((w4_gemv_kernel<R, B, NT, MODE, TAIL, true>), dim3(units), dim3(kBlock),
+                           w4_lds_bytes(L, MODE), s, L);
+    else
+        hipLaunchKernelGGL((w4_gemv_kernel<R, B, NT, MODE, TAIL, false>), dim3(units), dim3(kBlock),
+                           w4_lds_bytes(L, MODE), s, L);
     return hipGetLastError();
 }
 

@@ -182,9 +182,13 @@ struct W4Lin {
     int32_t kbs;           // k-blocks per slice, a multiple of 4 when S > 1
     int32_t tile_rtiles;   // 16-row tiles per work unit
     int32_t n_tiles;       // ceil(n_rtiles / tile_rtiles)
-    ArgOut arg;            // optional greedy token of each output row (S = 1: the units; S > 1: the reduce)
+    ArgOut arg;            // optional greedy token of each output row (where y is final)
     ConvOut conv;          // optional causal-conv1d step over y (M = 1; where y is final)
     uint16_t *y16;         // optional fp16 copy of y [M][N] (where y is final)
+    uint32_t *ctr;         // S > 1 and fuse: [n_tiles] arrival counters, zero between launches
+    int32_t fuse;          // S > 1: 0 = a reduce kernel sums the partials; 1 = the last unit of each
+                           // row tile does (partials written through at agent scope)
+    int32_t pad;
 };
 
 // One work unit of a grouped launch: linear `lin`, row tile `tile`, k-slice `s`.
