@@ -43,7 +43,10 @@ def _check(Wq, sw, x, splits=0, what="", dirty_ws=False):
     assert_within(host(y), y_ref, A, what)
 
 
-@pytest.mark.parametrize("N,K", [(1, 16), (17, 256), (100, 640), (1000, 2064), (14336, 4096), (4096, 14336)])
+# 8208..16384-wide rows (513..1024 code vectors) take the kernel that loads
+# the row ahead of the weights; the others the late order
+@pytest.mark.parametrize("N,K", [(1, 16), (17, 256), (100, 640), (1000, 2064), (14336, 4096), (4096, 14336),
+                                 (77, 8208), (300, 16384), (5, 9216)])
 def test_shapes(N, K):
     say(f"w8a8 dyn {N}x{K}")
     _check(*_case(N, K), what=f"{N}x{K}")
@@ -57,6 +60,8 @@ def test_splits(S, dirty):
     workspace (partials and scale slots full of NaN bits change nothing)."""
     say(f"w8a8 dyn splits={S} dirty={dirty}")
     _check(*_case(300, 7168, workload=141), splits=S, what=f"S={S}", dirty_ws=dirty)
+    # a row the early-order kernel holds, cut into S slices
+    _check(*_case(130, 12288, workload=142), splits=S, what=f"12288 S={S}", dirty_ws=dirty)
 
 
 def test_ties_to_even_and_clamp():

@@ -219,7 +219,7 @@ __device__ __forceinline__ void store_row(const DenseLin &L, int s, int64_t row,
 
 // One work unit: rows of row tile `tile` over k slice s.  Returns the
 // activation scale of the dynamically quantised kind (0 for the others).
-template <int KIND, int R, int CH, bool NT, bool TAIL, bool FUSED = false>
+template <int KIND, int R, int CH, bool NT, bool TAIL, bool FUSED = false, bool DYNEARLY = false>
 __device__ __forceinline__ float dense_unit(const DenseLin &L, int tile, int s, u32x4 *xs) {
     using Ops = DenseOps<KIND>;
     using Acc = typename Ops::Acc;
@@ -313,6 +313,79 @@ __device__ __forceinline__ float dense_unit(const DenseLin &L, int tile, int s, 
     };
     u32x4 bufA[R][CH], bufB[R][CH];
 
+    // The early order for fp16 activations quantised in the kernel
+    // (DYNEARLY: a kernel of its own, for rows of 513..1024 code vectors,
+    // which every thread holds 3 or 4 of): the row goes out first (every
+    // thread loads a clamped, in-bounds index, so the loads carry no branch
+    // and the wait for them does not include the weight loads behind them),
+    // then both weight steps; the maximum, the scale and the codes are
+    // computed while the weights are in flight.  Holding the row and both
+    // steps costs registers (87 against 70), so shorter rows keep the late
+    // order, in the other kernel: there it measured faster (int8 14336 x
+    // 4096: 11.8 against 12.8 us; 4096 x 14336: 13.1 against 13.9 us).
+    constexpr int kDynHold = 4;
+    if (DYNEARLY) {
+        u32x4 h[kDynHold][2];
+#pragma unroll
+        for (int j = 0; j < kDynHold; ++j) {
+            const int i = min(tid + j * kBlock, L.kvec - 1);  // a repeat does not change the maximum
+            h[j][0] = *glob(L.x + 2 * i);
+            h[j][1] = *glob(L.x + 2 * i + 1);
+        }
+        int gb = 0, cb = 0;
+        next(gb, cb);
+        // both steps always go out (a wave with fewer steps loads a row it
+        // owns, or the tile's last row, again): with no branch around them
+        // the waits for x below count exactly the weight loads behind it
+        load_step(bufA, 0, 0);
+        load_step(bufB, nsteps > 1 ? gb : 0, nsteps > 1 ? cb : 0);
+        __builtin_amdgcn_sched_barrier(0);  // every load is out before the maximum waits for x
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kDynHold; ++j)
+            amax = absmax8(h[j][1], absmax8(h[j][0], amax));
+        sx = block_max_f32(amax) / 127.0f;
+        const float rsx = 1.0f / sx;
+        const bool write_codes = L.xq_out != nullptr && tile == 0;
+        for (int i = nv + tid; i < nchunk * CHUNK; i += kBlock)
+            xs[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < kDynHold; ++j) {
+            const int i = tid + j * kBlock;
+            if (i >= kv0 && i < kv0 + nv) {
+                const u32x4 q = quantize16(h[j][0], h[j][1], sx, rsx);
+                xs[i - kv0] = q;
+                if (write_codes)
+                    *glob(reinterpret_cast<u32x4 *>(L.xq_out) + i) = q;
+            }
+        }
+        if (tile == 0 && s == 0 && tid == 0) {
+            if (L.sx_out != nullptr)
+                *glob(L.sx_out) = sx;
+            if (L.sx_part != nullptr)
+                *glob(L.sx_part) = sx;
+        }
+        __syncthreads();
+        // a buffer is refilled with the step after next once it is consumed
+        for (int st = 0; st < nsteps; st += 2) {
+            consume(bufA, ga, ca);
+            if (st + 2 < nsteps) {
+                next(ga, ca);
+                next(ga, ca);
+                load_step(bufA, ga, ca);
+            }
+            if (st + 1 >= nsteps)
+                break;
+            consume(bufB, gb, cb);
+            if (st + 3 < nsteps) {
+                next(gb, cb);
+                next(gb, cb);
+                load_step(bufB, gb, cb);
+            }
+        }
+        return sx;
+    }
+
     if (kEarly && nchunk >= 2) {
         constexpr int kXHold = 4;  // activation vectors per thread loaded ahead
         const u32x4 *xg = L.x + kv0;
@@ -399,6 +472,8 @@ __device__ __forceinline__ float dense_unit(const DenseLin &L, int tile, int s, 
                     put(i, quantize16(h[j][0], h[j][1], sx, rsx));
             }
         } else {
+            // a longer row: the scale from one pass over x, then the codes of
+            // this slice from a second
             sx = dyn_scale(L.x, (int64_t)L.kvec * 2);
             const float rsx = 1.0f / sx;
             for (int i = kv0 + tid; i < kv0 + nv; i += kBlock)
@@ -503,11 +578,11 @@ __device__ __forceinline__ void dense_last_arriver(const DenseLin &L, int tile, 
 // FUSED (split linears whose last unit per row tile sums the partials) is
 // a kernel of its own: the arrival code costs registers, and fewer resident
 // waves make the plain kernel slower (82 against 71.5 us on the lm_head).
-template <int KIND, int R, int CH, bool NT, bool TAIL, bool FUSED>
+template <int KIND, int R, int CH, bool NT, bool TAIL, bool FUSED, bool DYNEARLY = false>
 __global__ __launch_bounds__(kBlock) void dense_gemv_kernel(DenseLin L) {
     extern __shared__ u32x4 xs_dyn[];
     const int u = blockIdx.x;
-    const float sx = dense_unit<KIND, R, CH, NT, TAIL, FUSED>(L, u / L.S, u % L.S, xs_dyn);
+    const float sx = dense_unit<KIND, R, CH, NT, TAIL, FUSED, DYNEARLY>(L, u / L.S, u % L.S, xs_dyn);
     if constexpr (FUSED) {
         dense_last_arriver<KIND>(L, u / L.S, sx);
     } else if (L.S == 1 && (L.arg.keys != nullptr || L.conv.out != nullptr)) {
@@ -901,7 +976,19 @@ template <int KIND, int R, int CH, bool NT, bool TAIL>
 hipError_t launch_single(const DenseLin &L, hipStream_t s) {
     const int units = L.n_tiles * L.S;
     const int lds = dense_lds_bytes(L, CH);
-    if (L.S > 1 && L.fuse)
+    const bool fused = L.S > 1 && L.fuse;
+    if constexpr (KIND == kW8A8D) {
+        if (L.kvec > 2 * kBlock && L.kvec <= 4 * kBlock) {
+            if (fused)
+                hipLaunchKernelGGL((dense_gemv_kernel<KIND, R, CH, NT, TAIL, true, true>), dim3(units), dim3(kBlock),
+                                   lds, s, L);
+            else
+                hipLaunchKernelGGL((dense_gemv_kernel<KIND, R, CH, NT, TAIL, false, true>), dim3(units),
+                                   dim3(kBlock), lds, s, L);
+            return hipGetLastError();
+        }
+    }
+    if (fused)
         hipLaunchKernelGGL((dense_gemv_kernel<KIND, R, CH, NT, TAIL, true>), dim3(units), dim3(kBlock), lds, s, L);
     else
         hipLaunchKernelGGL((dense_gemv_kernel<KIND, R, CH, NT, TAIL, false>), dim3(units), dim3(kBlock), lds, s, L);
