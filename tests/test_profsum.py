@@ -75,7 +75,7 @@ def test_shader_counter_summary(tmp_path):
                                 "Counter_Value": f_ * v / 2, "Start_Timestamp": 1000, "End_Timestamp": 11000,
                                 "VGPR_Count": 152, "Accum_VGPR_Count": 0, "SGPR_Count": 96, "LDS_Block_Size": 25088})
     man = {"configs": [{"label": "c5_M4", "workload": "W4A16 step, M = 4", "kernels": ["w4_grouped_kernel<2, 4"],
-                        "steps": 2, "algorithmic_bytes": 1}]}
+                        "steps": 2, "algorithmic_bytes": 10 << 20}]}
     with open(tmp_path / "man.json", "w") as f:
         json.dump(man, f)
     recs = profsum.sq_per_config(str(tmp_path / "sq.csv"), man["configs"])
@@ -85,8 +85,9 @@ def test_shader_counter_summary(tmp_path):
     assert abs(d["valu_busy"] - 0.4) < 1e-9 and abs(d["mfma_busy"] - 0.1) < 1e-9
     assert abs(d["valu_per_wave"] - 50.0) < 1e-9 and abs(d["mfma_per_wave"] - 3.0) < 1e-9
     assert abs(d["grbm_per_ns"] - 6.4) < 1e-9          # 64000 cycles over 10000 ns
+    assert abs(d["valu_per_kib"] - 50000 / 10240) < 1e-9 and abs(d["mfma_per_kib"] - 3000 / 10240) < 1e-9
     profsum.main(["--sq", str(tmp_path / "sq.csv"), "--manifest", str(tmp_path / "man.json"),
                   "--out", str(tmp_path / "out.md"), "--command", "rocprofv3 ..."])
     text = (tmp_path / "out.md").read_text()
-    assert "| W4A16 step, M = 4 | `w4_grouped_kernel<2, 4` | 2 | 10.0 | 6.4 | 152/0/96 | 25088 | 2.50 | 40% | 10% " \
-           "| 50 | 3 | 7 |" in text
+    assert "| W4A16 step, M = 4 | `w4_grouped_kernel<2, 4` | 2 | 10.0 | 6.4 | 152/0/96 | 2.50 | 40% | 10% " \
+           "| 4.88 | 0.293 | 50 | 7 |" in text

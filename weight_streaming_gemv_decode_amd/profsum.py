@@ -153,8 +153,9 @@ def sq_per_config(path: str, manifest: List[dict]) -> List[dict]:
         for k, ds in got.items():
             avg = {c: sum(d["c"].get(c, 0.0) for d in ds) / len(ds) for c in SQ_COUNTERS}
             out.append({"label": e["label"], "workload": e["workload"], "kernel": k, "dispatches": len(ds),
+                        "per_step": len(ds) / e["steps"], "algorithmic_bytes": e["algorithmic_bytes"],
                         "ns": sum(d["ns"] for d in ds) / len(ds), "vgpr": ds[0]["vgpr"], "agpr": ds[0]["agpr"],
-                        "sgpr": ds[0]["sgpr"], "lds": ds[0]["lds"], **avg})
+                        "sgpr": ds[0]["sgpr"], **avg})
     return out
 
 
@@ -165,7 +166,10 @@ def sq_derived(r: dict) -> dict:
     and SQ_ACTIVE_INST_VALU count quad-cycles summed over all SIMDs;
     SQ_VALU_MFMA_BUSY_CYCLES counts cycles."""
     g = r["GRBM_GUI_ACTIVE"] / XCDS
+    kib = r["algorithmic_bytes"] / 1024.0 / r["per_step"] if r["per_step"] else 0.0  # per dispatch
     return {"grbm_per_ns": r["GRBM_GUI_ACTIVE"] / r["ns"] if r["ns"] else 0.0,
+            "valu_per_kib": r["SQ_INSTS_VALU"] / kib if kib else 0.0,
+            "mfma_per_kib": r["SQ_INSTS_MFMA"] / kib if kib else 0.0,
             "waves_per_simd": 4 * r["SQ_WAVE_CYCLES"] / (g * SIMDS) if g else 0.0,
             "valu_busy": 4 * r["SQ_ACTIVE_INST_VALU"] / (g * SIMDS) if g else 0.0,
             "mfma_busy": r["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * SIMDS) if g else 0.0,
@@ -182,16 +186,18 @@ def render_sq(recs: List[dict], commands: List[str], notes: List[str] = ()) -> s
              "Derived: one compute die was busy g = GRBM_GUI_ACTIVE / 8 cycles (GRBM_GUI_ACTIVE adds the 8 dies; "
              "the `GRBM/ns` column, about 20 = 8 dies at ~2.5 GHz, checks it against the dispatch timestamps); "
              "waves/SIMD = 4 SQ_WAVE_CYCLES / (g x 1024 SIMDs) (quad-cycles), VALU busy = 4 SQ_ACTIVE_INST_VALU "
-             "/ (g x 1024), MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (g x 1024). VGPR, AGPR and SGPR counts and "
-             "LDS bytes per workgroup are as the profiler reports them.", "",
-             "| Config | Kernel | Dispatches | us | GRBM/ns | VGPR/AGPR/SGPR | LDS B | waves/SIMD | VALU busy "
-             "| MFMA busy | VALU/wave | MFMA/wave | LDS/wave |", "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "/ (g x 1024), MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (g x 1024); VALU/KiB and MFMA/KiB are wave "
+             "instructions per KiB of the config's algorithmic bytes. VGPR, AGPR and SGPR are the counts the "
+             "profiler reports (in its allocation units, not the compiler's register numbers).", "",
+             "| Config | Kernel | Dispatches | us | GRBM/ns | VGPR/AGPR/SGPR | waves/SIMD | VALU busy "
+             "| MFMA busy | VALU/KiB | MFMA/KiB | VALU/wave | LDS/wave |", "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in recs:
         d = sq_derived(r)
         lines.append(f"| {r['workload']} | `{r['kernel']}` | {r['dispatches']} | {r['ns'] / 1e3:.1f} "
-                     f"| {d['grbm_per_ns']:.1f} | {r['vgpr']}/{r['agpr']}/{r['sgpr']} | {r['lds']} "
+                     f"| {d['grbm_per_ns']:.1f} | {r['vgpr']}/{r['agpr']}/{r['sgpr']} "
                      f"| {d['waves_per_simd']:.2f} | {100 * d['valu_busy']:.0f}% | {100 * d['mfma_busy']:.0f}% "
-                     f"| {d['valu_per_wave']:.0f} | {d['mfma_per_wave']:.0f} | {d['lds_per_wave']:.0f} |")
+                     f"| {d['valu_per_kib']:.2f} | {d['mfma_per_kib']:.3f} | {d['valu_per_wave']:.0f} "
+                     f"| {d['lds_per_wave']:.0f} |")
     lines.append("")
     lines += [n + "\n" for n in notes]
     return "\n".join(lines) + "\n"
