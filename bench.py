@@ -512,7 +512,7 @@ def main():
                 "single_launch_median_us": s["median_ms"] * 1e3}
         res["S=2"]["note"] = "split-K; the last workgroup of each row tile adds the two partials (no reduce kernel)"
         # ablation: the same split summed by a second, reduce kernel (same bits)
-        wsgemv.tune_set("dense_fuse", 0)
+        wsgemv.tune_set("split_fuse", 0)
         try:
             ws = wsgemv.workspace(wsgemv.F16, 1, lm.N, lm.K, 2, dev)
             y = torch.empty(lm.N, device=dev)
@@ -521,7 +521,7 @@ def main():
                 fn(i)
             t = region_time(torch, fn, 100, stream)
         finally:
-            wsgemv.tune_set("dense_fuse", -1)
+            wsgemv.tune_set("split_fuse", -1)
         res["S=2 reduce kernel"] = {"us": t * 1e3, "GBps": b / (t * 1e-3) / 1e9,
                                     "pct_peak": 100 * b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
         # the same lm_head with the greedy token fused into the kernel that writes the logits

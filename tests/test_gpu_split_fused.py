@@ -34,10 +34,10 @@ class _Reduce:
     """The reduce-kernel path for the duration of a with-block."""
 
     def __enter__(self):
-        wsgemv.tune_set("dense_fuse", 0)
+        wsgemv.tune_set("split_fuse", 0)
 
     def __exit__(self, *exc):
-        wsgemv.tune_set("dense_fuse", -1)
+        wsgemv.tune_set("split_fuse", -1)
 
 
 def _counters_zero(ws, kind, N, S, what):

@@ -65,7 +65,7 @@ struct Tune {
     int64_t chain_spin_limit = -1;    // persistent step: polls before a wait gives up
     int64_t chain_test_stale = -1;    // 1: consumers wait for a tag no producer writes (tests the give-up path)
     int64_t chain_sleep = -1;         // s_sleep(1) calls between polls of a waiting workgroup
-    int64_t dense_fuse = -1;          // split-K sum: 0 reduce kernel, 1 last unit of each row tile
+    int64_t split_fuse = -1;          // split-K sum: 0 reduce kernel, 1 last unit of each row tile
 };
 Tune g_tune;
 
@@ -91,12 +91,13 @@ struct DensePlan {
     int fuse;       // S > 1: how the partials are summed (DenseLin::fuse)
 };
 
-// How a split linear sums its partials (DenseLin::fuse): by default the last
+// How a split linear of any kind sums its partials (DenseLin::fuse,
+// W4Lin::fuse): by default the last
 // unit of each row tile does.  Measured on MI355X against the reduce kernel
 // (bit-identical results): 6.7-7.1 against 9.3-9.7 us on fp16 linears of
 // 128-896 rows that the launch table splits, 7.7-8.7 against 10.1 us on the
 // int8 ones, and 76.9 against 77.0 us on the 248320x1024 lm_head at S = 2.
-int dense_fuse_mode() { return g_tune.dense_fuse >= 0 ? (int)std::min<int64_t>(g_tune.dense_fuse, 1) : 1; }
+int split_fuse_mode() { return g_tune.split_fuse >= 0 ? (int)std::min<int64_t>(g_tune.split_fuse, 1) : 1; }
 
 int elem_per_vec(int kind) { return kind == kF16 ? 8 : 16; }
 
@@ -152,7 +153,7 @@ DensePlan plan_dense(int kind, int64_t N, int64_t K, int splits, bool token = fa
     if (g_tune.dense_rows > 0)
         tr = (int)g_tune.dense_rows;
     p.tile_rows = tr;
-    p.fuse = p.S > 1 ? dense_fuse_mode() : 0;
+    p.fuse = p.S > 1 ? split_fuse_mode() : 0;
     return p;
 }
 
@@ -402,7 +403,7 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K, int splits) {
     if (g_tune.w4_tiles > 0)
         tt = g_tune.w4_tiles;
     p.tile_rtiles = (int)tt;
-    p.fuse = p.S > 1 ? dense_fuse_mode() : 0;
+    p.fuse = p.S > 1 ? split_fuse_mode() : 0;
     if (g_tune.w4_R > 0)
         p.cfg.R = (int)g_tune.w4_R;
     if (g_tune.w4_B > 0)
@@ -891,7 +892,7 @@ wsg_status wsg_tune_set(const char *key, int64_t value) {
                  {"chain_spin_limit", &g_tune.chain_spin_limit},
                  {"chain_test_stale", &g_tune.chain_test_stale},
                  {"chain_sleep", &g_tune.chain_sleep},
-                 {"dense_fuse", &g_tune.dense_fuse}};
+                 {"split_fuse", &g_tune.split_fuse}};
     for (auto &t : table) {
         if (std::strcmp(key, t.name) == 0) {
             *t.slot = value < 0 ? -1 : value;
