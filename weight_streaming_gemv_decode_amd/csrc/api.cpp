@@ -92,11 +92,11 @@ struct DensePlan {
 };
 
 // How a split linear of any kind sums its partials (DenseLin::fuse,
-// W4Lin::fuse): by default the last
-// unit of each row tile does.  Measured on MI355X against the reduce kernel
-// (bit-identical results): 6.7-7.1 against 9.3-9.7 us on fp16 linears of
-// 128-896 rows that the launch table splits, 7.7-8.7 against 10.1 us on the
-// int8 ones, and 76.9 against 77.0 us on the 248320x1024 lm_head at S = 2.
+// W4Lin::fuse): by default the last unit of each row tile does.  Measured on
+// MI355X against the reduce kernel (bit-identical results): 6.7-7.1 against
+// 9.3-9.7 us on fp16 linears of 128-896 rows that the launch table splits,
+// 7.7-8.7 against 10.1 us on the int8 ones, and 76.9 against 77.0 us on the
+// 248320x1024 lm_head at S = 2.
 int split_fuse_mode() { return g_tune.split_fuse >= 0 ? (int)std::min<int64_t>(g_tune.split_fuse, 1) : 1; }
 
 int elem_per_vec(int kind) { return kind == kF16 ? 8 : 16; }
