@@ -91,3 +91,34 @@ def test_shader_counter_summary(tmp_path):
     text = (tmp_path / "out.md").read_text()
     assert "| W4A16 step, M = 4 | `w4_grouped_kernel<2, 4` | 2 | 10.0 | 6.4 | 152/0/96 | 2.50 | 40% | 10% " \
            "| 4.88 | 0.293 | 50 | 7 |" in text
+
+
+def test_memory_unit_pass(tmp_path):
+    """The memory-unit pass joins the shader pass by (config, kernel): busy
+    fractions over the same die-busy cycles, from hand-computed values."""
+    g = 10000.0
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp",
+            "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size"]
+
+    def write(path, values):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, cols)
+            w.writeheader()
+            for c, v in values.items():
+                w.writerow({"Dispatch_Id": 1, "Kernel_Name": "dense_grouped_kernel<0, 2, 2, true, false>",
+                            "Counter_Name": c, "Counter_Value": v, "Start_Timestamp": 0, "End_Timestamp": 4000,
+                            "VGPR_Count": 28, "Accum_VGPR_Count": 0, "SGPR_Count": 96, "LDS_Block_Size": 512})
+    write(tmp_path / "sq.csv", {c: 8 * g if c == "GRBM_GUI_ACTIVE" else 1000.0 for c in profsum.SQ_COUNTERS})
+    write(tmp_path / "mem.csv", {"TA_BUSY_avr": 0.7 * g, "TCP_TCP_TA_DATA_STALL_CYCLES_max": 0.25 * g,
+                                 "TCC_BUSY_avr": 0.5 * g, "GRBM_GUI_ACTIVE": 8 * g})
+    man = {"configs": [{"label": "c3", "workload": "step", "kernels": ["dense_grouped_kernel<0, 2, 2"], "steps": 1,
+                        "algorithmic_bytes": 1 << 20}]}
+    with open(tmp_path / "man.json", "w") as f:
+        json.dump(man, f)
+    mem = profsum.sq_per_config(str(tmp_path / "mem.csv"), man["configs"], profsum.MEM_COUNTERS)
+    d = profsum.mem_derived(mem[0])
+    assert abs(d["ta_busy"] - 0.7) < 1e-9 and abs(d["tcp_stall"] - 0.25) < 1e-9 and abs(d["tcc_busy"] - 0.5) < 1e-9
+    profsum.main(["--sq", str(tmp_path / "sq.csv"), "--mem", str(tmp_path / "mem.csv"), "--manifest",
+                  str(tmp_path / "man.json"), "--out", str(tmp_path / "out.md")])
+    text = (tmp_path / "out.md").read_text()
+    assert "| 70% | 25% | 50% |" in text and "TA busy | TCP stalled on TA | TCC busy |" in text

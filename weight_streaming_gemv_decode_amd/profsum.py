@@ -114,6 +114,10 @@ def per_config(path: str, counter: str, manifest: List[dict]) -> Dict[str, dict]
 # One counter pass on MI355X: at most 8 SQ_ and 2 GRBM_ counters.
 SQ_COUNTERS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_MFMA",
                "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
+# A second pass for the memory units: the vector-memory address unit's busy
+# cycles (average over its instances), the L1 cache's cycles stalled on it
+# (worst instance), and the L2's busy cycles (average over its channels).
+MEM_COUNTERS = ["TA_BUSY_avr", "TCP_TCP_TA_DATA_STALL_CYCLES_max", "TCC_BUSY_avr", "GRBM_GUI_ACTIVE"]
 XCDS, SIMDS = 8, 1024   # MI355X: 8 compute dies, 256 CUs of 4 SIMDs
 
 
@@ -131,7 +135,7 @@ def _sq_dispatches(path: str) -> List[dict]:
     return [rows[d] for d in sorted(rows)]
 
 
-def sq_per_config(path: str, manifest: List[dict]) -> List[dict]:
+def sq_per_config(path: str, manifest: List[dict], counters: List[str] = SQ_COUNTERS) -> List[dict]:
     """Average counters per dispatch of every (config, kernel), dispatches
     assigned to configs in launch order as in per_config."""
     disp = _sq_dispatches(path)
@@ -151,7 +155,7 @@ def sq_per_config(path: str, manifest: List[dict]) -> List[dict]:
         if n < need:
             raise ValueError(f"{e['label']}: found {n} of {need} dispatches of {kernels} in {path}")
         for k, ds in got.items():
-            avg = {c: sum(d["c"].get(c, 0.0) for d in ds) / len(ds) for c in SQ_COUNTERS}
+            avg = {c: sum(d["c"].get(c, 0.0) for d in ds) / len(ds) for c in counters}
             out.append({"label": e["label"], "workload": e["workload"], "kernel": k, "dispatches": len(ds),
                         "per_step": len(ds) / e["steps"], "algorithmic_bytes": e["algorithmic_bytes"],
                         "ns": sum(d["ns"] for d in ds) / len(ds), "vgpr": ds[0]["vgpr"], "agpr": ds[0]["agpr"],
@@ -178,7 +182,15 @@ def sq_derived(r: dict) -> dict:
             "lds_per_wave": r["SQ_INSTS_LDS"] / r["SQ_WAVES"] if r["SQ_WAVES"] else 0.0}
 
 
-def render_sq(recs: List[dict], commands: List[str], notes: List[str] = ()) -> str:
+def mem_derived(r: dict) -> dict:
+    """Busy fractions of the memory units over the same die-busy cycles g."""
+    g = r["GRBM_GUI_ACTIVE"] / XCDS
+    return {"ta_busy": r["TA_BUSY_avr"] / g if g else 0.0,
+            "tcp_stall": r["TCP_TCP_TA_DATA_STALL_CYCLES_max"] / g if g else 0.0,
+            "tcc_busy": r["TCC_BUSY_avr"] / g if g else 0.0}
+
+
+def render_sq(recs: List[dict], commands: List[str], notes: List[str] = (), mem: Optional[List[dict]] = None) -> str:
     lines = ["# Shader counters per config and kernel", "",
              "One counter pass on one MI355X over a `bench.py --counter-pass` run (every config a few steps, "
              f"in launch order), counters {', '.join(SQ_COUNTERS)}. Commands (repository root as `$REPO`, run "
@@ -188,16 +200,30 @@ def render_sq(recs: List[dict], commands: List[str], notes: List[str] = ()) -> s
              "waves/SIMD = 4 SQ_WAVE_CYCLES / (g x 1024 SIMDs) (quad-cycles), VALU busy = 4 SQ_ACTIVE_INST_VALU "
              "/ (g x 1024), MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (g x 1024); VALU/KiB and MFMA/KiB are wave "
              "instructions per KiB of the config's algorithmic bytes. VGPR, AGPR and SGPR are the counts the "
-             "profiler reports (in its allocation units, not the compiler's register numbers).", "",
+             "profiler reports (in its allocation units, not the compiler's register numbers)." +
+             (f" The memory-unit columns come from a second pass over the same run ({', '.join(MEM_COUNTERS)}), "
+              "each over the same g: the vector-memory address unit (TA) busy, averaged over its instances; the "
+              "L1 cache (TCP) stalled on TA data, worst instance; the L2 (TCC) busy, averaged over its channels."
+              if mem else ""), "",
              "| Config | Kernel | Dispatches | us | GRBM/ns | VGPR/AGPR/SGPR | waves/SIMD | VALU busy "
-             "| MFMA busy | VALU/KiB | MFMA/KiB | VALU/wave | LDS/wave |", "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "| MFMA busy | VALU/KiB | MFMA/KiB | VALU/wave | LDS/wave |" + (" TA busy | TCP stalled on TA | TCC busy |" if mem else ""),
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|" + ("---|---|---|" if mem else "")]
+    mem_by = {(m["label"], m["kernel"]): m for m in (mem or [])}
     for r in recs:
         d = sq_derived(r)
+        m = mem_by.get((r["label"], r["kernel"]))
+        extra = ""
+        if mem:
+            if m:
+                md = mem_derived(m)
+                extra = f" {100 * md['ta_busy']:.0f}% | {100 * md['tcp_stall']:.0f}% | {100 * md['tcc_busy']:.0f}% |"
+            else:
+                extra = " — | — | — |"
         lines.append(f"| {r['workload']} | `{r['kernel']}` | {r['dispatches']} | {r['ns'] / 1e3:.1f} "
                      f"| {d['grbm_per_ns']:.1f} | {r['vgpr']}/{r['agpr']}/{r['sgpr']} "
                      f"| {d['waves_per_simd']:.2f} | {100 * d['valu_busy']:.0f}% | {100 * d['mfma_busy']:.0f}% "
                      f"| {d['valu_per_kib']:.2f} | {d['mfma_per_kib']:.3f} | {d['valu_per_wave']:.0f} "
-                     f"| {d['lds_per_wave']:.0f} |")
+                     f"| {d['lds_per_wave']:.0f} |" + extra)
     lines.append("")
     lines += [n + "\n" for n in notes]
     return "\n".join(lines) + "\n"
@@ -259,6 +285,7 @@ def main(argv=None) -> None:
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--sq", help="a shader-counter pass (SQ_COUNTERS) instead of --fetch/--write")
+    ap.add_argument("--mem", help="with --sq: a memory-unit pass (MEM_COUNTERS) of the same run")
     ap.add_argument("--manifest", required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--command", action="append", default=[], help="a command line that produced the passes")
@@ -266,9 +293,11 @@ def main(argv=None) -> None:
     a = ap.parse_args(argv)
     if a.sq:
         with open(a.manifest) as f:
-            recs = sq_per_config(a.sq, json.load(f)["configs"])
+            entries = json.load(f)["configs"]
+        recs = sq_per_config(a.sq, entries)
+        mem = sq_per_config(a.mem, entries, MEM_COUNTERS) if a.mem else None
         with open(a.out, "w") as f:
-            f.write(render_sq(recs, a.command, a.note))
+            f.write(render_sq(recs, a.command, a.note, mem))
         for r in recs:
             d = sq_derived(r)
             print(f"{r['label']:24s} {r['kernel']:34s} waves/SIMD {d['waves_per_simd']:.2f} "
