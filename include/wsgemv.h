@@ -247,8 +247,9 @@ wsg_status wsg_topk_f32(const float *y, int64_t N, int32_t k, int32_t *idx, floa
 
 /*
  * gemv_f16_argmax: gemv_f16 (y = W . x, fp32 logits, written in full) with
- * the greedy token over y fused into the kernel that writes y (the k-split
- * reduce when splits > 1).  This is the lm_head of a decode step.
+ * the greedy token over y fused into the kernel that writes y (with
+ * splits > 1, into the last workgroup of each row tile, which adds the
+ * partials).  This is the lm_head of a decode step.
  *   N = 1..INT32_MAX; token int32 [1]; token_logit optional fp32 [1]
  *   ws           wsg_workspace_bytes(WSG_F16 | WSG_WITH_ARGMAX, 1, N, K,
  *                splits) bytes (the key array, then the split-K partials

@@ -168,9 +168,9 @@ void set_part(DenseLin &L, int kind, void *part, uint32_t *ctr) {
 }
 
 // Split-K workspace: S partial rows, and for fp16 activations quantised in
-// the kernel one more float, the scale, which the reduce reads; a fused
-// linear's arrival counters follow (zero before the first call, and every
-// call leaves them zero).
+// the kernel one more float, the scale (which the reduce kernel of the
+// unfused path reads); a fused linear's arrival counters follow (zero before
+// the first call, and every call leaves them zero).
 size_t dense_part_bytes(int kind, const DensePlan &p, int64_t N) {
     return p.S > 1 ? (size_t)p.S * (size_t)N * 4 + (kind == kW8A8D ? 256 : 0) : 0;
 }

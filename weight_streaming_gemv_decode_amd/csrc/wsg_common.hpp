@@ -160,7 +160,7 @@ struct DenseLin {
     uint16_t *y16;         // optional fp16 copy of y [N] (same place as y is final)
     int8_t *xq_out;        // kW8A8D: optional int8 codes [K] (written by the first row tile)
     float *sx_out;         // kW8A8D: optional activation scale [1]
-    float *sx_part;        // kW8A8D with S > 1: the activation scale, after the partials (for the reduce)
+    float *sx_part;        // kW8A8D with S > 1: the activation scale, after the partials (for the reduce kernel)
     uint32_t *ctr;         // fuse != 0: [n_tiles] arrival counters, zero between launches
 };
 
