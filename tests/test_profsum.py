@@ -122,3 +122,16 @@ def test_memory_unit_pass(tmp_path):
                   str(tmp_path / "man.json"), "--out", str(tmp_path / "out.md")])
     text = (tmp_path / "out.md").read_text()
     assert "| 70% | 25% | 50% |" in text and "TA busy | TCP stalled on TA | TCC busy |" in text
+
+
+def test_source_hash_ignores_comments(tmp_path, monkeypatch):
+    """The traffic records stay attached across comment edits, and detach on
+    a code change."""
+    src = tmp_path / "k.hip"
+    src.write_text("int f(int x) { return x + 1; }  // one\n")
+    monkeypatch.setattr(profsum, "SOURCES", ["k.hip"])
+    h0 = profsum.source_sha256(str(tmp_path))
+    src.write_text("/* a comment\n spanning lines */ int f(int x) {\n    return x + 1;   // two\n}\n")
+    assert profsum.source_sha256(str(tmp_path)) == h0
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert profsum.source_sha256(str(tmp_path)) != h0

@@ -32,6 +32,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 from typing import Dict, List, Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,11 +45,20 @@ COPY_KERNEL = "AUnaryFunctor"   # torch's elementwise multiply, the calibration 
 JSON_TAG = "traffic-json: "
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed, so that
+    a change of comments alone keeps the hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_sha256(repo: str = REPO) -> str:
+    """Hash of the code (not the comments) of every measured kernel source."""
     h = hashlib.sha256()
     for s in SOURCES:
-        with open(os.path.join(repo, s), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(repo, s), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
@@ -273,7 +283,8 @@ def render(recs: List[dict], cal: dict, commands: List[str], notes: List[str] = 
                      f"| {r['algorithmic_bytes']:,} | {r['ratio_to_algorithmic']:.4f} |")
     lines += ["", "Algorithmic bytes are weights + scales + activations + outputs that a step needs; split-K "
               "partials and re-read activations are excess and show up above 1.0. `source_sha256` hashes the "
-              "measured kernel sources; bench.py attaches a record to its results only while they are unchanged.",
+              "code of the measured kernel sources (comments and whitespace left out); bench.py attaches a record "
+              "to its results only while that code is unchanged.",
               ""]
     lines += [n + "\n" for n in notes]
     lines += [JSON_TAG + json.dumps(r) for r in recs]
