@@ -1,7 +1,6 @@
 """bench.py's contract on the CPU: more than one GPU is refused with a JSON
 message before any GPU work, and the counter-measured traffic of the grouped
 kernel is reported only while the kernel sources hash to the ones measured."""
-import hashlib
 import json
 import os
 import subprocess
@@ -31,11 +30,9 @@ def _summary(tmp_path, sha, label="c3_grouped"):
 
 def test_traffic_only_for_the_measured_sources(tmp_path):
     from weight_streaming_gemv_decode_amd import profsum
-    h = hashlib.sha256()
-    for s in profsum.SOURCES:
-        h.update(open(os.path.join(REPO, s), "rb").read())
-    assert bench.measured_traffic(_summary(tmp_path, h.hexdigest()))["bytes"] == 123
-    assert bench.measured_traffic(_summary(tmp_path, h.hexdigest(), "c1")) is None          # another config
-    assert bench.measured_traffic(_summary(tmp_path, h.hexdigest(), "c1"), "c1")["bytes"] == 123
+    h = profsum.source_sha256()   # of the sources' code (tests/test_profsum.py pins what it covers)
+    assert bench.measured_traffic(_summary(tmp_path, h))["bytes"] == 123
+    assert bench.measured_traffic(_summary(tmp_path, h, "c1")) is None          # another config
+    assert bench.measured_traffic(_summary(tmp_path, h, "c1"), "c1")["bytes"] == 123
     assert bench.measured_traffic(_summary(tmp_path, "0" * 64)) is None
     assert bench.measured_traffic(str(tmp_path / "missing.md")) is None
