@@ -318,12 +318,15 @@ __device__ __forceinline__ float dense_unit(const DenseLin &L, int tile, int s, 
     // which every thread holds 3 or 4 of): the row goes out first (every
     // thread loads a clamped, in-bounds index, so the loads carry no branch
     // and the wait for them does not include the weight loads behind them),
-    // then both weight steps; the maximum, the scale and the codes are
-    // computed while the weights are in flight.  Holding the row and both
-    // steps costs registers (87 against 70), so shorter rows keep the late
-    // order, in the other kernel: there it measured faster (int8 14336 x
-    // 4096: 11.8 against 12.8 us; 4096 x 14336: 13.1 against 13.9 us).
+    // then four weight steps (a ring of four buffers, refilled four steps
+    // ahead); the maximum, the scale and the codes are computed while the
+    // weights are in flight.  Four steps measured faster than two (4096 x
+    // 14336: 12.5-12.7 against 13.4 us) and than eight (14.6 us, 183
+    // VGPRs).  Holding the row and the steps costs registers (119 against
+    // 70), so shorter rows keep the late order, in the other kernel: there
+    // it measured faster (int8 14336 x 4096: 11.8 against 12.8 us).
     constexpr int kDynHold = 4;
+    constexpr int kDynDepth = 4;  // weight steps in flight
     if (DYNEARLY) {
         u32x4 h[kDynHold][2];
 #pragma unroll
@@ -332,13 +335,21 @@ __device__ __forceinline__ float dense_unit(const DenseLin &L, int tile, int s, 
             h[j][0] = *glob(L.x + 2 * i);
             h[j][1] = *glob(L.x + 2 * i + 1);
         }
-        int gb = 0, cb = 0;
-        next(gb, cb);
-        // both steps always go out (a wave with fewer steps loads a row it
-        // owns, or the tile's last row, again): with no branch around them
-        // the waits for x below count exactly the weight loads behind it
-        load_step(bufA, 0, 0);
-        load_step(bufB, nsteps > 1 ? gb : 0, nsteps > 1 ? cb : 0);
+        // four steps go out (a wave with fewer steps loads its first step
+        // again): with no branch around them the waits for x below count
+        // exactly the weight loads behind it
+        auto step_gc = [&](int st, int &g, int &c) {
+            const int q = st < nsteps ? st : 0;
+            g = q / nchunk;
+            c = q - g * nchunk;
+        };
+        u32x4 bufs[kDynDepth][R][CH];
+#pragma unroll
+        for (int j = 0; j < kDynDepth; ++j) {
+            int g, c;
+            step_gc(j, g, c);
+            load_step(bufs[j], g, c);
+        }
         __builtin_amdgcn_sched_barrier(0);  // every load is out before the maximum waits for x
         float amax = 0.0f;
 #pragma unroll
@@ -366,21 +377,19 @@ __device__ __forceinline__ float dense_unit(const DenseLin &L, int tile, int s, 
                 *glob(L.sx_part) = sx;
         }
         __syncthreads();
-        // a buffer is refilled with the step after next once it is consumed
-        for (int st = 0; st < nsteps; st += 2) {
-            consume(bufA, ga, ca);
-            if (st + 2 < nsteps) {
-                next(ga, ca);
-                next(ga, ca);
-                load_step(bufA, ga, ca);
-            }
-            if (st + 1 >= nsteps)
-                break;
-            consume(bufB, gb, cb);
-            if (st + 3 < nsteps) {
-                next(gb, cb);
-                next(gb, cb);
-                load_step(bufB, gb, cb);
+        // a buffer is refilled with the step kDynDepth ahead once it is consumed
+        for (int st = 0; st < nsteps; st += kDynDepth) {
+#pragma unroll
+            for (int j = 0; j < kDynDepth; ++j) {
+                if (st + j >= nsteps)
+                    break;
+                int g, c;
+                step_gc(st + j, g, c);
+                consume(bufs[j], g, c);
+                if (st + j + kDynDepth < nsteps) {
+                    step_gc(st + j + kDynDepth, g, c);
+                    load_step(bufs[j], g, c);
+                }
             }
         }
         return sx;
