@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--traffic", default=os.path.join(HERE, "profiles", "traffic_hbm_counters_per_config.md"),
                     help="profile summary holding the counter-measured per-launch HBM traffic of every config; "
                          "used only while the kernel sources still hash to the measured ones")
+    ap.add_argument("--chain-trace", default="", metavar="OUT_MD",
+                    help="trace one persistent step of the dependent C3 chain per work unit "
+                         "(wsg_decode_step_trace) and write the stage breakdown to OUT_MD, then exit")
     ap.add_argument("--counter-pass", default="", metavar="MANIFEST",
                     help="run every config a few times for a rocprofv3 counter pass (FETCH_SIZE, WRITE_SIZE), "
                          "after a copy kernel of known size, and write which launches belong to which config "
@@ -326,6 +329,42 @@ def counter_pass(args, torch, synth, wsgemv, dev, stream):
     log(f"manifest written: {args.counter_pass}")
 
 
+def chain_trace(args, torch, synth, wsgemv, profsum, dev, stream):
+    """The C3 linears as one dependent chain (each reads the leading K entries
+    of the previous linear's fp16 output, as in the chain extras), one
+    persistent launch per step: time untraced steps, trace one step per work
+    unit, and write where the stage time goes."""
+    step_in = synth.decode_step_f16(workload=3)
+    cl, names, x = [], [], torch.from_numpy(step_in[0][2]).to(dev)
+    for name, W, _ in step_in:
+        N, K = W.shape
+        y16 = torch.empty(N, dtype=torch.float16, device=dev)
+        cl.append(wsgemv.Linear(wsgemv.F16, torch.from_numpy(W).to(dev), x[:K], torch.empty(N, device=dev), N, K,
+                                y16=y16))
+        names.append(f"{name} {N}x{K}")
+        x = y16
+    pc = wsgemv.DecodeStep(cl, wsgemv.STEP_PERSISTENT, stream=stream)
+    for _ in range(5):
+        pc(stream)
+    step_us = statistics.median(region_time(torch, lambda i: pc(stream), 20, stream) for _ in range(3)) * 1e3
+    units = pc.info()[1]
+    buf = torch.zeros(4 * units, dtype=torch.int64, device=dev)
+    pc.set_trace(buf)
+    pc(stream)  # one traced step to warm up, then the one kept
+    traced_us = event_times(torch, lambda i: pc(stream), 1, stream)[0] * 1e3
+    pc.set_trace(None)
+    give_ups = pc.give_ups(stream)
+    words = [int(v) & 0xFFFFFFFFFFFFFFFF for v in buf.cpu().tolist()]
+    pc.close()
+    stats = profsum.chain_trace_stats(words)
+    cmd = f"python bench.py --chain-trace {args.chain_trace}"
+    notes = [f"Waits that gave up in the traced steps: {give_ups}."]
+    with open(args.chain_trace, "w") as f:
+        f.write(profsum.render_chain_trace(stats, names, cmd, step_us, traced_us, notes))
+    log(f"chain trace: {stats['units']} units, step {step_us:.1f} us untraced, {traced_us:.1f} us traced; "
+        f"median stage {stats['median_stage']['stage_us']:.2f} us; written {args.chain_trace}")
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -341,6 +380,11 @@ def main():
 
     if args.counter_pass:
         counter_pass(args, torch, synth, wsgemv, dev, stream)
+        return
+
+    if args.chain_trace:
+        from weight_streaming_gemv_decode_amd import profsum
+        chain_trace(args, torch, synth, wsgemv, profsum, dev, stream)
         return
 
     if args.calib_copy:

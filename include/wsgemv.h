@@ -379,6 +379,24 @@ wsg_status wsg_decode_step_info(const wsg_step *step, int32_t *launches, int64_t
 wsg_status wsg_decode_step_status(wsg_step *step, wsg_stream_t stream, uint32_t *give_ups);
 
 /*
+ * Per-unit timestamps of a WSG_STEP_PERSISTENT plan, to see where a
+ * dependent step spends its time (EdgeFM summary, section 2C: the step as
+ * one executable unit per decode iteration; the time between its linears is
+ * what remains to account for).  `trace`: a device buffer of at least
+ * 4 * units 64-bit words (units from wsg_decode_step_info), 8-byte aligned,
+ * owned by the caller and kept alive while traced steps run; NULL stops
+ * tracing.  Every step enqueued afterwards writes, for the plan's work unit u
+ * (units in list order, linear by linear): trace[4u] the chip's 100 MHz
+ * real-time clock when a workgroup starts the unit, trace[4u + 1] when its
+ * input is staged, trace[4u + 2] when the whole workgroup has finished it,
+ * and trace[4u + 3] = linear index | (workgroup << 32).  Tracing adds one
+ * workgroup barrier per unit; outputs are unchanged.  Errors: WSG_ERR_STATE
+ * for a NULL or destroyed plan, WSG_ERR_UNSUPPORTED for other modes,
+ * WSG_ERR_ALIGN, WSG_ERR_SHAPE when capacity (in words) < 4 * units.
+ */
+wsg_status wsg_decode_step_trace(wsg_step *step, uint64_t *trace, int64_t capacity);
+
+/*
  * Test hooks for plan creation on a machine without a GPU.  They only work
  * when the environment variable WSG_ENABLE_TEST_HOOKS is "1" (otherwise
  * WSG_ERR_UNSUPPORTED).  wsg_test_set_fault(mode): mode >= 0 makes

@@ -226,3 +226,44 @@ def test_give_up_path_ends_and_is_counted():
         assert_bits_equal(host(y16s[i]), want[i][1], f"stage {i} after the forced give-ups")
     assert step.give_ups() == 0
     step.close()
+
+
+def test_trace_records_every_unit_and_leaves_outputs_alone():
+    """A traced step (wsg_decode_step_trace) writes, for every work unit in
+    list order, start <= input staged <= finished on one clock, its linear
+    (non-decreasing along the list, every linear present) and a workgroup
+    inside the grid; its outputs equal the untraced step's bit for bit, and
+    with tracing stopped the buffer is no longer written."""
+    say("persistent trace")
+    K = 1024
+    r = synth.rng(185, 0)
+    Ws = [_signed_perm(r, K) for _ in range(5)] + [synth.f16_normal(185, 1, (3000, K), 1.0 / np.sqrt(K))]
+    x0 = r.integers(-64, 65, K).astype(np.float16)
+    lins, ys, y16s = _chain(Ws, x0)
+    step = wsgemv.DecodeStep(lins, wsgemv.STEP_PERSISTENT)
+    step()
+    plain = [host(y).copy() for y in ys]
+    units = step.info()[1]
+    with pytest.raises(wsgemv.WsgError):
+        step.set_trace(torch.zeros(4 * units - 1, dtype=torch.int64, device="cuda"))   # too small
+    buf = torch.zeros(4 * units, dtype=torch.int64, device="cuda")
+    step.set_trace(buf)
+    step()
+    traced = [host(y).copy() for y in ys]
+    for i in range(len(ys)):
+        assert_bits_equal(traced[i], plain[i], f"stage {i}: traced step")
+    t = host(buf).reshape(units, 4)
+    lin = t[:, 3] & 0xFFFFFFFF
+    wg = t[:, 3] >> 32
+    assert np.all(t[:, 0] > 0) and np.all(t[:, 0] <= t[:, 1]) and np.all(t[:, 1] <= t[:, 2])
+    assert np.all(np.diff(lin) >= 0) and set(lin.tolist()) == set(range(len(Ws)))
+    assert np.all(wg >= 0) and np.all(wg < units)
+    span_us = (t[:, 2].max() - t[:, 0].min()) * 0.01                      # 100 MHz clock
+    assert 0.5 < span_us < 1e5, span_us
+    step.set_trace(None)
+    buf.zero_()
+    step()
+    torch.cuda.synchronize()
+    assert int(buf.abs().sum().item()) == 0
+    assert step.give_ups() == 0
+    step.close()

@@ -91,6 +91,7 @@ def test_host_plan_then_destroyed_handle(L, name, make, mode):
     assert L.wsg_decode_step_info(h, ctypes.byref(n), None, None) == STATE
     gu = ctypes.c_uint32()
     assert L.wsg_decode_step_status(h, None, ctypes.byref(gu)) == STATE
+    assert L.wsg_decode_step_trace(h, None, 0) == STATE
     assert L.wsg_decode_step_destroy(h) == STATE
     assert L.wsg_decode_step_destroy(ctypes.c_void_p(FAKE)) == STATE   # never a plan
 
@@ -110,3 +111,27 @@ def test_injected_failure_frees_everything(L, name, make, mode, fault, want):
         assert got == want, (name, fault, got)
         assert not h.value                                  # no plan handed back
     assert L.wsg_test_live_blocks() == 0                    # and nothing left allocated
+
+
+def test_trace_arguments(L):
+    """wsg_decode_step_trace: persistent plans only; the buffer must be
+    8-byte aligned and hold 4 words per work unit; NULL stops tracing."""
+    assert L.wsg_test_set_fault(NONE) == OK
+    h = ctypes.c_void_p()
+    arr = _chain(4)
+    assert L.wsg_decode_step_create(arr, len(arr), 2, None, ctypes.byref(h)) == OK
+    u = ctypes.c_int64()
+    assert L.wsg_decode_step_info(h, None, ctypes.byref(u), None) == OK
+    n = 4 * u.value
+    assert L.wsg_decode_step_trace(h, ctypes.c_void_p(FAKE + 4), n) == ALIGN
+    assert L.wsg_decode_step_trace(h, ctypes.c_void_p(FAKE), n - 1) == SHAPE
+    assert L.wsg_decode_step_trace(h, ctypes.c_void_p(FAKE), n) == OK
+    assert L.wsg_decode_step_trace(h, None, 0) == OK
+    assert L.wsg_decode_step_destroy(h) == OK
+    g = ctypes.c_void_p()
+    arr = _lins(3)
+    assert L.wsg_decode_step_create(arr, len(arr), 1, None, ctypes.byref(g)) == OK
+    assert L.wsg_decode_step_trace(g, ctypes.c_void_p(FAKE), 1 << 20) == UNSUP
+    assert L.wsg_decode_step_destroy(g) == OK
+    assert L.wsg_decode_step_trace(None, None, 0) == STATE
+    assert L.wsg_test_live_blocks() == 0

@@ -135,3 +135,23 @@ def test_source_hash_ignores_comments(tmp_path, monkeypatch):
     assert profsum.source_sha256(str(tmp_path)) == h0
     src.write_text("int f(int x) { return x + 2; }\n")
     assert profsum.source_sha256(str(tmp_path)) != h0
+
+
+def test_chain_trace_stats_parts_of_a_stage():
+    """Three linears of two units each, timestamps in 100 MHz ticks: every
+    part of a stage follows from the per-unit records by hand."""
+    w = []
+    for t0, t1, t2, lin, wg in ((0, 100, 150, 0, 0), (0, 120, 160, 0, 1), (10, 300, 330, 1, 0),
+                                (10, 350, 400, 1, 1), (20, 500, 600, 2, 0), (20, 520, 700, 2, 1)):
+        w += [t0, t1, t2, lin | (wg << 32)]
+    s = profsum.chain_trace_stats(w)
+    assert s["units"] == 6 and s["linears"] == 3 and abs(s["span_us"] - 7.0) < 1e-9
+    l1 = s["per_linear"][1]
+    # linear 0 ends at 1.6 us; linear 1's inputs arrive at 3.0 and 3.5, it ends at 4.0
+    assert abs(l1["detect_us"] - 1.4) < 1e-9 and abs(l1["spread_us"] - 0.5) < 1e-9
+    assert abs(l1["tail_us"] - 0.5) < 1e-9 and abs(l1["stage_us"] - 2.4) < 1e-9
+    assert abs(l1["compute_median_us"] - 0.4) < 1e-9
+    # only the middle linear is a layer stage here
+    assert abs(s["median_stage"]["stage_us"] - 2.4) < 1e-9
+    md = profsum.render_chain_trace(s, ["a", "b", "c"], "cmd", 7.0, 7.1)
+    assert "| 1 | b | 2 |" in md and "cmd" in md

@@ -1004,6 +1004,7 @@ struct wsg_step {
     int chain_lds = 0;
     bool chain_tail = false;
     uint32_t chain_epoch = 0;
+    uint64_t *chain_trace = nullptr;  // caller's per-unit timestamp buffer, or nullptr
 };
 
 namespace {
@@ -1868,6 +1869,7 @@ hipError_t run_chain(wsg_step *st, hipStream_t s) {
     // polling again at once measured fastest on the C3 chain (sleeps of 2, 8
     // and 16 between polls cost 1, 3 and 7 %)
     a.sleep = g_tune.chain_sleep >= 0 ? (int)std::min<int64_t>(g_tune.chain_sleep, 64) : 0;
+    a.trace = st->chain_trace;
     return launch_chain(a, st->chain_grid, st->chain_lds, st->chain_tail, s);
 }
 
@@ -1955,6 +1957,25 @@ wsg_status wsg_decode_step_status(wsg_step *step, wsg_stream_t stream, uint32_t 
         if (e != hipSuccess)
             return hip_fail(e);
         *give_ups = v;
+        return WSG_OK;
+    });
+}
+
+wsg_status wsg_decode_step_trace(wsg_step *step, uint64_t *trace, int64_t capacity) {
+    return guarded([&]() -> wsg_status {
+        if (!plan_live(step))
+            return WSG_ERR_STATE;
+        if (!step->chain)
+            return WSG_ERR_UNSUPPORTED;
+        if (trace == nullptr) {
+            step->chain_trace = nullptr;
+            return WSG_OK;
+        }
+        if (!aligned(trace, 8))
+            return WSG_ERR_ALIGN;
+        if (capacity < 4 * step->units)
+            return WSG_ERR_SHAPE;
+        step->chain_trace = trace;
         return WSG_OK;
     });
 }

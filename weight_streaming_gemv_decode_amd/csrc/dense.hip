@@ -744,8 +744,10 @@ __device__ __forceinline__ void chain_stage(const ChainLin &L, const ChainArgs &
     }
 }
 
+// tr: the unit's trace record (four 64-bit words), or nullptr.
 template <int R, int CH, bool TAIL>
-__device__ __forceinline__ void chain_unit(const ChainLin &L, int tile, const ChainArgs &a, u32x4 *xs) {
+__device__ __forceinline__ void chain_unit(const ChainLin &L, int tile, const ChainArgs &a, u32x4 *xs,
+                                           uint64_t *tr) {
     using Ops = DenseOps<kF16>;
     constexpr int CHUNK = kWave * CH;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -830,6 +832,8 @@ __device__ __forceinline__ void chain_unit(const ChainLin &L, int tile, const Ch
     if (nsteps > 1)
         load_step(bufB, gb, cb);
     chain_stage(L, a, nv, nchunk * CHUNK, xs);
+    if (tr != nullptr && threadIdx.x == 0)
+        *glob(tr + 1) = __builtin_amdgcn_s_memrealtime();
     // a buffer is refilled with the step after next once it is consumed
     for (int st = 0; st < nsteps; st += 2) {
         consume(bufA, ga, ca);
@@ -849,14 +853,30 @@ __device__ __forceinline__ void chain_unit(const ChainLin &L, int tile, const Ch
     }
 }
 
-template <int R, int CH, bool TAIL>
+// TRACE (a kernel of its own, so that the untraced kernel carries none of
+// it): thread 0 records for unit u in a.trace, from the chip's 100 MHz
+// real-time clock (one time base for every compute unit), when the workgroup
+// starts the unit, when its input is staged, and when the whole workgroup
+// has finished it (after a barrier that only tracing adds), then the unit's
+// linear and workgroup.
+template <int R, int CH, bool TAIL, bool TRACE>
 __global__ __launch_bounds__(kBlock) void chain_kernel(ChainArgs a) {
     extern __shared__ u32x4 xs_dyn[];
     int k = 0;
     for (int u = blockIdx.x; u < a.n_units; u += gridDim.x, ++k) {
         const Unit un = a.units[u];
         const ChainLin L = a.lins[un.lin];
-        chain_unit<R, CH, TAIL>(L, un.tile, a, xs_dyn + (k & 1) * a.xs_vecs);
+        uint64_t *tr = TRACE ? a.trace + 4 * (int64_t)u : nullptr;
+        if (TRACE && threadIdx.x == 0)
+            *glob(tr) = __builtin_amdgcn_s_memrealtime();
+        chain_unit<R, CH, TAIL>(L, un.tile, a, xs_dyn + (k & 1) * a.xs_vecs, tr);
+        if constexpr (TRACE) {
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                *glob(tr + 2) = __builtin_amdgcn_s_memrealtime();
+                *glob(tr + 3) = (uint64_t)(uint32_t)un.lin | (uint64_t)blockIdx.x << 32;
+            }
+        }
     }
 }
 
@@ -1077,18 +1097,33 @@ hipError_t launch_dense_grouped(int kind, const DenseLin *lins, const Unit *unit
     return hipErrorInvalidValue;
 }
 
+static const void *chain_fn(bool tail, bool trace) {
+    if (trace)
+        return tail ? reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, true, true>)
+                    : reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, false, true>);
+    return tail ? reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, true, false>)
+                : reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, false, false>);
+}
+
 hipError_t launch_chain(const ChainArgs &a, int grid, int lds_bytes, bool tail, hipStream_t s) {
     ChainArgs args = a;
     void *kargs[] = {&args};
-    const void *f = tail ? reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, true>)
-                         : reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, false>);
-    return hipLaunchCooperativeKernel(f, dim3(grid), dim3(kBlock), kargs, (unsigned)lds_bytes, s);
+    return hipLaunchCooperativeKernel(chain_fn(tail, a.trace != nullptr), dim3(grid), dim3(kBlock), kargs,
+                                      (unsigned)lds_bytes, s);
 }
 
+// The smaller of the plain and the traced kernel's occupancy, so that one
+// grid fits either.
 hipError_t chain_blocks_per_cu(int lds_bytes, bool tail, int *blocks) {
-    const void *f = tail ? reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, true>)
-                         : reinterpret_cast<const void *>(&chain_kernel<kChainR, kChainCH, false>);
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, f, kBlock, (size_t)lds_bytes);
+    int b[2] = {0, 0};
+    for (int t = 0; t < 2; ++t) {
+        const hipError_t e =
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&b[t], chain_fn(tail, t == 1), kBlock, (size_t)lds_bytes);
+        if (e != hipSuccess)
+            return e;
+    }
+    *blocks = std::min(b[0], b[1]);
+    return hipSuccess;
 }
 
 int dense_reduce_blocks(int64_t N) { return (int)((N + kBlock - 1) / kBlock); }

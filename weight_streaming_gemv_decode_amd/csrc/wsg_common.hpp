@@ -236,6 +236,7 @@ struct ChainArgs {
     uint32_t want;           // inputs are current with this tag (== tag; tests may differ)
     uint32_t spin_limit;     // polls before a wait gives up
     int32_t sleep;           // s_sleep(1) calls between polls (0: poll again at once)
+    uint64_t *trace;         // per-unit timestamps [4 * n_units], or nullptr
 };
 
 struct DenseCfg {

@@ -291,6 +291,94 @@ def render(recs: List[dict], cal: dict, commands: List[str], notes: List[str] = 
     return "\n".join(lines) + "\n"
 
 
+# ---------------------------------------------------------- chain trace --
+#
+# A persistent step traced with wsg_decode_step_trace leaves four 64-bit words
+# per work unit: start, input staged, finished (the 100 MHz real-time clock,
+# one time base for the whole chip) and linear | workgroup << 32.  Per linear
+# j of the dependent chain: when its first and last units had their input,
+# when its last unit finished, and from these the parts of a stage.
+
+CHAIN_TICK_US = 0.01  # the real-time clock counts at 100 MHz
+
+
+def chain_trace_stats(words: List[int], tick_us: float = CHAIN_TICK_US) -> dict:
+    """words: the trace buffer, 4 words per unit in unit order."""
+    import statistics as st
+    n = len(words) // 4
+    if n == 0:
+        raise ValueError("empty trace")
+    rec = [words[4 * u:4 * u + 4] for u in range(n)]
+    base = min(r[0] for r in rec)
+    per: Dict[int, dict] = collections.OrderedDict()
+    for r in rec:
+        t0, t1, t2 = ((r[k] - base) * tick_us for k in range(3))
+        lin = r[3] & 0xFFFFFFFF
+        d = per.setdefault(lin, {"units": 0, "start": t0, "inputs": [], "end": t2, "compute": []})
+        d["units"] += 1
+        d["start"] = min(d["start"], t0)
+        d["end"] = max(d["end"], t2)
+        d["inputs"].append(t1)
+        d["compute"].append(t2 - t1)
+    lins = []
+    prev_end = 0.0
+    for j, d in per.items():
+        ins = sorted(d["inputs"])
+        row = {"linear": j, "units": d["units"], "start_us": d["start"], "input_first_us": ins[0],
+               "input_median_us": st.median(ins), "input_last_us": ins[-1], "end_us": d["end"],
+               "compute_median_us": st.median(d["compute"])}
+        row["detect_us"] = ins[0] - prev_end      # last producer done -> first consumer has its input
+        row["spread_us"] = ins[-1] - ins[0]       # first -> last consumer
+        row["tail_us"] = d["end"] - ins[-1]       # last input -> linear done
+        row["stage_us"] = d["end"] - prev_end
+        prev_end = d["end"]
+        lins.append(row)
+    # the layer stages: every linear but the first (its input is ready at
+    # launch) and the last (the head, bandwidth-bound over many units)
+    mid = lins[1:-1] if len(lins) > 2 else lins
+    med = {k: st.median(r[k] for r in mid) for k in ("stage_us", "detect_us", "spread_us", "compute_median_us",
+                                                     "tail_us")}
+    waits = sorted((r[1] - r[0]) * tick_us for r in rec)
+    return {"units": n, "linears": len(lins), "span_us": max(r["end_us"] for r in lins), "per_linear": lins,
+            "median_stage": med, "unit_wait_median_us": st.median(waits),
+            "unit_wait_p90_us": waits[int(0.9 * (len(waits) - 1))]}
+
+
+def render_chain_trace(stats: dict, names: List[str], command: str, step_us: float, traced_us: float,
+                       notes: List[str] = ()) -> str:
+    """Markdown summary of chain_trace_stats (names: one per linear, in order)."""
+    m = stats["median_stage"]
+    out = ["# Persistent dependent step: where a stage's time goes", "",
+           "Command (repository root as `$REPO`, one MI355X):", "", "```", command, "```", "",
+           f"One traced step of the dependent chain: {stats['units']:,} work units over {stats['linears']} "
+           f"linears. The step took {traced_us:.1f} us traced (HIP events) against {step_us:.1f} us untraced; "
+           f"the trace spans {stats['span_us']:.1f} us of the chip's 100 MHz real-time clock (a check on that "
+           "rate). Tracing adds one workgroup barrier per unit.", "",
+           "Per linear: `in first/median/last` is when its units had their input staged; `detect` is from the "
+           "previous linear's last finished unit to this linear's first staged input, `spread` from its first "
+           "to its last staged input, `tail` from its last input to its last finished unit, `compute` the "
+           "median time of a unit after its input (us).", "",
+           "| # | Linear | Units | Start | In first | In median | In last | End | Detect | Spread | Compute | Tail |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    rows = stats["per_linear"]
+    show = list(range(min(8, len(rows)))) + list(range(max(8, len(rows) - 5), len(rows)))
+    for i in show:
+        r = rows[i]
+        nm = names[r["linear"]] if r["linear"] < len(names) else str(r["linear"])
+        out.append(f"| {r['linear']} | {nm} | {r['units']} | {r['start_us']:.1f} | {r['input_first_us']:.1f} | "
+                   f"{r['input_median_us']:.1f} | {r['input_last_us']:.1f} | {r['end_us']:.1f} | "
+                   f"{r['detect_us']:.2f} | {r['spread_us']:.2f} | {r['compute_median_us']:.2f} | "
+                   f"{r['tail_us']:.2f} |")
+    out += ["", f"Medians over the layer stages (every linear but the first and the head): a stage "
+                f"{m['stage_us']:.2f} us end to end; detect {m['detect_us']:.2f}, spread {m['spread_us']:.2f}, "
+                f"compute {m['compute_median_us']:.2f}, tail {m['tail_us']:.2f}. A unit waited "
+                f"{stats['unit_wait_median_us']:.2f} us (median; p90 {stats['unit_wait_p90_us']:.2f}) from its "
+                "start, weight loads issued, to its staged input."]
+    for n_ in notes:
+        out += ["", n_]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--fetch")

@@ -75,6 +75,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "wsg_decode_step_destroy": ([P], I32),
         "wsg_decode_step_info": ([P, ctypes.POINTER(I32), ctypes.POINTER(I64), ctypes.POINTER(I32)], I32),
         "wsg_decode_step_status": ([P, P, ctypes.POINTER(ctypes.c_uint32)], I32),
+        "wsg_decode_step_trace": ([P, P, I64], I32),
         "wsg_chain_grid": ([I64, I32, I32, I32], I64),
         "wsg_test_set_fault": ([I32], I32),
         "wsg_test_live_blocks": ([], I64),
@@ -482,6 +483,20 @@ class DecodeStep:
         g = ctypes.c_uint32()
         _check(lib().wsg_decode_step_status(self._h, _stream(stream), ctypes.byref(g)), "wsg_decode_step_status")
         return int(g.value)
+
+    def set_trace(self, buf: Optional[torch.Tensor]) -> None:
+        """Per-unit timestamps of a persistent plan into `buf` (int64 on the
+        device, at least 4 words per work unit) for every later step; None
+        stops tracing (wsg_decode_step_trace).  The buffer is kept referenced
+        while it is set."""
+        if buf is None:
+            _check(lib().wsg_decode_step_trace(self._h, None, 0), "wsg_decode_step_trace")
+            self._trace = None
+            return
+        if buf.dtype != torch.int64 or not buf.is_cuda or not buf.is_contiguous():
+            raise ValueError("trace buffer: a contiguous int64 tensor on the device")
+        _check(lib().wsg_decode_step_trace(self._h, buf.data_ptr(), buf.numel()), "wsg_decode_step_trace")
+        self._trace = buf
 
     def uses_graph(self) -> bool:
         g = ctypes.c_int32()
