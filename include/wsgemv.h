@@ -437,11 +437,19 @@ int32_t wsg_read_probe_grid(size_t bytes);
  * wave step: 4, 8),
  * "w4_tiles" / "group_w4_tiles" (tiles per work unit), "w4_mfma_m1" (1: W4A16
  * at M = 1 on the matrix-core kernel), "probe_U" (loads in flight per lane:
- * 4, 8, 16), "probe_chunked" (0/1).  value < 0 restores the
+ * 4, 8, 16), "probe_chunked" (0/1), "split_fuse" (0: split-K partials summed
+ * by a separate reduce kernel instead of the last workgroup of each row tile),
+ * and for WSG_STEP_PERSISTENT plans "chain_unit_kb" (weight KiB per work
+ * unit) and "chain_blocks_per_cu" (cap on resident workgroups per compute
+ * unit), read when a plan is created, and "chain_spin_limit" (polls before a
+ * wait gives up), "chain_sleep" (s_sleep(1) calls between polls) and
+ * "chain_test_stale" (1: consumers wait for a tag no producer writes, to
+ * exercise the give-up path), read at every launch.  value < 0 restores the
  * table's choice.  Process-wide, not thread-safe; plans capture the values
- * in force when they are created.  No result depends on these settings
- * beyond the summation order.  Unknown keys and kernel shapes that are not
- * built return WSG_ERR_UNSUPPORTED and leave the setting unchanged.
+ * in force when they are created, except the three read at launch.  No
+ * result depends on these settings beyond the summation order, except
+ * chain_test_stale.  Unknown keys and kernel shapes that are not built
+ * return WSG_ERR_UNSUPPORTED and leave the setting unchanged.
  */
 wsg_status wsg_tune_set(const char *key, int64_t value);
 
