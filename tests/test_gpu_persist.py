@@ -267,3 +267,52 @@ def test_trace_records_every_unit_and_leaves_outputs_alone():
     assert int(buf.abs().sum().item()) == 0
     assert step.give_ups() == 0
     step.close()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_chains(seed):
+    """Seeded random chains: 3..7 stages, each reading K values (any multiple
+    of 8 up to 4096) that start any multiple of 8 into the previous stage's
+    y16, N up to 6000; two replays with new first inputs; every stage against
+    the oracle on the input it actually read, y16 its own y rounded."""
+    r = synth.rng(186, seed)
+    depth = int(r.integers(3, 8))
+    Ks, offs, Ns = [8 * int(r.integers(1, 513))], [0], []
+    for i in range(depth):
+        if i + 1 < depth:
+            Kn = 8 * int(r.integers(1, 513))
+            o = 8 * int(r.integers(0, 65))
+            Ns.append(int(r.integers(o + Kn, max(o + Kn, 6000) + 1)))
+            Ks.append(Kn)
+            offs.append(o)
+        else:
+            Ns.append(int(r.integers(1, 6001)))
+    say(f"persistent random chain seed={seed}: N={Ns} K={Ks} offsets={offs}")
+    Ws = [synth.f16_normal(187, 16 * seed + i, (Ns[i], Ks[i]), 1.0 / np.sqrt(Ks[i])) for i in range(depth)]
+    x_in = torch.empty(Ks[0], dtype=torch.float16, device="cuda")
+    lins, ys, y16s = [], [], []
+    x = x_in
+    for i in range(depth):
+        y = torch.empty(Ns[i], device="cuda")
+        y16 = torch.empty(Ns[i], dtype=torch.float16, device="cuda")
+        lins.append(wsgemv.Linear(wsgemv.F16, dev(Ws[i]), x, y, Ns[i], Ks[i], y16=y16))
+        ys.append(y)
+        y16s.append(y16)
+        if i + 1 < depth:
+            x = y16[offs[i + 1]:offs[i + 1] + Ks[i + 1]]
+    step = wsgemv.DecodeStep(lins, wsgemv.STEP_PERSISTENT)
+    for rep in range(2):
+        x0 = synth.f16_normal(188, 2 * seed + rep, (Ks[0],), 1.0)
+        x_in.copy_(torch.from_numpy(x0))
+        step()
+        xin = x0
+        for i in range(depth):
+            y_ref, A = oracle.gemv_f16(Ws[i], xin)
+            y = host(ys[i])
+            assert_within(y, y_ref, A, f"seed {seed} replay {rep} stage {i}")
+            y16 = host(y16s[i])
+            assert_bits_equal(y16, y.astype(np.float16), f"seed {seed} replay {rep} stage {i} y16")
+            if i + 1 < depth:
+                xin = y16[offs[i + 1]:offs[i + 1] + Ks[i + 1]]
+    assert step.give_ups() == 0
+    step.close()
