@@ -158,13 +158,23 @@ def summary(ts):
 
 
 def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, with its family and
+    model numbers (a virtualised host may give only a short name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            k = k.strip()
+            if k in ("model name", "cpu family", "model") and k not in fields:
+                fields[k] = v.strip()
+            if line.strip() == "":
+                break
     except OSError:
         pass
-    return platform.processor() or platform.machine()
+    name = fields.get("model name") or platform.processor() or platform.machine()
+    if "cpu family" in fields and "model" in fields:
+        name += f" (family {fields['cpu family']}, model {fields['model']})"
+    return name
 
 
 def oracle_per_config(oracle, synth, step_in, cores):
